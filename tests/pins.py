@@ -1,0 +1,348 @@
+"""Pins of the CPU oracle to facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` takes an oracle object (``oracle.Oracle``) and raises
+AssertionError when the oracle disagrees with a fact that does not come from
+the oracle itself:
+
+* hand-derived values of small worked matrices (``tests/golden/*.json``,
+  each with its citation and derivation) and of the pages' own worked
+  example of 4-bit dequantization;
+* closed forms: a one-hot activation reads out one weight column; all-zero
+  codes leave only the bias term; all-one / all-zero sign bits give plus /
+  minus the scaled activation sums;
+* exact integer arithmetic: with power-of-two scales and integer activations
+  every result is exactly representable, and is computed here independently
+  in int64;
+* invariants: linearity in x, permutation of activation rows, duplicate rows;
+* a second opinion from numpy's own half-precision decoding and bit
+  unpacking on random tiny matrices, including the extreme codes;
+* brute-force argmax on tiny vectors with ties.
+
+The same pins run against planted-mistake builds of the oracle
+(``test_oracle_mutants.py``) to show that each plausible mistake fails one.
+"""
+from __future__ import annotations
+
+import glob
+import json
+import os
+
+import numpy as np
+
+I8, U4, B1 = 1, 2, 3
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------------------
+# fixture loading
+# ---------------------------------------------------------------------------
+
+def load_fixture(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        d = json.load(f)
+    M, K = d["M"], d["K"]
+    codes = np.frombuffer(bytes.fromhex(d["codes_hex"]), dtype=np.uint8).copy()
+    if d["fmt"] == I8:
+        codes = codes.view(np.int8).reshape(M, K)
+        scales = np.asarray(d["scales_f32"], np.float32)
+    else:
+        codes = codes.reshape(M, -1)
+        scales = np.asarray(d["scales_bits"], np.uint16).reshape(M, -1)
+    biases = None if d.get("biases_bits") is None else \
+        np.asarray(d["biases_bits"], np.uint16).reshape(M, -1)
+    return d, codes, scales, biases
+
+
+def hand_fixtures():
+    return sorted(os.path.basename(p) for p in glob.glob(os.path.join(GOLDEN, "hw*.json")))
+
+
+# ---------------------------------------------------------------------------
+# an independent numpy decode (numpy's float16 and unpackbits, not the
+# oracle's bit-by-bit decoders)
+# ---------------------------------------------------------------------------
+
+def numpy_weights(fmt, codes, scales, biases, M, K):
+    if fmt == I8:
+        return codes.astype(np.float64) * scales.astype(np.float64)[:, None]
+    if fmt == U4:
+        q = np.empty((M, K), np.float64)
+        q[:, 0::2] = codes & 0x0F
+        q[:, 1::2] = codes >> 4
+        s = (scales.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        b = (biases.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        return q * np.repeat(s, 64, axis=1) + np.repeat(b, 64, axis=1)
+    if fmt == B1:
+        bits = np.unpackbits(codes, axis=1, bitorder="little").astype(np.float64)
+        s = scales.view(np.float16).astype(np.float64)
+        return (2.0 * bits - 1.0) * np.repeat(s, 128, axis=1)
+    raise ValueError(fmt)
+
+
+def random_tiny(fmt, M, K, rng, extremes=True):
+    """Random codes over the whole code range (extremes forced in), random
+    scales and biases of both signs, as raw bit patterns."""
+    if fmt == I8:
+        codes = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+        if extremes:
+            codes.flat[0], codes.flat[-1] = -128, 127
+        scales = rng.uniform(-2, 2, size=M).astype(np.float32)
+        return codes, scales, None
+    if fmt == U4:
+        codes = rng.integers(0, 256, size=(M, K // 2)).astype(np.uint8)
+        if extremes:
+            codes.flat[0], codes.flat[-1] = 0x00, 0xFF
+        f = rng.uniform(-1, 1, size=(2, M, K // 64)).astype(np.float32)
+        bits = (f.view(np.uint32) >> 16).astype(np.uint16)   # truncation: any bf16
+        return codes, bits[0], bits[1]
+    if fmt == B1:
+        codes = rng.integers(0, 256, size=(M, K // 8)).astype(np.uint8)
+        if extremes:
+            codes.flat[0], codes.flat[-1] = 0x00, 0xFF
+        scales = rng.uniform(-1, 1, size=(M, K // 128)).astype(np.float16).view(np.uint16)
+        return codes, scales, None
+    raise ValueError(fmt)
+
+
+def _close(a, b, rel=1e-12, what=""):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    scale = np.maximum(np.abs(b), 1e-300)
+    assert np.all(np.abs(a - b) <= rel * scale + 1e-300), \
+        f"{what}: max diff {np.max(np.abs(a - b))}"
+
+
+# ---------------------------------------------------------------------------
+# pins
+# ---------------------------------------------------------------------------
+
+def pin_hand_fixtures(orc):
+    """Hand-worked matrices: exact y, Σ|w·x| and argmax."""
+    for name in hand_fixtures():
+        d, codes, scales, biases = load_fixture(name)
+        x = np.asarray(d["x"], np.float32)
+        y, a = orc.qgemv(d["fmt"], codes, scales, biases, x, d["M"], d["K"])
+        assert np.array_equal(y, np.asarray(d["y"])), f"{name}: y {y} != {d['y']}"
+        assert np.array_equal(a, np.asarray(d["absdot"])), f"{name}: absdot {a}"
+        idx, _ = orc.argmax(y)
+        assert list(idx[: len(d["idx"])]) == d["idx"][: len(idx)], f"{name}: idx {idx}"
+
+
+def pin_decode_values(orc):
+    """bf16 and fp16 bit patterns decode to their IEEE values."""
+    with open(os.path.join(GOLDEN, "decode_values.json")) as f:
+        d = json.load(f)
+    for bits, v in d["bf16"]:
+        got = orc.bf16_value(bits)
+        assert got == v and np.signbit(got) == np.signbit(v), f"bf16 {bits:#x}: {got} != {v}"
+    for bits, v in d["fp16"]:
+        got = orc.fp16_value(bits)
+        assert got == v and np.signbit(got) == np.signbit(v), f"fp16 {bits:#x}: {got} != {v}"
+
+
+def pin_worked_example(orc):
+    """The pages' worked 4-bit example: code 9 -> ~0.28, 0 -> min, 15 -> max."""
+    d, codes, scales, biases = load_fixture("p3_worked_example.json")
+    w = orc.decode(d["fmt"], codes, scales, biases, d["M"], d["K"])
+    for k, want, tol in d["expect"]:
+        assert abs(w[0, k] - want) <= tol, f"w[{k}] = {w[0, k]}, expected {want}±{tol}"
+
+
+def pin_one_hot(orc):
+    """x = e_j reads out column j: y[m] = w[m][j] for every (m, j), with
+    the weights built here from known codes by this test's own packing."""
+    rng = np.random.default_rng(11)
+    M = 5
+    # I8: w = s*q
+    K = 32
+    q = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+    s = (2.0 ** rng.integers(-6, 3, size=M)).astype(np.float32)
+    x = np.eye(K, dtype=np.float32)
+    y, _ = orc.qgemv(I8, q, s, None, x, M, K)
+    assert np.array_equal(y, (q.astype(np.float64) * s[:, None]).T), "i8 one-hot"
+    # U4: w = s*q + b with q packed low nibble = even k
+    K = 128
+    qu = rng.integers(0, 16, size=(M, K))
+    packed = (qu[:, 0::2] | (qu[:, 1::2] << 4)).astype(np.uint8)
+    sv = 2.0 ** rng.integers(-6, 2, size=(M, K // 64))
+    bv = rng.integers(-8, 8, size=(M, K // 64)) / 16.0
+    sb = ((sv.astype(np.float32).view(np.uint32)) >> 16).astype(np.uint16)
+    bb = ((bv.astype(np.float32).view(np.uint32)) >> 16).astype(np.uint16)
+    x = np.eye(K, dtype=np.float32)
+    y, _ = orc.qgemv(U4, packed, sb, bb, x, M, K)
+    want = qu * np.repeat(sv, 64, axis=1) + np.repeat(bv, 64, axis=1)
+    assert np.array_equal(y, want.T), "u4 one-hot"
+    # B1: w = ±s, bit k%8 of byte k/8
+    K = 256
+    bits = rng.integers(0, 2, size=(M, K))
+    packed = np.zeros((M, K // 8), np.uint8)
+    for k in range(K):
+        packed[:, k // 8] |= (bits[:, k] << (k % 8)).astype(np.uint8)
+    sv = 2.0 ** rng.integers(-6, 2, size=(M, K // 128))
+    sh = sv.astype(np.float16).view(np.uint16)
+    x = np.eye(K, dtype=np.float32)
+    y, _ = orc.qgemv(B1, packed, sh, None, x, M, K)
+    want = np.where(bits == 1, 1.0, -1.0) * np.repeat(sv, 128, axis=1)
+    assert np.array_equal(y, want.T), "b1 one-hot"
+
+
+def pin_zero_and_sign_codes(orc):
+    """Closed forms of constant codes: U4 zeros -> y = Σ_g b_g Σ_{k∈g} x;
+    I8 zeros -> 0; B1 all ones -> +Σ_g s_g Σ x_g, all zeros -> the negation."""
+    rng = np.random.default_rng(12)
+    M, K, N = 3, 192, 2
+    x = rng.standard_normal((N, K)).astype(np.float32)
+    xg64 = x.astype(np.float64).reshape(N, K // 64, 64).sum(-1)
+    b = rng.uniform(-1, 1, size=(M, K // 64)).astype(np.float32)
+    bb = (b.view(np.uint32) >> 16).astype(np.uint16)
+    bval = (bb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    sb = np.full((M, K // 64), 0x3F80, np.uint16)
+    y, _ = orc.qgemv(U4, np.zeros((M, K // 2), np.uint8), sb, bb, x, M, K)
+    _close(y, xg64 @ bval.T, 1e-13, "u4 zero codes")
+    y, _ = orc.qgemv(I8, np.zeros((M, K), np.int8), np.ones(M, np.float32), None, x, M, K)
+    assert np.all(y == 0), "i8 zero codes"
+    K = 256
+    x = rng.standard_normal((N, K)).astype(np.float32)
+    xg128 = x.astype(np.float64).reshape(N, K // 128, 128).sum(-1)
+    s = rng.uniform(0.01, 1, size=(M, K // 128)).astype(np.float16)
+    ones, _ = orc.qgemv(B1, np.full((M, K // 8), 0xFF, np.uint8), s.view(np.uint16), None, x, M, K)
+    zeros, _ = orc.qgemv(B1, np.zeros((M, K // 8), np.uint8), s.view(np.uint16), None, x, M, K)
+    want = xg128 @ s.astype(np.float64).T
+    _close(ones, want, 1e-13, "b1 all ones")
+    _close(zeros, -want, 1e-13, "b1 all zeros")
+
+
+def pin_exact_integer_arithmetic(orc):
+    """Power-of-two scales, biases on a 2^-8 grid and integer x in [-8, 8]:
+    the result is an exact dyadic rational, computed here in int64."""
+    rng = np.random.default_rng(13)
+    M, K, N = 7, 384, 3
+    x = rng.integers(-8, 9, size=(N, K))
+    xf = x.astype(np.float32)
+    # I8
+    q = rng.integers(-128, 128, size=(M, K))
+    e = rng.integers(4, 8, size=M)                      # scale 2^-e
+    y, _ = orc.qgemv(I8, q.astype(np.int8), (2.0 ** -e).astype(np.float32), None, xf, M, K)
+    num = x @ q.T                                        # int64
+    assert np.array_equal(y * (2.0 ** e)[None, :], num.astype(np.float64)), "i8 exact"
+    # U4: y * 2^8 * 2^7 = Σ_g (q·x)_g * 2^(15-e) + (b*2^8)_g * Σx_g * 2^7
+    qu = rng.integers(0, 16, size=(M, K))
+    packed = (qu[:, 0::2] | (qu[:, 1::2] << 4)).astype(np.uint8)
+    G = K // 64
+    e = rng.integers(4, 8, size=(M, G))
+    bn = rng.integers(-64, 65, size=(M, G))              # bias = bn / 256
+    sb = ((2.0 ** -e).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    bb = ((bn / 256.0).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y, _ = orc.qgemv(U4, packed, sb, bb, xf, M, K)
+    want = np.zeros((N, M), np.int64)
+    for g in range(G):
+        sl = slice(64 * g, 64 * g + 64)
+        qx = x[:, sl] @ qu[:, sl].T
+        want += qx * (2 ** (15 - e[:, g]))[None, :] + (x[:, sl].sum(1)[:, None] * bn[:, g][None, :]) * 2 ** 7
+    assert np.array_equal(y * 2.0 ** 15, want.astype(np.float64)), "u4 exact"
+    # B1: y * 2^7 = Σ_g s_g*2^7 * Σ ±x
+    bits = rng.integers(0, 2, size=(M, K))
+    packed = np.zeros((M, K // 8), np.uint8)
+    for k in range(K):
+        packed[:, k // 8] |= (bits[:, k] << (k % 8)).astype(np.uint8)
+    G = K // 128
+    e = rng.integers(0, 8, size=(M, G))
+    sh = (2.0 ** -e).astype(np.float16).view(np.uint16)
+    y, _ = orc.qgemv(B1, packed, sh, None, xf, M, K)
+    sgn = 2 * bits - 1
+    want = np.zeros((N, M), np.int64)
+    for g in range(G):
+        sl = slice(128 * g, 128 * g + 128)
+        want += (x[:, sl] @ sgn[:, sl].T) * (2 ** (7 - e[:, g]))[None, :]
+    assert np.array_equal(y * 2.0 ** 7, want.astype(np.float64)), "b1 exact"
+
+
+def pin_numpy_second_opinion(orc):
+    """Random tiny matrices over the full code range, all three formats,
+    K <= 256, against numpy's float16 / bit unpacking and a float64 matmul."""
+    rng = np.random.default_rng(14)
+    for fmt, K in ((I8, 48), (I8, 256), (U4, 64), (U4, 256), (B1, 128), (B1, 256)):
+        for M in (1, 3, 17):
+            codes, scales, biases = random_tiny(fmt, M, K, rng)
+            x = rng.standard_normal((4, K)).astype(np.float32)
+            y, a = orc.qgemv(fmt, codes, scales, biases, x, M, K)
+            w = numpy_weights(fmt, codes, scales, biases, M, K)
+            ref = x.astype(np.float64) @ w.T
+            refa = np.abs(x.astype(np.float64)) @ np.abs(w).T
+            tol = 1e-12 * refa + 1e-300
+            assert np.all(np.abs(y - ref) <= tol), f"fmt {fmt} K {K} M {M}: y"
+            assert np.all(np.abs(a - refa) <= tol), f"fmt {fmt} K {K} M {M}: absdot"
+            wd = orc.decode(fmt, codes, scales, biases, M, K)
+            assert np.array_equal(wd, w), f"fmt {fmt} K {K} M {M}: decode"
+
+
+def pin_invariants(orc):
+    """Linearity in x, permuted activation rows, duplicate weight rows, and
+    the prefill product row n equal to the matvec of x[n]."""
+    rng = np.random.default_rng(15)
+    for fmt, K in ((I8, 64), (U4, 128), (B1, 256)):
+        M = 9
+        codes, scales, biases = random_tiny(fmt, M, K, rng)
+        # activations on a 1/8 grid, so that 2*x1 - x2 is exact in float32
+        x1 = (rng.integers(-64, 64, size=(3, K)) / 8.0).astype(np.float32)
+        x2 = (rng.integers(-64, 64, size=(3, K)) / 8.0).astype(np.float32)
+        y1, a1 = orc.qgemv(fmt, codes, scales, biases, x1, M, K)
+        y2, a2 = orc.qgemv(fmt, codes, scales, biases, x2, M, K)
+        # linearity with exactly representable combinations
+        y3, _ = orc.qgemv(fmt, codes, scales, biases, 2 * x1 - x2, M, K)
+        bound = 1e-12 * (2 * a1 + a2)
+        assert np.all(np.abs(y3 - (2 * y1 - y2)) <= bound), f"fmt {fmt}: linearity"
+        # permuting activation rows permutes outputs
+        p = np.array([2, 0, 1])
+        yp, _ = orc.qgemv(fmt, codes, scales, biases, x1[p], M, K)
+        assert np.array_equal(yp, y1[p]), f"fmt {fmt}: row permutation"
+        # each activation row alone gives the same row of the product
+        for n in range(3):
+            yn, _ = orc.qgemv(fmt, codes, scales, biases, x1[n:n + 1], M, K)
+            assert np.array_equal(yn[0], y1[n]), f"fmt {fmt}: row {n} alone"
+        # duplicate weight rows give identical outputs
+        c2 = codes.copy()
+        s2 = scales.copy()
+        b2 = None if biases is None else biases.copy()
+        c2[4] = c2[1]
+        s2[4] = s2[1]
+        if b2 is not None:
+            b2[4] = b2[1]
+        yd, _ = orc.qgemv(fmt, c2, s2, b2, x1, M, K)
+        assert np.array_equal(yd[:, 4], yd[:, 1]), f"fmt {fmt}: duplicate rows"
+        # zero activations give zero outputs
+        yz, _ = orc.qgemv(fmt, codes, scales, biases, np.zeros((1, K), np.float32), M, K)
+        assert np.all(yz == 0), f"fmt {fmt}: x = 0"
+
+
+def pin_argmax_brute_force(orc):
+    """Lowest index of the maximum, checked by brute force over all pairs;
+    ties at the ends, all-equal rows, and -0 against +0."""
+    rng = np.random.default_rng(16)
+    rows = [
+        np.array([1.0, 3.0, 3.0, 2.0]),
+        np.array([5.0, 1.0, 5.0]),
+        np.array([0.0, 0.0, 0.0]),
+        np.array([-0.0, 0.0]),
+        np.array([-1.0, -0.0, 0.0, -0.0]),
+        np.array([-3.0, -2.0, -2.0]),
+        np.array([1.0, 2.0, 7.0]),
+    ]
+    for _ in range(50):
+        rows.append(rng.integers(-3, 4, size=rng.integers(1, 12)).astype(np.float64))
+    for r in rows:
+        idx, gap = orc.argmax(r[None, :])
+        want = min(i for i in range(len(r)) if all(r[i] >= r[j] for j in range(len(r))))
+        assert idx[0] == want, f"argmax {r}: {idx[0]} != {want}"
+        others = [r[j] for j in range(len(r)) if j != want]
+        if others:
+            assert gap[0] == r[want] - max(others), f"gap {r}"
+    # several rows at once
+    y = np.array([[0.0, 2.0, 1.0], [4.0, 4.0, -1.0]])
+    idx, _ = orc.argmax(y)
+    assert list(idx) == [1, 0]
+
+
+PINS = [pin_hand_fixtures, pin_decode_values, pin_worked_example, pin_one_hot,
+        pin_zero_and_sign_codes, pin_exact_integer_arithmetic,
+        pin_numpy_second_opinion, pin_invariants, pin_argmax_brute_force]

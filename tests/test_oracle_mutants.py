@@ -1,0 +1,65 @@
+"""Planted mistakes in a copy of the oracle (on the CPU): every plausible
+mistake listed here must make at least one pin fail. This shows the pins
+would catch that mistake in the oracle itself."""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "qg_oracle.c")
+
+# (name, exact text in qg_oracle.c, replacement)
+MUTANTS = [
+    ("u4_nibbles_swapped", "(k % 2 == 0) ? (byte & 0x0f) : (byte >> 4)",
+     "(k % 2 == 1) ? (byte & 0x0f) : (byte >> 4)"),
+    ("b1_msb_first", "(byte >> (k % 8)) & 1", "(byte >> (7 - k % 8)) & 1"),
+    ("b1_sign_flipped", "return bit ? sc : -sc;", "return bit ? -sc : sc;"),
+    ("u4_bias_dropped", "* (double)q + oracle_bf16_value(b[g])", "* (double)q"),
+    ("u4_one_scale_per_row", "int64_t g = m * (K / 64) + k / 64;", "int64_t g = m * (K / 64);"),
+    ("u4_scales_transposed", "int64_t g = m * (K / 64) + k / 64;",
+     "int64_t g = (k / 64) * A->M + m;"),
+    ("i8_read_unsigned", "const int8_t *q = (const int8_t *)A->codes;",
+     "const uint8_t *q = (const uint8_t *)A->codes;"),
+    ("i8_scale_dropped", "return (double)s[m] * (double)q[m * K + k];",
+     "(void)s; return (double)q[m * K + k];"),
+    ("fp16_subnormal_as_normal", "v = ldexp((double)f, -24);", "v = ldexp((double)(1024 + f), -25);"),
+    ("fp16_exponent_bias", "v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
+    ("bf16_shift", "uint32_t u = (uint32_t)bits << 16;", "uint32_t u = (uint32_t)bits << 15;"),
+    ("x_first_row_only", "(double)x[n * A->K + k]", "(double)x[k]"),
+    ("absdot_signed", "mag += fabs(p);", "mag += p;"),
+    ("argmax_ties_highest", "if (row[m] > row[best])", "if (row[m] >= row[best])"),
+    ("b1_group_scale_per_row", "oracle_fp16_value(s[m * (K / 128) + k / 128])",
+     "oracle_fp16_value(s[m * (K / 128)])"),
+]
+
+
+@pytest.fixture(scope="module")
+def workdir():
+    d = tempfile.mkdtemp(prefix="oracle_mutants_")
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(workdir, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation site for {name} not found exactly once"
+    src = os.path.join(workdir, f"{name}.c")
+    lib = os.path.join(workdir, f"lib{name}.so")
+    with open(src, "w") as f:
+        f.write(text.replace(old, new))
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", src, "-o", lib, "-lm"],
+                   check=True)
+    mutant = oracle.Oracle(lib)
+    failed = []
+    for pin in pins.PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {name}"
