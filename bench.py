@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized matvec hot path on one MI355X.
+
+Default workload: 4-bit group-64 affine matrix-vector product at batch 1 on
+the 2B-model shapes 6144x2048 and 2048x6144 (one step = one call on each
+shape). Weights are cache-cold: every step reads a different copy, from a
+rotation of distinct copies that together exceed 512 MiB, so each read comes
+from HBM rather than from the L2 or the 256 MB Infinity Cache.
+
+Reported (one JSON line):
+  value          effective weight GB/s = weight bytes read per step / step time
+  roofline       the dominant kernel's algorithmic bytes per launch over its
+                 average launch duration (HIP events on its own stream), vs
+                 the 8 TB/s HBM peak; `traffic` from rocprofv3 counters when a
+                 profile of the current kernel source is committed
+  cpu_baseline   the CPU oracle on the same workload, on this host's cores
+
+Other workloads (--workload): any case name of gemm_qgemv_amd.synth.CASES, or
+a config prefix (c0, c1, c2b1, c2b8, c3, c4gemv, c4gemm). GEMM workloads report
+TFLOP/s.
+
+The timed region replays a HIP graph of the steps (captured once) so that the
+host's launch cost does not pace the GPU; inputs are resident in HBM before
+timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP32_MATRIX_PEAK_TFLOPS = 157.3
+BF16_MATRIX_PEAK_TFLOPS = 2500.0
+# bytes of weights per decoded token implied by the pages' measurements
+# (effective GB/s divided by tok/s): 8-bit 0.8B backbone, 4-bit 2B model,
+# 1-bit 27B model
+BYTES_PER_TOKEN = {1: 0.99e9, 2: 1.10e9, 3: 3.9e9}
+
+WORKLOADS = {
+    "c0": ["c0_i8_gemv_1024x1024"],
+    "c1": ["c1a_u4_gemv_6144x2048", "c1b_u4_gemv_2048x6144"],
+    "c2b1": ["c2_u4_head_151936x2048_b1"],
+    "c2b8": ["c2_u4_head_151936x2048_b8"],
+    "c3": ["c3a_i8_gemm_3584x1024_n2048", "c3b_i8_gemm_1024x3584_n2048",
+           "c3c_i8_gemm_3584x1024_n10240", "c3d_i8_gemm_1024x3584_n10240"],
+    "c4gemv": ["c4a_b1_gemv_17408x5120", "c4b_b1_gemv_5120x17408"],
+    "c4gemm": ["c4c_b1_gemm_17408x5120_n512", "c4d_b1_gemm_5120x17408_n512"],
+}
+METRIC = "effective weight GB/s and % of HBM peak, batch-1 qgemv; prefill qgemm TFLOP/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "gemm_qgemv_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Launch:
+    """One case on the device: rotated weight copies, x, y, workspace, and a
+    launcher that calls the C ABI with pre-resolved pointers."""
+
+    def __init__(self, case, rotate_bytes, torch, q, synth, tensors):
+        self.case = case
+        w, x = synth.case_inputs(case)
+        base = tensors.to_device(w)
+        self.copies = max(1, math.ceil(rotate_bytes / w.nbytes)) if case.op != "gemm" else 1
+        self.weights = [base] + [
+            tensors.DeviceWeights(base.fmt, base.M, base.K, base.codes.clone(), base.scales.clone(),
+                                  None if base.biases is None else base.biases.clone())
+            for _ in range(self.copies - 1)]
+        self.x = torch.from_numpy(x).cuda()
+        self.y = torch.empty(case.rows * case.M, dtype=torch.float32, device="cuda")
+        op = {"gemv": q.QG_OP_GEMV, "gemv_argmax": q.QG_OP_GEMV_ARGMAX, "gemm": q.QG_OP_GEMM}[case.op]
+        self.ws = tensors.workspace(op, case.fmt, case.M, case.K, case.rows)
+        self.ws_bytes = 0 if self.ws is None else self.ws.numel()
+        self.idx = torch.empty(case.rows, dtype=torch.int32, device="cuda")
+        self.lib = q._binding.lib()
+        self.ptrs = [(wd.codes.data_ptr(), wd.scales.data_ptr(),
+                      None if wd.biases is None else wd.biases.data_ptr()) for wd in self.weights]
+        self.host_w, self.host_x = w, x
+
+    def __call__(self, i, stream):
+        c, s, b = self.ptrs[i % self.copies]
+        L, case = self.lib, self.case
+        ws = None if self.ws is None else self.ws.data_ptr()
+        if case.op == "gemv":
+            st = L.qgemv(case.fmt, c, s, b, self.x.data_ptr(), self.y.data_ptr(), case.M, case.K,
+                         case.rows, ws, self.ws_bytes, stream)
+        elif case.op == "gemv_argmax":
+            st = L.qgemv_argmax(case.fmt, c, s, b, self.x.data_ptr(), self.y.data_ptr(),
+                                self.idx.data_ptr(), case.M, case.K, case.rows, ws,
+                                self.ws_bytes, stream)
+        else:
+            st = L.qgemm(case.fmt, c, s, b, self.x.data_ptr(), self.y.data_ptr(), case.M, case.K,
+                         case.rows, ws, self.ws_bytes, stream)
+        if st != 0:
+            raise RuntimeError(f"{case.name}: status {st}")
+
+    @property
+    def weight_bytes(self):
+        return self.case.weight_bytes
+
+
+def per_launch_ms(torch, fn, stream_handle, n):
+    """Average duration of one launch from HIP events recorded around it on
+    its own stream. A spin kernel queued first keeps the GPU busy while the
+    host enqueues, so each event pair brackets only its kernel."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e8))
+    for i in range(n):
+        starts[i].record()
+        fn(i, stream_handle)
+        ends[i].record()
+    torch.cuda.synchronize()
+    d = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return sum(d) / len(d), d[len(d) // 2]
+
+
+def cpu_baseline(launches, seconds):
+    import oracle
+    orc = oracle.get()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for L in launches:
+            w, x = L.host_w, L.host_x
+            c = L.case
+            if c.op == "gemm":
+                # bounded sample: the first 8 token rows
+                orc.qgemv(c.fmt, w.codes, w.scales, w.biases, x[:8], c.M, c.K)
+            else:
+                orc.qgemv(c.fmt, w.codes, w.scales, w.biases, x, c.M, c.K)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    gemm = launches[0].case.op == "gemm"
+    if gemm:
+        flops = sum(2 * L.case.M * L.case.K * 8 for L in launches) * reps
+        return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
+                "kind": "oracle",
+                "sample": f"first 8 token rows of each GEMM, {reps} repetitions, {el:.1f} s"}
+    wb = sum(L.weight_bytes for L in launches) * reps
+    return {"value": wb / el / 1e9, "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"the whole step ({' + '.join(L.case.name for L in launches)}), "
+                      f"{reps} repetitions, {el:.1f} s"}
+
+
+def load_traffic(workload, src_hash):
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != src_hash:
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=0, help="timed steps (default: about 2000 launches)")
+    ap.add_argument("--warmup", type=int, default=0)
+    ap.add_argument("--workload", default="c1")
+    ap.add_argument("--rotate-mib", type=int, default=640)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the kernels work on one "
+              "GPU's share of the matrix; there is no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gemm_qgemv_amd as q
+    from gemm_qgemv_amd import synth, tensors
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    names = WORKLOADS.get(args.workload, [args.workload])
+    cases = [synth.CASES_BY_NAME[n] for n in names]
+    gemm = cases[0].op == "gemm"
+    log(f"workload {args.workload}: {names}")
+    launches = [Launch(c, args.rotate_mib << 20, torch, q, synth, tensors) for c in cases]
+    rot = max(L.copies for L in launches)
+    log(f"weight copies rotated: {[L.copies for L in launches]}")
+
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+
+    def step(i, s):
+        for L in launches:
+            L(i, s)
+
+    per_step_launch_target = 2000 // len(launches) if not gemm else 20
+    steps = args.steps or max(rot, per_step_launch_target)
+    warmup = args.warmup or max(rot, 20 if not gemm else 3)
+    # graph of `rot` consecutive steps (one pass over the weight copies)
+    chunk = rot if not gemm else 1
+    steps = math.ceil(steps / chunk) * chunk
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            step(i, sh)
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(chunk):
+                step(i, stream.cuda_stream)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+
+    # ---- timed region -------------------------------------------------
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        ev0.record()
+        if graph is not None:
+            for _ in range(steps // chunk):
+                graph.replay()
+        else:
+            for i in range(steps):
+                step(i, sh)
+        ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / steps
+    log(f"timed {steps} steps: {ms_total:.3f} ms on the stream, {wall * 1e3:.3f} ms wall")
+
+    # ---- per-launch durations of each kernel call ------------------------
+    per_case = []
+    with torch.cuda.stream(stream):
+        for L in launches:
+            n = max(L.copies, 200 if not gemm else 10)
+            avg, med = per_launch_ms(torch, L, sh, n)
+            per_case.append((L, avg, med))
+            unit = L.weight_bytes / (avg * 1e-3) / 1e9
+            log(f"  {L.case.name}: {avg * 1e3:.2f} us avg ({med * 1e3:.2f} us median) per launch, "
+                f"{unit:.1f} GB/s weight" + (f", {L.case.flops / (avg * 1e-3) / 1e12:.2f} TFLOP/s" if gemm else ""))
+
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(args.workload, src_hash)
+    if gemm:
+        flops = sum(L.case.flops for L in launches)
+        value = flops / (ms_per_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        dom = max(per_case, key=lambda t: t[1])
+        ach = dom[0].case.flops / (dom[1] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 3), "peak": FP32_MATRIX_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / FP32_MATRIX_PEAK_TFLOPS, 4),
+                "traffic": traffic, "kernel_call": dom[0].case.name}
+        dtype = "f32"
+    else:
+        wbytes = sum(L.weight_bytes for L in launches)
+        value = wbytes / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+        tot_b = sum(L.weight_bytes for L, _, _ in per_case)
+        tot_t = sum(avg for _, avg, _ in per_case)
+        ach = tot_b / (tot_t * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel_calls": [L.case.name for L, _, _ in per_case]}
+        dtype = "f32"
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "cases": names,
+                   "shapes_MxK": [[c.M, c.K] for c in cases], "rows": [c.rows for c in cases],
+                   "format": synth.FORMAT_NAMES[cases[0].fmt],
+                   "weights": "cache-cold rotation" if not gemm else "resident",
+                   "weight_copies": [L.copies for L in launches],
+                   "launch": "hip graph" if graph is not None else "eager"},
+        "roofline": roof,
+    }
+    if not gemm:
+        out["pct_of_hbm_peak"] = round(100 * value / HBM_PEAK_GBS, 2)
+        out["tok_s_equiv"] = round(value * 1e9 / BYTES_PER_TOKEN[cases[0].fmt], 1)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(launches, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,377 @@
+// gemv.hpp -- dequantize-fused low-bit matrix-vector kernels (batch 1..16)
+// for gfx950, plus the split-K combine and the greedy-selection finalize.
+//
+// Mapping. A workgroup of 4 waves owns a contiguous range of output rows and
+// one K range (one "split"). The activations of that K range are staged
+// once into LDS; each wave then walks blocks of R rows. Within a row the 64
+// lanes walk the packed row in 16-byte slices (slice t goes to lane t mod
+// 64), so every wave instruction reads 64 consecutive 16-byte pieces of a
+// row: fully coalesced 1 KiB loads. The codes are unpacked and dequantized
+// in registers and never written anywhere (I Built an LLM Inference Engine
+// on a 15 year old GPU..., "Optimization 4: Quantized Kernels"). Each
+// activation value read from LDS serves all R rows of the block.
+//
+// Per format, one 16-byte slice holds:
+//   QG_I8_ROW   16 weights (k .. k+15), row scale applied once per row;
+//   QG_U4_G64   32 weights = half a group of 64: one (scale, bias) pair;
+//   QG_B1_G128 128 weights = one group of 128: one fp16 scale.
+// The affine and sign formats are evaluated per slice as
+//   U4:  s * sum(q * x) + b * sum(x)
+//   B1:  s * (2 * sum_{bit=1}(x) - sum(x))
+// with sum(x) over the slice precomputed once per workgroup.
+#pragma once
+
+#include "qg_device.hpp"
+
+namespace qg {
+
+enum { FMT_I8_ROW = 1, FMT_U4_G64 = 2, FMT_B1_G128 = 3 };
+
+template <int FMT> struct Fmt;
+template <> struct Fmt<FMT_I8_ROW>  { static constexpr int KPS = 16;  static constexpr bool kXsum = false; };
+template <> struct Fmt<FMT_U4_G64>  { static constexpr int KPS = 32;  static constexpr bool kXsum = true; };
+template <> struct Fmt<FMT_B1_G128> { static constexpr int KPS = 128; static constexpr bool kXsum = true; };
+
+struct GemvParams {
+    const uint8_t *codes;
+    const void *scales;
+    const void *biases;
+    const float *x;       // [nb][K]
+    float *y;             // [nb][M] final output (used when nsplit == 1)
+    float *part;          // [nsplit][nb][M] partial sums (used when nsplit > 1)
+    uint64_t *keys;       // [nb][nkeys] argmax keys, or nullptr
+    int64_t M;
+    int64_t K;
+    int64_t x_stride;     // floats between activation rows (== K)
+    int64_t rows_per_wg;  // multiple of 4 * R
+    int64_t kc;           // K per split, multiple of the slice width
+    int nb;               // actual batch (<= template B)
+    int nsplit;
+    int nkeys;            // keys per batch row (== gridDim.x of the keyed kernel)
+};
+
+// Chunk (float4) swizzle inside an activation plane. Lanes reading chunk
+// j of consecutive slices would all hit the same LDS banks; flipping the
+// low 3 chunk-index bits by the slice number spreads 8 consecutive lanes
+// over all 8 16-byte bank groups. It permutes chunks only within aligned
+// groups of 8, so planes are padded to a multiple of 32 floats.
+template <int CPS>
+__device__ __forceinline__ int swz(int c)
+{
+    return c ^ ((c / CPS) & 7);
+}
+
+__host__ __device__ constexpr int64_t plane_floats(int64_t kc)
+{
+    return (kc + 31) / 32 * 32;
+}
+
+template <int FMT>
+__host__ __device__ constexpr int64_t xsum_floats(int64_t kc)
+{
+    return Fmt<FMT>::kXsum ? (kc / Fmt<FMT>::KPS + 3) / 4 * 4 : 0;
+}
+
+// Stage x[b][k0 : k0+kc] into LDS planes (swizzled, zero beyond nb), with
+// odd k of the 4-bit format pre-divided by 16 (exact: a power of two) so that
+// the high nibble can be used without a shift. Then per-slice sums of the
+// unscaled activations.
+template <int FMT, int B>
+__device__ __forceinline__ void stage_x(const GemvParams &p, int64_t k0, int kc,
+                                        float4 *xl, float *xs)
+{
+    constexpr int KPS = Fmt<FMT>::KPS;
+    constexpr int CPS = KPS / 4;
+    const int pc = static_cast<int>(plane_floats(kc) / 4);  // chunks per plane
+    const int nchunk = kc / 4;
+    for (int i = threadIdx.x; i < B * pc; i += blockDim.x) {
+        const int b = i / pc, c = i % pc;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (b < p.nb && c < nchunk)
+            v = *reinterpret_cast<const float4 *>(p.x + b * p.x_stride + k0 + 4 * c);
+        if (FMT == FMT_U4_G64) {
+            v.y *= 0.0625f;
+            v.w *= 0.0625f;
+        }
+        xl[b * pc + swz<CPS>(c)] = v;
+    }
+    if (Fmt<FMT>::kXsum) {
+        const int ns = kc / KPS;
+        const int xsp = static_cast<int>(xsum_floats<FMT>(kc));
+        for (int i = threadIdx.x; i < B * ns; i += blockDim.x) {
+            const int b = i / ns, t = i % ns;
+            float s = 0.f;
+            if (b < p.nb) {
+                const float4 *src =
+                    reinterpret_cast<const float4 *>(p.x + b * p.x_stride + k0 + t * KPS);
+#pragma unroll 4
+                for (int j = 0; j < CPS; ++j) {
+                    float4 v = src[j];
+                    s += (v.x + v.y) + (v.z + v.w);
+                }
+            }
+            xs[b * xsp + t] = s;
+        }
+    }
+}
+
+// sum_i q_i * x_i for one dword of 4 int8 codes and 4 activations.
+__device__ __forceinline__ float dot_i8x4(uint32_t d, float4 x, float acc)
+{
+    acc = fmaf(static_cast<float>(static_cast<int8_t>(d & 0xff)), x.x, acc);
+    acc = fmaf(static_cast<float>(static_cast<int8_t>((d >> 8) & 0xff)), x.y, acc);
+    acc = fmaf(static_cast<float>(static_cast<int8_t>((d >> 16) & 0xff)), x.z, acc);
+    acc = fmaf(static_cast<float>(static_cast<int8_t>(d >> 24)), x.w, acc);
+    return acc;
+}
+
+// sum_i q_i * x_i for one dword of 8 nibbles (k = 8j .. 8j+7), given the
+// two activation chunks of those k with odd k pre-divided by 16: the low
+// nibbles (even k) are masked in place, the high nibbles (odd k) are masked
+// in place as 16*q; each byte then converts to float in one instruction.
+__device__ __forceinline__ float dot_u4x8(uint32_t d, float4 xa, float4 xb, float acc)
+{
+    // The masks go through opaque instructions: if the compiler could see
+    // them it would fold each "mask, then take byte i" into a bit-field
+    // extract plus a convert (two instructions per weight) instead of one
+    // byte-select convert (v_cvt_f32_ubyte0..3).
+    uint32_t lo, hi;
+    asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(d));
+    asm("v_and_b32 %0, 0xf0f0f0f0, %1" : "=v"(hi) : "v"(d));
+    acc = fmaf(static_cast<float>(lo & 0xff), xa.x, acc);
+    acc = fmaf(static_cast<float>(hi & 0xff), xa.y, acc);
+    acc = fmaf(static_cast<float>((lo >> 8) & 0xff), xa.z, acc);
+    acc = fmaf(static_cast<float>((hi >> 8) & 0xff), xa.w, acc);
+    acc = fmaf(static_cast<float>((lo >> 16) & 0xff), xb.x, acc);
+    acc = fmaf(static_cast<float>((hi >> 16) & 0xff), xb.y, acc);
+    acc = fmaf(static_cast<float>(lo >> 24), xb.z, acc);
+    acc = fmaf(static_cast<float>(hi >> 24), xb.w, acc);
+    return acc;
+}
+
+// sum over the set bits of one byte (k = 8j .. 8j+7) of x_k.
+__device__ __forceinline__ float sum_b1x8(uint32_t byte, float4 xa, float4 xb, float acc)
+{
+    acc += (byte & 0x01u) ? xa.x : 0.f;
+    acc += (byte & 0x02u) ? xa.y : 0.f;
+    acc += (byte & 0x04u) ? xa.z : 0.f;
+    acc += (byte & 0x08u) ? xa.w : 0.f;
+    acc += (byte & 0x10u) ? xb.x : 0.f;
+    acc += (byte & 0x20u) ? xb.y : 0.f;
+    acc += (byte & 0x40u) ? xb.z : 0.f;
+    acc += (byte & 0x80u) ? xb.w : 0.f;
+    return acc;
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4 &c, int j)
+{
+    return j == 0 ? c.x : j == 1 ? c.y : j == 2 ? c.z : c.w;
+}
+
+// Main kernel. B: batch rounded up to a power of two (x rows >= nb are
+// zero in LDS and their outputs are not written). R: rows per block.
+template <int FMT, int B, int R>
+__global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
+{
+    constexpr int KPS = Fmt<FMT>::KPS;
+    constexpr int CPS = KPS / 4;
+    constexpr int V = R * B;
+    static_assert(V <= 64, "R * B must not exceed the wave width");
+
+    extern __shared__ float4 lds[];
+    const int split = blockIdx.y;
+    const int64_t k0 = static_cast<int64_t>(split) * p.kc;
+    const int kc = static_cast<int>(min(p.kc, p.K - k0));
+    const int pc = static_cast<int>(plane_floats(kc) / 4);
+    const int xsp = static_cast<int>(xsum_floats<FMT>(kc));
+    float4 *xl = lds;
+    float *xs = reinterpret_cast<float *>(lds + B * pc);
+
+    stage_x<FMT, B>(p, k0, kc, xl, xs);
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int S = kc / KPS;                       // slices in this split
+    const int64_t row_bytes = FMT == FMT_I8_ROW ? p.K : FMT == FMT_U4_G64 ? p.K / 2 : p.K / 8;
+    const int64_t slice0 = k0 / KPS;              // first global slice of this split
+    const int64_t m_begin = static_cast<int64_t>(blockIdx.x) * p.rows_per_wg;
+    const int64_t m_end = min(p.M, m_begin + p.rows_per_wg);
+
+    // value index this lane ends up owning after the transpose reduction
+    constexpr int P = V == 1 ? 0 : V == 2 ? 1 : V == 4 ? 2 : V == 8 ? 3 : V == 16 ? 4 : V == 32 ? 5 : 6;
+    const int own = lane >> (6 - P);
+    const bool writer = (lane & ((1 << (6 - P)) - 1)) == 0;
+    const int own_r = own / B, own_b = own % B;
+    float best_v = 0.f;
+    int64_t best_m = -1;
+
+    for (int64_t rb = m_begin + wave * R; rb < m_end; rb += 4 * R) {
+        float acc[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = 0.f;
+
+        for (int t = lane; t < S; t += kWave) {
+            const int64_t gslice = slice0 + t;
+            uint4 c[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int64_t m = rb + r;
+                c[r] = make_uint4(0, 0, 0, 0);
+                if (m < m_end)
+                    c[r] = *reinterpret_cast<const uint4 *>(p.codes + m * row_bytes + gslice * 16);
+            }
+            if (FMT == FMT_I8_ROW) {
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const float4 *xp = xl + b * pc;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float4 xv = xp[swz<CPS>(t * CPS + j)];
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            acc[r * B + b] = dot_i8x4(word_of(c[r], j), xv, acc[r * B + b]);
+                    }
+                }
+            } else if (FMT == FMT_U4_G64) {
+                float s[R], bi[R];
+                const uint16_t *sp = static_cast<const uint16_t *>(p.scales);
+                const uint16_t *bp = static_cast<const uint16_t *>(p.biases);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int64_t m = rb + r;
+                    const int64_t gi = (m < m_end ? m : m_begin) * (p.K / 64) + gslice / 2;
+                    s[r] = bf16_bits_to_f32(sp[gi]);
+                    bi[r] = bf16_bits_to_f32(bp[gi]);
+                }
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const float4 *xp = xl + b * pc;
+                    float dot[R];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) dot[r] = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float4 xa = xp[swz<CPS>(t * CPS + 2 * j)];
+                        const float4 xb = xp[swz<CPS>(t * CPS + 2 * j + 1)];
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            dot[r] = dot_u4x8(word_of(c[r], j), xa, xb, dot[r]);
+                    }
+                    const float xsum = xs[b * xsp + t];
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        acc[r * B + b] = fmaf(s[r], dot[r], fmaf(bi[r], xsum, acc[r * B + b]));
+                }
+            } else {  // FMT_B1_G128
+                float s[R];
+                const uint16_t *sp = static_cast<const uint16_t *>(p.scales);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int64_t m = rb + r;
+                    s[r] = fp16_bits_to_f32(sp[(m < m_end ? m : m_begin) * (p.K / 128) + gslice]);
+                }
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const float4 *xp = xl + b * pc;
+                    float on[R];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) on[r] = 0.f;
+#pragma unroll
+                    for (int o = 0; o < 16; ++o) {
+                        const float4 xa = xp[swz<CPS>(t * CPS + 2 * o)];
+                        const float4 xb = xp[swz<CPS>(t * CPS + 2 * o + 1)];
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            on[r] = sum_b1x8((word_of(c[r], o >> 2) >> (8 * (o & 3))) & 0xffu,
+                                             xa, xb, on[r]);
+                    }
+                    const float xsum = xs[b * xsp + t];
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        acc[r * B + b] = fmaf(s[r], fmaf(2.f, on[r], -xsum), acc[r * B + b]);
+                }
+            }
+        }
+
+        wave_transpose_reduce<V>(acc, lane);
+
+        if (writer) {
+            const int64_t m = rb + own_r;
+            if (m < m_end && own_b < p.nb) {
+                float v = acc[0];
+                if (FMT == FMT_I8_ROW)
+                    v *= static_cast<const float *>(p.scales)[m];
+                if (p.nsplit == 1) {
+                    p.y[own_b * p.M + m] = v;
+                    if (best_m < 0 || v > best_v || (v == best_v && m < best_m)) {
+                        best_v = v;
+                        best_m = m;
+                    }
+                } else {
+                    p.part[(static_cast<int64_t>(split) * p.nb + own_b) * p.M + m] = v;
+                }
+            }
+        }
+    }
+
+    if (p.keys != nullptr && p.nsplit == 1) {
+        __shared__ unsigned long long wg_key[B];
+        __syncthreads();
+        if (threadIdx.x < B) wg_key[threadIdx.x] = 0ull;
+        __syncthreads();
+        if (writer && best_m >= 0)
+            atomicMax(&wg_key[own_b], static_cast<unsigned long long>(
+                                          argmax_key(best_v, static_cast<uint32_t>(best_m))));
+        __syncthreads();
+        if (threadIdx.x < p.nb)
+            p.keys[static_cast<int64_t>(threadIdx.x) * p.nkeys + blockIdx.x] = wg_key[threadIdx.x];
+    }
+}
+
+// y[b][m] = sum over splits of part[s][b][m], in split order; optionally
+// the per-workgroup argmax keys of the combined rows.
+__global__ __launch_bounds__(256) void gemv_combine_kernel(GemvParams p)
+{
+    __shared__ unsigned long long wg_key[16];
+    if (threadIdx.x < 16) wg_key[threadIdx.x] = 0ull;
+    __syncthreads();
+    const int64_t m_begin = static_cast<int64_t>(blockIdx.x) * p.rows_per_wg;
+    const int64_t m_end = min(p.M, m_begin + p.rows_per_wg);
+    for (int b = 0; b < p.nb; ++b) {
+        uint64_t best = 0;
+        for (int64_t m = m_begin + threadIdx.x; m < m_end; m += blockDim.x) {
+            float v = 0.f;
+            for (int s = 0; s < p.nsplit; ++s)
+                v += p.part[(static_cast<int64_t>(s) * p.nb + b) * p.M + m];
+            p.y[b * p.M + m] = v;
+            const uint64_t key = argmax_key(v, static_cast<uint32_t>(m));
+            best = key > best ? key : best;
+        }
+        if (p.keys != nullptr)
+            atomicMax(&wg_key[b], static_cast<unsigned long long>(best));
+    }
+    if (p.keys != nullptr) {
+        __syncthreads();
+        if (threadIdx.x < p.nb)
+            p.keys[static_cast<int64_t>(threadIdx.x) * p.nkeys + blockIdx.x] = wg_key[threadIdx.x];
+    }
+}
+
+// idx[b] = index of the largest key of batch row b (one workgroup per row).
+__global__ __launch_bounds__(256) void argmax_finalize_kernel(const uint64_t *keys, int nkeys,
+                                                              int32_t *idx)
+{
+    __shared__ unsigned long long best;
+    if (threadIdx.x == 0) best = 0ull;
+    __syncthreads();
+    const uint64_t *row = keys + static_cast<int64_t>(blockIdx.x) * nkeys;
+    uint64_t mine = 0;
+    for (int i = threadIdx.x; i < nkeys; i += blockDim.x)
+        mine = row[i] > mine ? row[i] : mine;
+    atomicMax(&best, static_cast<unsigned long long>(mine));
+    __syncthreads();
+    if (threadIdx.x == 0) idx[blockIdx.x] = static_cast<int32_t>(argmax_key_index(best));
+}
+
+}  // namespace qg

@@ -1,0 +1,361 @@
+// qg.hip -- libqg: host-side validation, shape dispatch and launches behind
+// the C ABI declared in include/qg.h. All arithmetic runs in the kernels of
+// gemv.hpp / gemm.hpp; this file only checks arguments, plans the launch
+// geometry from (format, M, K, rows) and enqueues work on the caller's
+// stream. It never allocates, copies or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/qg.h"
+#include "gemv.hpp"
+
+namespace {
+
+using qg::GemvParams;
+
+constexpr int64_t kMaxM = 0x7fffffffLL;
+constexpr int64_t kMaxK = int64_t(1) << 30;
+constexpr int64_t kMaxN = 0x7fffffffLL;
+// Dynamic LDS a GEMV workgroup may use for its activation tile.
+constexpr int64_t kLdsBudget = 60 * 1024;
+constexpr int64_t kAlign = 16;
+constexpr int kThreads = 256;
+
+int k_unit(int fmt) { return fmt == QG_I8_ROW ? 16 : fmt == QG_U4_G64 ? 64 : 128; }
+int k_per_slice(int fmt) { return fmt == QG_I8_ROW ? 16 : fmt == QG_U4_G64 ? 32 : 128; }
+
+int64_t row_bytes(int fmt, int64_t K)
+{
+    return fmt == QG_I8_ROW ? K : fmt == QG_U4_G64 ? K / 2 : K / 8;
+}
+int64_t scale_bytes(int fmt, int64_t M, int64_t K)
+{
+    return fmt == QG_I8_ROW ? 4 * M : fmt == QG_U4_G64 ? 2 * M * (K / 64) : 2 * M * (K / 128);
+}
+int64_t bias_bytes(int fmt, int64_t M, int64_t K)
+{
+    return fmt == QG_U4_G64 ? 2 * M * (K / 64) : 0;
+}
+
+bool aligned(const void *p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// ---------------------------------------------------------------------------
+// argument checks (host only, before anything is enqueued)
+// ---------------------------------------------------------------------------
+
+int check_weights(int fmt, const void *codes, const void *scales, const void *biases,
+                  const float *x, int64_t M, int64_t K)
+{
+    if (fmt != QG_I8_ROW && fmt != QG_U4_G64 && fmt != QG_B1_G128) return QG_ERR_FORMAT;
+    if (!codes || !scales || !x) return QG_ERR_NULL;
+    if ((fmt == QG_U4_G64) != (biases != nullptr)) return QG_ERR_NULL;
+    if (M < 1 || M > kMaxM || K < 1 || K > kMaxK || K % k_unit(fmt) != 0) return QG_ERR_SHAPE;
+    if (!aligned(codes, kAlign) || !aligned(scales, kAlign) || !aligned(x, kAlign) ||
+        (biases && !aligned(biases, kAlign)))
+        return QG_ERR_ALIGN;
+    return QG_OK;
+}
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void *p, int64_t bytes)
+{
+    uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+// Every written range must be disjoint from every other range.
+int check_alias(const Range *all, int n_all, const Range *written, int n_written)
+{
+    for (int i = 0; i < n_written; ++i)
+        for (int j = 0; j < n_all; ++j) {
+            if (written[i].lo == all[j].lo && written[i].hi == all[j].hi) continue;  // itself
+            if (overlap(written[i], all[j])) return QG_ERR_ALIAS;
+        }
+    for (int i = 0; i < n_written; ++i)
+        for (int j = i + 1; j < n_written; ++j)
+            if (overlap(written[i], written[j])) return QG_ERR_ALIAS;
+    return QG_OK;
+}
+
+int launch_status()
+{
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+// ---------------------------------------------------------------------------
+// GEMV plan: a pure function of (fmt, M, K, batch, argmax)
+// ---------------------------------------------------------------------------
+
+struct GemvPlan {
+    int B, R;
+    int64_t kc;
+    int nsplit;
+    int64_t rows_per_wg, grid_x;
+    size_t lds_bytes;
+    int64_t comb_rows_per_wg, comb_grid;
+    int nkeys;
+    size_t part_off, keys_off, ws_bytes;
+};
+
+GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
+{
+    GemvPlan pl{};
+    pl.B = nb <= 1 ? 1 : nb <= 2 ? 2 : nb <= 4 ? 4 : nb <= 8 ? 8 : 16;
+    const int kps = k_per_slice(fmt);
+    const bool xsum = fmt != QG_I8_ROW;
+    // activation planes (+ per-slice sums) must fit the LDS budget
+    const double bytes_per_k = pl.B * 4.0 * (1.0 + (xsum ? 1.0 / kps : 0.0));
+    int64_t kc_max = static_cast<int64_t>((kLdsBudget - 64 * pl.B) / bytes_per_k);
+    kc_max = kc_max / 128 * 128;
+    pl.nsplit = static_cast<int>(ceil_div(K, kc_max));
+    pl.kc = round_up(ceil_div(K, pl.nsplit), kps);
+    pl.nsplit = static_cast<int>(ceil_div(K, pl.kc));
+    // rows per block: as many as the wave width allows, fewer when the
+    // grid would leave compute units idle
+    pl.R = 64 / pl.B < 4 ? 64 / pl.B : 4;
+    while (pl.R > 1 && ceil_div(M, 4 * pl.R) * pl.nsplit < 256) pl.R /= 2;
+    const int64_t wg_target = 1024 / pl.nsplit > 0 ? 1024 / pl.nsplit : 1;
+    pl.rows_per_wg = round_up(ceil_div(M, wg_target), 4 * pl.R);
+    pl.grid_x = ceil_div(M, pl.rows_per_wg);
+    const int64_t pf = (pl.kc + 31) / 32 * 32;
+    const int64_t xsf = xsum ? (pl.kc / kps + 3) / 4 * 4 : 0;
+    pl.lds_bytes = static_cast<size_t>(pl.B * (pf + xsf) * 4);
+    size_t off = 0;
+    if (pl.nsplit > 1) {
+        pl.comb_rows_per_wg = round_up(ceil_div(M, 1024), 256);
+        pl.comb_grid = ceil_div(M, pl.comb_rows_per_wg);
+        pl.part_off = off;
+        off = align256(off + static_cast<size_t>(pl.nsplit) * nb * M * 4);
+    }
+    if (argmax) {
+        pl.nkeys = static_cast<int>(pl.nsplit > 1 ? pl.comb_grid : pl.grid_x);
+        pl.keys_off = off;
+        off = align256(off + static_cast<size_t>(nb) * pl.nkeys * 8);
+    }
+    pl.ws_bytes = off;
+    return pl;
+}
+
+template <int FMT, int B>
+void launch_gemv_b(const GemvPlan &pl, const GemvParams &p, hipStream_t s)
+{
+    dim3 grid(static_cast<unsigned>(pl.grid_x), static_cast<unsigned>(pl.nsplit));
+    switch (pl.R) {
+    case 4: hipLaunchKernelGGL((qg::gemv_kernel<FMT, B, 4>), grid, dim3(kThreads), pl.lds_bytes, s, p); break;
+    case 2: hipLaunchKernelGGL((qg::gemv_kernel<FMT, B, 2>), grid, dim3(kThreads), pl.lds_bytes, s, p); break;
+    default: hipLaunchKernelGGL((qg::gemv_kernel<FMT, B, 1>), grid, dim3(kThreads), pl.lds_bytes, s, p); break;
+    }
+}
+
+template <int FMT>
+void launch_gemv_fmt(const GemvPlan &pl, const GemvParams &p, hipStream_t s)
+{
+    switch (pl.B) {
+    case 1: launch_gemv_b<FMT, 1>(pl, p, s); break;
+    case 2: launch_gemv_b<FMT, 2>(pl, p, s); break;
+    case 4: launch_gemv_b<FMT, 4>(pl, p, s); break;
+    case 8: launch_gemv_b<FMT, 8>(pl, p, s); break;
+    default: launch_gemv_b<FMT, 16>(pl, p, s); break;
+    }
+}
+
+// Enqueue one planned GEMV (+ combine, + argmax finalize).
+void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales,
+              const void *biases, const float *x, float *y, int32_t *idx, int64_t M,
+              int64_t K, int nb, void *ws, hipStream_t s)
+{
+    GemvParams p{};
+    p.codes = static_cast<const uint8_t *>(codes);
+    p.scales = scales;
+    p.biases = biases;
+    p.x = x;
+    p.y = y;
+    p.part = pl.nsplit > 1 ? reinterpret_cast<float *>(static_cast<char *>(ws) + pl.part_off) : nullptr;
+    p.keys = idx ? reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + pl.keys_off) : nullptr;
+    p.M = M;
+    p.K = K;
+    p.x_stride = K;
+    p.rows_per_wg = pl.rows_per_wg;
+    p.kc = pl.kc;
+    p.nb = nb;
+    p.nsplit = pl.nsplit;
+    p.nkeys = pl.nkeys;
+    if (fmt == QG_I8_ROW) launch_gemv_fmt<qg::FMT_I8_ROW>(pl, p, s);
+    else if (fmt == QG_U4_G64) launch_gemv_fmt<qg::FMT_U4_G64>(pl, p, s);
+    else launch_gemv_fmt<qg::FMT_B1_G128>(pl, p, s);
+    if (pl.nsplit > 1) {
+        GemvParams c = p;
+        c.rows_per_wg = pl.comb_rows_per_wg;
+        hipLaunchKernelGGL(qg::gemv_combine_kernel, dim3(static_cast<unsigned>(pl.comb_grid)),
+                           dim3(kThreads), 0, s, c);
+    }
+    if (idx)
+        hipLaunchKernelGGL(qg::argmax_finalize_kernel, dim3(nb), dim3(kThreads), 0, s,
+                           static_cast<const uint64_t *>(p.keys), pl.nkeys, idx);
+}
+
+int gemv_entry(int fmt, const void *codes, const void *scales, const void *biases,
+               const float *x, float *y, int32_t *idx, int64_t M, int64_t K, int batch,
+               void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int st = check_weights(fmt, codes, scales, biases, x, M, K);
+    if (st != QG_OK) return st;
+    if (!y) return QG_ERR_NULL;
+    if (batch < 1 || batch > QG_MAX_GEMV_BATCH) return QG_ERR_SHAPE;
+    if (!aligned(y, kAlign)) return QG_ERR_ALIGN;
+    const bool argmax = idx != nullptr;
+    if (argmax && !aligned(idx, 4)) return QG_ERR_ALIGN;
+    const GemvPlan pl = plan_gemv(fmt, M, K, batch, argmax);
+    if (pl.ws_bytes > 0) {
+        if (!ws || ws_bytes < pl.ws_bytes) return QG_ERR_WORKSPACE;
+        if (!aligned(ws, kAlign)) return QG_ERR_ALIGN;
+    }
+    Range all[7];
+    int n = 0;
+    all[n++] = range_of(codes, M * row_bytes(fmt, K));
+    all[n++] = range_of(scales, scale_bytes(fmt, M, K));
+    if (biases) all[n++] = range_of(biases, bias_bytes(fmt, M, K));
+    all[n++] = range_of(x, int64_t(batch) * K * 4);
+    Range wr[3];
+    int nw = 0;
+    wr[nw++] = all[n++] = range_of(y, int64_t(batch) * M * 4);
+    if (argmax) wr[nw++] = all[n++] = range_of(idx, int64_t(batch) * 4);
+    if (pl.ws_bytes > 0) wr[nw++] = all[n++] = range_of(ws, static_cast<int64_t>(pl.ws_bytes));
+    st = check_alias(all, n, wr, nw);
+    if (st != QG_OK) return st;
+
+    (void)hipGetLastError();
+    run_gemv(fmt, pl, codes, scales, biases, x, y, idx, M, K, batch, ws, stream);
+    return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// GEMM: token rows in chunks of 16 through the matrix-vector kernel
+// ---------------------------------------------------------------------------
+
+constexpr int kGemmChunk = 16;
+
+size_t gemm_workspace(int fmt, int64_t M, int64_t K, int64_t N)
+{
+    return plan_gemv(fmt, M, K, static_cast<int>(N < kGemmChunk ? N : kGemmChunk), false).ws_bytes;
+}
+
+void run_gemm(int fmt, const void *codes, const void *scales, const float *x, float *y,
+              int64_t M, int64_t K, int64_t N, void *ws, hipStream_t s)
+{
+    for (int64_t n0 = 0; n0 < N; n0 += kGemmChunk) {
+        const int nb = static_cast<int>(N - n0 < kGemmChunk ? N - n0 : kGemmChunk);
+        const GemvPlan pl = plan_gemv(fmt, M, K, nb, false);
+        run_gemv(fmt, pl, codes, scales, nullptr, x + n0 * K, y + n0 * M, nullptr, M, K, nb, ws, s);
+    }
+}
+
+int gemm_entry(int fmt, const void *codes, const void *scales, const void *biases,
+               const float *x, float *y, int64_t M, int64_t K, int64_t N, void *ws,
+               size_t ws_bytes, hipStream_t stream)
+{
+    int st = check_weights(fmt, codes, scales, biases, x, M, K);
+    if (st != QG_OK) return st;
+    if (!y) return QG_ERR_NULL;
+    if (N < 1 || N > kMaxN) return QG_ERR_SHAPE;
+    if (!aligned(y, kAlign)) return QG_ERR_ALIGN;
+    if (fmt == QG_U4_G64) return QG_ERR_UNSUPPORTED;
+    const size_t need = gemm_workspace(fmt, M, K, N);
+    if (need > 0) {
+        if (!ws || ws_bytes < need) return QG_ERR_WORKSPACE;
+        if (!aligned(ws, kAlign)) return QG_ERR_ALIGN;
+    }
+    Range all[6];
+    int n = 0;
+    all[n++] = range_of(codes, M * row_bytes(fmt, K));
+    all[n++] = range_of(scales, scale_bytes(fmt, M, K));
+    all[n++] = range_of(x, N * K * 4);
+    Range wr[2];
+    int nw = 0;
+    wr[nw++] = all[n++] = range_of(y, N * M * 4);
+    if (need > 0) wr[nw++] = all[n++] = range_of(ws, static_cast<int64_t>(need));
+    st = check_alias(all, n, wr, nw);
+    if (st != QG_OK) return st;
+
+    (void)hipGetLastError();
+    run_gemm(fmt, codes, scales, x, y, M, K, N, ws, stream);
+    return launch_status();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+
+extern "C" {
+
+int qgemv(int fmt, const void *codes, const void *scales, const void *biases,
+          const float *x, float *y, int64_t M, int64_t K, int batch, void *ws,
+          size_t ws_bytes, hipStream_t stream)
+{
+    return gemv_entry(fmt, codes, scales, biases, x, y, nullptr, M, K, batch, ws, ws_bytes, stream);
+}
+
+int qgemv_argmax(int fmt, const void *codes, const void *scales, const void *biases,
+                 const float *x, float *logits, int32_t *idx, int64_t M, int64_t K,
+                 int batch, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (!idx) return QG_ERR_NULL;
+    return gemv_entry(fmt, codes, scales, biases, x, logits, idx, M, K, batch, ws, ws_bytes,
+                      stream);
+}
+
+int qgemm(int fmt, const void *codes, const void *scales, const void *biases,
+          const float *x, float *y, int64_t M, int64_t K, int64_t N, void *ws,
+          size_t ws_bytes, hipStream_t stream)
+{
+    return gemm_entry(fmt, codes, scales, biases, x, y, M, K, N, ws, ws_bytes, stream);
+}
+
+size_t qg_workspace_bytes(int op, int fmt, int64_t M, int64_t K, int64_t rows)
+{
+    if (fmt != QG_I8_ROW && fmt != QG_U4_G64 && fmt != QG_B1_G128) return 0;
+    if (M < 1 || M > kMaxM || K < 1 || K > kMaxK || K % k_unit(fmt) != 0) return 0;
+    if (op == QG_OP_GEMV || op == QG_OP_GEMV_ARGMAX) {
+        if (rows < 1 || rows > QG_MAX_GEMV_BATCH) return 0;
+        return plan_gemv(fmt, M, K, static_cast<int>(rows), op == QG_OP_GEMV_ARGMAX).ws_bytes;
+    }
+    if (op == QG_OP_GEMM) {
+        if (rows < 1 || rows > kMaxN || fmt == QG_U4_G64) return 0;
+        return gemm_workspace(fmt, M, K, rows);
+    }
+    return 0;
+}
+
+const char *qg_status_str(int status)
+{
+    switch (status) {
+    case QG_OK: return "ok";
+    case QG_ERR_NULL: return "a required pointer is NULL (or biases given for a format without them)";
+    case QG_ERR_FORMAT: return "unknown weight format";
+    case QG_ERR_SHAPE: return "M, K or rows out of range, or K not a multiple of the format's unit";
+    case QG_ERR_ALIGN: return "a pointer is not aligned as required";
+    case QG_ERR_WORKSPACE: return "workspace missing or smaller than qg_workspace_bytes()";
+    case QG_ERR_ALIAS: return "a written buffer overlaps another buffer";
+    case QG_ERR_LAUNCH: return "kernel launch failed";
+    case QG_ERR_UNSUPPORTED: return "combination not implemented by this library";
+    default: return "unknown status";
+    }
+}
+
+int qg_abi_version(void) { return QG_ABI_VERSION; }
+
+}  // extern "C"

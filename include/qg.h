@@ -1,0 +1,172 @@
+/*
+ * qg.h -- C ABI of libqg: dequantize-fused low-bit weight matrix-vector
+ * product (batch-1 LLM decode), its small-batch and prefill matrix-matrix
+ * form, and a fused greedy (argmax) output head, for AMD MI355X (gfx950).
+ *
+ * Notation. W is M x K (M outputs, K inputs). Activations x are float32
+ * [rows][K], outputs y are float32 [rows][M]; every array is row-major and
+ * contiguous. For every output,
+ *
+ *     y[n][m] = sum over k of w[m][k] * x[n][k]
+ *
+ * where w[m][k] is the real weight decoded from the packed format below,
+ * and the sum is carried in float32 (any order; the result is within
+ * 1e-5 * sum_k |w[m][k] * x[n][k]| of the exact value).
+ *
+ * Weight formats
+ *
+ *   QG_I8_ROW   codes  int8  [M][K]      two's complement, any value
+ *               scales fp32  [M]         w = scales[m] * q
+ *               biases must be NULL.  K must be a multiple of 16.
+ *     (MiniCPM-V-4.6 on a Tesla C2075, academ.us 2607.14568, section 2.3
+ *     "Quantization and residency" and section 3.3 "Decode, and why 4-bit
+ *     is slower": symmetric 8-bit weights with an FP32 scale, read without
+ *     unpacking; here the scale is per row.)
+ *
+ *   QG_U4_G64   codes  uint8 [M][K/2]    byte j of a row: k=2j in bits 0..3,
+ *                                        k=2j+1 in bits 4..7, q in 0..15
+ *               scales bf16  [M][K/64]   (uint16 bit patterns)
+ *               biases bf16  [M][K/64]
+ *               w = scales[m][k/64] * q + biases[m][k/64].  K multiple of 64.
+ *     (Pushing the limits of legacy hardware, "Start with the machine that
+ *     actually exists": group-64 affine 4-bit codes with bf16 scale and bias;
+ *     I Built an LLM Inference Engine on a 15 year old GPU..., "Quantization:
+ *     The Model Doesn't Run on INT4": code times scale plus the minimum.)
+ *
+ *   QG_B1_G128  codes  uint8 [M][K/8]    bit (k mod 8) of byte k/8, least
+ *                                        significant bit first
+ *               scales fp16  [M][K/128]  (uint16 bit patterns)
+ *               w = +scales[m][k/128] if the bit is 1, -scales[..] if 0.
+ *               biases must be NULL.  K multiple of 128.
+ *     (A 27B model on two 4GB Maxwell GPUs: inference tuning, "Why this
+ *     machine is awkward": binary weights with FP16 scales.)
+ *
+ * Conventions shared by every entry point
+ *
+ *   Ownership   The caller owns every buffer. All data pointers are device
+ *               pointers (hipMalloc'd or equivalent) and stay resident; the
+ *               library never allocates, frees, copies to or from the host,
+ *               or synchronizes. (I Built an LLM Inference Engine..., "The
+ *               memory movement problem" and "Cost 2": weights live on the
+ *               device, and nothing is allocated on the hot path.)
+ *   Streams     Work is enqueued on `stream` (0 = the null stream) and the
+ *               call returns without waiting for it.
+ *   Alignment   codes, scales, biases, x, y / logits and ws must be 16-byte
+ *               aligned; idx 4-byte aligned.
+ *   Aliasing    The written buffers (y or logits, idx, ws) must not overlap
+ *               each other or any input.
+ *   Errors      Every argument error is detected on the host before
+ *               anything is enqueued; the outputs are then left untouched
+ *               and a negative QG_ERR_* code is returned. QG_ERR_LAUNCH
+ *               reports a failed kernel launch (hipGetLastError).
+ *               (Pushing the limits of legacy hardware, "Build the execution
+ *               path, then share the weights": a request that cannot be
+ *               served fails before changing live state.)
+ *   Threads     The library keeps no mutable state; calls are reentrant.
+ *               Calls that share a workspace must not overlap in time.
+ *   Workspace   `ws` is device scratch of at least qg_workspace_bytes(...)
+ *               bytes for the same (op, fmt, M, K, rows); it may be NULL
+ *               when that size is 0. Its contents on entry do not matter.
+ */
+#ifndef QG_H
+#define QG_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QG_ABI_VERSION 1
+
+typedef enum {
+    QG_I8_ROW = 1,
+    QG_U4_G64 = 2,
+    QG_B1_G128 = 3
+} qg_format;
+
+typedef enum {
+    QG_OP_GEMV = 1,
+    QG_OP_GEMM = 2,
+    QG_OP_GEMV_ARGMAX = 3
+} qg_op;
+
+enum {
+    QG_OK = 0,
+    QG_ERR_NULL = -1,        /* a required pointer is NULL, or biases given where none belong */
+    QG_ERR_FORMAT = -2,      /* unknown format */
+    QG_ERR_SHAPE = -3,       /* M, K or rows out of range, or K not a multiple of the format's unit */
+    QG_ERR_ALIGN = -4,       /* a pointer is not aligned as required */
+    QG_ERR_WORKSPACE = -5,   /* ws_bytes smaller than qg_workspace_bytes(...) */
+    QG_ERR_ALIAS = -6,       /* a written buffer overlaps another buffer */
+    QG_ERR_LAUNCH = -7,      /* the kernel launch failed */
+    QG_ERR_UNSUPPORTED = -8  /* a combination this library does not implement */
+};
+
+/* Largest batch of qgemv / qgemv_argmax. */
+#define QG_MAX_GEMV_BATCH 16
+
+/*
+ * qgemv -- batch-1 (up to QG_MAX_GEMV_BATCH) quantized matrix-vector product.
+ *   y[n][m] = sum_k w[m][k] * x[n][k],  0 <= n < batch, 0 <= m < M.
+ * Every packed weight is read once per call, dequantized in registers and
+ * never written out. (MiniCPM-V-4.6 on a Tesla C2075, section 3.3: decode
+ * reads each weight once and is bandwidth-bound; I Built an LLM Inference
+ * Engine..., "Optimization 4: Quantized Kernels": dequantization is fused
+ * into the product.)
+ *   x  float32 [batch][K];  y  float32 [batch][M] (overwritten).
+ *   1 <= M <= 2^31-1, 1 <= K <= 2^30, 1 <= batch <= QG_MAX_GEMV_BATCH.
+ */
+int qgemv(int fmt, const void *codes, const void *scales, const void *biases,
+          const float *x, float *y, int64_t M, int64_t K, int batch,
+          void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * qgemm -- prefill form: the same product over N token rows.
+ *   Y[n][m] = sum_k w[m][k] * X[n][k],  0 <= n < N.
+ * (MiniCPM-V-4.6 on a Tesla C2075, section 3.1 "Prefill projections": the
+ * prefill projection is a genuine matrix-matrix product; A 27B model on two
+ * 4GB Maxwell GPUs, "A packed Q1 prefill kernel with a narrow dispatch
+ * window": the weights may be consumed packed.)
+ *   X  float32 [N][K];  Y  float32 [N][M] (overwritten).  1 <= N <= 2^31-1.
+ *   Formats: QG_I8_ROW and QG_B1_G128 (QG_U4_G64 returns QG_ERR_UNSUPPORTED).
+ */
+int qgemm(int fmt, const void *codes, const void *scales, const void *biases,
+          const float *x, float *y, int64_t M, int64_t K, int64_t N,
+          void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * qgemv_argmax -- qgemv followed by greedy selection, fused.
+ *   logits[n][m] = y[n][m] as qgemv computes it (float32, written),
+ *   idx[n]       = the lowest m whose logits[n][m] is the maximum of row n
+ *                  (ties go to the lowest index; -0 equals +0).
+ * (Pushing the limits of legacy hardware, "Build the execution path, then
+ * share the weights": the head keeps per-tile maxima with their original
+ * indices, and greedy selection stays on the device.)
+ *   logits  float32 [batch][M] (must not be NULL);  idx int32 [batch].
+ *   Same shape limits as qgemv. Needs a workspace.
+ */
+int qgemv_argmax(int fmt, const void *codes, const void *scales,
+                 const void *biases, const float *x, float *logits,
+                 int32_t *idx, int64_t M, int64_t K, int batch,
+                 void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of device workspace the call (op, fmt, M, K, rows) needs; rows is
+ * the batch for QG_OP_GEMV / QG_OP_GEMV_ARGMAX and N for QG_OP_GEMM.
+ * Returns 0 when no workspace is needed, and also for arguments the entry
+ * point would reject (the entry point then reports the error). */
+size_t qg_workspace_bytes(int op, int fmt, int64_t M, int64_t K, int64_t rows);
+
+/* Static text for a status code. */
+const char *qg_status_str(int status);
+
+/* QG_ABI_VERSION of the built library. */
+int qg_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QG_H */

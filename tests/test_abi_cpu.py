@@ -1,0 +1,115 @@
+"""The C-ABI library on the CPU (no GPU needed): it loads, exports every
+function include/qg.h declares, reports its version and status strings, sizes
+its workspace, and rejects bad arguments on the host before anything is
+enqueued. Every call here fails validation, so none reaches the GPU."""
+import os
+import re
+
+import pytest
+
+import gemm_qgemv_amd as q
+from gemm_qgemv_amd import _binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "qg.h")
+
+A = 1 << 20   # fake, 16-byte aligned "device" addresses (never dereferenced)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(q\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert header_functions() == sorted(_binding.EXPORTS)
+
+
+def test_library_exports_every_declared_function():
+    lib = _binding.lib()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert q.qg_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+        assert q.qg_status_str(st) and q.qg_status_str(st) != "unknown status"
+    assert q.qg_status_str(12345) == "unknown status"
+
+
+def test_workspace_sizes():
+    # the greedy head needs a workspace for its keys; plain GEMV at these
+    # shapes does not
+    assert q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_U4_G64, 151936, 2048, 1) > 0
+    assert q.qg_workspace_bytes(q.QG_OP_GEMV, q.QG_U4_G64, 6144, 2048, 1) == 0
+    # invalid requests report 0 (the entry point reports the error)
+    assert q.qg_workspace_bytes(q.QG_OP_GEMV, 9, 10, 64, 1) == 0
+    assert q.qg_workspace_bytes(q.QG_OP_GEMV, q.QG_U4_G64, 10, 65, 1) == 0
+    assert q.qg_workspace_bytes(q.QG_OP_GEMV, q.QG_U4_G64, 10, 64, 17) == 0
+    assert q.qg_workspace_bytes(77, q.QG_U4_G64, 10, 64, 1) == 0
+
+
+def _err(fn, *args, **kw):
+    with pytest.raises(q.QGError) as e:
+        fn(*args, stream=0, **kw)
+    return e.value.status
+
+
+def test_bad_format():
+    assert _err(q.qgemv, 9, A, A + 4096, None, A + 8192, A + 16384, 4, 64, 1) == q.QG_ERR_FORMAT
+
+
+def test_null_pointers():
+    assert _err(q.qgemv, q.QG_I8_ROW, None, A, None, A, A, 4, 64, 1) == q.QG_ERR_NULL
+    assert _err(q.qgemv, q.QG_I8_ROW, A, A, None, A, None, 4, 64, 1) == q.QG_ERR_NULL
+    # biases are required for the affine format and forbidden for the others
+    assert _err(q.qgemv, q.QG_U4_G64, A, A + 4096, None, A + 8192, A + 16384, 4, 64, 1) == q.QG_ERR_NULL
+    assert _err(q.qgemv, q.QG_I8_ROW, A, A + 4096, A + 12288, A + 8192, A + 16384, 4, 64, 1) == q.QG_ERR_NULL
+    assert _err(q.qgemv_argmax, q.QG_U4_G64, A, A + 4096, A + 12288, A + 8192, A + 16384, None,
+                4, 64, 1) == q.QG_ERR_NULL
+
+
+def test_bad_shapes():
+    for fmt, K in ((q.QG_I8_ROW, 24), (q.QG_U4_G64, 96), (q.QG_B1_G128, 192), (q.QG_U4_G64, 0)):
+        b = A + 12288 if fmt == q.QG_U4_G64 else None
+        assert _err(q.qgemv, fmt, A, A + 4096, b, A + 8192, A + 65536, 4, K, 1) == q.QG_ERR_SHAPE
+    assert _err(q.qgemv, q.QG_I8_ROW, A, A + 4096, None, A + 8192, A + 65536, 0, 64, 1) == q.QG_ERR_SHAPE
+    assert _err(q.qgemv, q.QG_I8_ROW, A, A + 4096, None, A + 8192, A + 65536, 4, 64, 0) == q.QG_ERR_SHAPE
+    assert _err(q.qgemv, q.QG_I8_ROW, A, A + 4096, None, A + 8192, A + 65536, 4, 64, 17) == q.QG_ERR_SHAPE
+    assert _err(q.qgemm, q.QG_I8_ROW, A, A + 4096, None, A + 8192, A + 65536, 4, 64, 0) == q.QG_ERR_SHAPE
+
+
+def test_misaligned_pointers():
+    assert _err(q.qgemv, q.QG_I8_ROW, A + 4, A + 4096, None, A + 8192, A + 65536, 4, 64, 1) == q.QG_ERR_ALIGN
+    assert _err(q.qgemv, q.QG_I8_ROW, A, A + 4096, None, A + 8200, A + 65536, 4, 64, 1) == q.QG_ERR_ALIGN
+    assert _err(q.qgemv, q.QG_I8_ROW, A, A + 4096, None, A + 8192, A + 65544, 4, 64, 1) == q.QG_ERR_ALIGN
+    assert _err(q.qgemv_argmax, q.QG_I8_ROW, A, A + 4096, None, A + 8192, A + 65536, A + 90002,
+                4, 64, 1, ws=A + 131072, ws_bytes=1 << 20) == q.QG_ERR_ALIGN
+
+
+def test_workspace_too_small():
+    M, K = 151936, 2048
+    need = q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_U4_G64, M, K, 1)
+    codes, scales, biases = A, A + (1 << 28), A + (1 << 29)
+    x, y, idx, ws = A + (1 << 30), A + (1 << 31), A + (1 << 32), A + (1 << 33)
+    assert _err(q.qgemv_argmax, q.QG_U4_G64, codes, scales, biases, x, y, idx, M, K, 1,
+                ws=ws, ws_bytes=need - 1) == q.QG_ERR_WORKSPACE
+    assert _err(q.qgemv_argmax, q.QG_U4_G64, codes, scales, biases, x, y, idx, M, K, 1,
+                ws=None, ws_bytes=0) == q.QG_ERR_WORKSPACE
+
+
+def test_aliasing_outputs():
+    # y overlapping x, y overlapping the codes, idx inside y
+    assert _err(q.qgemv, q.QG_I8_ROW, A, A + 4096, None, A + 8192, A + 8192, 4, 64, 1) == q.QG_ERR_ALIAS
+    assert _err(q.qgemv, q.QG_I8_ROW, A, A + 4096, None, A + 8192, A + 128, 4, 64, 1) == q.QG_ERR_ALIAS
+    M, K = 4096, 64
+    need = q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_I8_ROW, M, K, 1)
+    base = 1 << 30
+    assert _err(q.qgemv_argmax, q.QG_I8_ROW, A, base, None, base + 65536, base + 131072,
+                base + 131072 + 64, M, K, 1, ws=base + (1 << 24), ws_bytes=need) == q.QG_ERR_ALIAS
+
+
+def test_prefill_affine_format_unsupported():
+    assert _err(q.qgemm, q.QG_U4_G64, A, A + 4096, A + 12288, A + 8192, A + 65536, 4, 64, 8) == \
+        q.QG_ERR_UNSUPPORTED

@@ -1,0 +1,299 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bar: every output finite and within 1e-5 * sum_k |w[m][k] x[n][k]| of the
+oracle's exact value; argmax indices equal to the oracle's, and equal to the
+lowest-index maximum of the float32 logits the call returned; exact-arithmetic
+inputs (power-of-two scales, small integer activations) bit-exact; repeated
+calls bit-identical; guard bands around outputs untouched.
+"""
+import numpy as np
+import pytest
+
+import gemm_qgemv_amd as q
+import oracle
+import pins
+from gemm_qgemv_amd import synth, tensors
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+PAD = 64          # guard floats on each side of every output
+CANARY = 1234.5
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "these tests need the GPU"
+    return t
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+class Out:
+    """An output buffer with guard bands."""
+
+    def __init__(self, torch, n, dtype="float32"):
+        dt = getattr(torch, dtype)
+        self.full = torch.full((n + 2 * PAD,), CANARY if dtype == "float32" else -7,
+                               dtype=dt, device="cuda")
+        self.t = self.full[PAD:PAD + n]
+
+    def check_guards(self):
+        f = self.full.cpu().numpy()
+        assert np.all(f[:PAD] == f[0]) and np.all(f[-PAD:] == f[0]), "guard band overwritten"
+
+
+def gpu_gemv(torch, w, x, argmax=False, ws_fill=None):
+    """Run qgemv (or qgemv_argmax) on device weights w for x [batch][K];
+    returns (y [batch][M] float32, idx or None)."""
+    batch = x.shape[0]
+    xd = torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
+    y = Out(torch, batch * w.M)
+    op = q.QG_OP_GEMV_ARGMAX if argmax else q.QG_OP_GEMV
+    ws = tensors.workspace(op, w.fmt, w.M, w.K, batch)
+    if ws is not None and ws_fill is not None:
+        ws.fill_(ws_fill)
+    idx = None
+    if argmax:
+        idx = Out(torch, batch, "int32")
+        q.qgemv_argmax(w.fmt, w.codes, w.scales, w.biases, xd, y.t, idx.t, w.M, w.K, batch, ws)
+    else:
+        q.qgemv(w.fmt, w.codes, w.scales, w.biases, xd, y.t, w.M, w.K, batch, ws)
+    torch.cuda.synchronize()
+    y.check_guards()
+    yh = y.t.cpu().numpy().reshape(batch, w.M)
+    ih = None
+    if argmax:
+        idx.check_guards()
+        ih = idx.t.cpu().numpy()
+    return yh, ih
+
+
+def gpu_gemm(torch, w, x):
+    N = x.shape[0]
+    xd = torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
+    y = Out(torch, N * w.M)
+    ws = tensors.workspace(q.QG_OP_GEMM, w.fmt, w.M, w.K, N)
+    q.qgemm(w.fmt, w.codes, w.scales, w.biases, xd, y.t, w.M, w.K, N, ws)
+    torch.cuda.synchronize()
+    y.check_guards()
+    return y.t.cpu().numpy().reshape(N, w.M)
+
+
+def check_bound(y, ref, absdot, what):
+    y = np.asarray(y, np.float64)
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    err = np.abs(y - ref)
+    bound = TOL * absdot
+    bad = err > bound
+    ratio = np.max(np.where(bound > 0, err / np.where(bound > 0, bound, 1), np.where(err > 0, np.inf, 0)))
+    say(f"  {what}: max err/bound = {ratio:.3g}")
+    assert not bad.any(), f"{what}: {bad.sum()} outputs outside the bound (worst ratio {ratio:.3g})"
+
+
+def check_argmax(idx, y_gpu, ref, absdot, orc, what):
+    want, gap = orc.argmax(ref)
+    lowest = np.array([int(np.argmax(r)) for r in y_gpu])   # first occurrence of the max
+    for n in range(len(idx)):
+        bound = TOL * absdot[n, want[n]]
+        margin = gap[n] / (2 * bound) if bound > 0 else np.inf
+        say(f"  {what} row {n}: idx {idx[n]} oracle {want[n]} margin {margin:.3g}")
+    assert np.array_equal(idx, lowest), f"{what}: idx is not the lowest-index max of the logits"
+    assert np.array_equal(idx, want), f"{what}: idx differs from the oracle"
+
+
+def dev(w):
+    return tensors.to_device(w)
+
+
+# ---------------------------------------------------------------------------
+# hand-worked fixtures and exact arithmetic
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", pins.hand_fixtures())
+def test_hand_fixture(torch, orc, name):
+    say(f"hand fixture {name}")
+    d, codes, scales, biases = pins.load_fixture(name)
+    w = dev(synth.QWeights(d["fmt"], d["M"], d["K"], codes, scales, biases))
+    x = np.asarray(d["x"], np.float32)
+    ref, a = orc.qgemv(d["fmt"], codes, scales, biases, x, d["M"], d["K"])
+    y, idx = gpu_gemv(torch, w, x, argmax=True)
+    check_bound(y, ref, a, name)
+    assert list(idx) == d["idx"]
+
+
+def exact_inputs(fmt, M, K, N, rng):
+    """Power-of-two scales, biases on a 2^-8 grid, integer activations in
+    [-8, 8]: every partial sum is exact in float32 at these sizes, so any
+    correct kernel, in any summation order, matches the oracle bit for bit."""
+    x = rng.integers(-8, 9, size=(N, K)).astype(np.float32)
+    if fmt == synth.I8_ROW:
+        codes = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+        scales = (2.0 ** -rng.integers(4, 8, size=M)).astype(np.float32)
+        return synth.QWeights(fmt, M, K, codes, scales, None), x
+    if fmt == synth.U4_G64:
+        codes = rng.integers(0, 256, size=(M, K // 2)).astype(np.uint8)
+        s = (2.0 ** -rng.integers(4, 8, size=(M, K // 64))).astype(np.float32)
+        b = (rng.integers(-64, 65, size=(M, K // 64)) / 256.0).astype(np.float32)
+        return synth.QWeights(fmt, M, K, codes, synth.to_bf16_bits(s), synth.to_bf16_bits(b)), x
+    codes = rng.integers(0, 256, size=(M, K // 8)).astype(np.uint8)
+    s = (2.0 ** -rng.integers(0, 8, size=(M, K // 128))).astype(np.float32)
+    return synth.QWeights(fmt, M, K, codes, synth.to_fp16_bits(s), None), x
+
+
+@pytest.mark.parametrize("fmt,M,K,N", [
+    (synth.I8_ROW, 129, 1024, 1), (synth.I8_ROW, 70, 528, 5), (synth.I8_ROW, 33, 1024, 16),
+    (synth.U4_G64, 129, 1024, 1), (synth.U4_G64, 65, 576, 3), (synth.U4_G64, 300, 1024, 8),
+    (synth.B1_G128, 129, 1024, 1), (synth.B1_G128, 17, 1152, 6), (synth.B1_G128, 257, 1024, 16),
+])
+def test_exact_arithmetic_bit_exact(torch, orc, fmt, M, K, N):
+    say(f"exact fmt={fmt} M={M} K={K} N={N}")
+    rng = np.random.default_rng([fmt, M, K, N])
+    w, x = exact_inputs(fmt, M, K, N, rng)
+    ref, _ = orc.qgemv(fmt, w.codes, w.scales, w.biases, x, M, K)
+    want = ref.astype(np.float32)
+    assert np.array_equal(want.astype(np.float64), ref), "fixture is not exact in float32"
+    y, _ = gpu_gemv(torch, dev(w), x)
+    assert np.array_equal(y, want), f"gemv not bit-exact: max diff {np.max(np.abs(y - want))}"
+    if fmt != synth.U4_G64:
+        yg = gpu_gemm(torch, dev(w), x)
+        assert np.array_equal(yg, want), "gemm not bit-exact"
+
+
+# ---------------------------------------------------------------------------
+# random inputs at small sizes: several tiles, ragged tails, every batch
+# ---------------------------------------------------------------------------
+
+SMALL = [
+    (synth.I8_ROW, 1, 16, 1), (synth.I8_ROW, 63, 1040, 2), (synth.I8_ROW, 1000, 1024, 1),
+    (synth.I8_ROW, 127, 3072, 3), (synth.I8_ROW, 129, 16384, 1), (synth.I8_ROW, 45, 20000, 2),
+    (synth.U4_G64, 1, 64, 1), (synth.U4_G64, 127, 2112, 1), (synth.U4_G64, 1187, 2048, 4),
+    (synth.U4_G64, 129, 6144, 5), (synth.U4_G64, 64, 8192, 16), (synth.U4_G64, 31, 18048, 7),
+    (synth.B1_G128, 1, 128, 1), (synth.B1_G128, 129, 5120, 1), (synth.B1_G128, 1000, 1152, 2),
+    (synth.B1_G128, 63, 17408, 1), (synth.B1_G128, 33, 2048, 16), (synth.B1_G128, 8, 640, 9),
+]
+
+
+@pytest.mark.parametrize("fmt,M,K,N", SMALL)
+def test_random_small(torch, orc, fmt, M, K, N):
+    say(f"random fmt={fmt} M={M} K={K} N={N}")
+    rng = synth.rng_for(100 + fmt, M * 7 + N)
+    w = synth.draw_weights(fmt, M, K, rng)
+    x = synth.draw_x(N, K, rng)
+    ref, a = orc.qgemv(fmt, w.codes, w.scales, w.biases, x, M, K)
+    y, idx = gpu_gemv(torch, dev(w), x, argmax=True, ws_fill=0xA5)
+    check_bound(y, ref, a, f"gemv {fmt} {M}x{K} b{N}")
+    check_argmax(idx, y, ref, a, orc, "argmax")
+    if fmt != synth.U4_G64:
+        yg = gpu_gemm(torch, dev(w), x)
+        check_bound(yg, ref, a, "gemm")
+
+
+def test_argmax_ties_and_signed_zero(torch, orc):
+    """Duplicate maximum rows (first row, last row, across workgroups, in the
+    tail), all-equal logits, and -0 against +0."""
+    say("argmax ties")
+    rng = np.random.default_rng(7)
+    M, K = 9000, 256
+    w = synth.draw_weights(synth.U4_G64, M, K, rng)
+    x = synth.draw_x(3, K, rng)
+    ref, _ = orc.qgemv(synth.U4_G64, w.codes, w.scales, w.biases, x, M, K)
+    top = int(np.argmax(ref[0]))
+    for dst in (0, M - 1, 4500, 8999 - 130):
+        for arr in (w.codes, w.scales, w.biases):
+            arr[dst] = arr[top]
+    ref, a = orc.qgemv(synth.U4_G64, w.codes, w.scales, w.biases, x, M, K)
+    y, idx = gpu_gemv(torch, dev(w), x, argmax=True)
+    check_bound(y, ref, a, "ties")
+    assert y[0, 0] == y[0, M - 1] == y[0, top], "duplicate rows must give identical logits"
+    check_argmax(idx, y, ref, a, orc, "ties")
+    assert idx[0] == 0
+    # all-equal logits: x = 0
+    y, idx = gpu_gemv(torch, dev(w), np.zeros((2, K), np.float32), argmax=True)
+    assert np.all(y == 0) and list(idx) == [0, 0]
+    # -0 against +0: zero codes with a negative scale give -0, a positive scale +0
+    M, K = 12, 64
+    codes = np.zeros((M, K), np.int8)
+    codes[[0, 1, 2, 4, 5, 6, 8, 9, 10, 11]] = -1
+    scales = np.ones(M, np.float32)
+    scales[3] = -1.0
+    wi = synth.QWeights(synth.I8_ROW, M, K, codes, scales, None)
+    y, idx = gpu_gemv(torch, dev(wi), np.ones((1, K), np.float32), argmax=True)
+    assert np.signbit(y[0, 3]) and y[0, 3] == 0 and y[0, 7] == 0 and not np.signbit(y[0, 7])
+    assert idx[0] == 3
+
+
+def test_zero_codes_give_bias_times_sum(torch, orc):
+    say("zero codes")
+    rng = np.random.default_rng(8)
+    M, K = 300, 2048
+    w = synth.draw_weights(synth.U4_G64, M, K, rng)
+    w.codes[:] = 0
+    x = synth.draw_x(2, K, rng)
+    ref, a = orc.qgemv(synth.U4_G64, w.codes, w.scales, w.biases, x, M, K)
+    y, _ = gpu_gemv(torch, dev(w), x)
+    check_bound(y, ref, a, "zero codes")
+
+
+# ---------------------------------------------------------------------------
+# the configurations at full size
+# ---------------------------------------------------------------------------
+
+GEMV_CASES = [c for c in synth.CASES if c.op != "gemm"]
+GEMM_CASES = [c for c in synth.CASES if c.op == "gemm"]
+
+
+@pytest.mark.parametrize("case", GEMV_CASES, ids=lambda c: c.name)
+def test_config_gemv_full(torch, orc, case):
+    say(f"config {case.name}")
+    w, x = synth.case_inputs(case)
+    ref, a = orc.qgemv(case.fmt, w.codes, w.scales, w.biases, x, case.M, case.K)
+    wd = dev(w)
+    argmax = case.op == "gemv_argmax"
+    y, idx = gpu_gemv(torch, wd, x, argmax=argmax)
+    check_bound(y, ref, a, case.name)
+    if argmax:
+        check_argmax(idx, y, ref, a, orc, case.name)
+    # a second call gives identical bits
+    y2, idx2 = gpu_gemv(torch, wd, x, argmax=argmax)
+    assert np.array_equal(y, y2), "repeated call differs"
+    if argmax:
+        assert np.array_equal(idx, idx2)
+
+
+def sample_pairs(N, M, rng, count=3000):
+    ns = [0, N - 1, min(15, N - 1), min(16, N - 1), min(127, N - 1), min(128, N - 1)]
+    ms = [0, M - 1, min(127, M - 1), min(128, M - 1), min(255, M - 1), min(256, M - 1)]
+    n = np.concatenate([np.repeat(ns, len(ms)), rng.integers(0, N, count)])
+    m = np.concatenate([np.tile(ms, len(ns)), rng.integers(0, M, count)])
+    return n.astype(np.int64), m.astype(np.int64)
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=lambda c: c.name)
+def test_config_gemm_sampled(torch, orc, case):
+    say(f"config {case.name}")
+    w, x = synth.case_inputs(case)
+    y = gpu_gemm(torch, dev(w), x)
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(case.variant)
+    n, m = sample_pairs(case.rows, case.M, rng)
+    ref, a = orc.qgemv_sample(case.fmt, w.codes, w.scales, w.biases, x, case.M, case.K, n, m)
+    check_bound(y[n, m], ref, a, case.name + " sampled")
+    # whole rows: prefill row n equals the matvec of x[n] (both within bound)
+    for nn in (0, case.rows // 2, case.rows - 1):
+        yv, _ = gpu_gemv(torch, dev(w), x[nn:nn + 1])
+        refr, ar = orc.qgemv(case.fmt, w.codes, w.scales, w.biases, x[nn:nn + 1], case.M, case.K)
+        check_bound(y[nn:nn + 1], refr, ar, f"{case.name} row {nn}")
+        check_bound(yv, refr, ar, f"{case.name} gemv row {nn}")
