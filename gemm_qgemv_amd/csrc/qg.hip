@@ -9,7 +9,9 @@
 #include <string.h>
 
 #include "../../include/qg.h"
+#include "gemm.hpp"
 #include "gemv.hpp"
+#include "gemv1.hpp"
 
 namespace {
 
@@ -99,6 +101,9 @@ int launch_status()
 // ---------------------------------------------------------------------------
 
 struct GemvPlan {
+    bool one;            // batch-1 kernel (8-bit / 4-bit, activations in registers)
+    int ns;              // batch-1 kernel: slices per lane
+    int64_t rows_per_wave;
     int B, R;
     int64_t kc;
     int nsplit;
@@ -112,6 +117,22 @@ struct GemvPlan {
 GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
 {
     GemvPlan pl{};
+    if (nb == 1 && fmt != QG_B1_G128 && ceil_div(K / k_per_slice(fmt), 64) <= 4) {
+        // batch 1: one wave per workgroup, each wave a contiguous run of rows
+        pl.one = true;
+        pl.ns = static_cast<int>(ceil_div(K / k_per_slice(fmt), 64));
+        pl.R = M >= 4096 ? 4 : M >= 2048 ? 2 : 1;
+        if (pl.ns >= 3 && pl.R > 2) pl.R = 2;
+        pl.rows_per_wave = round_up(ceil_div(M, 2048), pl.R);
+        pl.grid_x = ceil_div(M, pl.rows_per_wave);
+        pl.nsplit = 1;
+        if (argmax) {
+            pl.nkeys = static_cast<int>(pl.grid_x);
+            pl.keys_off = 0;
+            pl.ws_bytes = align256(static_cast<size_t>(pl.nkeys) * 8);
+        }
+        return pl;
+    }
     pl.B = nb <= 1 ? 1 : nb <= 2 ? 2 : nb <= 4 ? 4 : nb <= 8 ? 8 : 16;
     const int kps = k_per_slice(fmt);
     const bool xsum = fmt != QG_I8_ROW;
@@ -171,11 +192,52 @@ void launch_gemv_fmt(const GemvPlan &pl, const GemvParams &p, hipStream_t s)
     }
 }
 
+template <int FMT, int NS>
+void launch_gemv1_ns(const GemvPlan &pl, const qg::Gemv1Params &p, hipStream_t s)
+{
+    dim3 grid(static_cast<unsigned>(pl.grid_x));
+    switch (pl.R) {
+    case 4: hipLaunchKernelGGL((qg::gemv1_kernel<FMT, NS, 4>), grid, dim3(64), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((qg::gemv1_kernel<FMT, NS, 2>), grid, dim3(64), 0, s, p); break;
+    default: hipLaunchKernelGGL((qg::gemv1_kernel<FMT, NS, 1>), grid, dim3(64), 0, s, p); break;
+    }
+}
+
+template <int FMT>
+void launch_gemv1_fmt(const GemvPlan &pl, const qg::Gemv1Params &p, hipStream_t s)
+{
+    switch (pl.ns) {
+    case 1: launch_gemv1_ns<FMT, 1>(pl, p, s); break;
+    case 2: launch_gemv1_ns<FMT, 2>(pl, p, s); break;
+    case 3: launch_gemv1_ns<FMT, 3>(pl, p, s); break;
+    default: launch_gemv1_ns<FMT, 4>(pl, p, s); break;
+    }
+}
+
 // Enqueue one planned GEMV (+ combine, + argmax finalize).
 void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales,
               const void *biases, const float *x, float *y, int32_t *idx, int64_t M,
               int64_t K, int nb, void *ws, hipStream_t s)
 {
+    if (pl.one) {
+        qg::Gemv1Params q{};
+        q.codes = static_cast<const uint8_t *>(codes);
+        q.scales = scales;
+        q.biases = biases;
+        q.x = x;
+        q.y = y;
+        q.keys = idx ? reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + pl.keys_off) : nullptr;
+        q.M = M;
+        q.K = K;
+        q.rows_per_wave = pl.rows_per_wave;
+        q.nkeys = pl.nkeys;
+        if (fmt == QG_I8_ROW) launch_gemv1_fmt<qg::FMT_I8_ROW>(pl, q, s);
+        else launch_gemv1_fmt<qg::FMT_U4_G64>(pl, q, s);
+        if (idx)
+            hipLaunchKernelGGL(qg::argmax_finalize_kernel, dim3(1), dim3(kThreads), 0, s,
+                               static_cast<const uint64_t *>(q.keys), pl.nkeys, idx);
+        return;
+    }
     GemvParams p{};
     p.codes = static_cast<const uint8_t *>(codes);
     p.scales = scales;
@@ -242,24 +304,48 @@ int gemv_entry(int fmt, const void *codes, const void *scales, const void *biase
 }
 
 // ---------------------------------------------------------------------------
-// GEMM: token rows in chunks of 16 through the matrix-vector kernel
+// GEMM: up to 16 token rows go through the matrix-vector kernel (one pass
+// over the weights serves all rows); more rows go to the MFMA kernel.
 // ---------------------------------------------------------------------------
 
-constexpr int kGemmChunk = 16;
+constexpr int kGemmViaGemv = 16;
 
 size_t gemm_workspace(int fmt, int64_t M, int64_t K, int64_t N)
 {
-    return plan_gemv(fmt, M, K, static_cast<int>(N < kGemmChunk ? N : kGemmChunk), false).ws_bytes;
+    if (N <= kGemmViaGemv) return plan_gemv(fmt, M, K, static_cast<int>(N), false).ws_bytes;
+    return 0;
+}
+
+bool gemm_shape_ok(int64_t M, int64_t N)
+{
+    if (N <= kGemmViaGemv) return true;
+    return ceil_div(M, qg::GT_M) * ceil_div(N, qg::GT_N) <= 0x7fffffffLL;
 }
 
 void run_gemm(int fmt, const void *codes, const void *scales, const float *x, float *y,
               int64_t M, int64_t K, int64_t N, void *ws, hipStream_t s)
 {
-    for (int64_t n0 = 0; n0 < N; n0 += kGemmChunk) {
-        const int nb = static_cast<int>(N - n0 < kGemmChunk ? N - n0 : kGemmChunk);
+    if (N <= kGemmViaGemv) {
+        const int nb = static_cast<int>(N);
         const GemvPlan pl = plan_gemv(fmt, M, K, nb, false);
-        run_gemv(fmt, pl, codes, scales, nullptr, x + n0 * K, y + n0 * M, nullptr, M, K, nb, ws, s);
+        run_gemv(fmt, pl, codes, scales, nullptr, x, y, nullptr, M, K, nb, ws, s);
+        return;
     }
+    qg::GemmParams p{};
+    p.codes = static_cast<const uint8_t *>(codes);
+    p.scales = scales;
+    p.x = x;
+    p.y = y;
+    p.M = M;
+    p.K = K;
+    p.N = N;
+    p.tiles_m = static_cast<int>(ceil_div(M, qg::GT_M));
+    p.tiles_n = static_cast<int>(ceil_div(N, qg::GT_N));
+    const dim3 grid(static_cast<unsigned>(int64_t(p.tiles_m) * p.tiles_n));
+    if (fmt == QG_I8_ROW)
+        hipLaunchKernelGGL(qg::gemm_kernel<qg::FMT_I8_ROW>, grid, dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL(qg::gemm_kernel<qg::FMT_B1_G128>, grid, dim3(kThreads), 0, s, p);
 }
 
 int gemm_entry(int fmt, const void *codes, const void *scales, const void *biases,
@@ -269,7 +355,7 @@ int gemm_entry(int fmt, const void *codes, const void *scales, const void *biase
     int st = check_weights(fmt, codes, scales, biases, x, M, K);
     if (st != QG_OK) return st;
     if (!y) return QG_ERR_NULL;
-    if (N < 1 || N > kMaxN) return QG_ERR_SHAPE;
+    if (N < 1 || N > kMaxN || !gemm_shape_ok(M, N)) return QG_ERR_SHAPE;
     if (!aligned(y, kAlign)) return QG_ERR_ALIGN;
     if (fmt == QG_U4_G64) return QG_ERR_UNSUPPORTED;
     const size_t need = gemm_workspace(fmt, M, K, N);

@@ -172,6 +172,38 @@ def test_exact_arithmetic_bit_exact(torch, orc, fmt, M, K, N):
         assert np.array_equal(yg, want), "gemm not bit-exact"
 
 
+@pytest.mark.parametrize("fmt,M,K,N", [
+    (synth.I8_ROW, 129, 1024, 17), (synth.I8_ROW, 300, 1040, 130), (synth.I8_ROW, 7, 48, 257),
+    (synth.I8_ROW, 1024, 3584, 64), (synth.B1_G128, 129, 1024, 17), (synth.B1_G128, 260, 640, 300),
+    (synth.B1_G128, 5, 128, 129),
+])
+def test_exact_arithmetic_prefill_bit_exact(torch, orc, fmt, M, K, N):
+    """The matrix-core prefill path (more than 16 token rows) on exact inputs."""
+    say(f"exact prefill fmt={fmt} M={M} K={K} N={N}")
+    rng = np.random.default_rng([fmt, M, K, N, 1])
+    w, x = exact_inputs(fmt, M, K, N, rng)
+    ref, _ = orc.qgemv(fmt, w.codes, w.scales, w.biases, x, M, K)
+    want = ref.astype(np.float32)
+    assert np.array_equal(want.astype(np.float64), ref), "fixture is not exact in float32"
+    yg = gpu_gemm(torch, dev(w), x)
+    assert np.array_equal(yg, want), f"prefill not bit-exact: max diff {np.max(np.abs(yg - want))}"
+
+
+@pytest.mark.parametrize("fmt,M,K,N", [
+    (synth.I8_ROW, 1, 16, 17), (synth.I8_ROW, 127, 1040, 129), (synth.I8_ROW, 1000, 1024, 300),
+    (synth.I8_ROW, 130, 3584, 33), (synth.B1_G128, 1, 128, 40), (synth.B1_G128, 250, 5120, 131),
+    (synth.B1_G128, 129, 1152, 256),
+])
+def test_random_prefill_small(torch, orc, fmt, M, K, N):
+    say(f"random prefill fmt={fmt} M={M} K={K} N={N}")
+    rng = synth.rng_for(200 + fmt, M * 11 + N)
+    w = synth.draw_weights(fmt, M, K, rng)
+    x = synth.draw_x(N, K, rng)
+    ref, a = orc.qgemv(fmt, w.codes, w.scales, w.biases, x, M, K)
+    yg = gpu_gemm(torch, dev(w), x)
+    check_bound(yg, ref, a, f"prefill {fmt} {M}x{K} n{N}")
+
+
 # ---------------------------------------------------------------------------
 # random inputs at small sizes: several tiles, ragged tails, every batch
 # ---------------------------------------------------------------------------
