@@ -13,6 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "qg.hip")
 OUT = os.path.join(HERE, "libqg.so")
+PROBE_SRC = os.path.join(HERE, "csrc", "probe.hip")
+PROBE_OUT = os.path.join(HERE, "libqgprobe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -32,14 +34,20 @@ FLAGS = [
 
 
 def build(out: str = OUT, extra: list[str] | None = None, verbose: bool = False) -> str:
+    """Build libqg.so and the measurement-only libqgprobe.so."""
+    _hipcc(PROBE_SRC, PROBE_OUT, extra, verbose)
+    return _hipcc(SRC, out, extra, verbose)
+
+
+def _hipcc(src: str, out: str, extra: list[str] | None, verbose: bool) -> str:
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra or []), SRC, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *(extra or []), src, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed to build libqg.so")
+        raise RuntimeError(f"hipcc failed to build {os.path.basename(out)}")
     errs = [l for l in res.stderr.splitlines()
             if "warning" in l and "packed-fp32-ops" not in l]
     if errs and verbose:

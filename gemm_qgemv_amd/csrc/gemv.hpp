@@ -1,5 +1,5 @@
 // gemv.hpp -- dequantize-fused low-bit matrix-vector kernels (batch 1..16)
-// for gfx950, plus the split-K combine and the greedy-selection finalize.
+// for gfx950, plus the split-K combine and the fused greedy selection.
 //
 // Mapping. A workgroup of 4 waves owns a contiguous range of output rows and
 // one K range (one "split"). The activations of that K range are staged
@@ -23,6 +23,10 @@
 
 #include "qg_device.hpp"
 
+#ifndef QG_GREEDY_SLOTS
+#define QG_GREEDY_SLOTS 16
+#endif
+
 namespace qg {
 
 enum { FMT_I8_ROW = 1, FMT_U4_G64 = 2, FMT_B1_G128 = 3 };
@@ -39,7 +43,8 @@ struct GemvParams {
     const float *x;       // [nb][K]
     float *y;             // [nb][M] final output (used when nsplit == 1)
     float *part;          // [nsplit][nb][M] partial sums (used when nsplit > 1)
-    uint64_t *keys;       // [nb][nkeys] argmax keys, or nullptr
+    struct GreedyCtl *ctl; // greedy head control words, or nullptr
+    int32_t *idx;         // [nb] greedy indices
     int64_t M;
     int64_t K;
     int64_t x_stride;     // floats between activation rows (== K)
@@ -47,7 +52,7 @@ struct GemvParams {
     int64_t kc;           // K per split, multiple of the slice width
     int nb;               // actual batch (<= template B)
     int nsplit;
-    int nkeys;            // keys per batch row (== gridDim.x of the keyed kernel)
+    int nkeys;            // workgroups of the kernel that finishes the greedy head
 };
 
 // Chunk (float4) swizzle inside an activation plane. Lanes reading chunk
@@ -168,6 +173,51 @@ __device__ __forceinline__ uint32_t word_of(const uint4 &c, int j)
     return j == 0 ? c.x : j == 1 ? c.y : j == 2 ? c.z : c.w;
 }
 
+// Greedy selection across workgroups, without fences. wg_key[b] (b < nb,
+// in LDS) is this workgroup's best key of batch row b. The control words
+// hold one 64-bit slot per batch row and a counter of finished workgroups,
+// all zero on entry. Every workgroup folds its keys into the slots with
+// device-scope atomic maxima (performed at the device's coherence point; the
+// maximum does not depend on their order), then increments the counter; the
+// increment takes its address through the maxima's returned values, so it is
+// issued only after they have been performed. The workgroup that brings the
+// counter to nkeys therefore sees every key in the slots: it writes idx[b]
+// and puts the slots and the counter back to zero. No cache writeback is
+// needed because only atomics carry data between workgroups.
+// Must be reached by all threads of the workgroup.
+struct GreedyCtl {
+    unsigned long long slot[QG_GREEDY_SLOTS];
+    unsigned counter;
+};
+
+__device__ __forceinline__ void greedy_finish(const unsigned long long *wg_key, int nb,
+                                              GreedyCtl *ctl, int32_t *idx, int nkeys)
+{
+    __shared__ unsigned s_last;
+    if (threadIdx.x == 0) {
+        uint32_t dep = 0;
+        for (int b = 0; b < nb; ++b) {
+            const unsigned long long old = __hip_atomic_fetch_max(
+                &ctl->slot[b], wg_key[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            dep |= static_cast<uint32_t>(old) | static_cast<uint32_t>(old >> 32);
+        }
+        uint32_t zero;
+        asm volatile("v_and_b32 %0, 0, %1" : "=v"(zero) : "v"(dep));  // 0, after the maxima return
+        const unsigned t = __hip_atomic_fetch_add(&ctl->counter + zero, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (t == static_cast<unsigned>(nkeys) - 1u);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    if (threadIdx.x < nb) {
+        const unsigned long long best = __hip_atomic_exchange(
+            &ctl->slot[threadIdx.x], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        idx[threadIdx.x] = static_cast<int32_t>(argmax_key_index(best));
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&ctl->counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Main kernel. B: batch rounded up to a power of two (x rows >= nb are
 // zero in LDS and their outputs are not written). R: rows per block.
 template <int FMT, int B, int R>
@@ -198,10 +248,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
     const int64_t m_begin = static_cast<int64_t>(blockIdx.x) * p.rows_per_wg;
     const int64_t m_end = min(p.M, m_begin + p.rows_per_wg);
 
-    // value index this lane ends up owning after the transpose reduction
+    // value index this lane ends up owning after the cross-lane reduction
+    // (DPP exchanges up to 16 values, the LDS butterfly beyond)
     constexpr int P = V == 1 ? 0 : V == 2 ? 1 : V == 4 ? 2 : V == 8 ? 3 : V == 16 ? 4 : V == 32 ? 5 : 6;
-    const int own = lane >> (6 - P);
-    const bool writer = (lane & ((1 << (6 - P)) - 1)) == 0;
+    const int own = V <= 16 ? dpp_owner<V <= 16 ? V : 1>(lane) : lane >> (6 - P);
+    const bool writer = V <= 16 ? dpp_writer<V <= 16 ? V : 1>(lane)
+                                : (lane & ((1 << (6 - P)) - 1)) == 0;
     const int own_r = own / B, own_b = own % B;
     float best_v = 0.f;
     int64_t best_m = -1;
@@ -221,7 +273,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
                 if (m < m_end)
                     c[r] = *reinterpret_cast<const uint4 *>(p.codes + m * row_bytes + gslice * 16);
             }
-            if (FMT == FMT_I8_ROW) {
+            if constexpr (FMT == FMT_I8_ROW) {
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
                     const float4 *xp = xl + b * pc;
@@ -233,7 +285,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
                             acc[r * B + b] = dot_i8x4(word_of(c[r], j), xv, acc[r * B + b]);
                     }
                 }
-            } else if (FMT == FMT_U4_G64) {
+            } else if constexpr (FMT == FMT_U4_G64) {
                 float s[R], bi[R];
                 const uint16_t *sp = static_cast<const uint16_t *>(p.scales);
                 const uint16_t *bp = static_cast<const uint16_t *>(p.biases);
@@ -294,7 +346,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
             }
         }
 
-        wave_transpose_reduce<V>(acc, lane);
+        if constexpr (V <= 16) wave_reduce_dpp<V>(acc, lane);
+        else wave_transpose_reduce<V>(acc, lane);
 
         if (writer) {
             const int64_t m = rb + own_r;
@@ -315,7 +368,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
         }
     }
 
-    if (p.keys != nullptr && p.nsplit == 1) {
+    if (p.ctl != nullptr && p.nsplit == 1) {
         __shared__ unsigned long long wg_key[B];
         __syncthreads();
         if (threadIdx.x < B) wg_key[threadIdx.x] = 0ull;
@@ -324,8 +377,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
             atomicMax(&wg_key[own_b], static_cast<unsigned long long>(
                                           argmax_key(best_v, static_cast<uint32_t>(best_m))));
         __syncthreads();
-        if (threadIdx.x < p.nb)
-            p.keys[static_cast<int64_t>(threadIdx.x) * p.nkeys + blockIdx.x] = wg_key[threadIdx.x];
+        greedy_finish(wg_key, p.nb, p.ctl, p.idx, p.nkeys);
     }
 }
 
@@ -348,30 +400,13 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvParams p)
             const uint64_t key = argmax_key(v, static_cast<uint32_t>(m));
             best = key > best ? key : best;
         }
-        if (p.keys != nullptr)
+        if (p.ctl != nullptr)
             atomicMax(&wg_key[b], static_cast<unsigned long long>(best));
     }
-    if (p.keys != nullptr) {
+    if (p.ctl != nullptr) {
         __syncthreads();
-        if (threadIdx.x < p.nb)
-            p.keys[static_cast<int64_t>(threadIdx.x) * p.nkeys + blockIdx.x] = wg_key[threadIdx.x];
+        greedy_finish(wg_key, p.nb, p.ctl, p.idx, p.nkeys);
     }
-}
-
-// idx[b] = index of the largest key of batch row b (one workgroup per row).
-__global__ __launch_bounds__(256) void argmax_finalize_kernel(const uint64_t *keys, int nkeys,
-                                                              int32_t *idx)
-{
-    __shared__ unsigned long long best;
-    if (threadIdx.x == 0) best = 0ull;
-    __syncthreads();
-    const uint64_t *row = keys + static_cast<int64_t>(blockIdx.x) * nkeys;
-    uint64_t mine = 0;
-    for (int i = threadIdx.x; i < nkeys; i += blockDim.x)
-        mine = row[i] > mine ? row[i] : mine;
-    atomicMax(&best, static_cast<unsigned long long>(mine));
-    __syncthreads();
-    if (threadIdx.x == 0) idx[blockIdx.x] = static_cast<int32_t>(argmax_key_index(best));
 }
 
 }  // namespace qg

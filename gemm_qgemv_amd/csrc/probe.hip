@@ -1,0 +1,57 @@
+// probe.hip -- libqgprobe: two plain streaming kernels used only to measure
+// the machine, never by the product path.
+//   qg_probe_read  reads `bytes` with 16-byte loads (grid-stride, 256 threads
+//                  per workgroup) and writes one word per workgroup: the
+//                  achievable HBM read rate for a given size.
+//   qg_probe_copy  copies `bytes` with 16-byte loads and stores: a kernel of
+//                  known traffic for calibrating the FETCH_SIZE / WRITE_SIZE
+//                  counters.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+__global__ __launch_bounds__(256) void qg_probe_read_kernel(const uint4 *p, int64_t n, uint32_t *out)
+{
+    uint32_t acc = 0;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const uint4 v = p[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    // keep the loads: one word per workgroup (xor over lanes via LDS atomics)
+    __shared__ uint32_t s;
+    if (threadIdx.x == 0) s = 0;
+    __syncthreads();
+    atomicXor(&s, acc);
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void qg_probe_copy_kernel(const uint4 *src, uint4 *dst, int64_t n)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+        dst[i] = src[i];
+}
+
+extern "C" {
+
+// out must hold `grid` words. bytes must be a multiple of 16; pointers 16-byte aligned.
+int qg_probe_read(const void *p, int64_t bytes, uint32_t *out, int grid, hipStream_t stream)
+{
+    if (!p || !out || bytes < 16 || bytes % 16 || grid < 1) return -1;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(qg_probe_read_kernel, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const uint4 *>(p), bytes / 16, out);
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+int qg_probe_copy(const void *src, void *dst, int64_t bytes, int grid, hipStream_t stream)
+{
+    if (!src || !dst || bytes < 16 || bytes % 16 || grid < 1) return -1;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(qg_probe_copy_kernel, dim3(grid), dim3(256), 0, stream,
+                       static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+}  // extern "C"

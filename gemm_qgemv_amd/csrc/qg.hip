@@ -100,9 +100,30 @@ int launch_status()
 // GEMV plan: a pure function of (fmt, M, K, batch, argmax)
 // ---------------------------------------------------------------------------
 
+// Batch-1 kernel tuning (compile-time; the plan is a pure function of the
+// call's shape).
+#ifndef QG_GEMV1_WAVES
+#define QG_GEMV1_WAVES 2048   // waves the rows are spread over (at most)
+#endif
+#ifndef QG_GEMV1_NT
+#define QG_GEMV1_NT 1         // non-temporal weight loads (streamed once)
+#endif
+#ifndef QG_GEMV1_R
+#define QG_GEMV1_R 4          // rows per block when K fits in one or two slices per lane
+#endif
+#ifndef QG_GEMV1_MINWAVES
+#define QG_GEMV1_MINWAVES 1024  // fewer rows per block until this many waves
+#endif
+
+// Workspace: the first 256 bytes are control words (the greedy head's
+// workgroup counter) that every call leaves at zero; the rest is scratch.
+constexpr size_t kCtlBytes = 256;
+static_assert(sizeof(qg::GreedyCtl) <= kCtlBytes, "control words exceed their area");
+
 struct GemvPlan {
     bool one;            // batch-1 kernel (8-bit / 4-bit, activations in registers)
     int ns;              // batch-1 kernel: slices per lane
+    bool full;           // batch-1 kernel: every lane owns all NS slices
     int64_t rows_per_wave;
     int B, R;
     int64_t kc;
@@ -111,25 +132,27 @@ struct GemvPlan {
     size_t lds_bytes;
     int64_t comb_rows_per_wg, comb_grid;
     int nkeys;
-    size_t part_off, keys_off, ws_bytes;
+    size_t part_off, ws_bytes;
 };
 
 GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
 {
     GemvPlan pl{};
-    if (nb == 1 && fmt != QG_B1_G128 && ceil_div(K / k_per_slice(fmt), 64) <= 4) {
-        // batch 1: one wave per workgroup, each wave a contiguous run of rows
+    const int64_t S = K / k_per_slice(fmt);
+    if (nb == 1 && fmt != QG_B1_G128 && ceil_div(S, 64) <= 4) {
+        // batch 1: workgroups of 4 independent waves, each wave a
+        // contiguous run of rows
         pl.one = true;
-        pl.ns = static_cast<int>(ceil_div(K / k_per_slice(fmt), 64));
-        pl.R = M >= 4096 ? 4 : M >= 2048 ? 2 : 1;
-        if (pl.ns >= 3 && pl.R > 2) pl.R = 2;
-        pl.rows_per_wave = round_up(ceil_div(M, 2048), pl.R);
-        pl.grid_x = ceil_div(M, pl.rows_per_wave);
+        pl.ns = static_cast<int>(ceil_div(S, 64));
+        pl.full = S % 64 == 0;
+        pl.R = pl.ns >= 3 ? 2 : QG_GEMV1_R;
+        while (pl.R > 1 && ceil_div(M, pl.R) < QG_GEMV1_MINWAVES) pl.R /= 2;
+        pl.rows_per_wave = round_up(ceil_div(M, QG_GEMV1_WAVES), pl.R);
+        pl.grid_x = ceil_div(ceil_div(M, pl.rows_per_wave), 4);
         pl.nsplit = 1;
         if (argmax) {
             pl.nkeys = static_cast<int>(pl.grid_x);
-            pl.keys_off = 0;
-            pl.ws_bytes = align256(static_cast<size_t>(pl.nkeys) * 8);
+            pl.ws_bytes = kCtlBytes;
         }
         return pl;
     }
@@ -153,19 +176,16 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
     const int64_t pf = (pl.kc + 31) / 32 * 32;
     const int64_t xsf = xsum ? (pl.kc / kps + 3) / 4 * 4 : 0;
     pl.lds_bytes = static_cast<size_t>(pl.B * (pf + xsf) * 4);
-    size_t off = 0;
+    // scratch (partial sums, keys) always starts after the control words
+    size_t off = kCtlBytes;
     if (pl.nsplit > 1) {
         pl.comb_rows_per_wg = round_up(ceil_div(M, 1024), 256);
         pl.comb_grid = ceil_div(M, pl.comb_rows_per_wg);
         pl.part_off = off;
         off = align256(off + static_cast<size_t>(pl.nsplit) * nb * M * 4);
     }
-    if (argmax) {
-        pl.nkeys = static_cast<int>(pl.nsplit > 1 ? pl.comb_grid : pl.grid_x);
-        pl.keys_off = off;
-        off = align256(off + static_cast<size_t>(nb) * pl.nkeys * 8);
-    }
-    pl.ws_bytes = off;
+    if (argmax) pl.nkeys = static_cast<int>(pl.nsplit > 1 ? pl.comb_grid : pl.grid_x);
+    pl.ws_bytes = (off > kCtlBytes || argmax) ? off : 0;
     return pl;
 }
 
@@ -192,15 +212,24 @@ void launch_gemv_fmt(const GemvPlan &pl, const GemvParams &p, hipStream_t s)
     }
 }
 
+template <int FMT, int NS, bool FULL>
+void launch_gemv1_full(const GemvPlan &pl, const qg::Gemv1Params &p, hipStream_t s)
+{
+    constexpr bool NT = QG_GEMV1_NT != 0;
+    dim3 grid(static_cast<unsigned>(pl.grid_x));
+    switch (pl.R) {
+    case 8: hipLaunchKernelGGL((qg::gemv1_kernel<FMT, NS, 8, FULL, NT>), grid, dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((qg::gemv1_kernel<FMT, NS, 4, FULL, NT>), grid, dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((qg::gemv1_kernel<FMT, NS, 2, FULL, NT>), grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((qg::gemv1_kernel<FMT, NS, 1, FULL, NT>), grid, dim3(256), 0, s, p); break;
+    }
+}
+
 template <int FMT, int NS>
 void launch_gemv1_ns(const GemvPlan &pl, const qg::Gemv1Params &p, hipStream_t s)
 {
-    dim3 grid(static_cast<unsigned>(pl.grid_x));
-    switch (pl.R) {
-    case 4: hipLaunchKernelGGL((qg::gemv1_kernel<FMT, NS, 4>), grid, dim3(64), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((qg::gemv1_kernel<FMT, NS, 2>), grid, dim3(64), 0, s, p); break;
-    default: hipLaunchKernelGGL((qg::gemv1_kernel<FMT, NS, 1>), grid, dim3(64), 0, s, p); break;
-    }
+    if (pl.full) launch_gemv1_full<FMT, NS, true>(pl, p, s);
+    else launch_gemv1_full<FMT, NS, false>(pl, p, s);
 }
 
 template <int FMT>
@@ -214,7 +243,8 @@ void launch_gemv1_fmt(const GemvPlan &pl, const qg::Gemv1Params &p, hipStream_t 
     }
 }
 
-// Enqueue one planned GEMV (+ combine, + argmax finalize).
+// Enqueue one planned GEMV (+ split-K combine). The greedy selection
+// finishes inside the last kernel.
 void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales,
               const void *biases, const float *x, float *y, int32_t *idx, int64_t M,
               int64_t K, int nb, void *ws, hipStream_t s)
@@ -226,16 +256,13 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         q.biases = biases;
         q.x = x;
         q.y = y;
-        q.keys = idx ? reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + pl.keys_off) : nullptr;
+        q.ctl = idx ? static_cast<qg::GreedyCtl *>(ws) : nullptr;
+        q.idx = idx;
         q.M = M;
         q.K = K;
         q.rows_per_wave = pl.rows_per_wave;
-        q.nkeys = pl.nkeys;
         if (fmt == QG_I8_ROW) launch_gemv1_fmt<qg::FMT_I8_ROW>(pl, q, s);
         else launch_gemv1_fmt<qg::FMT_U4_G64>(pl, q, s);
-        if (idx)
-            hipLaunchKernelGGL(qg::argmax_finalize_kernel, dim3(1), dim3(kThreads), 0, s,
-                               static_cast<const uint64_t *>(q.keys), pl.nkeys, idx);
         return;
     }
     GemvParams p{};
@@ -245,7 +272,8 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
     p.x = x;
     p.y = y;
     p.part = pl.nsplit > 1 ? reinterpret_cast<float *>(static_cast<char *>(ws) + pl.part_off) : nullptr;
-    p.keys = idx ? reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + pl.keys_off) : nullptr;
+    p.ctl = idx ? static_cast<qg::GreedyCtl *>(ws) : nullptr;
+    p.idx = idx;
     p.M = M;
     p.K = K;
     p.x_stride = K;
@@ -263,9 +291,6 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         hipLaunchKernelGGL(qg::gemv_combine_kernel, dim3(static_cast<unsigned>(pl.comb_grid)),
                            dim3(kThreads), 0, s, c);
     }
-    if (idx)
-        hipLaunchKernelGGL(qg::argmax_finalize_kernel, dim3(nb), dim3(kThreads), 0, s,
-                           static_cast<const uint64_t *>(p.keys), pl.nkeys, idx);
 }
 
 int gemv_entry(int fmt, const void *codes, const void *scales, const void *biases,

@@ -83,4 +83,107 @@ __device__ __forceinline__ void wave_transpose_reduce(float (&vals)[V], int lane
     }
 }
 
+// ---------------------------------------------------------------------------
+// Cross-lane sums without LDS: DPP and the gfx950 permlane swaps.
+//
+// pair_sum<S>(x) adds to x the value of another lane at exchange step S:
+//   S=0  DPP quad_perm [1,0,3,2]        lane ^ 1
+//   S=1  DPP quad_perm [2,3,0,1]        lane ^ 2
+//   S=2  DPP row_ror:4                  lane rotated by 4 within its 16-lane row
+//   S=3  DPP row_ror:8                  lane rotated by 8 within its 16-lane row
+//   S=4  v_permlane16_swap              lane ^ 16
+//   S=5  v_permlane32_swap              lane ^ 32
+// S=0,1,4,5 pair each lane with its xor partner. S=2 followed by S=3 sums
+// the four lanes that differ only in bits 2 and 3 (as a cyclic sum), so the
+// two are only ever used together, on values that do not depend on those
+// bits. The swap steps return both halves of the exchange; their sum is the
+// lane's value plus its partner's on every lane.
+// ---------------------------------------------------------------------------
+
+template <int S>
+__device__ __forceinline__ float pair_sum(float x)
+{
+    if constexpr (S <= 3) {
+        constexpr int ctrl = S == 0 ? 0xB1 : S == 1 ? 0x4E : S == 2 ? 0x124 : 0x128;
+        return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, false));
+    } else if constexpr (S == 4) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+}
+
+// Exchange steps used to halve the value count: partners must hold the same
+// value indices, so only the xor steps (bits 0, 1, 4, 5) qualify. The other
+// steps then sum the single remaining value.
+template <int V> struct Halving;
+template <> struct Halving<1>  { static constexpr int n = 0; static constexpr int bits[1] = {0}; };
+template <> struct Halving<2>  { static constexpr int n = 1; static constexpr int bits[1] = {0}; };
+template <> struct Halving<4>  { static constexpr int n = 2; static constexpr int bits[2] = {0, 1}; };
+template <> struct Halving<8>  { static constexpr int n = 3; static constexpr int bits[3] = {0, 1, 4}; };
+template <> struct Halving<16> { static constexpr int n = 4; static constexpr int bits[4] = {0, 1, 4, 5}; };
+
+template <int V>
+__host__ __device__ constexpr int halving_mask()
+{
+    int m = 0;
+    for (int h = 0; h < Halving<V>::n; ++h) m |= 1 << Halving<V>::bits[h];
+    return m;
+}
+
+template <int V, int H>
+__device__ __forceinline__ void halving_step(float (&v)[V], int lane)
+{
+    if constexpr (H < Halving<V>::n) {
+        constexpr int S = Halving<V>::bits[H];
+        constexpr int n = V >> H;
+        const bool upper = (lane >> S) & 1;
+#pragma unroll
+        for (int i = 0; i < n / 2; ++i) {
+            const float lo = pair_sum<S>(v[i]);
+            const float hi = pair_sum<S>(v[i + n / 2]);
+            v[i] = upper ? hi : lo;
+        }
+        halving_step<V, H + 1>(v, lane);
+    }
+}
+
+template <int V, int S>
+__device__ __forceinline__ void plain_steps(float &x)
+{
+    if constexpr (S <= 5) {
+        if constexpr (((halving_mask<V>() >> S) & 1) == 0) x = pair_sum<S>(x);
+        plain_steps<V, S + 1>(x);
+    }
+}
+
+// Reduce V <= 16 per-lane values across the wave. On return v[0] of lane l
+// holds the total of value index dpp_owner<V>(l); lanes with
+// dpp_writer<V>(l) true hold V distinct indices, one each. The order of the
+// additions is fixed and the same for every value index.
+template <int V>
+__device__ __forceinline__ void wave_reduce_dpp(float (&v)[V], int lane)
+{
+    halving_step<V, 0>(v, lane);
+    plain_steps<V, 0>(v[0]);
+}
+
+template <int V>
+__device__ __forceinline__ int dpp_owner(int lane)
+{
+    int own = 0;
+#pragma unroll
+    for (int h = 0; h < Halving<V>::n; ++h)
+        own += ((lane >> Halving<V>::bits[h]) & 1) * (V >> (h + 1));
+    return own;
+}
+
+template <int V>
+__device__ __forceinline__ bool dpp_writer(int lane)
+{
+    return (lane & (63 & ~halving_mask<V>())) == 0;
+}
+
 }  // namespace qg

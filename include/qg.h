@@ -64,9 +64,14 @@
  *               served fails before changing live state.)
  *   Threads     The library keeps no mutable state; calls are reentrant.
  *               Calls that share a workspace must not overlap in time.
- *   Workspace   `ws` is device scratch of at least qg_workspace_bytes(...)
+ *   Workspace   `ws` is device memory of at least qg_workspace_bytes(...)
  *               bytes for the same (op, fmt, M, K, rows); it may be NULL
- *               when that size is 0. Its contents on entry do not matter.
+ *               when that size is 0. Its first QG_WS_CONTROL_BYTES bytes are
+ *               control words (the greedy head counts finished workgroups
+ *               there): they must be zero before the first call that uses the
+ *               workspace, and every call leaves them zero again, so one
+ *               zero-filled workspace serves any sequence of calls. The rest
+ *               is scratch whose contents on entry do not matter.
  */
 #ifndef QG_H
 #define QG_H
@@ -104,6 +109,9 @@ enum {
     QG_ERR_LAUNCH = -7,      /* the kernel launch failed */
     QG_ERR_UNSUPPORTED = -8  /* a combination this library does not implement */
 };
+
+/* Control words at the start of every workspace (see Workspace above). */
+#define QG_WS_CONTROL_BYTES 256
 
 /* Largest batch of qgemv / qgemv_argmax. */
 #define QG_MAX_GEMV_BATCH 16

@@ -39,9 +39,12 @@ def test_version_and_status_strings():
 
 
 def test_workspace_sizes():
-    # the greedy head needs a workspace for its keys; plain GEMV at these
-    # shapes does not
-    assert q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_U4_G64, 151936, 2048, 1) > 0
+    # the greedy head needs a workspace (control words + keys); plain GEMV at
+    # these shapes does not
+    assert q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_U4_G64, 151936, 2048, 1) > \
+        q.QG_WS_CONTROL_BYTES
+    assert q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_U4_G64, 151936, 2048, 8) > \
+        q.QG_WS_CONTROL_BYTES
     assert q.qg_workspace_bytes(q.QG_OP_GEMV, q.QG_U4_G64, 6144, 2048, 1) == 0
     # invalid requests report 0 (the entry point reports the error)
     assert q.qg_workspace_bytes(q.QG_OP_GEMV, 9, 10, 64, 1) == 0

@@ -64,7 +64,7 @@ def gpu_gemv(torch, w, x, argmax=False, ws_fill=None):
     op = q.QG_OP_GEMV_ARGMAX if argmax else q.QG_OP_GEMV
     ws = tensors.workspace(op, w.fmt, w.M, w.K, batch)
     if ws is not None and ws_fill is not None:
-        ws.fill_(ws_fill)
+        ws[q.QG_WS_CONTROL_BYTES:].fill_(ws_fill)   # scratch may hold anything
     idx = None
     if argmax:
         idx = Out(torch, batch, "int32")
@@ -78,6 +78,9 @@ def gpu_gemv(torch, w, x, argmax=False, ws_fill=None):
     if argmax:
         idx.check_guards()
         ih = idx.t.cpu().numpy()
+    if ws is not None:
+        ctl = ws[:q.QG_WS_CONTROL_BYTES].cpu().numpy()
+        assert not ctl.any(), "control words not left at zero"
     return yh, ih
 
 
@@ -329,3 +332,79 @@ def test_config_gemm_sampled(torch, orc, case):
         refr, ar = orc.qgemv(case.fmt, w.codes, w.scales, w.biases, x[nn:nn + 1], case.M, case.K)
         check_bound(y[nn:nn + 1], refr, ar, f"{case.name} row {nn}")
         check_bound(yv, refr, ar, f"{case.name} gemv row {nn}")
+
+
+# ---------------------------------------------------------------------------
+# one workspace across many calls, and HIP graph replay
+# ---------------------------------------------------------------------------
+
+def test_shared_workspace_sequence(torch, orc):
+    """One zero-filled workspace (sized for the largest call) serves a
+    sequence of greedy-head calls of different shapes and batches; the
+    control words return to zero after each."""
+    say("shared workspace")
+    shapes = [(synth.U4_G64, 5000, 2048, 1), (synth.U4_G64, 3000, 1024, 8),
+              (synth.I8_ROW, 7000, 1024, 1), (synth.B1_G128, 2000, 1280, 3),
+              (synth.U4_G64, 5000, 2048, 1)]
+    need = max(q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, f, M, K, n) for f, M, K, n in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, (fmt, M, K, n) in enumerate(shapes):
+        rng = synth.rng_for(300, i)
+        w = synth.draw_weights(fmt, M, K, rng)
+        x = synth.draw_x(n, K, rng)
+        wd = dev(w)
+        xd = torch.from_numpy(x).cuda()
+        y = torch.empty(n * M, device="cuda")
+        idx = torch.empty(n, dtype=torch.int32, device="cuda")
+        q.qgemv_argmax(fmt, wd.codes, wd.scales, wd.biases, xd, y, idx, M, K, n, ws)
+        torch.cuda.synchronize()
+        ref, a = orc.qgemv(fmt, w.codes, w.scales, w.biases, x, M, K)
+        yh = y.cpu().numpy().reshape(n, M)
+        check_bound(yh, ref, a, f"call {i}")
+        check_argmax(idx.cpu().numpy(), yh, ref, a, orc, f"call {i}")
+        assert not ws[:q.QG_WS_CONTROL_BYTES].cpu().numpy().any()
+
+
+def test_graph_replay_matches_eager(torch, orc):
+    """A HIP graph holding a greedy-head call, a matvec and a prefill call,
+    replayed several times with eager work and synchronizations between
+    replays: every replay equals the eager result bit for bit."""
+    say("graph replay")
+    rng = synth.rng_for(301, 0)
+    wu = synth.draw_weights(synth.U4_G64, 20000, 2048, rng)
+    wi = synth.draw_weights(synth.I8_ROW, 3000, 1024, rng)
+    xu = torch.from_numpy(synth.draw_x(1, 2048, rng)).cuda()
+    xi = torch.from_numpy(synth.draw_x(200, 1024, rng)).cuda()
+    du, di = dev(wu), dev(wi)
+    logits = torch.empty(20000, device="cuda")
+    idx = torch.empty(1, dtype=torch.int32, device="cuda")
+    yv = torch.empty(3000, device="cuda")
+    yg = torch.empty(200 * 3000, device="cuda")
+    ws = tensors.workspace(q.QG_OP_GEMV_ARGMAX, wu.fmt, 20000, 2048, 1)
+    s = torch.cuda.Stream()
+
+    def work(stream):
+        q.qgemv_argmax(wu.fmt, du.codes, du.scales, du.biases, xu, logits, idx, 20000, 2048, 1, ws,
+                       stream=stream)
+        q.qgemv(wi.fmt, di.codes, di.scales, None, xi[:1], yv, 3000, 1024, 1, stream=stream)
+        q.qgemm(wi.fmt, di.codes, di.scales, None, xi, yg, 3000, 1024, 200, stream=stream)
+
+    work(s)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (logits, idx, yv, yg)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        work(s)
+    for rep in range(4):
+        for t in (logits, yv, yg):
+            t.fill_(float("nan"))
+        idx.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((logits, idx, yv, yg), want):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager result"
+        # eager work between replays
+        work(s)
+        torch.cuda.synchronize()
+    assert not ws[:q.QG_WS_CONTROL_BYTES].cpu().numpy().any()
