@@ -190,6 +190,50 @@ struct GreedyCtl {
     unsigned counter;
 };
 
+// Control words of a workspace: the greedy head's slots and counter, then
+// one counter per row tile for the fused split-K combine.
+constexpr int kCtlBytes = 4096;
+constexpr int kCtlTileOffset = 256;
+constexpr int kCtlTileCounters = (kCtlBytes - kCtlTileOffset) / 4;
+
+__device__ __forceinline__ unsigned *tile_counters(GreedyCtl *ctl)
+{
+    return reinterpret_cast<unsigned *>(reinterpret_cast<char *>(ctl) + kCtlTileOffset);
+}
+
+// Fused split-K combine without fences, used when several workgroups own
+// the same rows, each for a different chunk of K. splitk_put stores one
+// partial sum with a returning device-scope atomic exchange (performed at
+// the device's coherence point) and waits for its return; splitk_arrive then
+// counts the workgroup in on its row tile's counter (zero on entry), so the
+// count moves only after every partial of the workgroup is in place. The
+// workgroup that completes the count reads all partials back with
+// device-scope atomic loads, in split order (splitk_get), and puts the
+// counter back to zero. All threads of the workgroup call splitk_arrive.
+__device__ __forceinline__ void splitk_put(float *dst, float v)
+{
+    const float old = __hip_atomic_exchange(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" ::"v"(old));   // the exchange has returned
+}
+
+__device__ __forceinline__ float splitk_get(const float *src)
+{
+    return __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool splitk_arrive(unsigned *counter, int nsplit)
+{
+    __shared__ unsigned s_last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned t = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (t == static_cast<unsigned>(nsplit) - 1u);
+        if (s_last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    return s_last != 0;
+}
+
 __device__ __forceinline__ void greedy_finish(const unsigned long long *wg_key, int nb,
                                               GreedyCtl *ctl, int32_t *idx, int nkeys)
 {
@@ -274,46 +318,96 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
                     c[r] = *reinterpret_cast<const uint4 *>(p.codes + m * row_bytes + gslice * 16);
             }
             if constexpr (FMT == FMT_I8_ROW) {
+                // each dword of codes is converted once and used for every
+                // activation row
 #pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    const float4 *xp = xl + b * pc;
+                for (int j = 0; j < 4; ++j) {
+                    float qv[R][4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float4 xv = xp[swz<CPS>(t * CPS + j)];
+                    for (int r = 0; r < R; ++r) {
+                        const uint32_t d = word_of(c[r], j);
+                        qv[r][0] = static_cast<float>(static_cast<int8_t>(d & 0xff));
+                        qv[r][1] = static_cast<float>(static_cast<int8_t>((d >> 8) & 0xff));
+                        qv[r][2] = static_cast<float>(static_cast<int8_t>((d >> 16) & 0xff));
+                        qv[r][3] = static_cast<float>(static_cast<int8_t>(d >> 24));
+                    }
 #pragma unroll
-                        for (int r = 0; r < R; ++r)
-                            acc[r * B + b] = dot_i8x4(word_of(c[r], j), xv, acc[r * B + b]);
+                    for (int b = 0; b < B; ++b) {
+                        const float4 xv = xl[b * pc + swz<CPS>(t * CPS + j)];
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            float a = acc[r * B + b];
+                            a = fmaf(qv[r][0], xv.x, a);
+                            a = fmaf(qv[r][1], xv.y, a);
+                            a = fmaf(qv[r][2], xv.z, a);
+                            a = fmaf(qv[r][3], xv.w, a);
+                            acc[r * B + b] = a;
+                        }
                     }
                 }
             } else if constexpr (FMT == FMT_U4_G64) {
-                float s[R], bi[R];
+                float sc[R], bi[R];
                 const uint16_t *sp = static_cast<const uint16_t *>(p.scales);
                 const uint16_t *bp = static_cast<const uint16_t *>(p.biases);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const int64_t m = rb + r;
                     const int64_t gi = (m < m_end ? m : m_begin) * (p.K / 64) + gslice / 2;
-                    s[r] = bf16_bits_to_f32(sp[gi]);
+                    sc[r] = bf16_bits_to_f32(sp[gi]);
                     bi[r] = bf16_bits_to_f32(bp[gi]);
                 }
+                // dot[r][b] over this slice; each dword of codes is converted
+                // once (low nibbles in place, high nibbles as 16*q against
+                // activations pre-divided by 16) and used for every row b
+                float dot[R][B];
 #pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    const float4 *xp = xl + b * pc;
-                    float dot[R];
+                for (int r = 0; r < R; ++r)
 #pragma unroll
-                    for (int r = 0; r < R; ++r) dot[r] = 0.f;
+                    for (int b = 0; b < B; ++b) dot[r][b] = 0.f;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < 4; ++j) {
+                    float qv[R][8];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const uint32_t d = word_of(c[r], j);
+                        uint32_t lo, hi;
+                        asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(d));
+                        asm("v_and_b32 %0, 0xf0f0f0f0, %1" : "=v"(hi) : "v"(d));
+                        qv[r][0] = static_cast<float>(lo & 0xff);
+                        qv[r][1] = static_cast<float>(hi & 0xff);
+                        qv[r][2] = static_cast<float>((lo >> 8) & 0xff);
+                        qv[r][3] = static_cast<float>((hi >> 8) & 0xff);
+                        qv[r][4] = static_cast<float>((lo >> 16) & 0xff);
+                        qv[r][5] = static_cast<float>((hi >> 16) & 0xff);
+                        qv[r][6] = static_cast<float>(lo >> 24);
+                        qv[r][7] = static_cast<float>(hi >> 24);
+                    }
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        const float4 *xp = xl + b * pc;
                         const float4 xa = xp[swz<CPS>(t * CPS + 2 * j)];
                         const float4 xb = xp[swz<CPS>(t * CPS + 2 * j + 1)];
 #pragma unroll
-                        for (int r = 0; r < R; ++r)
-                            dot[r] = dot_u4x8(word_of(c[r], j), xa, xb, dot[r]);
+                        for (int r = 0; r < R; ++r) {
+                            float a = dot[r][b];
+                            a = fmaf(qv[r][0], xa.x, a);
+                            a = fmaf(qv[r][1], xa.y, a);
+                            a = fmaf(qv[r][2], xa.z, a);
+                            a = fmaf(qv[r][3], xa.w, a);
+                            a = fmaf(qv[r][4], xb.x, a);
+                            a = fmaf(qv[r][5], xb.y, a);
+                            a = fmaf(qv[r][6], xb.z, a);
+                            a = fmaf(qv[r][7], xb.w, a);
+                            dot[r][b] = a;
+                        }
                     }
+                }
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
                     const float xsum = xs[b * xsp + t];
 #pragma unroll
                     for (int r = 0; r < R; ++r)
-                        acc[r * B + b] = fmaf(s[r], dot[r], fmaf(bi[r], xsum, acc[r * B + b]));
+                        acc[r * B + b] = fmaf(sc[r], dot[r][b], fmaf(bi[r], xsum, acc[r * B + b]));
                 }
             } else {  // FMT_B1_G128
                 float s[R];

@@ -12,6 +12,7 @@
 #include "gemm.hpp"
 #include "gemv.hpp"
 #include "gemv1.hpp"
+#include "gemv_b1.hpp"
 
 namespace {
 
@@ -20,8 +21,10 @@ using qg::GemvParams;
 constexpr int64_t kMaxM = 0x7fffffffLL;
 constexpr int64_t kMaxK = int64_t(1) << 30;
 constexpr int64_t kMaxN = 0x7fffffffLL;
-// Dynamic LDS a GEMV workgroup may use for its activation tile.
-constexpr int64_t kLdsBudget = 60 * 1024;
+// Dynamic LDS a GEMV workgroup may use for its activation tile (gfx950 has
+// 160 KiB per compute unit; this leaves room for two workgroups' worth of
+// smaller tiles or one large one).
+constexpr int64_t kLdsBudget = 96 * 1024;
 constexpr int64_t kAlign = 16;
 constexpr int kThreads = 256;
 
@@ -117,10 +120,15 @@ int launch_status()
 
 // Workspace: the first 256 bytes are control words (the greedy head's
 // workgroup counter) that every call leaves at zero; the rest is scratch.
-constexpr size_t kCtlBytes = 256;
-static_assert(sizeof(qg::GreedyCtl) <= kCtlBytes, "control words exceed their area");
+constexpr size_t kCtlBytes = qg::kCtlBytes;
+static_assert(kCtlBytes == QG_WS_CONTROL_BYTES, "control area and header disagree");
+static_assert(sizeof(qg::GreedyCtl) <= qg::kCtlTileOffset, "greedy control words exceed their area");
+
+constexpr int kB1Chunk = 1024;  // K per workgroup of the 1-bit lookup kernel
 
 struct GemvPlan {
+    bool lut;            // batch-1 1-bit kernel (table lookup, lanes along rows)
+    bool fused;          // split-K combined inside the kernel (per-tile counters)
     bool one;            // batch-1 kernel (8-bit / 4-bit, activations in registers)
     int ns;              // batch-1 kernel: slices per lane
     bool full;           // batch-1 kernel: every lane owns all NS slices
@@ -156,6 +164,26 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
         }
         return pl;
     }
+    if (nb == 1 && fmt == QG_B1_G128) {
+        // batch 1, 1-bit: 256 rows x 1024 inputs per workgroup, partial sums
+        // of the K chunks combined in order
+        pl.lut = true;
+        pl.B = 1;
+        pl.kc = kB1Chunk;
+        pl.nsplit = static_cast<int>(ceil_div(K, kB1Chunk));
+        pl.grid_x = ceil_div(M, 256);
+        pl.fused = pl.nsplit > 1 && pl.grid_x <= qg::kCtlTileCounters;
+        size_t off = kCtlBytes;
+        if (pl.nsplit > 1) {
+            pl.comb_rows_per_wg = round_up(ceil_div(M, 1024), 256);
+            pl.comb_grid = ceil_div(M, pl.comb_rows_per_wg);
+            pl.part_off = off;
+            off = align256(off + static_cast<size_t>(pl.nsplit) * M * 4);
+        }
+        if (argmax) pl.nkeys = static_cast<int>(pl.nsplit > 1 && !pl.fused ? pl.comb_grid : pl.grid_x);
+        pl.ws_bytes = (off > kCtlBytes || argmax) ? off : 0;
+        return pl;
+    }
     pl.B = nb <= 1 ? 1 : nb <= 2 ? 2 : nb <= 4 ? 4 : nb <= 8 ? 8 : 16;
     const int kps = k_per_slice(fmt);
     const bool xsum = fmt != QG_I8_ROW;
@@ -189,14 +217,34 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
     return pl;
 }
 
+// Allow a kernel the full dynamic LDS budget (set once per kernel).
+template <typename Kernel>
+void allow_lds(Kernel k)
+{
+    static const bool done = [&] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  static_cast<int>(kLdsBudget));
+        return true;
+    }();
+    (void)done;
+}
+
+template <int FMT, int B, int R>
+void launch_gemv_r(const GemvPlan &pl, const GemvParams &p, hipStream_t s)
+{
+    allow_lds(qg::gemv_kernel<FMT, B, R>);
+    dim3 grid(static_cast<unsigned>(pl.grid_x), static_cast<unsigned>(pl.nsplit));
+    hipLaunchKernelGGL((qg::gemv_kernel<FMT, B, R>), grid, dim3(kThreads), pl.lds_bytes, s, p);
+}
+
 template <int FMT, int B>
 void launch_gemv_b(const GemvPlan &pl, const GemvParams &p, hipStream_t s)
 {
-    dim3 grid(static_cast<unsigned>(pl.grid_x), static_cast<unsigned>(pl.nsplit));
     switch (pl.R) {
-    case 4: hipLaunchKernelGGL((qg::gemv_kernel<FMT, B, 4>), grid, dim3(kThreads), pl.lds_bytes, s, p); break;
-    case 2: hipLaunchKernelGGL((qg::gemv_kernel<FMT, B, 2>), grid, dim3(kThreads), pl.lds_bytes, s, p); break;
-    default: hipLaunchKernelGGL((qg::gemv_kernel<FMT, B, 1>), grid, dim3(kThreads), pl.lds_bytes, s, p); break;
+    case 4: launch_gemv_r<FMT, B, 4>(pl, p, s); break;
+    case 2: launch_gemv_r<FMT, B, 2>(pl, p, s); break;
+    default: launch_gemv_r<FMT, B, 1>(pl, p, s); break;
     }
 }
 
@@ -263,6 +311,39 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         q.rows_per_wave = pl.rows_per_wave;
         if (fmt == QG_I8_ROW) launch_gemv1_fmt<qg::FMT_I8_ROW>(pl, q, s);
         else launch_gemv1_fmt<qg::FMT_U4_G64>(pl, q, s);
+        return;
+    }
+    if (pl.lut) {
+        qg::B1LutParams q{};
+        q.codes = static_cast<const uint8_t *>(codes);
+        q.scales = static_cast<const uint16_t *>(scales);
+        q.x = x;
+        q.y = y;
+        q.part = pl.nsplit > 1 ? reinterpret_cast<float *>(static_cast<char *>(ws) + pl.part_off) : nullptr;
+        q.ctl = static_cast<qg::GreedyCtl *>(ws);
+        q.idx = (pl.nsplit == 1 || pl.fused) ? idx : nullptr;
+        q.M = M;
+        q.K = K;
+        q.nsplit = pl.nsplit;
+        q.fused = pl.fused;
+        hipLaunchKernelGGL(qg::gemv_b1_lut_kernel<kB1Chunk>,
+                           dim3(static_cast<unsigned>(pl.grid_x), static_cast<unsigned>(pl.nsplit)),
+                           dim3(256), 0, s, q);
+        if (pl.nsplit > 1 && !pl.fused) {
+            GemvParams c{};
+            c.y = y;
+            c.part = q.part;
+            c.ctl = idx ? static_cast<qg::GreedyCtl *>(ws) : nullptr;
+            c.idx = idx;
+            c.M = M;
+            c.K = K;
+            c.rows_per_wg = pl.comb_rows_per_wg;
+            c.nb = 1;
+            c.nsplit = pl.nsplit;
+            c.nkeys = pl.nkeys;
+            hipLaunchKernelGGL(qg::gemv_combine_kernel, dim3(static_cast<unsigned>(pl.comb_grid)),
+                               dim3(kThreads), 0, s, c);
+        }
         return;
     }
     GemvParams p{};

@@ -58,29 +58,33 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask)
 // its values to its partner and keeps the other half, so the work is about
 // V shuffles instead of 6 * V. On return vals[0] of lane l holds the total
 // of value index (l >> (6 - P)); the order of additions is fixed, so the
-// result is deterministic.
+// result is deterministic. Every step is instantiated at compile time, so
+// all register indices are constants.
+template <int V, int O, int N>
+__device__ __forceinline__ void transpose_step(float (&vals)[V], int lane)
+{
+    if constexpr (O >= 1) {
+        if constexpr (N > 1) {
+            const bool upper = (lane & O) != 0;
+#pragma unroll
+            for (int i = 0; i < N / 2; ++i) {
+                const float send = upper ? vals[i] : vals[i + N / 2];
+                const float keep = upper ? vals[i + N / 2] : vals[i];
+                vals[i] = keep + __shfl_xor(send, O);
+            }
+            transpose_step<V, O / 2, N / 2>(vals, lane);
+        } else {
+            vals[0] += __shfl_xor(vals[0], O);
+            transpose_step<V, O / 2, 1>(vals, lane);
+        }
+    }
+}
+
 template <int V>
 __device__ __forceinline__ void wave_transpose_reduce(float (&vals)[V], int lane)
 {
     static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V must be a power of two <= 64");
-    int n = V;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        if (n > 1) {
-            const bool upper = (lane & o) != 0;
-#pragma unroll
-            for (int i = 0; i < V / 2; ++i) {
-                if (i < n / 2) {
-                    float send = upper ? vals[i] : vals[i + n / 2];
-                    float keep = upper ? vals[i + n / 2] : vals[i];
-                    vals[i] = keep + __shfl_xor(send, o);
-                }
-            }
-            n >>= 1;
-        } else {
-            vals[0] += __shfl_xor(vals[0], o);
-        }
-    }
+    transpose_step<V, 32, V>(vals, lane);
 }
 
 // ---------------------------------------------------------------------------

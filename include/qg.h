@@ -67,8 +67,9 @@
  *   Workspace   `ws` is device memory of at least qg_workspace_bytes(...)
  *               bytes for the same (op, fmt, M, K, rows); it may be NULL
  *               when that size is 0. Its first QG_WS_CONTROL_BYTES bytes are
- *               control words (the greedy head counts finished workgroups
- *               there): they must be zero before the first call that uses the
+ *               control words (counters of finished workgroups, for the
+ *               greedy head and for combining partial sums of K chunks):
+ *               they must be zero before the first call that uses the
  *               workspace, and every call leaves them zero again, so one
  *               zero-filled workspace serves any sequence of calls. The rest
  *               is scratch whose contents on entry do not matter.
@@ -111,7 +112,7 @@ enum {
 };
 
 /* Control words at the start of every workspace (see Workspace above). */
-#define QG_WS_CONTROL_BYTES 256
+#define QG_WS_CONTROL_BYTES 4096
 
 /* Largest batch of qgemv / qgemv_argmax. */
 #define QG_MAX_GEMV_BATCH 16
