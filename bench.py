@@ -170,6 +170,50 @@ def cpu_baseline(launches, seconds):
                       f"{reps} repetitions, {el:.1f} s"}
 
 
+def run_probe(args, torch, synth):
+    import ctypes
+    L = ctypes.CDLL(os.path.join(ROOT, "gemm_qgemv_amd", "libqgprobe.so"))
+    L.qg_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                ctypes.c_void_p]
+    L.qg_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                ctypes.c_void_p]
+    s = torch.cuda.current_stream().cuda_stream
+    if args.probe == "copy":
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        for _ in range(8):
+            assert L.qg_probe_copy(src.data_ptr(), dst.data_ptr(), n, 4096, s) == 0
+        torch.cuda.synchronize()
+        print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n, "launches": 8}))
+        return
+    names = WORKLOADS.get(args.workload, [args.workload])
+    size = sum(synth.CASES_BY_NAME[nm].weight_bytes for nm in names) // 16 * 16
+    copies = max(1, math.ceil((args.rotate_mib << 20) / size))
+    bufs = [torch.empty(size, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    out = torch.empty(4096, dtype=torch.int32, device="cuda")
+    best = None
+    for grid in (1024, 2048, 4096):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for b in bufs:
+                assert L.qg_probe_read(b.data_ptr(), size, out.data_ptr(), grid,
+                                       torch.cuda.current_stream().cuda_stream) == 0
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(1, 200 // copies)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+        best = us if best is None else min(best, us)
+    print(json.dumps({"probe": "read", "bytes": size, "us": round(best, 3),
+                      "GB/s": round(size / best / 1e3, 1)}))
+
+
 def load_traffic(workload, src_hash):
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
@@ -191,6 +235,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
+    ap.add_argument("--launch-only", action="store_true",
+                    help="only run the warmup and the steps, eagerly, and print nothing else "
+                         "(for counter collection under rocprofv3 --pmc)")
+    ap.add_argument("--probe", choices=["copy", "read"],
+                    help="run only a measurement probe: 'copy' copies 256 MiB 8 times (a kernel of "
+                         "known traffic, to calibrate FETCH_SIZE / WRITE_SIZE); 'read' times cold "
+                         "streaming reads of the workload's weight size")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -204,6 +255,9 @@ def main():
     from gemm_qgemv_amd import synth, tensors
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
+    if args.probe:
+        run_probe(args, torch, synth)
+        return
     names = WORKLOADS.get(args.workload, [args.workload])
     cases = [synth.CASES_BY_NAME[n] for n in names]
     gemm = cases[0].op == "gemm"
@@ -230,6 +284,13 @@ def main():
         for i in range(warmup):
             step(i, sh)
     torch.cuda.synchronize()
+    if args.launch_only:
+        with torch.cuda.stream(stream):
+            for i in range(steps):
+                step(i, sh)
+        torch.cuda.synchronize()
+        log(f"launched {warmup} + {steps} steps of {args.workload}")
+        return
 
     graph = None
     if not args.no_graph:

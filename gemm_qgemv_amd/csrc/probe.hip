@@ -11,9 +11,18 @@
 
 __global__ __launch_bounds__(256) void qg_probe_read_kernel(const uint4 *p, int64_t n, uint32_t *out)
 {
+    // four independent 16-byte loads in flight per thread per iteration
     uint32_t acc = 0;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+        const uint4 a = p[i];
+        const uint4 b = p[i + stride];
+        const uint4 c = p[i + 2 * stride];
+        const uint4 d = p[i + 3 * stride];
+        acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
+    }
+    for (; i < n; i += stride) {
         const uint4 v = p[i];
         acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
