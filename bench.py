@@ -68,7 +68,8 @@ def log(*a):
 def kernel_source_hash() -> str:
     """sha256 (16 hex digits) of the sources libqg.so is built from."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "gemm_qgemv_amd", "csrc", "*")) if not p.endswith("probe.hip")):
+    for p in sorted(q for q in glob.glob(os.path.join(ROOT, "gemm_qgemv_amd", "csrc", "*"))
+                    if not q.endswith("probe.hip")):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
