@@ -8,11 +8,14 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/qg.h"
 #include "gemm.hpp"
 #include "gemv.hpp"
 #include "gemv1.hpp"
 #include "gemv_b1.hpp"
+#include "gemv_mfma.hpp"
 
 namespace {
 
@@ -25,6 +28,12 @@ constexpr int64_t kMaxN = 0x7fffffffLL;
 // 160 KiB per compute unit; this leaves room for two workgroups' worth of
 // smaller tiles or one large one).
 constexpr int64_t kLdsBudget = 96 * 1024;
+// All of a compute unit's LDS: the small-batch matrix-core kernel runs one
+// workgroup per compute unit and keeps the whole activation operand there.
+constexpr int64_t kLdsMax = 160 * 1024;
+constexpr int64_t kLdsStaticReserve = 1024;   // static LDS of a kernel (keys, flags)
+// Compute units of the MI355X (one small-batch matrix-core workgroup each).
+constexpr int64_t kComputeUnits = 256;
 constexpr int64_t kAlign = 16;
 constexpr int kThreads = 256;
 
@@ -127,6 +136,7 @@ static_assert(sizeof(qg::GreedyCtl) <= qg::kCtlTileOffset, "greedy control words
 constexpr int kB1Chunk = 1024;  // K per workgroup of the 1-bit lookup kernel
 
 struct GemvPlan {
+    bool mfma;           // small-batch 4-bit kernel on the matrix cores
     bool lut;            // batch-1 1-bit kernel (table lookup, lanes along rows)
     bool fused;          // split-K combined inside the kernel (per-tile counters)
     bool one;            // batch-1 kernel (8-bit / 4-bit, activations in registers)
@@ -182,6 +192,20 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
         }
         if (argmax) pl.nkeys = static_cast<int>(pl.nsplit > 1 && !pl.fused ? pl.comb_grid : pl.grid_x);
         pl.ws_bytes = (off > kCtlBytes || argmax) ? off : 0;
+        return pl;
+    }
+    if (fmt == QG_U4_G64 && nb >= 2 && nb <= 8 && K % (64 * qg::kMfmaChunk) == 0 &&
+        static_cast<int64_t>(qg::gemv_mfma_lds_bytes(K)) + kLdsStaticReserve <= kLdsMax) {
+        // 2..8 rows, 4-bit: matrix cores, one workgroup of 8 waves per
+        // compute unit, at least one 16-row tile per wave
+        pl.mfma = true;
+        pl.grid_x = std::min<int64_t>(kComputeUnits, ceil_div(ceil_div(M, 16), qg::kMfmaWaves));
+        pl.lds_bytes = qg::gemv_mfma_lds_bytes(K);
+        pl.nsplit = 1;
+        if (argmax) {
+            pl.nkeys = static_cast<int>(pl.grid_x);
+            pl.ws_bytes = kCtlBytes;
+        }
         return pl;
     }
     pl.B = nb <= 1 ? 1 : nb <= 2 ? 2 : nb <= 4 ? 4 : nb <= 8 ? 8 : 16;
@@ -297,6 +321,31 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
               const void *biases, const float *x, float *y, int32_t *idx, int64_t M,
               int64_t K, int nb, void *ws, hipStream_t s)
 {
+    if (pl.mfma) {
+        qg::GemvMfmaParams q{};
+        q.codes = static_cast<const uint8_t *>(codes);
+        q.scales = static_cast<const uint16_t *>(scales);
+        q.biases = static_cast<const uint16_t *>(biases);
+        q.x = x;
+        q.y = y;
+        q.ctl = idx ? static_cast<qg::GreedyCtl *>(ws) : nullptr;
+        q.idx = idx;
+        q.M = M;
+        q.K = K;
+        q.nb = nb;
+        // dynamic LDS up to the plan's limit (the kernel's few static bytes
+        // come on top, within the compute unit's 160 KiB)
+        static const bool lds_set = [] {
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(qg::gemv_mfma_u4_kernel),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      static_cast<int>(kLdsMax - kLdsStaticReserve));
+            return true;
+        }();
+        (void)lds_set;
+        hipLaunchKernelGGL(qg::gemv_mfma_u4_kernel, dim3(static_cast<unsigned>(pl.grid_x)),
+                           dim3(64 * qg::kMfmaWaves), pl.lds_bytes, s, q);
+        return;
+    }
     if (pl.one) {
         qg::Gemv1Params q{};
         q.codes = static_cast<const uint8_t *>(codes);

@@ -283,6 +283,68 @@ def test_zero_codes_give_bias_times_sum(torch, orc):
 
 
 # ---------------------------------------------------------------------------
+# the small-batch 4-bit matrix-core path: 2..8 rows, K a multiple of 512 up
+# to 3072 (16-row tiles, up to several per wave, chunks of 512 inputs);
+# K = 3584 and 9 rows take the vector path and are checked alongside
+# ---------------------------------------------------------------------------
+
+MFMA_SHAPES = [
+    (16, 512, 8), (17, 1024, 5), (300, 1536, 2), (40007, 512, 3), (70001, 2048, 8),
+    (5000, 3072, 2), (9001, 3072, 7), (1000, 3584, 4), (2049, 2048, 9),
+]
+
+
+@pytest.mark.parametrize("M,K,N", MFMA_SHAPES)
+def test_small_batch_u4_exact(torch, orc, M, K, N):
+    say(f"small-batch exact M={M} K={K} N={N}")
+    rng = np.random.default_rng([9, M, K, N])
+    w, x = exact_inputs(synth.U4_G64, M, K, N, rng)
+    ref, a = orc.qgemv(synth.U4_G64, w.codes, w.scales, w.biases, x, M, K)
+    want = ref.astype(np.float32)
+    assert np.array_equal(want.astype(np.float64), ref), "fixture is not exact in float32"
+    y, idx = gpu_gemv(torch, dev(w), x, argmax=True, ws_fill=0x5A)
+    assert np.array_equal(y, want), f"not bit-exact: max diff {np.max(np.abs(y - want))}"
+    assert list(idx) == [int(np.argmax(r)) for r in want]
+
+
+@pytest.mark.parametrize("M,K,N", MFMA_SHAPES)
+def test_small_batch_u4_random(torch, orc, M, K, N):
+    say(f"small-batch random M={M} K={K} N={N}")
+    rng = synth.rng_for(400, M * 13 + K + N)
+    w = synth.draw_weights(synth.U4_G64, M, K, rng)
+    x = synth.draw_x(N, K, rng)
+    ref, a = orc.qgemv(synth.U4_G64, w.codes, w.scales, w.biases, x, M, K)
+    y, idx = gpu_gemv(torch, dev(w), x, argmax=True, ws_fill=0xA5)
+    check_bound(y, ref, a, f"small-batch {M}x{K} b{N}")
+    check_argmax(idx, y, ref, a, orc, "argmax")
+    y2, idx2 = gpu_gemv(torch, dev(w), x, argmax=True)
+    assert np.array_equal(y, y2) and np.array_equal(idx, idx2), "repeated call differs"
+
+
+def test_small_batch_u4_ties(torch, orc):
+    """Equal maxima in different waves and workgroups (first row, last row,
+    the middle), per activation row."""
+    say("small-batch ties")
+    rng = np.random.default_rng(10)
+    M, K, N = 40000, 512, 4
+    w = synth.draw_weights(synth.U4_G64, M, K, rng)
+    x = synth.draw_x(N, K, rng)
+    ref, _ = orc.qgemv(synth.U4_G64, w.codes, w.scales, w.biases, x, M, K)
+    tops = [int(np.argmax(ref[n])) for n in range(N)]
+    dsts = {0: [M - 1, 20011], 1: [0], 2: [30001], 3: [19999, 20000]}
+    for n, ds in dsts.items():
+        for dst in ds:
+            if dst in tops:
+                continue
+            for arr in (w.codes, w.scales, w.biases):
+                arr[dst] = arr[tops[n]]
+    ref, a = orc.qgemv(synth.U4_G64, w.codes, w.scales, w.biases, x, M, K)
+    y, idx = gpu_gemv(torch, dev(w), x, argmax=True)
+    check_bound(y, ref, a, "ties")
+    check_argmax(idx, y, ref, a, orc, "ties")
+
+
+# ---------------------------------------------------------------------------
 # the configurations at full size
 # ---------------------------------------------------------------------------
 
