@@ -10,27 +10,36 @@
 // One v_mfma_f32_16x16x32_bf16 computes D[i][m] += sum_k A[i][k] B[k][m] for
 // 16 operand rows i and 16 weight rows m. Operand A row i < 8 holds the top
 // bf16 piece of activation row n = i, row 8 + n its middle piece; a second
-// MFMA adds the bottom pieces (rows 0..7; rows 8..15 read zeros). Each
-// float32 activation is the exact sum of its three pieces (top, middle and
-// bottom 8 significant bits, split by truncation), codes 0..15 are exact in
-// bf16, and the products accumulate in float32; the two halves of D (rows
-// n and 8 + n) are added once per tile.
+// MFMA adds the bottom pieces (rows 0..7; rows 8..15 read a zero entry).
+// Each float32 activation is the exact sum of its three pieces (top, middle
+// and bottom 8 significant bits, split by truncation), codes 0..15 are exact
+// in bf16, and the products accumulate in float32; the two halves of D
+// (rows n and 8 + n) are added once per tile.
 //
-// Affine groups: the scale and bias change every 64 inputs, so each group is
-// accumulated on its own and folded in as
-//     acc += scale * tmp + bias * sum_{k in group} x[n][k].
-// The k order inside a group is permuted so that each MFMA stays inside one
-// group: lane l (operand row r = l % 16, quarter q = l / 16) holds, at k-step
-// s (0, 1), the inputs k = 64 g + 16 q + 8 s + e (e = 0..7). On the weight
-// side that is 4 bytes of row r at byte 32 g + 8 q + 4 s, so a lane reads
-// its 8 bytes of a group with one load. Odd k take the high nibble in place
-// (16 * code) against activations pre-divided by 16.
+// Codes to bf16: a byte holding one code (0..15) is, read as an OCP e4m3
+// number, exactly code * 2^-9; the gfx950 scaled fp8 -> bf16 conversion
+// turns two such bytes into two exact bf16 codes in one instruction.
+//
+// Affine groups: the scale changes every 64 inputs, so each group is
+// accumulated on its own and folded in as acc += scale * tmp. The bias term
+// sum_g bias[m][g] * X[n][g], X the group sums of the activations, is one
+// more contraction over the groups, done with the same MFMA per tile (the
+// biases are bf16 already; X is split into three pieces like x).
+//
+// Operand order. Lane l is operand row r = l % 16, quarter q = l / 16. Each
+// lane loads 16 bytes of its weight row per pair of groups (byte 64 p + 16 q):
+// quarters 0, 1 hold group 2p, quarters 2, 3 group 2p + 1. One permlane32
+// swap per dword pair hands each quarter 8 inputs of both groups, so that at
+// k-step s of group g lane (r, q) holds inputs
+//     k = 64 g + 32 (q & 1) + 16 (q >> 1) + 8 s + {0, 2, 4, 6, 1, 3, 5, 7}
+// (the last term: even-k nibbles first, as the conversion produces them).
+// The activation pieces are staged in LDS in exactly this order.
 //
 // Mapping. One workgroup of 8 waves per compute unit. The workgroup stages
-// the activation pieces of all K in LDS, already in operand order (3 KiB per
-// group, 96 KiB for K = 2048), plus the group sums; each wave then streams
-// its contiguous run of 16-row tiles in chunks of 8 groups held in a ring
-// of register buffers, so two chunks are in flight while one is reduced.
+// the activation pieces of all K in LDS (3 KiB per group, 97 KiB for
+// K = 2048) and the pieces of the group sums; each wave then streams its
+// contiguous run of 16-row tiles in chunks of 8 groups held in a ring of
+// register buffers, so two chunks are in flight while one is reduced.
 #pragma once
 
 #include "gemm.hpp"
@@ -53,38 +62,37 @@ struct GemvMfmaParams {
 constexpr int kMfmaWaves = 8;           // waves per workgroup
 constexpr int kMfmaChunk = 8;           // groups per register chunk
 constexpr int kMfmaBufs = 3;            // register chunks in the ring
-// LDS per (group, k-step): 1 KiB top/middle pieces, 512 B bottom pieces and
-// a 16-byte zero entry (read by operand rows 8..15 in the bottom pass)
-constexpr int kMfmaHalfBytes = 1024 + 512 + 16;
-constexpr int kMfmaGroupBytes = 2 * kMfmaHalfBytes + 64;   // + 16 group sums
+// One operand block in LDS: 1 KiB top/middle pieces [q][row 16], 512 B bottom
+// pieces [q][n 8] and a 16-byte zero entry (read by rows 8..15 in the bottom
+// pass). A group has two (one per k-step); each 32 groups of the bias
+// contraction have one.
+constexpr int kMfmaBlockBytes = 1024 + 512 + 16;
+constexpr int kMfmaGroupBytes = 2 * kMfmaBlockBytes;
 
-// LDS bytes of one workgroup: per group two k-steps and the sums.
+__host__ __device__ constexpr int gemv_mfma_bias_steps(int64_t K)
+{
+    return static_cast<int>((K / 64 + 31) / 32);
+}
+
+// LDS bytes of one workgroup: the group blocks, then the bias blocks.
 __host__ __device__ constexpr size_t gemv_mfma_lds_bytes(int64_t K)
 {
-    return static_cast<size_t>(K / 64) * kMfmaGroupBytes;
+    return static_cast<size_t>(K / 64) * kMfmaGroupBytes +
+           static_cast<size_t>(gemv_mfma_bias_steps(K)) * kMfmaBlockBytes;
 }
 
-typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-
-// bf16 pair (lo in the low half) of two float32 values that are exact in
-// bf16: their top halves, gathered with one byte permute.
-__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi)
-{
-    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
+typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
 
 // 8 nibbles of one dword (8 consecutive inputs, even k in the low nibbles)
-// -> 8 bf16 operand values: even k as the code, odd k as 16 * code.
+// -> 8 bf16 codes in the order k = 0, 2, 4, 6, 1, 3, 5, 7.
 __device__ __forceinline__ bf16x8_t nibbles_to_bf16(uint32_t d)
 {
-    uint32_t lo, hi;
-    asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(d));
-    asm("v_and_b32 %0, 0xf0f0f0f0, %1" : "=v"(hi) : "v"(d));
+    const uint32_t lo = d & 0x0f0f0f0fu, hi = (d >> 4) & 0x0f0f0f0fu;
     uint4 v;
-    v.x = bf16_pair(static_cast<float>(lo & 0xff), static_cast<float>(hi & 0xff));
-    v.y = bf16_pair(static_cast<float>((lo >> 8) & 0xff), static_cast<float>((hi >> 8) & 0xff));
-    v.z = bf16_pair(static_cast<float>((lo >> 16) & 0xff), static_cast<float>((hi >> 16) & 0xff));
-    v.w = bf16_pair(static_cast<float>(lo >> 24), static_cast<float>(hi >> 24));
+    v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false));
+    v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true));
+    v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false));
+    v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true));
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
@@ -100,10 +108,21 @@ __device__ __forceinline__ float bf16_at(const uint4 &v, int j)
     return (j & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
 }
 
-// One chunk of one lane: 8 groups of codes (8 bytes each), and the 8 scales
-// and biases of its weight row.
+// Split float32 v exactly into three bf16 bit patterns (truncation).
+__device__ __forceinline__ void split3(float v, uint32_t &hi, uint32_t &mid, uint32_t &lo)
+{
+    const uint32_t h = __float_as_uint(v) & 0xFFFF0000u;
+    const float r = v - __uint_as_float(h);
+    const uint32_t m = __float_as_uint(r) & 0xFFFF0000u;
+    hi = h >> 16;
+    mid = m >> 16;
+    lo = __float_as_uint(r - __uint_as_float(m)) >> 16;
+}
+
+// One chunk of one lane: 4 pairs of groups of codes (16 bytes each), the 8
+// scales of its weight row, and (first chunks of a tile only) 8 biases.
 struct MfmaChunk {
-    u32x2_t c[kMfmaChunk];
+    uint4 c[kMfmaChunk / 2];
     uint4 s, b;
 };
 
@@ -113,6 +132,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_u4_kernel(GemvMfmaP
     uint8_t *lds = reinterpret_cast<uint8_t *>(lds_f4);
     const int G = static_cast<int>(p.K / 64);
     const int C = G / kMfmaChunk;
+    const int NBS = gemv_mfma_bias_steps(p.K);
+    uint8_t *bias_blocks = lds + static_cast<size_t>(G) * kMfmaGroupBytes;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
@@ -134,24 +155,27 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_u4_kernel(GemvMfmaP
     int64_t lc_tile = tb;
     auto point = [&](int64_t t) {
         const int64_t m = min(t * 16 + r, p.M - 1);
-        lc_c = p.codes + m * row_bytes + 8 * q;
+        lc_c = p.codes + m * row_bytes + 16 * q;
         lc_s = p.scales + m * G;
-        lc_b = p.biases + m * G;
+        lc_b = p.biases + m * G + 8 * q;
         lc_chunk = 0;
         lc_tile = t;
     };
     auto load = [&](MfmaChunk &k) {
 #pragma unroll
-        for (int j = 0; j < kMfmaChunk; ++j)
-            k.c[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(lc_c + 32 * j));
+        for (int j = 0; j < kMfmaChunk / 2; ++j) {
+            const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(lc_c + 64 * j));
+            k.c[j] = make_uint4(v.x, v.y, v.z, v.w);
+        }
         k.s = *reinterpret_cast<const uint4 *>(lc_s);
-        k.b = *reinterpret_cast<const uint4 *>(lc_b);
+        if (lc_chunk < NBS)   // biases of groups 32 c + 8 q .. + 7
+            k.b = 32 * lc_chunk + 8 * q < G ? *reinterpret_cast<const uint4 *>(lc_b + 32 * lc_chunk)
+                                            : make_uint4(0u, 0u, 0u, 0u);
         if (++lc_chunk == C) {
             point(lc_tile + 1);
         } else {
             lc_c += 32 * kMfmaChunk;
             lc_s += kMfmaChunk;
-            lc_b += kMfmaChunk;
         }
     };
 
@@ -161,31 +185,35 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_u4_kernel(GemvMfmaP
     for (int u = 0; u < kMfmaBufs - 1; ++u)
         if (u < total) load(buf[u]);
 
-    // 1. activation pieces in operand order, zero entries, group sums.
-    //    Consecutive threads read consecutive 32-byte pieces of one row.
+    // 1a. activation pieces in operand order, zero entries. Item (n, g, qq, s)
+    //     covers 8 inputs of activation row n.
     for (int it = tid; it < 8 * G * 8; it += blockDim.x) {
         const int n = it / (G * 8), rem = it - n * (G * 8);
         const int g = rem >> 3, qq = (rem >> 1) & 3, s = rem & 1;
         uint32_t h[4] = {0u, 0u, 0u, 0u}, md[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
         if (n < p.nb) {
-            const float4 *src = reinterpret_cast<const float4 *>(p.x + static_cast<int64_t>(n) * p.K + 8 * rem);
+            const int k0 = 64 * g + 32 * (qq & 1) + 16 * (qq >> 1) + 8 * s;
+            const float4 *src = reinterpret_cast<const float4 *>(p.x + static_cast<int64_t>(n) * p.K + k0);
             const float4 a = src[0], b = src[1];
-            const float v[8] = {a.x, a.y * 0.0625f, a.z, a.w * 0.0625f, b.x, b.y * 0.0625f, b.z, b.w * 0.0625f};
+            // operand order k0 + {0, 2, 4, 6, 1, 3, 5, 7}
+            const float v[8] = {a.x, a.z, b.x, b.z, a.y, a.w, b.y, b.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) split3_pair(v[2 * j], v[2 * j + 1], h[j], md[j], lo[j]);
         }
-        uint8_t *blk = lds + static_cast<size_t>(g) * kMfmaGroupBytes + s * kMfmaHalfBytes;
+        uint8_t *blk = lds + static_cast<size_t>(g) * kMfmaGroupBytes + s * kMfmaBlockBytes;
         *reinterpret_cast<uint4 *>(blk + (qq * 16 + n) * 16) = make_uint4(h[0], h[1], h[2], h[3]);
         *reinterpret_cast<uint4 *>(blk + (qq * 16 + 8 + n) * 16) = make_uint4(md[0], md[1], md[2], md[3]);
         *reinterpret_cast<uint4 *>(blk + 1024 + (qq * 8 + n) * 16) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         if (rem < 2 * G && n == 0)   // one thread per (group, k-step)
             *reinterpret_cast<uint4 *>(lds + static_cast<size_t>(rem >> 1) * kMfmaGroupBytes +
-                                       (rem & 1) * kMfmaHalfBytes + 1536) = make_uint4(0u, 0u, 0u, 0u);
+                                       (rem & 1) * kMfmaBlockBytes + 1536) = make_uint4(0u, 0u, 0u, 0u);
     }
-    for (int it = tid; it < G * 16; it += blockDim.x) {
-        const int n = it & 15, g = it >> 4;
+    // 1b. group sums X[n][g] as bias-contraction operand: group g is input
+    //     k = g % 32 of bias step g / 32 (quarter (g / 8) % 4, element g % 8)
+    for (int it = tid; it < NBS * 32 * 8; it += blockDim.x) {
+        const int n = it & 7, g = it >> 3;
         float sum = 0.f;
-        if (n < p.nb) {
+        if (n < p.nb && g < G) {
             const float4 *src = reinterpret_cast<const float4 *>(p.x + static_cast<int64_t>(n) * p.K + 64 * g);
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
@@ -193,7 +221,15 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_u4_kernel(GemvMfmaP
                 sum += (v.x + v.y) + (v.z + v.w);
             }
         }
-        *reinterpret_cast<float *>(lds + static_cast<size_t>(g) * kMfmaGroupBytes + 2 * kMfmaHalfBytes + 4 * n) = sum;
+        uint32_t h, md, lo;
+        split3(sum, h, md, lo);
+        uint8_t *blk = bias_blocks + static_cast<size_t>(g >> 5) * kMfmaBlockBytes;
+        const int qq = (g >> 3) & 3, e = g & 7;
+        *reinterpret_cast<uint16_t *>(blk + (qq * 16 + n) * 16 + 2 * e) = static_cast<uint16_t>(h);
+        *reinterpret_cast<uint16_t *>(blk + (qq * 16 + 8 + n) * 16 + 2 * e) = static_cast<uint16_t>(md);
+        *reinterpret_cast<uint16_t *>(blk + 1024 + (qq * 8 + n) * 16 + 2 * e) = static_cast<uint16_t>(lo);
+        if ((g & 31) == 0 && n == 0)
+            *reinterpret_cast<uint4 *>(blk + 1536) = make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
 
@@ -206,33 +242,45 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_u4_kernel(GemvMfmaP
     int cc = 0;            // chunk within the tile being reduced
     int64_t ct = tb;       // tile being reduced
 
+    auto mfma = [](uint4 a, bf16x8_t b, floatx4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), b, c, 0, 0, 0);
+    };
     auto reduce = [&](const MfmaChunk &k) {
         const uint8_t *gb = lds + static_cast<size_t>(cc) * kMfmaChunk * kMfmaGroupBytes;
 #pragma unroll
-        for (int j = 0; j < kMfmaChunk; ++j) {
-            const uint8_t *b = gb + j * kMfmaGroupBytes;
-            const bf16x8_t w0 = nibbles_to_bf16(k.c[j].x), w1 = nibbles_to_bf16(k.c[j].y);
-            const uint4 h0 = *reinterpret_cast<const uint4 *>(b + hm_off);
-            const uint4 l0 = *reinterpret_cast<const uint4 *>(b + lo_off);
-            const uint4 h1 = *reinterpret_cast<const uint4 *>(b + kMfmaHalfBytes + hm_off);
-            const uint4 l1 = *reinterpret_cast<const uint4 *>(b + kMfmaHalfBytes + lo_off);
-            floatx4_t t = {0.f, 0.f, 0.f, 0.f};
-            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, h0), w0, t, 0, 0, 0);
-            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, l0), w0, t, 0, 0, 0);
-            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, h1), w1, t, 0, 0, 0);
-            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, l1), w1, t, 0, 0, 0);
-            // lane (r, q) holds D rows 4q..4q+3 of column r: quarters 0, 1 the
-            // top+bottom sums of activation rows 4q + i, quarters 2, 3 the
-            // middle sums of rows 4(q - 2) + i (their group sums read zero)
-            const float4 xs = *reinterpret_cast<const float4 *>(b + 2 * kMfmaHalfBytes + 16 * q);
-            const float sc = bf16_at(k.s, j), bi = bf16_at(k.b, j);
-            acc[0] = fmaf(sc, t[0], fmaf(bi, xs.x, acc[0]));
-            acc[1] = fmaf(sc, t[1], fmaf(bi, xs.y, acc[1]));
-            acc[2] = fmaf(sc, t[2], fmaf(bi, xs.z, acc[2]));
-            acc[3] = fmaf(sc, t[3], fmaf(bi, xs.w, acc[3]));
+        for (int j = 0; j < kMfmaChunk / 2; ++j) {
+            // quarters 0, 1 hold group 2j, quarters 2, 3 group 2j + 1: swap
+            // halves between quarters q and q ^ 2
+            const auto s0 = __builtin_amdgcn_permlane32_swap(k.c[j].x, k.c[j].z, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(k.c[j].y, k.c[j].w, false, false);
+            const uint32_t dw[2][2] = {{s0[0], s1[0]}, {s0[1], s1[1]}};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int g = 2 * j + h;
+                const uint8_t *b = gb + g * kMfmaGroupBytes;
+                const bf16x8_t w0 = nibbles_to_bf16(dw[h][0]), w1 = nibbles_to_bf16(dw[h][1]);
+                floatx4_t t = {0.f, 0.f, 0.f, 0.f};
+                t = mfma(*reinterpret_cast<const uint4 *>(b + hm_off), w0, t);
+                t = mfma(*reinterpret_cast<const uint4 *>(b + lo_off), w0, t);
+                t = mfma(*reinterpret_cast<const uint4 *>(b + kMfmaBlockBytes + hm_off), w1, t);
+                t = mfma(*reinterpret_cast<const uint4 *>(b + kMfmaBlockBytes + lo_off), w1, t);
+                const float sc = bf16_at(k.s, g);
+                acc[0] = fmaf(sc, t[0], acc[0]);
+                acc[1] = fmaf(sc, t[1], acc[1]);
+                acc[2] = fmaf(sc, t[2], acc[2]);
+                acc[3] = fmaf(sc, t[3], acc[3]);
+            }
+        }
+        if (cc < NBS) {
+            // bias contraction, groups 32 cc .. 32 cc + 31
+            const uint8_t *b = bias_blocks + static_cast<size_t>(cc) * kMfmaBlockBytes;
+            const bf16x8_t wb = __builtin_bit_cast(bf16x8_t, k.b);
+            acc = mfma(*reinterpret_cast<const uint4 *>(b + hm_off), wb, acc);
+            acc = mfma(*reinterpret_cast<const uint4 *>(b + lo_off), wb, acc);
         }
         if (++cc == C) {
-            // tile done: add the middle-piece half (lane ^ 32), store
+            // tile done: lane (r, q) holds D rows 4q..4q+3 of column r; add
+            // the middle-piece half (quarters 2, 3) to the rest and store
             const int64_t m = ct * 16 + r;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
