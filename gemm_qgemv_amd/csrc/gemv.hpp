@@ -262,6 +262,48 @@ __device__ __forceinline__ void greedy_finish(const unsigned long long *wg_key, 
         __hip_atomic_store(&ctl->counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Greedy finish for grids whose workgroups all end at about the same time:
+// rather than folding its keys into shared slots (contended atomics on one
+// line, serialized at the coherence point), each workgroup parks its nb
+// keys in its own row of `keys` ([workgroups][8], any initial contents)
+// with returning device-scope exchanges, then counts itself in once. The
+// last workgroup reads every row back with device-scope atomic loads,
+// reduces them, writes the indices and puts the counter back to zero.
+__device__ __forceinline__ void greedy_finish_rows(const unsigned long long *wg_key, int nb,
+                                                   GreedyCtl *ctl, unsigned long long *keys,
+                                                   int32_t *idx, int nwg)
+{
+    __shared__ unsigned s_last;
+    __shared__ unsigned long long s_best[8];
+    if (threadIdx.x == 0) {
+        uint32_t dep = 0;
+        for (int b = 0; b < nb; ++b) {
+            const unsigned long long old = __hip_atomic_exchange(
+                &keys[static_cast<int64_t>(blockIdx.x) * 8 + b], wg_key[b], __ATOMIC_RELAXED,
+                __HIP_MEMORY_SCOPE_AGENT);
+            dep |= static_cast<uint32_t>(old) | static_cast<uint32_t>(old >> 32);
+        }
+        uint32_t zero;
+        asm volatile("v_and_b32 %0, 0, %1" : "=v"(zero) : "v"(dep));  // 0, after the exchanges return
+        const unsigned t = __hip_atomic_fetch_add(&ctl->counter + zero, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (t == static_cast<unsigned>(nwg) - 1u);
+    }
+    if (threadIdx.x < 8) s_best[threadIdx.x] = 0ull;
+    __syncthreads();
+    if (!s_last) return;
+    for (int i = threadIdx.x; i < nwg * nb; i += blockDim.x) {
+        const int w = i / nb, b = i - w * nb;
+        const unsigned long long k = __hip_atomic_load(&keys[static_cast<int64_t>(w) * 8 + b],
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        atomicMax(&s_best[b], k);
+    }
+    __syncthreads();
+    if (threadIdx.x < nb) idx[threadIdx.x] = static_cast<int32_t>(argmax_key_index(s_best[threadIdx.x]));
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&ctl->counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Main kernel. B: batch rounded up to a power of two (x rows >= nb are
 // zero in LDS and their outputs are not written). R: rows per block.
 template <int FMT, int B, int R>

@@ -54,14 +54,22 @@ struct GemvMfmaParams {
     const float *x;        // [nb][K]
     float *y;              // [nb][M]
     GreedyCtl *ctl;        // greedy head control words, or nullptr
+    unsigned long long *keys;   // greedy head: [workgroups][8] scratch
     int32_t *idx;          // [nb] greedy indices, or nullptr
     int64_t M, K;
     int nb;                // 1..8
+    int stage_out;         // outputs staged in LDS, written at the end
 };
 
 constexpr int kMfmaWaves = 8;           // waves per workgroup
 constexpr int kMfmaChunk = 8;           // groups per register chunk
-constexpr int kMfmaBufs = 3;            // register chunks in the ring
+#ifndef QG_MFMA_BUFS
+#define QG_MFMA_BUFS 3
+#endif
+constexpr int kMfmaBufs = QG_MFMA_BUFS; // register chunks in the ring
+#ifndef QG_MFMA_NT
+#define QG_MFMA_NT 1                    // non-temporal code loads
+#endif
 // One operand block in LDS: 1 KiB top/middle pieces [q][row 16], 512 B bottom
 // pieces [q][n 8] and a 16-byte zero entry (read by rows 8..15 in the bottom
 // pass). A group has two (one per k-step); each 32 groups of the bias
@@ -80,6 +88,9 @@ __host__ __device__ constexpr size_t gemv_mfma_lds_bytes(int64_t K)
     return static_cast<size_t>(K / 64) * kMfmaGroupBytes +
            static_cast<size_t>(gemv_mfma_bias_steps(K)) * kMfmaBlockBytes;
 }
+
+// Outputs of one 16-row tile staged in LDS: [8 activation rows][16] floats.
+constexpr int kMfmaTileOutBytes = 8 * 16 * 4;
 
 typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
 
@@ -146,6 +157,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_u4_kernel(GemvMfmaP
     const int64_t gw = static_cast<int64_t>(blockIdx.x) * kMfmaWaves + wave;
     const int64_t tb = gw * ntiles / W, te = (gw + 1) * ntiles / W;
     const int64_t total = (te - tb) * C;   // chunks to reduce
+    // the workgroup's tiles (its waves' runs are adjacent); with stage_out
+    // their outputs collect in LDS after the operand blocks, so that no
+    // store waits in the same in-order memory counter as the weight loads
+    const int64_t tb_wg = static_cast<int64_t>(blockIdx.x) * ntiles / gridDim.x;
+    const int64_t te_wg = static_cast<int64_t>(blockIdx.x + 1) * ntiles / gridDim.x;
+    float *out_stage = reinterpret_cast<float *>(bias_blocks + static_cast<size_t>(NBS) * kMfmaBlockBytes);
 
     // load cursor: this lane's weight row in the tile being loaded (rows
     // past M read row M - 1; their outputs are not written)
@@ -164,8 +181,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_u4_kernel(GemvMfmaP
     auto load = [&](MfmaChunk &k) {
 #pragma unroll
         for (int j = 0; j < kMfmaChunk / 2; ++j) {
+#if QG_MFMA_NT
             const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(lc_c + 64 * j));
             k.c[j] = make_uint4(v.x, v.y, v.z, v.w);
+#else
+            k.c[j] = *reinterpret_cast<const uint4 *>(lc_c + 64 * j);
+#endif
         }
         k.s = *reinterpret_cast<const uint4 *>(lc_s);
         if (lc_chunk < NBS)   // biases of groups 32 c + 8 q .. + 7
@@ -287,7 +308,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_u4_kernel(GemvMfmaP
                 const float v = pair_sum<5>(acc[i]);
                 const int n = 4 * q + i;
                 if (q < 2 && n < p.nb && m < p.M) {
-                    p.y[static_cast<int64_t>(n) * p.M + m] = v;
+                    if (p.stage_out)
+                        out_stage[((ct - tb_wg) * 8 + n) * 16 + r] = v;
+                    else
+                        p.y[static_cast<int64_t>(n) * p.M + m] = v;
                     if (best_m[i] < 0 || v > best_v[i]) {   // rows arrive in increasing order
                         best_v[i] = v;
                         best_m[i] = m;
@@ -320,6 +344,16 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_u4_kernel(GemvMfmaP
         }
     }
 
+    if (p.stage_out) {
+        __syncthreads();
+        const int64_t m0 = tb_wg * 16, rows = min(te_wg * 16, p.M) - m0;
+        for (int n = 0; n < p.nb; ++n)
+            for (int64_t j = tid; j < rows; j += blockDim.x) {
+                const int64_t tl = j >> 4;
+                p.y[static_cast<int64_t>(n) * p.M + m0 + j] = out_stage[(tl * 8 + n) * 16 + (j & 15)];
+            }
+    }
+
     if (p.ctl != nullptr) {
         __shared__ unsigned long long wg_key[8];
         if (tid < 8) wg_key[tid] = 0ull;
@@ -337,7 +371,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_u4_kernel(GemvMfmaP
             if (r == 0 && q < 2 && n < p.nb) atomicMax(&wg_key[n], static_cast<unsigned long long>(key));
         }
         __syncthreads();
-        greedy_finish(wg_key, p.nb, p.ctl, p.idx, static_cast<int>(gridDim.x));
+        greedy_finish_rows(wg_key, p.nb, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x));
     }
 }
 

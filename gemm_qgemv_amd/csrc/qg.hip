@@ -138,7 +138,8 @@ constexpr int kB1Chunk = 1024;  // K per workgroup of the 1-bit lookup kernel
 struct GemvPlan {
     bool mfma;           // small-batch 4-bit kernel on the matrix cores
     bool lut;            // batch-1 1-bit kernel (table lookup, lanes along rows)
-    bool fused;          // split-K combined inside the kernel (per-tile counters)
+    bool fused;          // split-K combined inside the kernel (per-tile counters);
+                         // small-batch kernel: outputs staged in LDS
     bool one;            // batch-1 kernel (8-bit / 4-bit, activations in registers)
     int ns;              // batch-1 kernel: slices per lane
     bool full;           // batch-1 kernel: every lane owns all NS slices
@@ -199,12 +200,19 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
         // 2..8 rows, 4-bit: matrix cores, one workgroup of 8 waves per
         // compute unit, at least one 16-row tile per wave
         pl.mfma = true;
-        pl.grid_x = std::min<int64_t>(kComputeUnits, ceil_div(ceil_div(M, 16), qg::kMfmaWaves));
+        const int64_t ntiles = ceil_div(M, 16);
+        pl.grid_x = std::min<int64_t>(kComputeUnits, ceil_div(ntiles, qg::kMfmaWaves));
         pl.lds_bytes = qg::gemv_mfma_lds_bytes(K);
+        // stage the outputs in LDS when the workgroup's tiles fit
+        const size_t out_bytes = static_cast<size_t>(ceil_div(ntiles, pl.grid_x)) * qg::kMfmaTileOutBytes;
+        pl.fused = static_cast<int64_t>(pl.lds_bytes + out_bytes) + kLdsStaticReserve <= kLdsMax;
+        if (pl.fused) pl.lds_bytes += out_bytes;
         pl.nsplit = 1;
         if (argmax) {
+            // per-workgroup greedy keys after the control words
             pl.nkeys = static_cast<int>(pl.grid_x);
-            pl.ws_bytes = kCtlBytes;
+            pl.part_off = kCtlBytes;
+            pl.ws_bytes = align256(kCtlBytes + static_cast<size_t>(pl.grid_x) * 8 * 8);
         }
         return pl;
     }
@@ -329,10 +337,12 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         q.x = x;
         q.y = y;
         q.ctl = idx ? static_cast<qg::GreedyCtl *>(ws) : nullptr;
+        q.keys = idx ? reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + pl.part_off) : nullptr;
         q.idx = idx;
         q.M = M;
         q.K = K;
         q.nb = nb;
+        q.stage_out = pl.fused;
         // dynamic LDS up to the plan's limit (the kernel's few static bytes
         // come on top, within the compute unit's 160 KiB)
         static const bool lds_set = [] {
