@@ -8,13 +8,14 @@
 // batching lets many sequences reuse one pass over the weights).
 //
 // One v_mfma_f32_16x16x32_bf16 computes D[i][m] += sum_k A[i][k] B[k][m] for
-// 16 operand rows i and 16 weight rows m. Operand A row i < 8 holds the top
-// bf16 piece of activation row n = i, row 8 + n its middle piece; a second
-// MFMA adds the bottom pieces (rows 0..7; rows 8..15 read a zero entry).
-// Each float32 activation is the exact sum of its three pieces (top, middle
-// and bottom 8 significant bits, split by truncation), codes 0..15 are exact
-// in bf16, and the products accumulate in float32; the two halves of D
-// (rows n and 8 + n) are added once per tile.
+// 16 operand rows i and 16 weight rows m. Each float32 activation is split
+// by truncation into three bf16 pieces (top, middle and bottom 8 significant
+// bits) whose sum is exact. Operand A row i < 8 holds the top piece of
+// activation row n = i, row 8 + n its middle piece; a second MFMA gives
+// both rows n and 8 + n half the bottom piece (halving is exact). The two
+// halves of D (rows n and 8 + n) are added once per tile, which restores
+// top + middle + bottom. Codes 0..15 are exact in bf16 and the products
+// accumulate in float32.
 //
 // Codes to bf16: a byte holding one code (0..15) is, read as an OCP e4m3
 // number, exactly code * 2^-9; the gfx950 scaled fp8 -> bf16 conversion
@@ -62,19 +63,23 @@ struct GemvMfmaParams {
 };
 
 constexpr int kMfmaWaves = 8;           // waves per workgroup
+constexpr int kMfmaThreads = 64 * kMfmaWaves;
+constexpr int kStageItems = 8;          // staging items per thread: K <= 4096
 constexpr int kMfmaChunk = 8;           // groups per register chunk
 #ifndef QG_MFMA_BUFS
 #define QG_MFMA_BUFS 3
 #endif
 constexpr int kMfmaBufs = QG_MFMA_BUFS; // register chunks in the ring
+#ifndef QG_MFMA_CHAINS
+#define QG_MFMA_CHAINS 1                // accumulation chains per group
+#endif
 #ifndef QG_MFMA_NT
 #define QG_MFMA_NT 1                    // non-temporal code loads
 #endif
-// One operand block in LDS: 1 KiB top/middle pieces [q][row 16], 512 B bottom
-// pieces [q][n 8] and a 16-byte zero entry (read by rows 8..15 in the bottom
-// pass). A group has two (one per k-step); each 32 groups of the bias
-// contraction have one.
-constexpr int kMfmaBlockBytes = 1024 + 512 + 16;
+// One operand block in LDS: 1 KiB top/middle pieces [q][row 16] and 512 B
+// halved bottom pieces [q][n 8] (read by operand rows n and 8 + n). A group
+// has two (one per k-step); each 32 groups of the bias contraction have one.
+constexpr int kMfmaBlockBytes = 1024 + 512;
 constexpr int kMfmaGroupBytes = 2 * kMfmaBlockBytes;
 
 __host__ __device__ constexpr int gemv_mfma_bias_steps(int64_t K)
@@ -119,15 +124,28 @@ __device__ __forceinline__ float bf16_at(const uint4 &v, int j)
     return (j & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
 }
 
-// Split float32 v exactly into three bf16 bit patterns (truncation).
-__device__ __forceinline__ void split3(float v, uint32_t &hi, uint32_t &mid, uint32_t &lo)
+// Split float32 v exactly into top, middle and half the bottom bf16 piece
+// (truncation; v = top + middle + 2 * half), as bf16 bit patterns.
+__device__ __forceinline__ void split3h(float v, uint32_t &hi, uint32_t &mid, uint32_t &half)
 {
     const uint32_t h = __float_as_uint(v) & 0xFFFF0000u;
-    const float r = v - __uint_as_float(h);
+    const float r = v - __uint_as_float(h);                 // exact
     const uint32_t m = __float_as_uint(r) & 0xFFFF0000u;
     hi = h >> 16;
     mid = m >> 16;
-    lo = __float_as_uint(r - __uint_as_float(m)) >> 16;
+    half = __float_as_uint((r - __uint_as_float(m)) * 0.5f) >> 16;   // 8 bits, exact
+}
+
+// The same for two values, packed as bf16 pairs (a in the low half).
+__device__ __forceinline__ void split3h_pair(float a, float b, uint32_t &hi, uint32_t &mid,
+                                             uint32_t &half)
+{
+    uint32_t ha, ma, la, hb, mb, lb;
+    split3h(a, ha, ma, la);
+    split3h(b, hb, mb, lb);
+    hi = ha | (hb << 16);
+    mid = ma | (mb << 16);
+    half = la | (lb << 16);
 }
 
 // One chunk of one lane: 4 pairs of groups of codes (16 bytes each), the 8
@@ -137,7 +155,7 @@ struct MfmaChunk {
     uint4 s, b;
 };
 
-__global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_u4_kernel(GemvMfmaParams p)
+__global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_u4_kernel(GemvMfmaParams p)
 {
     extern __shared__ float4 lds_f4[];
     uint8_t *lds = reinterpret_cast<uint8_t *>(lds_f4);
@@ -206,28 +224,41 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_u4_kernel(GemvMfmaP
     for (int u = 0; u < kMfmaBufs - 1; ++u)
         if (u < total) load(buf[u]);
 
-    // 1a. activation pieces in operand order, zero entries. Item (n, g, qq, s)
-    //     covers 8 inputs of activation row n.
-    for (int it = tid; it < 8 * G * 8; it += blockDim.x) {
+    // 1a. activation pieces in operand order. Item (n, g, qq, s)
+    //     covers 8 inputs of activation row n; a thread's items (at most
+    //     kStageItems) load first, then split and store.
+    const int nitems = 8 * G * 8;
+    float4 xa[kStageItems], xb[kStageItems];
+#pragma unroll
+    for (int u = 0; u < kStageItems; ++u) {
+        const int it = tid + u * kMfmaThreads;
+        xa[u] = xb[u] = make_float4(0.f, 0.f, 0.f, 0.f);
         const int n = it / (G * 8), rem = it - n * (G * 8);
-        const int g = rem >> 3, qq = (rem >> 1) & 3, s = rem & 1;
-        uint32_t h[4] = {0u, 0u, 0u, 0u}, md[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
-        if (n < p.nb) {
+        if (it < nitems && n < p.nb) {
+            const int g = rem >> 3, qq = (rem >> 1) & 3, s = rem & 1;
             const int k0 = 64 * g + 32 * (qq & 1) + 16 * (qq >> 1) + 8 * s;
             const float4 *src = reinterpret_cast<const float4 *>(p.x + static_cast<int64_t>(n) * p.K + k0);
-            const float4 a = src[0], b = src[1];
+            xa[u] = src[0];
+            xb[u] = src[1];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kStageItems; ++u) {
+        const int it = tid + u * kMfmaThreads;
+        if (it < nitems) {
+            const int n = it / (G * 8), rem = it - n * (G * 8);
+            const int g = rem >> 3, qq = (rem >> 1) & 3, s = rem & 1;
+            const float4 a = xa[u], b = xb[u];
             // operand order k0 + {0, 2, 4, 6, 1, 3, 5, 7}
             const float v[8] = {a.x, a.z, b.x, b.z, a.y, a.w, b.y, b.w};
+            uint32_t h[4], md[4], lo[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) split3_pair(v[2 * j], v[2 * j + 1], h[j], md[j], lo[j]);
+            for (int j = 0; j < 4; ++j) split3h_pair(v[2 * j], v[2 * j + 1], h[j], md[j], lo[j]);
+            uint8_t *blk = lds + static_cast<size_t>(g) * kMfmaGroupBytes + s * kMfmaBlockBytes;
+            *reinterpret_cast<uint4 *>(blk + (qq * 16 + n) * 16) = make_uint4(h[0], h[1], h[2], h[3]);
+            *reinterpret_cast<uint4 *>(blk + (qq * 16 + 8 + n) * 16) = make_uint4(md[0], md[1], md[2], md[3]);
+            *reinterpret_cast<uint4 *>(blk + 1024 + (qq * 8 + n) * 16) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         }
-        uint8_t *blk = lds + static_cast<size_t>(g) * kMfmaGroupBytes + s * kMfmaBlockBytes;
-        *reinterpret_cast<uint4 *>(blk + (qq * 16 + n) * 16) = make_uint4(h[0], h[1], h[2], h[3]);
-        *reinterpret_cast<uint4 *>(blk + (qq * 16 + 8 + n) * 16) = make_uint4(md[0], md[1], md[2], md[3]);
-        *reinterpret_cast<uint4 *>(blk + 1024 + (qq * 8 + n) * 16) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        if (rem < 2 * G && n == 0)   // one thread per (group, k-step)
-            *reinterpret_cast<uint4 *>(lds + static_cast<size_t>(rem >> 1) * kMfmaGroupBytes +
-                                       (rem & 1) * kMfmaBlockBytes + 1536) = make_uint4(0u, 0u, 0u, 0u);
     }
     // 1b. group sums X[n][g] as bias-contraction operand: group g is input
     //     k = g % 32 of bias step g / 32 (quarter (g / 8) % 4, element g % 8)
@@ -243,20 +274,18 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_u4_kernel(GemvMfmaP
             }
         }
         uint32_t h, md, lo;
-        split3(sum, h, md, lo);
+        split3h(sum, h, md, lo);
         uint8_t *blk = bias_blocks + static_cast<size_t>(g >> 5) * kMfmaBlockBytes;
         const int qq = (g >> 3) & 3, e = g & 7;
         *reinterpret_cast<uint16_t *>(blk + (qq * 16 + n) * 16 + 2 * e) = static_cast<uint16_t>(h);
         *reinterpret_cast<uint16_t *>(blk + (qq * 16 + 8 + n) * 16 + 2 * e) = static_cast<uint16_t>(md);
         *reinterpret_cast<uint16_t *>(blk + 1024 + (qq * 8 + n) * 16 + 2 * e) = static_cast<uint16_t>(lo);
-        if ((g & 31) == 0 && n == 0)
-            *reinterpret_cast<uint4 *>(blk + 1536) = make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
 
     // 2. reduce the chunks
     const int hm_off = lane * 16;
-    const int lo_off = r < 8 ? 1024 + (q * 8 + r) * 16 : 1536;   // rows 8..15: zero entry
+    const int lo_off = 1024 + (q * 8 + (r & 7)) * 16;   // rows n and 8 + n: same half piece
     float best_v[4] = {0.f, 0.f, 0.f, 0.f};
     int64_t best_m[4] = {-1, -1, -1, -1};
     floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -280,16 +309,25 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_u4_kernel(GemvMfmaP
                 const int g = 2 * j + h;
                 const uint8_t *b = gb + g * kMfmaGroupBytes;
                 const bf16x8_t w0 = nibbles_to_bf16(dw[h][0]), w1 = nibbles_to_bf16(dw[h][1]);
+                const float sc = bf16_at(k.s, g);
+#if QG_MFMA_CHAINS == 2
+                // two independent accumulation chains (top/middle, bottom)
+                floatx4_t t = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+                t = mfma(*reinterpret_cast<const uint4 *>(b + hm_off), w0, t);
+                u = mfma(*reinterpret_cast<const uint4 *>(b + lo_off), w0, u);
+                t = mfma(*reinterpret_cast<const uint4 *>(b + kMfmaBlockBytes + hm_off), w1, t);
+                u = mfma(*reinterpret_cast<const uint4 *>(b + kMfmaBlockBytes + lo_off), w1, u);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, u[i], fmaf(sc, t[i], acc[i]));
+#else
                 floatx4_t t = {0.f, 0.f, 0.f, 0.f};
                 t = mfma(*reinterpret_cast<const uint4 *>(b + hm_off), w0, t);
                 t = mfma(*reinterpret_cast<const uint4 *>(b + lo_off), w0, t);
                 t = mfma(*reinterpret_cast<const uint4 *>(b + kMfmaBlockBytes + hm_off), w1, t);
                 t = mfma(*reinterpret_cast<const uint4 *>(b + kMfmaBlockBytes + lo_off), w1, t);
-                const float sc = bf16_at(k.s, g);
-                acc[0] = fmaf(sc, t[0], acc[0]);
-                acc[1] = fmaf(sc, t[1], acc[1]);
-                acc[2] = fmaf(sc, t[2], acc[2]);
-                acc[3] = fmaf(sc, t[3], acc[3]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, t[i], acc[i]);
+#endif
             }
         }
         if (cc < NBS) {
@@ -301,7 +339,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void gemv_mfma_u4_kernel(GemvMfmaP
         }
         if (++cc == C) {
             // tile done: lane (r, q) holds D rows 4q..4q+3 of column r; add
-            // the middle-piece half (quarters 2, 3) to the rest and store
+            // the half from operand rows 8..15 (quarters 2, 3) and store
             const int64_t m = ct * 16 + r;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {

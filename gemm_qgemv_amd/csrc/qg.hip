@@ -196,6 +196,7 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
         return pl;
     }
     if (fmt == QG_U4_G64 && nb >= 2 && nb <= 8 && K % (64 * qg::kMfmaChunk) == 0 &&
+        K <= static_cast<int64_t>(qg::kStageItems) * qg::kMfmaThreads &&
         static_cast<int64_t>(qg::gemv_mfma_lds_bytes(K)) + kLdsStaticReserve <= kLdsMax) {
         // 2..8 rows, 4-bit: matrix cores, one workgroup of 8 waves per
         // compute unit, at least one 16-row tile per wave
