@@ -62,7 +62,10 @@ struct GemvMfmaParams {
     int stage_out;         // outputs staged in LDS, written at the end
 };
 
-constexpr int kMfmaWaves = 8;           // waves per workgroup
+#ifndef QG_MFMA_WAVES
+#define QG_MFMA_WAVES 8
+#endif
+constexpr int kMfmaWaves = QG_MFMA_WAVES;   // waves per workgroup
 constexpr int kMfmaThreads = 64 * kMfmaWaves;
 constexpr int kStageItems = 8;          // staging items per thread: K <= 4096
 constexpr int kMfmaChunk = 8;           // groups per register chunk
