@@ -13,12 +13,17 @@
 // prefill projections are genuine matrix-matrix products; this kernel keeps
 // the weights packed instead of dequantizing them to a float scratch first.)
 //
-// Tiling. A workgroup of 4 waves computes a 128 (m) x 128 (n) tile of Y; the
-// waves form a 2 x 2 grid of 64 x 64 sub-tiles, i.e. 4 x 4 MFMA 16x16 tiles
-// per wave. Each k-step stages 32 k of W (converted to bf16) and X (split
-// into 3 bf16 planes) in LDS; rows are padded to 80 bytes so that the
-// 16-byte fragment reads of 8 consecutive lanes hit 8 distinct bank groups.
-// The next k-step's global loads are issued before the current MFMAs.
+// Tiling. A workgroup of 4 waves computes a BM (m) x BN (n) tile of Y
+// (128 x 128, 64 x 128 or 64 x 64, chosen by the host so that the grid fills
+// the 256 compute units); the waves sit side by side along n, each covering
+// all BM weight rows, so a wave reads BM / 16 weight fragments and 3 * BN / 64
+// activation fragments per k-step for 3 * BM * BN / 1024 MFMAs. A k-step
+// stages 32 k of W (converted to bf16) and X (split into 3 bf16 planes) in
+// LDS, double-buffered: the step after the current one is staged from
+// registers while the current MFMAs run, and the loads of the step after
+// that are issued behind it, so one barrier per step suffices. LDS rows are
+// 64 bytes with an XOR swizzle of their four 16-byte chunks (conflict-free
+// fragment reads).
 //
 // MFMA 16x16x32 bf16 operand layout (lane l of 64):
 //   A (16 x 32, here W rows):    row l % 16, k = 8 * (l / 16) .. + 7
@@ -43,9 +48,6 @@ struct GemmParams {
     int64_t M, K, N;
     int tiles_m, tiles_n;
 };
-
-constexpr int GT_M = 128, GT_N = 128, GT_K = 32;
-constexpr int G_ROW = 40;  // bf16 per padded LDS row (32 + 8 pad)
 
 // Exact three-way bf16 split of float32 values a, b (two consecutive k):
 // returns packed bf16x2 words (a in the low half) for each piece.
@@ -78,11 +80,42 @@ __device__ __forceinline__ uint32_t signpair_to_bf16x2(uint32_t nbits2)
     return ((nbits2 * 0x40008000u) & 0x80008000u) | 0x3F803F80u;
 }
 
-template <int FMT>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p)
+constexpr int GT_K = 32;    // k per step
+constexpr int kGemmThreads = 256;
+// k-steps of loads in flight (register sets); the 1-bit format also holds
+// its per-group accumulators, so it keeps fewer sets
+#ifndef QG_GEMM_DEPTH_I8
+#define QG_GEMM_DEPTH_I8 3
+#endif
+#ifndef QG_GEMM_DEPTH_B1
+#define QG_GEMM_DEPTH_B1 4
+#endif
+#ifndef QG_GEMM_INTERLEAVE
+#define QG_GEMM_INTERLEAVE 6   // staging VALU instructions issued after each MFMA
+#endif
+
+// Physical 16-byte chunk of logical chunk c (0..3) in LDS row r (rows of
+// 64 bytes). Under this XOR swizzle any 16 consecutive rows read at one
+// logical chunk hit 16 distinct 16-byte bank groups of a 256-byte bank
+// cycle, and any 8 consecutive rows 8 distinct groups of a 128-byte cycle.
+__device__ __forceinline__ int swz_chunk(int r, int c)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t lw[GT_M * G_ROW];
-    __shared__ __attribute__((aligned(16))) uint16_t lx[3][GT_N * G_ROW];
+    return c ^ (((r >> 1) ^ (r >> 3)) & 3);
+}
+
+// Workgroup tile BM (weight rows m) x BN (token rows n); 4 waves side by
+// side along n, each covering all BM rows and BN / 4 tokens.
+template <int FMT, int BM, int BN>
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
+{
+    constexpr int TI = BM / 16;   // 16-row weight blocks per wave
+    constexpr int TJ = BN / 64;   // 16-token blocks per wave
+    static_assert(TI >= 1 && TJ >= 1 && BM * 2 <= kGemmThreads && BN * 2 <= kGemmThreads,
+                  "one staging item per thread");
+    // double-buffered stages: [buffer][row][4 chunks of 8 bf16]
+    __shared__ uint4 lw[2][BM * 4];
+    __shared__ uint4 lx[2][3][BN * 4];
+    __shared__ float ls[2][BM];   // 1-bit format: scales of the current and next group
 
     // XCD-aware order: consecutive workgroup ids go round-robin to the 8
     // XCDs; give each XCD a contiguous run of tiles (m fastest) so the tiles
@@ -91,129 +124,181 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p)
     int bid = blockIdx.x;
     if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
     const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
-    const int64_t m0 = static_cast<int64_t>(tm) * GT_M, n0 = static_cast<int64_t>(tn) * GT_N;
+    const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+    const int wn = wave * (BN / 4);
+    const int fr = lane & 15, fq = lane >> 4;
 
     // staging assignment: thread -> (row, half of the 32-k step)
     const int sr = tid >> 1, sh = tid & 1;
+    const bool wst = 2 * BM >= kGemmThreads || sr < BM;   // constant when every thread stages
+    const bool xst = 2 * BN >= kGemmThreads || sr < BN;
     const int64_t wrow = m0 + sr, xrow = n0 + sr;
-    const bool wvalid = wrow < p.M, xvalid = xrow < p.N;
+    const bool wvalid = wst && wrow < p.M, xvalid = xst && xrow < p.N;
     const int64_t row_bytes = FMT == FMT_I8_ROW ? p.K : p.K / 8;
     const uint8_t *wsrc = p.codes + (wvalid ? wrow : 0) * row_bytes;
     const float *xsrc = p.x + (xvalid ? xrow : 0) * p.K;
+    const int nk = static_cast<int>((p.K + GT_K - 1) / GT_K);   // K is a multiple of 16
+    const int64_t groups = p.K / 128;
+    const uint16_t *ssrc = static_cast<const uint16_t *>(p.scales);
 
-    const int nk = static_cast<int>((p.K + GT_K - 1) / GT_K);
+    struct Regs {
+        uint4 w;          // I8: 16 codes; B1: low 16 bits = 16 sign bits
+        float4 x[4];
+        uint32_t s;       // 1-bit format, first step of a group: fp16 scale of row m0 + tid
+    };
 
-    // prefetch registers
-    uint4 wreg;          // I8: 16 codes; B1: low 16 bits = 16 sign bits
-    float4 xreg[4];
-
-    auto load = [&](int kt) {
+    auto load = [&](Regs &R, int kt) {
         const int64_t k = static_cast<int64_t>(kt) * GT_K + 16 * sh;
-        const bool kin = k < p.K;  // K is a multiple of 16
-        if (FMT == FMT_I8_ROW) {
-            wreg = (wvalid && kin) ? *reinterpret_cast<const uint4 *>(wsrc + k) : make_uint4(0, 0, 0, 0);
-        } else {
-            wreg.x = (wvalid && kin) ? *reinterpret_cast<const uint16_t *>(wsrc + k / 8) : 0u;
-        }
+        const bool kin = k < p.K;   // the last step of an odd number of 16-k halves
+        if (FMT == FMT_I8_ROW)
+            R.w = (wvalid && kin) ? *reinterpret_cast<const uint4 *>(wsrc + k) : make_uint4(0, 0, 0, 0);
+        else
+            R.w.x = (wvalid && kin) ? *reinterpret_cast<const uint16_t *>(wsrc + k / 8) : 0u;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            xreg[j] = (xvalid && kin) ? *reinterpret_cast<const float4 *>(xsrc + k + 4 * j)
-                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+            R.x[j] = (xvalid && kin) ? *reinterpret_cast<const float4 *>(xsrc + k + 4 * j)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (FMT == FMT_B1_G128 && (kt & 3) == 0 && tid < BM)
+            R.s = m0 + tid < p.M ? ssrc[(m0 + tid) * groups + kt / 4] : 0u;
     };
 
-    auto stage = [&]() {
-        uint32_t wv[8];
-        if (FMT == FMT_I8_ROW) {
-            const uint32_t d[4] = {wreg.x, wreg.y, wreg.z, wreg.w};
+    auto stage = [&](const Regs &R, int kt, int b) {
+        if (wst) {
+            uint32_t wv[8];
+            if (FMT == FMT_I8_ROW) {
+                const uint32_t d[4] = {R.w.x, R.w.y, R.w.z, R.w.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    wv[2 * j] = i8pair_to_bf16x2(d[j], 0);
+                    wv[2 * j + 1] = i8pair_to_bf16x2(d[j], 2);
+                }
+            } else {
+                // rows beyond M carry no codes: their (unused) weights become -1
+                const uint32_t nbits = ~R.w.x;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) wv[j] = signpair_to_bf16x2((nbits >> (2 * j)) & 3u);
+            }
+            lw[b][sr * 4 + swz_chunk(sr, 2 * sh)] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+            lw[b][sr * 4 + swz_chunk(sr, 2 * sh + 1)] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+        }
+        if (xst) {
+            uint32_t h[8], md[8], lo[8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                wv[2 * j] = i8pair_to_bf16x2(d[j], 0);
-                wv[2 * j + 1] = i8pair_to_bf16x2(d[j], 2);
+                split3_pair(R.x[j].x, R.x[j].y, h[2 * j], md[2 * j], lo[2 * j]);
+                split3_pair(R.x[j].z, R.x[j].w, h[2 * j + 1], md[2 * j + 1], lo[2 * j + 1]);
             }
-        } else {
-            // rows beyond M carry no codes: their (unused) weights become -1
-            const uint32_t nb = ~wreg.x;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) wv[j] = signpair_to_bf16x2((nb >> (2 * j)) & 3u);
+            const int c0 = sr * 4 + swz_chunk(sr, 2 * sh), c1 = sr * 4 + swz_chunk(sr, 2 * sh + 1);
+            lx[b][0][c0] = make_uint4(h[0], h[1], h[2], h[3]);
+            lx[b][0][c1] = make_uint4(h[4], h[5], h[6], h[7]);
+            lx[b][1][c0] = make_uint4(md[0], md[1], md[2], md[3]);
+            lx[b][1][c1] = make_uint4(md[4], md[5], md[6], md[7]);
+            lx[b][2][c0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            lx[b][2][c1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
         }
-        uint4 *dw = reinterpret_cast<uint4 *>(lw + sr * G_ROW + 16 * sh);
-        dw[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-        dw[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
-        uint32_t h[8], md[8], lo[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            split3_pair(xreg[j].x, xreg[j].y, h[2 * j], md[2 * j], lo[2 * j]);
-            split3_pair(xreg[j].z, xreg[j].w, h[2 * j + 1], md[2 * j + 1], lo[2 * j + 1]);
-        }
-        uint4 *d0 = reinterpret_cast<uint4 *>(lx[0] + sr * G_ROW + 16 * sh);
-        uint4 *d1 = reinterpret_cast<uint4 *>(lx[1] + sr * G_ROW + 16 * sh);
-        uint4 *d2 = reinterpret_cast<uint4 *>(lx[2] + sr * G_ROW + 16 * sh);
-        d0[0] = make_uint4(h[0], h[1], h[2], h[3]);
-        d0[1] = make_uint4(h[4], h[5], h[6], h[7]);
-        d1[0] = make_uint4(md[0], md[1], md[2], md[3]);
-        d1[1] = make_uint4(md[4], md[5], md[6], md[7]);
-        d2[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        d2[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+        if (FMT == FMT_B1_G128 && (kt & 3) == 0 && tid < BM)
+            ls[(kt >> 2) & 1][tid] = fp16_bits_to_f32(static_cast<uint16_t>(R.s));
     };
 
-    floatx4_t acc[4][4];
-    floatx4_t gacc[4][4];  // 1-bit format: sums of the current 128-k group
+    floatx4_t acc[TI][TJ];
+    floatx4_t gacc[TI][TJ];  // 1-bit format: sums of the current 128-k group
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < TJ; ++j) {
             acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
             gacc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
         }
 
-    const int fr = lane & 15, fk = 8 * (lane >> 4);
-    load(0);
-    for (int kt = 0; kt < nk; ++kt) {
-        __syncthreads();
-        stage();
-        __syncthreads();
-        if (kt + 1 < nk) load(kt + 1);
-
-        bf16x8_t a[4];
+    auto compute = [&](int kt) {
+        const int b = kt & 1;
+        bf16x8_t a[TI];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a[i] = __builtin_bit_cast(bf16x8_t,
-                                      *reinterpret_cast<const uint4 *>(lw + (wm + 16 * i + fr) * G_ROW + fk));
+        for (int i = 0; i < TI; ++i) {
+            const int r = 16 * i + fr;
+            a[i] = __builtin_bit_cast(bf16x8_t, lw[b][r * 4 + swz_chunk(r, fq)]);
+        }
 #pragma unroll
         for (int pc = 0; pc < 3; ++pc) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x8_t b = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const uint4 *>(lx[pc] + (wn + 16 * j + fr) * G_ROW + fk));
+            for (int j = 0; j < TJ; ++j) {
+                const int r = wn + 16 * j + fr;
+                const bf16x8_t bx = __builtin_bit_cast(bf16x8_t, lx[b][pc][r * 4 + swz_chunk(r, fq)]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < TI; ++i) {
                     if (FMT == FMT_I8_ROW)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bx, acc[i][j], 0, 0, 0);
                     else
-                        gacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, gacc[i][j], 0, 0, 0);
+                        gacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bx, gacc[i][j], 0, 0, 0);
                 }
             }
         }
-
-        if (FMT == FMT_B1_G128 && ((kt & 3) == 3 || kt + 1 == nk)) {
+        if (FMT == FMT_B1_G128 && (kt & 3) == 3) {
             // close the 128-k group: acc += scale[m][g] * group sum
-            const int64_t g = kt >> 2;
-            const uint16_t *sp = static_cast<const uint16_t *>(p.scales);
+            const float *sg = ls[(kt >> 2) & 1];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < TI; ++i) {
+                const float4 s4 = *reinterpret_cast<const float4 *>(sg + 16 * i + 4 * fq);
+                const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int64_t m = m0 + wm + 16 * i + 4 * (lane >> 4) + r;
-                    const float s = m < p.M ? fp16_bits_to_f32(sp[m * (p.K / 128) + g]) : 0.f;
+                for (int r = 0; r < 4; ++r)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        acc[i][j][r] = fmaf(s, gacc[i][j][r], acc[i][j][r]);
+                    for (int j = 0; j < TJ; ++j) {
+                        acc[i][j][r] = fmaf(sv[r], gacc[i][j][r], acc[i][j][r]);
                         gacc[i][j][r] = 0.f;
                     }
+            }
+        }
+    };
+
+    // pipeline: LDS buffer kt & 1 holds step kt; register set s % D holds
+    // step s from its load (D steps before it is staged) until it is staged
+    // (one step before it is computed)
+    constexpr int D = FMT == FMT_I8_ROW ? QG_GEMM_DEPTH_I8 : QG_GEMM_DEPTH_B1;
+    Regs R[D];
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+        if (u < nk) load(R[u], u);
+    stage(R[0], 0, 0);
+    if (D < nk) load(R[0], D);
+    __syncthreads();
+    int kt0 = 0;
+    // steady state: every step stages the next one and loads D ahead
+    for (; kt0 + 2 * D < nk; kt0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int kt = kt0 + u;
+            compute(kt);
+            stage(R[(u + 1) % D], kt + 1, (kt + 1) & 1);
+            load(R[(u + 1) % D], kt + 1 + D);
+#if QG_GEMM_INTERLEAVE
+            // issue order: the fragment reads, then each MFMA followed by a
+            // few staging VALU instructions, so that the conversion of the
+            // next step runs while the matrix pipe is busy
+            __builtin_amdgcn_sched_group_barrier(0x100, TI + 3 * TJ, 0);
+#pragma unroll
+            for (int i = 0; i < 3 * TI * TJ; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, QG_GEMM_INTERLEAVE, 0);
+            }
+#endif
+            __syncthreads();
+        }
+    }
+    // drain
+    for (; kt0 < nk; kt0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int kt = kt0 + u;
+            if (kt < nk) {
+                compute(kt);
+                if (kt + 1 < nk) {
+                    stage(R[(u + 1) % D], kt + 1, (kt + 1) & 1);
+                    if (kt + 1 + D < nk) load(R[(u + 1) % D], kt + 1 + D);
                 }
+                __syncthreads();
             }
         }
     }
@@ -221,8 +306,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p)
     // epilogue: row scale (int8), store Y[n][m .. m+3]
     const bool vec = (p.M & 3) == 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t mb = m0 + wm + 16 * i + 4 * (lane >> 4);
+    for (int i = 0; i < TI; ++i) {
+        const int64_t mb = m0 + 16 * i + 4 * fq;
         float s[4] = {1.f, 1.f, 1.f, 1.f};
         if (FMT == FMT_I8_ROW) {
             const float *sp = static_cast<const float *>(p.scales);
@@ -230,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p)
             for (int r = 0; r < 4; ++r) s[r] = mb + r < p.M ? sp[mb + r] : 0.f;
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < TJ; ++j) {
             const int64_t n = n0 + wn + 16 * j + fr;
             if (n >= p.N) continue;
             float *dst = p.y + n * p.M + mb;

@@ -485,7 +485,7 @@ size_t gemm_workspace(int fmt, int64_t M, int64_t K, int64_t N)
 bool gemm_shape_ok(int64_t M, int64_t N)
 {
     if (N <= kGemmViaGemv) return true;
-    return ceil_div(M, qg::GT_M) * ceil_div(N, qg::GT_N) <= 0x7fffffffLL;
+    return ceil_div(M, 64) * ceil_div(N, 64) <= 0x7fffffffLL;   // smallest tile
 }
 
 void run_gemm(int fmt, const void *codes, const void *scales, const float *x, float *y,
@@ -505,13 +505,25 @@ void run_gemm(int fmt, const void *codes, const void *scales, const float *x, fl
     p.M = M;
     p.K = K;
     p.N = N;
-    p.tiles_m = static_cast<int>(ceil_div(M, qg::GT_M));
-    p.tiles_n = static_cast<int>(ceil_div(N, qg::GT_N));
+    // the largest tile that still gives every compute unit a workgroup
+    auto tiles = [&](int bm, int bn) { return ceil_div(M, bm) * ceil_div(N, bn); };
+    // (1-bit: at most 64 x 128, its per-group accumulators double the
+    // accumulator registers)
+    int bm = 64, bn = 64;
+    if (fmt == QG_I8_ROW && tiles(128, 128) >= kComputeUnits) bm = 128, bn = 128;
+    else if (tiles(64, 128) >= kComputeUnits) bn = 128;
+    p.tiles_m = static_cast<int>(ceil_div(M, bm));
+    p.tiles_n = static_cast<int>(ceil_div(N, bn));
     const dim3 grid(static_cast<unsigned>(int64_t(p.tiles_m) * p.tiles_n));
-    if (fmt == QG_I8_ROW)
-        hipLaunchKernelGGL(qg::gemm_kernel<qg::FMT_I8_ROW>, grid, dim3(kThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL(qg::gemm_kernel<qg::FMT_B1_G128>, grid, dim3(kThreads), 0, s, p);
+    const dim3 block(qg::kGemmThreads);
+    if (fmt == QG_I8_ROW) {
+        if (bm == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_ROW, 128, 128>), grid, block, 0, s, p);
+        else if (bn == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_ROW, 64, 128>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_ROW, 64, 64>), grid, block, 0, s, p);
+    } else {
+        if (bn == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_B1_G128, 64, 128>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_B1_G128, 64, 64>), grid, block, 0, s, p);
+    }
 }
 
 int gemm_entry(int fmt, const void *codes, const void *scales, const void *biases,
