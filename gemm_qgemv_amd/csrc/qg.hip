@@ -507,6 +507,7 @@ void run_gemm(int fmt, const void *codes, const void *scales, const float *x, fl
     p.N = N;
     // the largest tile that still gives every compute unit a workgroup
     auto tiles = [&](int bm, int bn) { return ceil_div(M, bm) * ceil_div(N, bn); };
+    const dim3 block(qg::kGemmThreads);
     // (1-bit: at most 64 x 128, its per-group accumulators double the
     // accumulator registers)
     int bm = 64, bn = 64;
@@ -515,7 +516,6 @@ void run_gemm(int fmt, const void *codes, const void *scales, const float *x, fl
     p.tiles_m = static_cast<int>(ceil_div(M, bm));
     p.tiles_n = static_cast<int>(ceil_div(N, bn));
     const dim3 grid(static_cast<unsigned>(int64_t(p.tiles_m) * p.tiles_n));
-    const dim3 block(qg::kGemmThreads);
     if (fmt == QG_I8_ROW) {
         if (bm == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_ROW, 128, 128>), grid, block, 0, s, p);
         else if (bn == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_ROW, 64, 128>), grid, block, 0, s, p);

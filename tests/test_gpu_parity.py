@@ -192,8 +192,23 @@ def test_exact_arithmetic_prefill_bit_exact(torch, orc, fmt, M, K, N):
     assert np.array_equal(yg, want), f"prefill not bit-exact: max diff {np.max(np.abs(yg - want))}"
 
 
+@pytest.mark.parametrize("M,K,N", [(4001, 160, 1503), (4096, 176, 1536), (3841, 1040, 1665)])
+def test_exact_arithmetic_prefill_large_grid(torch, orc, M, K, N):
+    """8-bit prefill on grids of several hundred 128 x 128 tiles: ragged M
+    and N, K with a half step at the end."""
+    say(f"exact prefill large grid M={M} K={K} N={N}")
+    rng = np.random.default_rng([11, M, K, N])
+    w, x = exact_inputs(synth.I8_ROW, M, K, N, rng)
+    ref, _ = orc.qgemv(synth.I8_ROW, w.codes, w.scales, w.biases, x, M, K)
+    want = ref.astype(np.float32)
+    assert np.array_equal(want.astype(np.float64), ref), "fixture is not exact in float32"
+    yg = gpu_gemm(torch, dev(w), x)
+    assert np.array_equal(yg, want), f"prefill not bit-exact: max diff {np.max(np.abs(yg - want))}"
+
+
 @pytest.mark.parametrize("fmt,M,K,N", [
     (synth.I8_ROW, 1, 16, 17), (synth.I8_ROW, 127, 1040, 129), (synth.I8_ROW, 1000, 1024, 300),
+    (synth.I8_ROW, 4001, 1040, 1503),
     (synth.I8_ROW, 130, 3584, 33), (synth.B1_G128, 1, 128, 40), (synth.B1_G128, 250, 5120, 131),
     (synth.B1_G128, 129, 1152, 256),
 ])
