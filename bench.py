@@ -172,6 +172,62 @@ def cpu_baseline(launches, seconds):
                       f"{reps} repetitions, {el:.1f} s"}
 
 
+def vendor_ceiling(launches, torch, stream):
+    """Benchmark-only comparison for prefill workloads (never a library
+    path): the weights dequantized once into float32 with torch operations,
+    then the vendor FP32 GEMM (torch.mm, i.e. rocBLAS / hipBLASLt) on them.
+    Reports both times per call, the GEMM's TFLOP/s, and the largest error
+    of a sample of its outputs against the oracle, as a fraction of the
+    1e-5 * sum|w x| bound."""
+    import numpy as np
+    import oracle
+    orc = oracle.get()
+    res = []
+    for L in launches:
+        c, wd = L.case, L.weights[0]
+        codes = wd.codes
+
+        def dequant():
+            if c.fmt == 1:      # 8-bit, per-row fp32 scale
+                return codes.float() * wd.scales[:, None]
+            # 1-bit, fp16 scale per 128 inputs (stored as int16 bits)
+            bits = (codes.view(torch.uint8)[..., None].int() >> torch.arange(8, device="cuda")) & 1
+            signs = (bits * 2 - 1).float().reshape(c.M, c.K)
+            sc = wd.scales.view(torch.float16).float().repeat_interleave(128, dim=1)
+            return signs * sc
+
+        W = dequant()
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        reps = 5
+        with torch.cuda.stream(stream):
+            dequant()
+            torch.mm(L.x.view(c.rows, c.K), W.t())
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                dequant()
+            e1.record()
+            for _ in range(reps):
+                Y = torch.mm(L.x.view(c.rows, c.K), W.t())
+            e2.record()
+        torch.cuda.synchronize()
+        dq_ms, mm_ms = e0.elapsed_time(e1) / reps, e1.elapsed_time(e2) / reps
+        rng = np.random.default_rng(0)
+        n = rng.integers(0, c.rows, 2000).astype(np.int64)
+        m = rng.integers(0, c.M, 2000).astype(np.int64)
+        ref, a = orc.qgemv_sample(c.fmt, L.host_w.codes, L.host_w.scales, L.host_w.biases,
+                                  L.host_x, c.M, c.K, n, m)
+        got = Y.cpu().numpy()[n, m].astype(np.float64)
+        ratio = float(np.max(np.abs(got - ref) / (1e-5 * a)))
+        res.append({"case": c.name, "dequant_us": round(dq_ms * 1e3, 2), "sgemm_us": round(mm_ms * 1e3, 2),
+                    "sgemm_tflops": round(c.flops / (mm_ms * 1e-3) / 1e12, 2),
+                    "max_err_over_bound": round(ratio, 4)})
+        log(f"  vendor {c.name}: dequantize {dq_ms * 1e3:.1f} us, FP32 GEMM {mm_ms * 1e3:.1f} us "
+            f"({c.flops / (mm_ms * 1e-3) / 1e12:.1f} TFLOP/s), max err/bound {ratio:.3g}")
+        del W, Y
+    return res
+
+
 def run_probe(args, torch, synth):
     import ctypes
     L = ctypes.CDLL(os.path.join(ROOT, "gemm_qgemv_amd", "libqgprobe.so"))
@@ -240,6 +296,9 @@ def main():
     ap.add_argument("--launch-only", action="store_true",
                     help="only run the warmup and the steps, eagerly, and print nothing else "
                          "(for counter collection under rocprofv3 --pmc)")
+    ap.add_argument("--vendor", action="store_true",
+                    help="prefill workloads: also time the vendor FP32 GEMM on weights dequantized "
+                         "once (benchmark-only comparison, reported as vendor_ceiling)")
     ap.add_argument("--probe", choices=["copy", "read"],
                     help="run only a measurement probe: 'copy' copies 256 MiB 8 times (a kernel of "
                          "known traffic, to calibrate FETCH_SIZE / WRITE_SIZE); 'read' times cold "
@@ -385,6 +444,8 @@ def main():
     if not gemm:
         out["pct_of_hbm_peak"] = round(100 * value / HBM_PEAK_GBS, 2)
         out["tok_s_equiv"] = round(value * 1e9 / BYTES_PER_TOKEN[cases[0].fmt], 1)
+    if gemm and args.vendor:
+        out["vendor_ceiling"] = vendor_ceiling(launches, torch, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(launches, args.cpu_seconds)
     else:
