@@ -57,6 +57,7 @@ WORKLOADS = {
            "c3c_i8_gemm_3584x1024_n10240", "c3d_i8_gemm_1024x3584_n10240"],
     "c4gemv": ["c4a_b1_gemv_17408x5120", "c4b_b1_gemv_5120x17408"],
     "c4gemm": ["c4c_b1_gemm_17408x5120_n512", "c4d_b1_gemm_5120x17408_n512"],
+    "u4gemm": ["n2a_u4_gemm_6144x2048_n2048", "n2b_u4_gemm_2048x6144_n2048"],
 }
 METRIC = "effective weight GB/s and % of HBM peak, batch-1 qgemv; prefill qgemm TFLOP/s"
 
@@ -190,6 +191,11 @@ def vendor_ceiling(launches, torch, stream):
         def dequant():
             if c.fmt == 1:      # 8-bit, per-row fp32 scale
                 return codes.float() * wd.scales[:, None]
+            if c.fmt == 2:      # 4-bit, bf16 scale and bias per 64 inputs (int16 bits)
+                b = codes.view(torch.uint8).int()
+                q4 = torch.stack((b & 15, b >> 4), dim=-1).reshape(c.M, c.K).float()
+                bf = lambda t: (t.int() << 16).view(torch.float32).repeat_interleave(64, dim=1)
+                return q4 * bf(wd.scales) + bf(wd.biases)
             # 1-bit, fp16 scale per 128 inputs (stored as int16 bits)
             bits = (codes.view(torch.uint8)[..., None].int() >> torch.arange(8, device="cuda")) & 1
             signs = (bits * 2 - 1).float().reshape(c.M, c.K)

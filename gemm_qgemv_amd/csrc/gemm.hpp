@@ -43,11 +43,28 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 struct GemmParams {
     const uint8_t *codes;
     const void *scales;
+    const uint16_t *biases;   // 4-bit format: bf16 [M][K/64]
     const float *x;   // [N][K]
     float *y;         // [N][M]
     int64_t M, K, N;
     int tiles_m, tiles_n;
 };
+
+// 8 nibbles of one dword (8 consecutive inputs, even k in the low nibbles)
+// -> 8 bf16 codes in the order k = 0, 2, 4, 6, 1, 3, 5, 7. A byte holding one
+// code (0..15) is, read as an OCP e4m3 number, exactly code * 2^-9; the
+// gfx950 scaled fp8 -> bf16 conversion turns two such bytes into two exact
+// bf16 codes in one instruction.
+__device__ __forceinline__ bf16x8_t nibbles_to_bf16(uint32_t d)
+{
+    const uint32_t lo = d & 0x0f0f0f0fu, hi = (d >> 4) & 0x0f0f0f0fu;
+    uint4 v;
+    v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false));
+    v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true));
+    v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false));
+    v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true));
+    return __builtin_bit_cast(bf16x8_t, v);
+}
 
 // Exact three-way bf16 split of float32 values a, b (two consecutive k):
 // returns packed bf16x2 words (a in the low half) for each piece.
@@ -90,6 +107,9 @@ constexpr int kGemmThreads = 256;
 #ifndef QG_GEMM_DEPTH_B1
 #define QG_GEMM_DEPTH_B1 4
 #endif
+#ifndef QG_GEMM_DEPTH_U4
+#define QG_GEMM_DEPTH_U4 2
+#endif
 #ifndef QG_GEMM_INTERLEAVE
 #define QG_GEMM_INTERLEAVE 6   // staging VALU instructions issued after each MFMA
 #endif
@@ -115,7 +135,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
     // double-buffered stages: [buffer][row][4 chunks of 8 bf16]
     __shared__ uint4 lw[2][BM * 4];
     __shared__ uint4 lx[2][3][BN * 4];
-    __shared__ float ls[2][BM];   // 1-bit format: scales of the current and next group
+    // per-group coefficients of the current and next group: scales (1-bit
+    // and 4-bit), biases and activation group sums (4-bit)
+    constexpr bool GROUPED = FMT != FMT_I8_ROW;
+    constexpr int GSTEPS = FMT == FMT_B1_G128 ? 4 : 2;   // 32-k steps per group
+    __shared__ float ls[2][BM];
+    __shared__ float lb[2][FMT == FMT_U4_G64 ? BM : 1];
+    __shared__ float lxs[2][FMT == FMT_U4_G64 ? BN : 1];
 
     // XCD-aware order: consecutive workgroup ids go round-robin to the 8
     // XCDs; give each XCD a contiguous run of tiles (m fastest) so the tiles
@@ -136,32 +162,41 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
     const bool xst = 2 * BN >= kGemmThreads || sr < BN;
     const int64_t wrow = m0 + sr, xrow = n0 + sr;
     const bool wvalid = wst && wrow < p.M, xvalid = xst && xrow < p.N;
-    const int64_t row_bytes = FMT == FMT_I8_ROW ? p.K : p.K / 8;
+    const int64_t row_bytes = FMT == FMT_I8_ROW ? p.K : FMT == FMT_U4_G64 ? p.K / 2 : p.K / 8;
     const uint8_t *wsrc = p.codes + (wvalid ? wrow : 0) * row_bytes;
     const float *xsrc = p.x + (xvalid ? xrow : 0) * p.K;
     const int nk = static_cast<int>((p.K + GT_K - 1) / GT_K);   // K is a multiple of 16
-    const int64_t groups = p.K / 128;
+    const int64_t groups = p.K / (32 * GSTEPS);
     const uint16_t *ssrc = static_cast<const uint16_t *>(p.scales);
+    float xsum = 0.f;   // 4-bit format: this thread's part of its activation row's group sum
 
     struct Regs {
-        uint4 w;          // I8: 16 codes; B1: low 16 bits = 16 sign bits
+        uint4 w;          // I8: 16 codes; U4: w.x, w.y = 16 nibbles; B1: low 16 bits = 16 sign bits
         float4 x[4];
-        uint32_t s;       // 1-bit format, first step of a group: fp16 scale of row m0 + tid
+        uint32_t s, b;    // grouped formats, first step of a group: scale (and bias) bits of row m0 + tid
     };
 
     auto load = [&](Regs &R, int kt) {
         const int64_t k = static_cast<int64_t>(kt) * GT_K + 16 * sh;
         const bool kin = k < p.K;   // the last step of an odd number of 16-k halves
-        if (FMT == FMT_I8_ROW)
+        if (FMT == FMT_I8_ROW) {
             R.w = (wvalid && kin) ? *reinterpret_cast<const uint4 *>(wsrc + k) : make_uint4(0, 0, 0, 0);
-        else
+        } else if (FMT == FMT_U4_G64) {
+            const uint2 v = (wvalid && kin) ? *reinterpret_cast<const uint2 *>(wsrc + k / 2) : make_uint2(0, 0);
+            R.w.x = v.x;
+            R.w.y = v.y;
+        } else {
             R.w.x = (wvalid && kin) ? *reinterpret_cast<const uint16_t *>(wsrc + k / 8) : 0u;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             R.x[j] = (xvalid && kin) ? *reinterpret_cast<const float4 *>(xsrc + k + 4 * j)
                                      : make_float4(0.f, 0.f, 0.f, 0.f);
-        if (FMT == FMT_B1_G128 && (kt & 3) == 0 && tid < BM)
-            R.s = m0 + tid < p.M ? ssrc[(m0 + tid) * groups + kt / 4] : 0u;
+        if (GROUPED && kt % GSTEPS == 0 && tid < BM) {
+            const int64_t gi = (m0 + tid) * groups + kt / GSTEPS;
+            R.s = m0 + tid < p.M ? ssrc[gi] : 0u;
+            if (FMT == FMT_U4_G64) R.b = m0 + tid < p.M ? p.biases[gi] : 0u;
+        }
     };
 
     auto stage = [&](const Regs &R, int kt, int b) {
@@ -174,6 +209,12 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
                     wv[2 * j] = i8pair_to_bf16x2(d[j], 0);
                     wv[2 * j + 1] = i8pair_to_bf16x2(d[j], 2);
                 }
+            } else if (FMT == FMT_U4_G64) {
+                // codes in the order k = 0, 2, 4, 6, 1, 3, 5, 7 of each 8
+                const uint4 c0 = __builtin_bit_cast(uint4, nibbles_to_bf16(R.w.x));
+                const uint4 c1 = __builtin_bit_cast(uint4, nibbles_to_bf16(R.w.y));
+                wv[0] = c0.x; wv[1] = c0.y; wv[2] = c0.z; wv[3] = c0.w;
+                wv[4] = c1.x; wv[5] = c1.y; wv[6] = c1.z; wv[7] = c1.w;
             } else {
                 // rows beyond M carry no codes: their (unused) weights become -1
                 const uint32_t nbits = ~R.w.x;
@@ -185,10 +226,35 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
         }
         if (xst) {
             uint32_t h[8], md[8], lo[8];
+            if (FMT == FMT_U4_G64) {
+                // the weight operand's order: k = 0, 2, 4, 6, 1, 3, 5, 7 of each 8
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                split3_pair(R.x[j].x, R.x[j].y, h[2 * j], md[2 * j], lo[2 * j]);
-                split3_pair(R.x[j].z, R.x[j].w, h[2 * j + 1], md[2 * j + 1], lo[2 * j + 1]);
+                for (int c = 0; c < 2; ++c) {
+                    const float4 a = R.x[2 * c], e = R.x[2 * c + 1];
+                    split3_pair(a.x, a.z, h[4 * c], md[4 * c], lo[4 * c]);
+                    split3_pair(e.x, e.z, h[4 * c + 1], md[4 * c + 1], lo[4 * c + 1]);
+                    split3_pair(a.y, a.w, h[4 * c + 2], md[4 * c + 2], lo[4 * c + 2]);
+                    split3_pair(e.y, e.w, h[4 * c + 3], md[4 * c + 3], lo[4 * c + 3]);
+                }
+                // group sums of the activations, for the bias term: this
+                // thread's 16 inputs per step, two steps per group, and the
+                // other half of the row from the neighbouring lane
+                float part = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) part += (R.x[j].x + R.x[j].y) + (R.x[j].z + R.x[j].w);
+                if (kt % GSTEPS == 0) {
+                    xsum = part;
+                } else {
+                    xsum += part;
+                    const float total = xsum + __shfl_xor(xsum, 1);
+                    if (sh == 0) lxs[(kt / GSTEPS) & 1][sr] = total;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    split3_pair(R.x[j].x, R.x[j].y, h[2 * j], md[2 * j], lo[2 * j]);
+                    split3_pair(R.x[j].z, R.x[j].w, h[2 * j + 1], md[2 * j + 1], lo[2 * j + 1]);
+                }
             }
             const int c0 = sr * 4 + swz_chunk(sr, 2 * sh), c1 = sr * 4 + swz_chunk(sr, 2 * sh + 1);
             lx[b][0][c0] = make_uint4(h[0], h[1], h[2], h[3]);
@@ -198,8 +264,15 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
             lx[b][2][c0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
             lx[b][2][c1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
         }
-        if (FMT == FMT_B1_G128 && (kt & 3) == 0 && tid < BM)
-            ls[(kt >> 2) & 1][tid] = fp16_bits_to_f32(static_cast<uint16_t>(R.s));
+        if (GROUPED && kt % GSTEPS == 0 && tid < BM) {
+            const int gb = (kt / GSTEPS) & 1;
+            if (FMT == FMT_B1_G128) {
+                ls[gb][tid] = fp16_bits_to_f32(static_cast<uint16_t>(R.s));
+            } else {
+                ls[gb][tid] = bf16_bits_to_f32(R.s);
+                lb[gb][tid] = bf16_bits_to_f32(R.b);
+            }
+        }
     };
 
     floatx4_t acc[TI][TJ];
@@ -235,18 +308,29 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
                 }
             }
         }
-        if (FMT == FMT_B1_G128 && (kt & 3) == 3) {
-            // close the 128-k group: acc += scale[m][g] * group sum
-            const float *sg = ls[(kt >> 2) & 1];
+        if (GROUPED && kt % GSTEPS == GSTEPS - 1) {
+            // close the group: acc += scale[m][g] * (sum of code * x over the
+            // group) [+ bias[m][g] * (sum of x over the group), 4-bit]
+            const int gb = (kt / GSTEPS) & 1;
+            float xs[TJ];
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) xs[j] = FMT == FMT_U4_G64 ? lxs[gb][wn + 16 * j + fr] : 0.f;
 #pragma unroll
             for (int i = 0; i < TI; ++i) {
-                const float4 s4 = *reinterpret_cast<const float4 *>(sg + 16 * i + 4 * fq);
+                const float4 s4 = *reinterpret_cast<const float4 *>(&ls[gb][16 * i + 4 * fq]);
                 const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+                float bv[4] = {0.f, 0.f, 0.f, 0.f};
+                if (FMT == FMT_U4_G64) {
+                    const float4 b4 = *reinterpret_cast<const float4 *>(&lb[gb][16 * i + 4 * fq]);
+                    bv[0] = b4.x; bv[1] = b4.y; bv[2] = b4.z; bv[3] = b4.w;
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
 #pragma unroll
                     for (int j = 0; j < TJ; ++j) {
-                        acc[i][j][r] = fmaf(sv[r], gacc[i][j][r], acc[i][j][r]);
+                        float a = acc[i][j][r];
+                        if (FMT == FMT_U4_G64) a = fmaf(bv[r], xs[j], a);
+                        acc[i][j][r] = fmaf(sv[r], gacc[i][j][r], a);
                         gacc[i][j][r] = 0.f;
                     }
             }
@@ -256,7 +340,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
     // pipeline: LDS buffer kt & 1 holds step kt; register set s % D holds
     // step s from its load (D steps before it is staged) until it is staged
     // (one step before it is computed)
-    constexpr int D = FMT == FMT_I8_ROW ? QG_GEMM_DEPTH_I8 : QG_GEMM_DEPTH_B1;
+    constexpr int D = FMT == FMT_I8_ROW ? QG_GEMM_DEPTH_I8 : FMT == FMT_U4_G64 ? QG_GEMM_DEPTH_U4 : QG_GEMM_DEPTH_B1;
     Regs R[D];
 #pragma unroll
     for (int u = 0; u < D; ++u)

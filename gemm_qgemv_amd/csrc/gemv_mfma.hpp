@@ -102,19 +102,6 @@ constexpr int kMfmaTileOutBytes = 8 * 16 * 4;
 
 typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
 
-// 8 nibbles of one dword (8 consecutive inputs, even k in the low nibbles)
-// -> 8 bf16 codes in the order k = 0, 2, 4, 6, 1, 3, 5, 7.
-__device__ __forceinline__ bf16x8_t nibbles_to_bf16(uint32_t d)
-{
-    const uint32_t lo = d & 0x0f0f0f0fu, hi = (d >> 4) & 0x0f0f0f0fu;
-    uint4 v;
-    v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false));
-    v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true));
-    v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false));
-    v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true));
-    return __builtin_bit_cast(bf16x8_t, v);
-}
-
 __device__ __forceinline__ uint32_t u4_word(const uint4 &v, int i)
 {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;

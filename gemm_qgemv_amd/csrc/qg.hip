@@ -488,18 +488,19 @@ bool gemm_shape_ok(int64_t M, int64_t N)
     return ceil_div(M, 64) * ceil_div(N, 64) <= 0x7fffffffLL;   // smallest tile
 }
 
-void run_gemm(int fmt, const void *codes, const void *scales, const float *x, float *y,
-              int64_t M, int64_t K, int64_t N, void *ws, hipStream_t s)
+void run_gemm(int fmt, const void *codes, const void *scales, const void *biases, const float *x,
+              float *y, int64_t M, int64_t K, int64_t N, void *ws, hipStream_t s)
 {
     if (N <= kGemmViaGemv) {
         const int nb = static_cast<int>(N);
         const GemvPlan pl = plan_gemv(fmt, M, K, nb, false);
-        run_gemv(fmt, pl, codes, scales, nullptr, x, y, nullptr, M, K, nb, ws, s);
+        run_gemv(fmt, pl, codes, scales, biases, x, y, nullptr, M, K, nb, ws, s);
         return;
     }
     qg::GemmParams p{};
     p.codes = static_cast<const uint8_t *>(codes);
     p.scales = scales;
+    p.biases = static_cast<const uint16_t *>(biases);
     p.x = x;
     p.y = y;
     p.M = M;
@@ -508,8 +509,8 @@ void run_gemm(int fmt, const void *codes, const void *scales, const float *x, fl
     // the largest tile that still gives every compute unit a workgroup
     auto tiles = [&](int bm, int bn) { return ceil_div(M, bm) * ceil_div(N, bn); };
     const dim3 block(qg::kGemmThreads);
-    // (1-bit: at most 64 x 128, its per-group accumulators double the
-    // accumulator registers)
+    // (4-bit and 1-bit: at most 64 x 128, their per-group accumulators
+    // double the accumulator registers)
     int bm = 64, bn = 64;
     if (fmt == QG_I8_ROW && tiles(128, 128) >= kComputeUnits) bm = 128, bn = 128;
     else if (tiles(64, 128) >= kComputeUnits) bn = 128;
@@ -520,6 +521,9 @@ void run_gemm(int fmt, const void *codes, const void *scales, const float *x, fl
         if (bm == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_ROW, 128, 128>), grid, block, 0, s, p);
         else if (bn == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_ROW, 64, 128>), grid, block, 0, s, p);
         else hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_ROW, 64, 64>), grid, block, 0, s, p);
+    } else if (fmt == QG_U4_G64) {
+        if (bn == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_U4_G64, 64, 128>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_U4_G64, 64, 64>), grid, block, 0, s, p);
     } else {
         if (bn == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_B1_G128, 64, 128>), grid, block, 0, s, p);
         else hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_B1_G128, 64, 64>), grid, block, 0, s, p);
@@ -535,16 +539,16 @@ int gemm_entry(int fmt, const void *codes, const void *scales, const void *biase
     if (!y) return QG_ERR_NULL;
     if (N < 1 || N > kMaxN || !gemm_shape_ok(M, N)) return QG_ERR_SHAPE;
     if (!aligned(y, kAlign)) return QG_ERR_ALIGN;
-    if (fmt == QG_U4_G64) return QG_ERR_UNSUPPORTED;
     const size_t need = gemm_workspace(fmt, M, K, N);
     if (need > 0) {
         if (!ws || ws_bytes < need) return QG_ERR_WORKSPACE;
         if (!aligned(ws, kAlign)) return QG_ERR_ALIGN;
     }
-    Range all[6];
+    Range all[7];
     int n = 0;
     all[n++] = range_of(codes, M * row_bytes(fmt, K));
     all[n++] = range_of(scales, scale_bytes(fmt, M, K));
+    if (biases) all[n++] = range_of(biases, bias_bytes(fmt, M, K));
     all[n++] = range_of(x, N * K * 4);
     Range wr[2];
     int nw = 0;
@@ -554,7 +558,7 @@ int gemm_entry(int fmt, const void *codes, const void *scales, const void *biase
     if (st != QG_OK) return st;
 
     (void)hipGetLastError();
-    run_gemm(fmt, codes, scales, x, y, M, K, N, ws, stream);
+    run_gemm(fmt, codes, scales, biases, x, y, M, K, N, ws, stream);
     return launch_status();
 }
 
@@ -598,7 +602,7 @@ size_t qg_workspace_bytes(int op, int fmt, int64_t M, int64_t K, int64_t rows)
         return plan_gemv(fmt, M, K, static_cast<int>(rows), op == QG_OP_GEMV_ARGMAX).ws_bytes;
     }
     if (op == QG_OP_GEMM) {
-        if (rows < 1 || rows > kMaxN || fmt == QG_U4_G64) return 0;
+        if (rows < 1 || rows > kMaxN) return 0;
         return gemm_workspace(fmt, M, K, rows);
     }
     return 0;
@@ -615,7 +619,7 @@ const char *qg_status_str(int status)
     case QG_ERR_WORKSPACE: return "workspace missing or smaller than qg_workspace_bytes()";
     case QG_ERR_ALIAS: return "a written buffer overlaps another buffer";
     case QG_ERR_LAUNCH: return "kernel launch failed";
-    case QG_ERR_UNSUPPORTED: return "combination not implemented by this library";
+    case QG_ERR_UNSUPPORTED: return "combination not implemented by this library (reserved)";
     default: return "unknown status";
     }
 }

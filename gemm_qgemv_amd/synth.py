@@ -143,7 +143,13 @@ CASES = [
     Case("c4c_b1_gemm_17408x5120_n512", "gemm", B1_G128, 17408, 5120, 512, 4, 2),
     Case("c4d_b1_gemm_5120x17408_n512", "gemm", B1_G128, 5120, 17408, 512, 4, 3),
 ]
-CASES_BY_NAME = {c.name: c for c in CASES}
+# Measurement cases of widened rows (not configurations): the 4-bit prefill
+# at the 4-bit matvec shapes, with a 2048-token prompt.
+NEXT_CASES = [
+    Case("n2a_u4_gemm_6144x2048_n2048", "gemm", U4_G64, 6144, 2048, 2048, 5, 0),
+    Case("n2b_u4_gemm_2048x6144_n2048", "gemm", U4_G64, 2048, 6144, 2048, 5, 1),
+]
+CASES_BY_NAME = {c.name: c for c in CASES + NEXT_CASES}
 
 
 def case_inputs(c: Case) -> tuple[QWeights, np.ndarray]:

@@ -108,7 +108,8 @@ enum {
     QG_ERR_WORKSPACE = -5,   /* ws_bytes smaller than qg_workspace_bytes(...) */
     QG_ERR_ALIAS = -6,       /* a written buffer overlaps another buffer */
     QG_ERR_LAUNCH = -7,      /* the kernel launch failed */
-    QG_ERR_UNSUPPORTED = -8  /* a combination this library does not implement */
+    QG_ERR_UNSUPPORTED = -8  /* reserved: a combination this library does not implement
+                                (no entry point returns it at this ABI version) */
 };
 
 /* Control words at the start of every workspace (see Workspace above). */
@@ -140,7 +141,8 @@ int qgemv(int fmt, const void *codes, const void *scales, const void *biases,
  * 4GB Maxwell GPUs, "A packed Q1 prefill kernel with a narrow dispatch
  * window": the weights may be consumed packed.)
  *   X  float32 [N][K];  Y  float32 [N][M] (overwritten).  1 <= N <= 2^31-1.
- *   Formats: QG_I8_ROW and QG_B1_G128 (QG_U4_G64 returns QG_ERR_UNSUPPORTED).
+ *   All three formats; for QG_U4_G64 the bias term sum_g b[m][g] * (sum of
+ *   X[n][k] over group g) is added per group beside the scaled code sums.
  */
 int qgemm(int fmt, const void *codes, const void *scales, const void *biases,
           const float *x, float *y, int64_t M, int64_t K, int64_t N,

@@ -113,6 +113,9 @@ def test_aliasing_outputs():
                 base + 131072 + 64, M, K, 1, ws=base + (1 << 24), ws_bytes=need) == q.QG_ERR_ALIAS
 
 
-def test_prefill_affine_format_unsupported():
-    assert _err(q.qgemm, q.QG_U4_G64, A, A + 4096, A + 12288, A + 8192, A + 65536, 4, 64, 8) == \
-        q.QG_ERR_UNSUPPORTED
+def test_prefill_affine_format_checks():
+    # the 4-bit prefill needs its biases, and its biases must not overlap Y
+    assert _err(q.qgemm, q.QG_U4_G64, A, A + 4096, None, A + 8192, A + 65536, 4, 64, 8) == \
+        q.QG_ERR_NULL
+    assert _err(q.qgemm, q.QG_U4_G64, A, A + 4096, A + 65536, A + 8192, A + 65536, 4, 64, 8) == \
+        q.QG_ERR_ALIAS

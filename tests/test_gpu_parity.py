@@ -170,15 +170,15 @@ def test_exact_arithmetic_bit_exact(torch, orc, fmt, M, K, N):
     assert np.array_equal(want.astype(np.float64), ref), "fixture is not exact in float32"
     y, _ = gpu_gemv(torch, dev(w), x)
     assert np.array_equal(y, want), f"gemv not bit-exact: max diff {np.max(np.abs(y - want))}"
-    if fmt != synth.U4_G64:
-        yg = gpu_gemm(torch, dev(w), x)
-        assert np.array_equal(yg, want), "gemm not bit-exact"
+    yg = gpu_gemm(torch, dev(w), x)
+    assert np.array_equal(yg, want), "gemm not bit-exact"
 
 
 @pytest.mark.parametrize("fmt,M,K,N", [
     (synth.I8_ROW, 129, 1024, 17), (synth.I8_ROW, 300, 1040, 130), (synth.I8_ROW, 7, 48, 257),
     (synth.I8_ROW, 1024, 3584, 64), (synth.B1_G128, 129, 1024, 17), (synth.B1_G128, 260, 640, 300),
-    (synth.B1_G128, 5, 128, 129),
+    (synth.B1_G128, 5, 128, 129), (synth.U4_G64, 129, 1024, 17), (synth.U4_G64, 300, 1088, 130),
+    (synth.U4_G64, 7, 64, 257), (synth.U4_G64, 1024, 2048, 64), (synth.U4_G64, 4001, 192, 1503),
 ])
 def test_exact_arithmetic_prefill_bit_exact(torch, orc, fmt, M, K, N):
     """The matrix-core prefill path (more than 16 token rows) on exact inputs."""
@@ -210,7 +210,8 @@ def test_exact_arithmetic_prefill_large_grid(torch, orc, M, K, N):
     (synth.I8_ROW, 1, 16, 17), (synth.I8_ROW, 127, 1040, 129), (synth.I8_ROW, 1000, 1024, 300),
     (synth.I8_ROW, 4001, 1040, 1503),
     (synth.I8_ROW, 130, 3584, 33), (synth.B1_G128, 1, 128, 40), (synth.B1_G128, 250, 5120, 131),
-    (synth.B1_G128, 129, 1152, 256),
+    (synth.B1_G128, 129, 1152, 256), (synth.U4_G64, 1, 64, 40), (synth.U4_G64, 1000, 2048, 300),
+    (synth.U4_G64, 127, 6144, 129), (synth.U4_G64, 6144, 2048, 2048),
 ])
 def test_random_prefill_small(torch, orc, fmt, M, K, N):
     say(f"random prefill fmt={fmt} M={M} K={K} N={N}")
@@ -246,9 +247,8 @@ def test_random_small(torch, orc, fmt, M, K, N):
     y, idx = gpu_gemv(torch, dev(w), x, argmax=True, ws_fill=0xA5)
     check_bound(y, ref, a, f"gemv {fmt} {M}x{K} b{N}")
     check_argmax(idx, y, ref, a, orc, "argmax")
-    if fmt != synth.U4_G64:
-        yg = gpu_gemm(torch, dev(w), x)
-        check_bound(yg, ref, a, "gemm")
+    yg = gpu_gemm(torch, dev(w), x)
+    check_bound(yg, ref, a, "gemm")
 
 
 def test_argmax_ties_and_signed_zero(torch, orc):
