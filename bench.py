@@ -58,6 +58,8 @@ WORKLOADS = {
     "c4gemv": ["c4a_b1_gemv_17408x5120", "c4b_b1_gemv_5120x17408"],
     "c4gemm": ["c4c_b1_gemm_17408x5120_n512", "c4d_b1_gemm_5120x17408_n512"],
     "u4gemm": ["n2a_u4_gemm_6144x2048_n2048", "n2b_u4_gemm_2048x6144_n2048"],
+    "head64": ["n1a_u4_head_151936x2048_b64", "n1b_u4_head_151936x2048_b64_nologits"],
+    "head128": ["n1c_u4_head_151936x2048_b128", "n1d_u4_head_151936x2048_b128_nologits"],
 }
 METRIC = "effective weight GB/s and % of HBM peak, batch-1 qgemv; prefill qgemm TFLOP/s"
 
@@ -91,7 +93,8 @@ class Launch:
             for _ in range(self.copies - 1)]
         self.x = torch.from_numpy(x).cuda()
         self.y = torch.empty(case.rows * case.M, dtype=torch.float32, device="cuda")
-        op = {"gemv": q.QG_OP_GEMV, "gemv_argmax": q.QG_OP_GEMV_ARGMAX, "gemm": q.QG_OP_GEMM}[case.op]
+        op = {"gemv": q.QG_OP_GEMV, "gemv_argmax": q.QG_OP_GEMV_ARGMAX, "greedy": q.QG_OP_GEMV_ARGMAX,
+              "gemm": q.QG_OP_GEMM}[case.op]
         self.ws = tensors.workspace(op, case.fmt, case.M, case.K, case.rows)
         self.ws_bytes = 0 if self.ws is None else self.ws.numel()
         self.idx = torch.empty(case.rows, dtype=torch.int32, device="cuda")
@@ -107,8 +110,9 @@ class Launch:
         if case.op == "gemv":
             st = L.qgemv(case.fmt, c, s, b, self.x.data_ptr(), self.y.data_ptr(), case.M, case.K,
                          case.rows, ws, self.ws_bytes, stream)
-        elif case.op == "gemv_argmax":
-            st = L.qgemv_argmax(case.fmt, c, s, b, self.x.data_ptr(), self.y.data_ptr(),
+        elif case.op in ("gemv_argmax", "greedy"):
+            y = self.y.data_ptr() if case.op == "gemv_argmax" else None
+            st = L.qgemv_argmax(case.fmt, c, s, b, self.x.data_ptr(), y,
                                 self.idx.data_ptr(), case.M, case.K, case.rows, ws,
                                 self.ws_bytes, stream)
         else:
@@ -397,7 +401,7 @@ def main():
         per_case.append((L, avg, avg))
         unit = L.weight_bytes / (avg * 1e-3) / 1e9
         log(f"  {L.case.name}: {avg * 1e3:.2f} us per launch, {unit:.1f} GB/s weight"
-            + (f", {L.case.flops / (avg * 1e-3) / 1e12:.2f} TFLOP/s" if gemm else ""))
+            + (f", {L.case.flops / (avg * 1e-3) / 1e12:.2f} TFLOP/s" if gemm or L.case.rows > 1 else ""))
 
     src_hash = kernel_source_hash()
     traffic = load_traffic(args.workload, src_hash)

@@ -45,7 +45,8 @@ struct GemmParams {
     const void *scales;
     const uint16_t *biases;   // 4-bit format: bf16 [M][K/64]
     const float *x;   // [N][K]
-    float *y;         // [N][M]
+    float *y;         // [N][M], or nullptr (greedy head without logits)
+    unsigned long long *keys;  // greedy head: [N][tiles_m] tile keys, or nullptr
     int64_t M, K, N;
     int tiles_m, tiles_n;
 };
@@ -387,8 +388,12 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
         }
     }
 
-    // epilogue: row scale (int8), store Y[n][m .. m+3]
+    // epilogue: row scale (int8), store Y[n][m .. m+3]; greedy head: the
+    // tile's best (value, lowest index) key per token row
     const bool vec = (p.M & 3) == 0;
+    uint64_t best[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) best[j] = 0ull;
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
         const int64_t mb = m0 + 16 * i + 4 * fq;
@@ -402,18 +407,66 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
         for (int j = 0; j < TJ; ++j) {
             const int64_t n = n0 + wn + 16 * j + fr;
             if (n >= p.N) continue;
+            const float v[4] = {s[0] * acc[i][j][0], s[1] * acc[i][j][1], s[2] * acc[i][j][2],
+                                s[3] * acc[i][j][3]};
+            if (p.keys != nullptr) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (mb + r < p.M) {
+                        const uint64_t k = argmax_key(v[r], static_cast<uint32_t>(mb + r));
+                        best[j] = k > best[j] ? k : best[j];
+                    }
+            }
+            if (p.y == nullptr) continue;
             float *dst = p.y + n * p.M + mb;
-            const float v0 = s[0] * acc[i][j][0], v1 = s[1] * acc[i][j][1];
-            const float v2 = s[2] * acc[i][j][2], v3 = s[3] * acc[i][j][3];
             if (vec && mb + 3 < p.M) {
-                *reinterpret_cast<float4 *>(dst) = make_float4(v0, v1, v2, v3);
+                *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
             } else {
-                if (mb < p.M) dst[0] = v0;
-                if (mb + 1 < p.M) dst[1] = v1;
-                if (mb + 2 < p.M) dst[2] = v2;
-                if (mb + 3 < p.M) dst[3] = v3;
+                if (mb < p.M) dst[0] = v[0];
+                if (mb + 1 < p.M) dst[1] = v[1];
+                if (mb + 2 < p.M) dst[2] = v[2];
+                if (mb + 3 < p.M) dst[3] = v[3];
             }
         }
+    }
+    if (p.keys != nullptr) {
+        // lanes fr, fr + 16, fr + 32, fr + 48 hold the same token rows
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+            uint64_t k = best[j];
+            uint64_t o = shfl_xor_u64(k, 16);
+            k = o > k ? o : k;
+            o = shfl_xor_u64(k, 32);
+            k = o > k ? o : k;
+            const int64_t n = n0 + wn + 16 * j + fr;
+            if (fq == 0 && n < p.N) p.keys[n * p.tiles_m + tm] = k;
+        }
+    }
+}
+
+// Greedy selection over the tile keys of the prefill-shaped head: one
+// workgroup per token row n reduces keys[n][0 .. tiles_m) and writes idx[n]
+// (the key order makes the result the lowest index of the maximum).
+__global__ __launch_bounds__(256) void argmax_keys_kernel(const unsigned long long *keys, int tiles_m,
+                                                          int32_t *idx)
+{
+    __shared__ unsigned long long s_best[4];
+    const int64_t n = blockIdx.x;
+    uint64_t best = 0ull;
+    for (int t = threadIdx.x; t < tiles_m; t += blockDim.x) {
+        const uint64_t k = keys[n * tiles_m + t];
+        best = k > best ? k : best;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const uint64_t other = shfl_xor_u64(best, o);
+        best = other > best ? other : best;
+    }
+    if ((threadIdx.x & 63) == 0) s_best[threadIdx.x >> 6] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < 4; ++w) best = s_best[w] > best ? s_best[w] : best;
+        idx[n] = static_cast<int32_t>(argmax_key_index(best));
     }
 }
 

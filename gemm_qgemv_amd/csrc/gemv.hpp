@@ -492,7 +492,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
                 if (FMT == FMT_I8_ROW)
                     v *= static_cast<const float *>(p.scales)[m];
                 if (p.nsplit == 1) {
-                    p.y[own_b * p.M + m] = v;
+                    if (p.y) p.y[own_b * p.M + m] = v;
                     if (best_m < 0 || v > best_v || (v == best_v && m < best_m)) {
                         best_v = v;
                         best_m = m;
@@ -532,7 +532,7 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvParams p)
             float v = 0.f;
             for (int s = 0; s < p.nsplit; ++s)
                 v += p.part[(static_cast<int64_t>(s) * p.nb + b) * p.M + m];
-            p.y[b * p.M + m] = v;
+            if (p.y) p.y[b * p.M + m] = v;
             const uint64_t key = argmax_key(v, static_cast<uint32_t>(m));
             best = key > best ? key : best;
         }

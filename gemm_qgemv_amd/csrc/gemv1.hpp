@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256) void gemv1_kernel(Gemv1Params p)
         if (writer && m < m_end) {
             float v = acc[0];
             if constexpr (FMT == FMT_I8_ROW) v *= blk.rs;
-            p.y[m] = v;
+            if (p.y) p.y[m] = v;
             if (best_m < 0 || v > best_v) {  // rows arrive in increasing order
                 best_v = v;
                 best_m = m;

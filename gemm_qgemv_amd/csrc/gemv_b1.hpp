@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void gemv_b1_lut_kernel(B1LutParams p)
             return;
         }
     }
-    if (mv) p.y[m] = acc;
+    if (mv && p.y) p.y[m] = acc;
     if (p.idx != nullptr) {
         __shared__ unsigned long long s_key;
         if (tid == 0) s_key = 0ull;

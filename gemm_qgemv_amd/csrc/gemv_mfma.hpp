@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_u4_kernel(GemvMfmaPara
                 if (q < 2 && n < p.nb && m < p.M) {
                     if (p.stage_out)
                         out_stage[((ct - tb_wg) * 8 + n) * 16 + r] = v;
-                    else
+                    else if (p.y)
                         p.y[static_cast<int64_t>(n) * p.M + m] = v;
                     if (best_m[i] < 0 || v > best_v[i]) {   // rows arrive in increasing order
                         best_v[i] = v;
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_u4_kernel(GemvMfmaPara
         }
     }
 
-    if (p.stage_out) {
+    if (p.stage_out && p.y) {
         __syncthreads();
         const int64_t m0 = tb_wg * 16, rows = min(te_wg * 16, p.M) - m0;
         for (int n = 0; n < p.nb; ++n)

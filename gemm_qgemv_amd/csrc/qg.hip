@@ -440,10 +440,10 @@ int gemv_entry(int fmt, const void *codes, const void *scales, const void *biase
 {
     int st = check_weights(fmt, codes, scales, biases, x, M, K);
     if (st != QG_OK) return st;
-    if (!y) return QG_ERR_NULL;
-    if (batch < 1 || batch > QG_MAX_GEMV_BATCH) return QG_ERR_SHAPE;
-    if (!aligned(y, kAlign)) return QG_ERR_ALIGN;
     const bool argmax = idx != nullptr;
+    if (!y && !argmax) return QG_ERR_NULL;   // the greedy head may skip its logits
+    if (batch < 1 || batch > QG_MAX_GEMV_BATCH) return QG_ERR_SHAPE;
+    if (y && !aligned(y, kAlign)) return QG_ERR_ALIGN;
     if (argmax && !aligned(idx, 4)) return QG_ERR_ALIGN;
     const GemvPlan pl = plan_gemv(fmt, M, K, batch, argmax);
     if (pl.ws_bytes > 0) {
@@ -458,7 +458,7 @@ int gemv_entry(int fmt, const void *codes, const void *scales, const void *biase
     all[n++] = range_of(x, int64_t(batch) * K * 4);
     Range wr[3];
     int nw = 0;
-    wr[nw++] = all[n++] = range_of(y, int64_t(batch) * M * 4);
+    if (y) wr[nw++] = all[n++] = range_of(y, int64_t(batch) * M * 4);
     if (argmax) wr[nw++] = all[n++] = range_of(idx, int64_t(batch) * 4);
     if (pl.ws_bytes > 0) wr[nw++] = all[n++] = range_of(ws, static_cast<int64_t>(pl.ws_bytes));
     st = check_alias(all, n, wr, nw);
@@ -488,35 +488,44 @@ bool gemm_shape_ok(int64_t M, int64_t N)
     return ceil_div(M, 64) * ceil_div(N, 64) <= 0x7fffffffLL;   // smallest tile
 }
 
-void run_gemm(int fmt, const void *codes, const void *scales, const void *biases, const float *x,
-              float *y, int64_t M, int64_t K, int64_t N, void *ws, hipStream_t s)
+// The largest tile that still gives every compute unit a workgroup
+// (4-bit and 1-bit: at most 64 x 128, their per-group accumulators double
+// the accumulator registers).
+void gemm_tile(int fmt, int64_t M, int64_t N, int &bm, int &bn)
 {
-    if (N <= kGemmViaGemv) {
-        const int nb = static_cast<int>(N);
-        const GemvPlan pl = plan_gemv(fmt, M, K, nb, false);
-        run_gemv(fmt, pl, codes, scales, biases, x, y, nullptr, M, K, nb, ws, s);
-        return;
-    }
+    auto tiles = [&](int tm, int tn) { return ceil_div(M, tm) * ceil_div(N, tn); };
+    bm = 64;
+    bn = 64;
+    // 128 token rows per tile only where that pads no more than 64 would
+    // (64 token rows with 128-row tiles would halve the useful MFMA work)
+    const bool n128 = N % 128 == 0 || N % 128 > 64;
+    if (!n128) return;
+    if (fmt == QG_I8_ROW && tiles(128, 128) >= kComputeUnits) bm = 128, bn = 128;
+    else if (tiles(64, 128) >= kComputeUnits) bn = 128;
+}
+
+// Enqueue the matrix-core prefill kernel; with `keys`, the greedy head's
+// tile keys [N][tiles_m] as well (y may then be nullptr).
+void launch_gemm(int fmt, const void *codes, const void *scales, const void *biases,
+                 const float *x, float *y, unsigned long long *keys, int64_t M, int64_t K,
+                 int64_t N, hipStream_t s)
+{
     qg::GemmParams p{};
     p.codes = static_cast<const uint8_t *>(codes);
     p.scales = scales;
     p.biases = static_cast<const uint16_t *>(biases);
     p.x = x;
     p.y = y;
+    p.keys = keys;
     p.M = M;
     p.K = K;
     p.N = N;
-    // the largest tile that still gives every compute unit a workgroup
-    auto tiles = [&](int bm, int bn) { return ceil_div(M, bm) * ceil_div(N, bn); };
-    const dim3 block(qg::kGemmThreads);
-    // (4-bit and 1-bit: at most 64 x 128, their per-group accumulators
-    // double the accumulator registers)
-    int bm = 64, bn = 64;
-    if (fmt == QG_I8_ROW && tiles(128, 128) >= kComputeUnits) bm = 128, bn = 128;
-    else if (tiles(64, 128) >= kComputeUnits) bn = 128;
+    int bm, bn;
+    gemm_tile(fmt, M, N, bm, bn);
     p.tiles_m = static_cast<int>(ceil_div(M, bm));
     p.tiles_n = static_cast<int>(ceil_div(N, bn));
     const dim3 grid(static_cast<unsigned>(int64_t(p.tiles_m) * p.tiles_n));
+    const dim3 block(qg::kGemmThreads);
     if (fmt == QG_I8_ROW) {
         if (bm == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_ROW, 128, 128>), grid, block, 0, s, p);
         else if (bn == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_ROW, 64, 128>), grid, block, 0, s, p);
@@ -528,6 +537,66 @@ void run_gemm(int fmt, const void *codes, const void *scales, const void *biases
         if (bn == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_B1_G128, 64, 128>), grid, block, 0, s, p);
         else hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_B1_G128, 64, 64>), grid, block, 0, s, p);
     }
+}
+
+void run_gemm(int fmt, const void *codes, const void *scales, const void *biases, const float *x,
+              float *y, int64_t M, int64_t K, int64_t N, void *ws, hipStream_t s)
+{
+    if (N <= kGemmViaGemv) {
+        const int nb = static_cast<int>(N);
+        const GemvPlan pl = plan_gemv(fmt, M, K, nb, false);
+        run_gemv(fmt, pl, codes, scales, biases, x, y, nullptr, M, K, nb, ws, s);
+        return;
+    }
+    launch_gemm(fmt, codes, scales, biases, x, y, nullptr, M, K, N, s);
+}
+
+// ---------------------------------------------------------------------------
+// Greedy head over more than QG_MAX_GEMV_BATCH rows: the prefill kernel with
+// tile keys in the workspace (after the control words), then one workgroup
+// per row reduces its keys. The logits may be skipped (y == nullptr).
+// ---------------------------------------------------------------------------
+
+size_t wide_argmax_workspace(int fmt, int64_t M, int64_t N)
+{
+    int bm, bn;
+    gemm_tile(fmt, M, N, bm, bn);
+    return align256(kCtlBytes + static_cast<size_t>(N) * ceil_div(M, bm) * 8);
+}
+
+int wide_argmax_entry(int fmt, const void *codes, const void *scales, const void *biases,
+                      const float *x, float *y, int32_t *idx, int64_t M, int64_t K, int64_t N,
+                      void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int st = check_weights(fmt, codes, scales, biases, x, M, K);
+    if (st != QG_OK) return st;
+    if (N < 1 || N > QG_MAX_ARGMAX_BATCH) return QG_ERR_SHAPE;
+    if ((y && !aligned(y, kAlign)) || !aligned(idx, 4)) return QG_ERR_ALIGN;
+    const size_t need = wide_argmax_workspace(fmt, M, N);
+    if (!ws || ws_bytes < need) return QG_ERR_WORKSPACE;
+    if (!aligned(ws, kAlign)) return QG_ERR_ALIGN;
+    Range all[8];
+    int n = 0;
+    all[n++] = range_of(codes, M * row_bytes(fmt, K));
+    all[n++] = range_of(scales, scale_bytes(fmt, M, K));
+    if (biases) all[n++] = range_of(biases, bias_bytes(fmt, M, K));
+    all[n++] = range_of(x, N * K * 4);
+    Range wr[3];
+    int nw = 0;
+    if (y) wr[nw++] = all[n++] = range_of(y, N * M * 4);
+    wr[nw++] = all[n++] = range_of(idx, N * 4);
+    wr[nw++] = all[n++] = range_of(ws, static_cast<int64_t>(need));
+    st = check_alias(all, n, wr, nw);
+    if (st != QG_OK) return st;
+
+    (void)hipGetLastError();
+    auto *keys = reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + kCtlBytes);
+    launch_gemm(fmt, codes, scales, biases, x, y, keys, M, K, N, stream);
+    int bm, bn;
+    gemm_tile(fmt, M, N, bm, bn);
+    hipLaunchKernelGGL(qg::argmax_keys_kernel, dim3(static_cast<unsigned>(N)), dim3(256), 0, stream,
+                       keys, static_cast<int>(ceil_div(M, bm)), idx);
+    return launch_status();
 }
 
 int gemm_entry(int fmt, const void *codes, const void *scales, const void *biases,
@@ -582,6 +651,9 @@ int qgemv_argmax(int fmt, const void *codes, const void *scales, const void *bia
                  int batch, void *ws, size_t ws_bytes, hipStream_t stream)
 {
     if (!idx) return QG_ERR_NULL;
+    if (batch > QG_MAX_GEMV_BATCH)
+        return wide_argmax_entry(fmt, codes, scales, biases, x, logits, idx, M, K, batch, ws,
+                                 ws_bytes, stream);
     return gemv_entry(fmt, codes, scales, biases, x, logits, idx, M, K, batch, ws, ws_bytes,
                       stream);
 }
@@ -597,6 +669,8 @@ size_t qg_workspace_bytes(int op, int fmt, int64_t M, int64_t K, int64_t rows)
 {
     if (fmt != QG_I8_ROW && fmt != QG_U4_G64 && fmt != QG_B1_G128) return 0;
     if (M < 1 || M > kMaxM || K < 1 || K > kMaxK || K % k_unit(fmt) != 0) return 0;
+    if (op == QG_OP_GEMV_ARGMAX && rows > QG_MAX_GEMV_BATCH && rows <= QG_MAX_ARGMAX_BATCH)
+        return wide_argmax_workspace(fmt, M, rows);
     if (op == QG_OP_GEMV || op == QG_OP_GEMV_ARGMAX) {
         if (rows < 1 || rows > QG_MAX_GEMV_BATCH) return 0;
         return plan_gemv(fmt, M, K, static_cast<int>(rows), op == QG_OP_GEMV_ARGMAX).ws_bytes;

@@ -110,7 +110,7 @@ def draw_x(rows: int, K: int, rng: np.random.Generator) -> np.ndarray:
 @dataclasses.dataclass(frozen=True)
 class Case:
     name: str
-    op: str          # "gemv", "gemv_argmax" or "gemm"
+    op: str          # "gemv", "gemv_argmax", "greedy" (argmax, no logits) or "gemm"
     fmt: int
     M: int
     K: int
@@ -144,10 +144,15 @@ CASES = [
     Case("c4d_b1_gemm_5120x17408_n512", "gemm", B1_G128, 5120, 17408, 512, 4, 3),
 ]
 # Measurement cases of widened rows (not configurations): the 4-bit prefill
-# at the 4-bit matvec shapes, with a 2048-token prompt.
+# at the 4-bit matvec shapes, with a 2048-token prompt; the greedy head at 64
+# and 128 rows, with logits and without ("greedy": qgemv_argmax, logits NULL).
 NEXT_CASES = [
     Case("n2a_u4_gemm_6144x2048_n2048", "gemm", U4_G64, 6144, 2048, 2048, 5, 0),
     Case("n2b_u4_gemm_2048x6144_n2048", "gemm", U4_G64, 2048, 6144, 2048, 5, 1),
+    Case("n1a_u4_head_151936x2048_b64", "gemv_argmax", U4_G64, 151936, 2048, 64, 2, 0, x_variant=6),
+    Case("n1b_u4_head_151936x2048_b64_nologits", "greedy", U4_G64, 151936, 2048, 64, 2, 0, x_variant=6),
+    Case("n1c_u4_head_151936x2048_b128", "gemv_argmax", U4_G64, 151936, 2048, 128, 2, 0, x_variant=7),
+    Case("n1d_u4_head_151936x2048_b128_nologits", "greedy", U4_G64, 151936, 2048, 128, 2, 0, x_variant=7),
 ]
 CASES_BY_NAME = {c.name: c for c in CASES + NEXT_CASES}
 

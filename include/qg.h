@@ -117,6 +117,9 @@ enum {
 
 /* Largest batch of qgemv / qgemv_argmax. */
 #define QG_MAX_GEMV_BATCH 16
+/* Largest batch of the greedy head (qgemv_argmax); above QG_MAX_GEMV_BATCH
+ * it runs as the prefill product with per-tile argmax keys. */
+#define QG_MAX_ARGMAX_BATCH 256
 
 /*
  * qgemv -- batch-1 (up to QG_MAX_GEMV_BATCH) quantized matrix-vector product.
@@ -156,8 +159,15 @@ int qgemm(int fmt, const void *codes, const void *scales, const void *biases,
  * (Pushing the limits of legacy hardware, "Build the execution path, then
  * share the weights": the head keeps per-tile maxima with their original
  * indices, and greedy selection stays on the device.)
- *   logits  float32 [batch][M] (must not be NULL);  idx int32 [batch].
- *   Same shape limits as qgemv. Needs a workspace.
+ *   logits  float32 [batch][M], or NULL: then no logits are written (the
+ *           greedy-only head; the maxima still come from the same float32
+ *           values a non-NULL call writes).
+ *   idx     int32 [batch].
+ *   1 <= batch <= QG_MAX_ARGMAX_BATCH; other limits as qgemv. Up to
+ *   QG_MAX_GEMV_BATCH rows use the matrix-vector kernels; more rows use the
+ *   prefill kernels, which keep one (value, index) key per 64- or 128-row
+ *   tile and token row in the workspace and reduce them in a second launch
+ *   (the head's "tile maxima" of the page above). Needs a workspace.
  */
 int qgemv_argmax(int fmt, const void *codes, const void *scales,
                  const void *biases, const float *x, float *logits,

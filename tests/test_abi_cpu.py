@@ -119,3 +119,29 @@ def test_prefill_affine_format_checks():
         q.QG_ERR_NULL
     assert _err(q.qgemm, q.QG_U4_G64, A, A + 4096, A + 65536, A + 8192, A + 65536, 4, 64, 8) == \
         q.QG_ERR_ALIAS
+
+
+def test_wide_greedy_head_checks():
+    """More than QG_MAX_GEMV_BATCH rows of the greedy head: tile keys in the
+    workspace (after the control words), at most QG_MAX_ARGMAX_BATCH rows;
+    logits may be NULL there as for small batches, but plain qgemv needs y."""
+    hdr = open(HEADER).read()
+    assert f"#define QG_MAX_ARGMAX_BATCH {q.QG_MAX_ARGMAX_BATCH}" in hdr
+    M, K = 151936, 2048
+    for n in (17, 64, 128, q.QG_MAX_ARGMAX_BATCH):
+        need = q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_U4_G64, M, K, n)
+        assert need >= q.QG_WS_CONTROL_BYTES + n * (M // 64) * 8
+    assert q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_U4_G64, M, K,
+                                q.QG_MAX_ARGMAX_BATCH + 1) == 0
+    codes, scales, biases = A, A + (1 << 28), A + (1 << 29)
+    x, idx, ws = A + (1 << 30), A + (1 << 32), A + (1 << 33)
+    need = q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_U4_G64, M, K, 64)
+    assert _err(q.qgemv_argmax, q.QG_U4_G64, codes, scales, biases, x, None, idx, M, K, 64,
+                ws=ws, ws_bytes=need - 1) == q.QG_ERR_WORKSPACE
+    assert _err(q.qgemv_argmax, q.QG_U4_G64, codes, scales, biases, x, None, idx, M, K,
+                q.QG_MAX_ARGMAX_BATCH + 1, ws=ws, ws_bytes=1 << 30) == q.QG_ERR_SHAPE
+    # idx inside the keys area of the workspace
+    assert _err(q.qgemv_argmax, q.QG_U4_G64, codes, scales, biases, x, None, ws + 8192, M, K, 64,
+                ws=ws, ws_bytes=need) == q.QG_ERR_ALIAS
+    # qgemv without an output
+    assert _err(q.qgemv, q.QG_U4_G64, codes, scales, biases, x, None, M, K, 1) == q.QG_ERR_NULL

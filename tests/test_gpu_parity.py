@@ -360,6 +360,75 @@ def test_small_batch_u4_ties(torch, orc):
 
 
 # ---------------------------------------------------------------------------
+# the greedy head without logits, and over more rows than the matrix-vector
+# kernels take (prefill kernels with per-tile keys)
+# ---------------------------------------------------------------------------
+
+def gpu_greedy(torch, w, x, logits=True):
+    """qgemv_argmax through the C ABI; returns (logits or None, idx)."""
+    batch = x.shape[0]
+    xd = torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
+    y = Out(torch, batch * w.M) if logits else None
+    idx = Out(torch, batch, "int32")
+    ws = tensors.workspace(q.QG_OP_GEMV_ARGMAX, w.fmt, w.M, w.K, batch)
+    ws[q.QG_WS_CONTROL_BYTES:].fill_(0x3C)   # scratch may hold anything
+    q.qgemv_argmax(w.fmt, w.codes, w.scales, w.biases, xd, None if y is None else y.t, idx.t,
+                   w.M, w.K, batch, ws)
+    torch.cuda.synchronize()
+    idx.check_guards()
+    assert not ws[:q.QG_WS_CONTROL_BYTES].cpu().numpy().any(), "control words not left at zero"
+    if y is None:
+        return None, idx.t.cpu().numpy()
+    y.check_guards()
+    return y.t.cpu().numpy().reshape(batch, w.M), idx.t.cpu().numpy()
+
+
+@pytest.mark.parametrize("fmt,M,K,N", [
+    (synth.U4_G64, 9000, 2048, 1), (synth.I8_ROW, 5000, 1024, 1), (synth.B1_G128, 3000, 1280, 1),
+    (synth.U4_G64, 40007, 512, 3), (synth.I8_ROW, 777, 1040, 5), (synth.B1_G128, 1000, 6144, 9),
+    (synth.U4_G64, 30001, 2048, 64), (synth.I8_ROW, 9000, 1024, 100), (synth.B1_G128, 5000, 1280, 17),
+    (synth.U4_G64, 20000, 2048, 128), (synth.U4_G64, 4099, 1024, 256),
+])
+def test_greedy_head_with_and_without_logits(torch, orc, fmt, M, K, N):
+    say(f"greedy fmt={fmt} M={M} K={K} N={N}")
+    rng = synth.rng_for(500 + fmt, M * 3 + N)
+    w = synth.draw_weights(fmt, M, K, rng)
+    x = synth.draw_x(N, K, rng)
+    ref, a = orc.qgemv(fmt, w.codes, w.scales, w.biases, x, M, K)
+    wd = dev(w)
+    y, idx = gpu_greedy(torch, wd, x, logits=True)
+    check_bound(y, ref, a, f"greedy {fmt} {M}x{K} n{N}")
+    check_argmax(idx, y, ref, a, orc, "greedy")
+    _, idx2 = gpu_greedy(torch, wd, x, logits=False)
+    assert np.array_equal(idx, idx2), "logits-free call chose other rows"
+
+
+def test_wide_greedy_head_ties():
+    """Equal maxima in different 64-row tiles (first row, last row, the
+    middle) with 64 rows of activations."""
+    import torch as t
+    orc = oracle.get()
+    say("wide greedy ties")
+    rng = np.random.default_rng(12)
+    M, K, N = 20000, 1024, 64
+    w = synth.draw_weights(synth.U4_G64, M, K, rng)
+    x = synth.draw_x(N, K, rng)
+    ref, _ = orc.qgemv(synth.U4_G64, w.codes, w.scales, w.biases, x, M, K)
+    top = int(np.argmax(ref[0]))
+    for dst in (0, M - 1, 10000, 10063):
+        if dst != top:
+            for arr in (w.codes, w.scales, w.biases):
+                arr[dst] = arr[top]
+    ref, a = orc.qgemv(synth.U4_G64, w.codes, w.scales, w.biases, x, M, K)
+    y, idx = gpu_greedy(t, dev(w), x, logits=True)
+    check_bound(y, ref, a, "wide ties")
+    check_argmax(idx, y, ref, a, orc, "wide ties")
+    assert idx[0] == min(0, top) == 0
+    _, idx2 = gpu_greedy(t, dev(w), x, logits=False)
+    assert np.array_equal(idx, idx2)
+
+
+# ---------------------------------------------------------------------------
 # the configurations at full size
 # ---------------------------------------------------------------------------
 
