@@ -50,6 +50,10 @@ class Oracle:
         lib.oracle_fp16_value.argtypes = [ctypes.c_uint16]
         lib.oracle_fp16_value.restype = D
         lib.oracle_num_threads.restype = I32
+        lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+        lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+        lib.oracle_embed.argtypes = [P, P, P, P, I64, I64, I64, P]
+        lib.oracle_embed.restype = I32
         for f in (lib.oracle_decode, lib.oracle_qgemv, lib.oracle_qgemv_sample,
                   lib.oracle_argmax):
             f.restype = I32
@@ -118,6 +122,19 @@ class Oracle:
             M, K, x.shape[0], self._ptr(n_idx), self._ptr(m_idx), n_idx.shape[0],
             self._ptr(y), self._ptr(a)), "qgemv_sample")
         return y, a
+
+    def f32_to_f16(self, v: float) -> int:
+        """IEEE binary16 bits of float32 v, rounded to nearest even."""
+        return int(self.lib.oracle_f32_to_f16(v))
+
+    def embed(self, codes, scales, biases, ids, M, K):
+        """Embedding rows e[t][k] of the 4-bit format (float32 [n][K])."""
+        c, s, b = self._prep(codes, scales, biases)
+        ids = np.ascontiguousarray(ids, np.int32)
+        out = np.empty((len(ids), K), np.float32)
+        self._check(self.lib.oracle_embed(self._ptr(c), self._ptr(s), self._ptr(b), self._ptr(ids),
+                                           M, K, len(ids), self._ptr(out)), "embed")
+        return out
 
     def argmax(self, y):
         """Lowest index of the row maximum, and the top-2 gap, per row."""

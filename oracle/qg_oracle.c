@@ -53,6 +53,19 @@
  * within one double rounding; the sum over K carries a relative error of
  * at most about K * 2^-53 of a[n][m], far below any tolerance applied.
  *
+ * Embedding rows (4-bit format only): e[t][k] = the decoded weight of row
+ * ids[t], input k, as a float32 the way the pages' decoder produces it: the
+ * affine operations done separately in float32 (scale * code, exact, then
+ * + bias, rounded to nearest even), the result rounded to an IEEE binary16
+ * (nearest even, subnormals and signed zero kept) and widened back to
+ * float32. (Pushing the limits of legacy hardware, "Half a billion values,
+ * and one negative zero": the direct decoder kept the separate affine
+ * operations and the inherited FP16 round-trip, and the GPU lookup needed
+ * exact denormal, signed-zero and round-to-nearest-even behaviour.) Rows of
+ * ids outside [0, M) come out as quiet NaN. The float32 operations are
+ * plain C float arithmetic (IEEE binary32 on this host; ISO C mode, so no
+ * contraction); the binary16 rounding is written out bit by bit below.
+ *
  * Threads: the (n, m) loop runs under OpenMP when built with -fopenmp;
  * nothing else is parallel, tiled or reordered.
  */
@@ -93,6 +106,52 @@ double oracle_fp16_value(uint16_t bits)
     else
         v = ldexp((double)(1024 + f), e - 25);  /* (1 + f/1024) * 2^(e-15) */
     return sign ? -v : v;
+}
+
+/* float32 -> IEEE binary16 bit pattern, rounding to nearest, ties to even;
+ * subnormal results and the sign of zero kept; overflow to infinity; NaN to
+ * a quiet NaN. The float32 value is sig * 2^E with an integer significand;
+ * the binary16 quantum at its magnitude is 2^max(L - 10, -24), L the
+ * exponent of its leading bit. */
+uint16_t oracle_f32_to_f16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    const int e = (int)((u >> 23) & 0xffu);
+    const uint32_t man = u & 0x7fffffu;
+    if (e == 0xff)
+        return (uint16_t)(sign | (man ? 0x7e00u : 0x7c00u));
+    if (e == 0 && man == 0)
+        return sign;
+    uint64_t sig = e ? (man | 0x800000u) : man;
+    const int E = e ? e - 150 : -149;
+    int L = E;
+    for (uint64_t t = sig; t > 1; t >>= 1)
+        ++L;                                   /* L = floor(log2(sig)) + E */
+    int qe = L - 10 > -24 ? L - 10 : -24;      /* exponent of the quantum */
+    const int shift = qe - E;                  /* low bits to drop, >= 0 here */
+    uint64_t r;
+    if (shift <= 0) {
+        r = sig << (-shift);
+    } else if (shift > 40) {
+        r = 0;                                 /* below half the quantum */
+    } else {
+        r = sig >> shift;
+        const uint64_t rem = sig & ((1ull << shift) - 1), half = 1ull << (shift - 1);
+        if (rem > half || (rem == half && (r & 1)))
+            ++r;
+    }
+    if (r >= 2048) {                           /* rounding carried into the next binade */
+        r >>= 1;
+        ++qe;
+    }
+    if (r < 1024)                              /* subnormal (qe == -24) or zero */
+        return (uint16_t)(sign | r);
+    const int e16 = qe + 25;                   /* value = r * 2^qe = (r/1024) * 2^(e16-15) */
+    if (e16 >= 31)
+        return (uint16_t)(sign | 0x7c00u);
+    return (uint16_t)(sign | ((uint32_t)e16 << 10) | (uint32_t)(r - 1024));
 }
 
 /* ---- the weight ------------------------------------------------------ */
@@ -243,6 +302,31 @@ int oracle_argmax(const double *y, int64_t M, int64_t N, int32_t *idx,
                 second = row[m];
         idx[n] = (int32_t)best;
         gap[n] = (M > 1) ? row[best] - second : INFINITY;
+    }
+    return OR_OK;
+}
+
+/* Embedding rows of the 4-bit format (see the header comment). */
+int oracle_embed(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
+                 const int32_t *ids, int64_t M, int64_t K, int64_t n, float *out)
+{
+    if (!shape_ok(OR_U4_G64, M, K) || n < 0)
+        return OR_BAD_SHAPE;
+    for (int64_t t = 0; t < n; ++t) {
+        const int64_t id = ids[t];
+        for (int64_t k = 0; k < K; ++k) {
+            float v = NAN;
+            if (id >= 0 && id < M) {
+                const uint8_t byte = codes[id * (K / 2) + k / 2];
+                const int q = (k & 1) ? byte >> 4 : byte & 15;
+                const float s = (float)oracle_bf16_value(scales[id * (K / 64) + k / 64]);
+                const float b = (float)oracle_bf16_value(biases[id * (K / 64) + k / 64]);
+                const float prod = s * (float)q;   /* exact: 8 x 4 significant bits */
+                const float a = prod + b;          /* one float32 rounding */
+                v = (float)oracle_fp16_value(oracle_f32_to_f16(a));
+            }
+            out[t * K + k] = v;
+        }
     }
     return OR_OK;
 }

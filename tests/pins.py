@@ -16,7 +16,13 @@ the oracle itself:
 * invariants: linearity in x, permutation of activation rows, duplicate rows;
 * a second opinion from numpy's own half-precision decoding and bit
   unpacking on random tiny matrices, including the extreme codes;
-* brute-force argmax on tiny vectors with ties.
+* brute-force argmax on tiny vectors with ties;
+* embedding rows: float32 -> binary16 rounding against numpy's own
+  conversion over every binary16 value, its neighbours and the midpoints
+  between them; whole rows against an exact-rational reference (the affine
+  value as a fraction, rounded to float32 here in integer arithmetic, then
+  numpy's binary16 round trip) and against hand-derived IEEE cases (ties to
+  even, signed zeros, the smallest subnormal, overflow).
 
 The same pins run against planted-mistake builds of the oracle
 (``test_oracle_mutants.py``) to show that each plausible mistake fails one.
@@ -343,6 +349,138 @@ def pin_argmax_brute_force(orc):
     assert list(idx) == [1, 0]
 
 
+# ---------------------------------------------------------------------------
+# embedding rows (4-bit format)
+# ---------------------------------------------------------------------------
+
+def pin_f16_rounding(orc):
+    """The oracle's float32 -> binary16 rounding equals numpy's on every
+    binary16 value, one float32 step either side of it, and the float32
+    midpoints between neighbouring binary16 values (ties) with a float32
+    step either side."""
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = h.view(np.float16).astype(np.float32)
+    fin = np.isfinite(v)
+    v = v[fin]
+    nxt = np.nextafter(v, np.float32(np.inf))
+    prv = np.nextafter(v, np.float32(-np.inf))
+    hf = h[fin].view(np.float16)
+    up = np.nextafter(hf, np.float16(np.inf)).astype(np.float32)
+    mid = ((v.astype(np.float64) + up.astype(np.float64)) / 2).astype(np.float32)   # exact
+    cases = np.concatenate([v, nxt, prv, mid, np.nextafter(mid, np.float32(np.inf)),
+                            np.nextafter(mid, np.float32(-np.inf)),
+                            np.array([np.inf, -np.inf, 65520.0, -65520.0, 1e-30, -1e-30], np.float32)])
+    cases = cases[np.isfinite(cases) | np.isinf(cases)]
+    with np.errstate(over="ignore"):
+        want = cases.astype(np.float16).view(np.uint16)
+    got = np.array([orc.f32_to_f16(float(c)) for c in cases], np.uint16)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"binary16 rounding differs for {cases[bad[:5]]}: {got[bad[:5]]} vs {want[bad[:5]]}"
+
+
+def _f32_nearest_even(fr):
+    """float32 nearest (ties to even) to the exact rational fr."""
+    from fractions import Fraction
+    if fr == 0:
+        return np.float32(0.0)
+    sign = -1.0 if fr < 0 else 1.0
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    qe = max(e - 23, -149)                     # exponent of the float32 quantum
+    sc = a / Fraction(2) ** qe
+    n = sc.numerator // sc.denominator
+    rem = sc - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    if n * 2.0 ** qe >= 2.0 ** 128:
+        return np.float32(sign * np.inf)
+    return np.float32(sign * n * 2.0 ** qe)
+
+
+def _embed_reference(scale_bits, bias_bits, q):
+    """The embedding value written out: exact scale * code + bias, one
+    rounding to float32, one to binary16, widened back (float32 bits)."""
+    from fractions import Fraction
+    sf = np.array([scale_bits << 16], np.uint32).view(np.float32)[0]
+    bf = np.array([bias_bits << 16], np.uint32).view(np.float32)[0]
+    exact = Fraction(float(sf)) * q + Fraction(float(bf))
+    if exact != 0:
+        a = _f32_nearest_even(exact)
+    elif Fraction(float(sf)) * q == 0 and bf == 0:
+        # both terms are zeros: the product carries the scale's sign (q >= 0),
+        # and a sum of zeros is -0 only when both are -0 (round to nearest)
+        a = np.float32(-0.0) if (np.signbit(sf) and np.signbit(bf)) else np.float32(0.0)
+    else:
+        a = np.float32(0.0)                     # x + (-x) = +0 (round to nearest)
+    return np.float32(a).astype(np.float16).astype(np.float32).view(np.uint32)
+
+
+def _bf16(v):
+    return int(np.array([v], np.float32).view(np.uint32)[0] >> 16)
+
+
+def _embed_one(orc, scale_bits, bias_bits, q, K=64):
+    """Oracle embedding value of code q (input 0 of a one-row table)."""
+    codes = np.full((1, K // 2), q | (q << 4), np.uint8)
+    e = orc.embed(codes, np.array([[scale_bits]], np.uint16), np.array([[bias_bits]], np.uint16),
+                  np.array([0], np.int32), 1, K)
+    return e[0, 0]
+
+
+def pin_embed_hand_cases(orc):
+    """Hand-derived IEEE cases: (scale, bias, code) -> value."""
+    cases = [
+        (0.5, -1.0, 3, 0.5),                    # 0.5 * 3 - 1, exact everywhere
+        (1.0, -2.0 ** -30, 0, -0.0),            # below half the smallest binary16 subnormal: -0
+        (1.0, -3 * 2.0 ** -26, 0, -2.0 ** -24), # three quarters of it rounds to the subnormal
+        (1.0, -2.0 ** -25, 0, -0.0),            # exactly half: tie to even, the zero
+        (8192.0, 0.0, 15, np.inf),              # 122880 overflows binary16
+        (1.0, 2.0 ** -11, 1, 1.0),              # 1 + half a binary16 ulp: tie to even, 1
+        (1.0, 3 * 2.0 ** -12, 1, 1.0 + 2.0 ** -10),  # above the tie: rounds up
+        (-0.5, 0.0, 0, 0.0),                    # -0 + +0 = +0
+        (-0.5, -0.0, 0, -0.0),                  # -0 + -0 = -0
+        (2.0 ** -10, 2.0 ** -14, 1, 2.0 ** -14 + 2.0 ** -10),   # normal binary16, exact
+    ]
+    for s, b, q, want in cases:
+        got = _embed_one(orc, _bf16(s), _bf16(b), q)
+        assert (np.isinf(want) and got == want) or \
+            (got == want and np.signbit(got) == np.signbit(want)), \
+            f"embed({s}, {b}, {q}) = {got!r}, expected {want!r}"
+
+
+def pin_embed_exact_reference(orc):
+    """Random rows (scales of both signs, biases from tiny to large) against
+    the exact-rational reference, bit for bit; ids outside the table give
+    NaN rows."""
+    rng = np.random.default_rng(77)
+    M, K = 5, 256
+    codes = rng.integers(0, 256, size=(M, K // 2)).astype(np.uint8)
+    sc = rng.uniform(-0.05, 0.05, size=(M, K // 64)).astype(np.float32)
+    bi = (rng.choice([-1.0, 1.0], size=(M, K // 64)) *
+          2.0 ** rng.integers(-40, 2, size=(M, K // 64))).astype(np.float32)
+    sc[1, 1], bi[1, 1] = -0.0, -0.0          # signed zeros in both terms
+    sc[2, 0], bi[2, 0] = 0.0, -0.0
+    sc[3, 2], bi[3, 2] = -0.0, 0.0
+    bi[4, 3] = 0.0
+    sb = (sc.view(np.uint32) >> 16).astype(np.uint16)
+    bb = (bi.view(np.uint32) >> 16).astype(np.uint16)
+    ids = np.array([3, 0, 4, 4, -1, 5, 1], np.int32)
+    e = orc.embed(codes, sb, bb, ids, M, K)
+    for t, i in enumerate(ids):
+        if i < 0 or i >= M:
+            assert np.all(np.isnan(e[t])), "rows outside the table must be NaN"
+            continue
+        for k in range(K):
+            byte = int(codes[i, k // 2])
+            q = (byte >> 4) if k & 1 else (byte & 15)
+            want = _embed_reference(int(sb[i, k // 64]), int(bb[i, k // 64]), q)
+            got = e[t, k:k + 1].view(np.uint32)[0]
+            assert got == want, f"row {i} k {k}: {got:#x} vs {want:#x}"
+
+
 PINS = [pin_hand_fixtures, pin_decode_values, pin_worked_example, pin_one_hot,
         pin_zero_and_sign_codes, pin_exact_integer_arithmetic,
-        pin_numpy_second_opinion, pin_invariants, pin_argmax_brute_force]
+        pin_numpy_second_opinion, pin_invariants, pin_argmax_brute_force,
+        pin_f16_rounding, pin_embed_hand_cases, pin_embed_exact_reference]

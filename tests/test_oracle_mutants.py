@@ -35,6 +35,15 @@ MUTANTS = [
     ("argmax_ties_highest", "if (row[m] > row[best])", "if (row[m] >= row[best])"),
     ("b1_group_scale_per_row", "oracle_fp16_value(s[m * (K / 128) + k / 128])",
      "oracle_fp16_value(s[m * (K / 128)])"),
+    ("f16_ties_away", "if (rem > half || (rem == half && (r & 1)))", "if (rem >= half)"),
+    ("f16_ties_down", "if (rem > half || (rem == half && (r & 1)))", "if (rem > half)"),
+    ("f16_no_subnormals", "int qe = L - 10 > -24 ? L - 10 : -24;", "int qe = L - 10;"),
+    ("f16_zero_loses_sign", "        return sign;\n", "        return 0;\n"),
+    ("f16_no_overflow", "if (e16 >= 31)", "if (e16 >= 32)"),
+    ("embed_no_f16_round_trip", "v = (float)oracle_fp16_value(oracle_f32_to_f16(a));", "v = a;"),
+    ("embed_bias_dropped", "const float a = prod + b;", "const float a = prod + 0.0f * b;"),
+    ("embed_group_index", "biases[id * (K / 64) + k / 64]", "biases[id * (K / 64)]"),
+    ("embed_out_of_range_zero", "            float v = NAN;", "            float v = 0.0f;"),
 ]
 
 
