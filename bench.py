@@ -19,8 +19,9 @@ Reported (one JSON line):
   cpu_baseline   the CPU oracle on the same workload, on this host's cores
 
 Other workloads (--workload): any case name of gemm_qgemv_amd.synth.CASES, or
-a config prefix (c0, c1, c2b1, c2b8, c3, c4gemv, c4gemm). GEMM workloads report
-TFLOP/s.
+a config prefix (c0, c1, c2b1, c2b8, c3, c4gemv, c4gemm), or one of the widened
+rows (u4gemm, head64, head128, embed). GEMM workloads report TFLOP/s; the
+embedding gather reports the GB/s of its ids, packed rows and float32 rows.
 
 The timed region replays a HIP graph of the steps (captured once) so that the
 host's launch cost does not pace the GPU; inputs are resident in HBM before
@@ -60,8 +61,10 @@ WORKLOADS = {
     "u4gemm": ["n2a_u4_gemm_6144x2048_n2048", "n2b_u4_gemm_2048x6144_n2048"],
     "head64": ["n1a_u4_head_151936x2048_b64", "n1b_u4_head_151936x2048_b64_nologits"],
     "head128": ["n1c_u4_head_151936x2048_b128", "n1d_u4_head_151936x2048_b128_nologits"],
+    "embed": ["n3_u4_embed_151936x2048_t2048"],
 }
 METRIC = "effective weight GB/s and % of HBM peak, batch-1 qgemv; prefill qgemm TFLOP/s"
+EMBED_METRIC = "embedding gather GB/s (ids + packed rows read + float32 rows written)"
 
 
 def log(*a):
@@ -84,7 +87,7 @@ class Launch:
 
     def __init__(self, case, rotate_bytes, torch, q, synth, tensors):
         self.case = case
-        w, x = synth.case_inputs(case)
+        w, x = synth.case_inputs(case)     # x: token ids for "embed"
         base = tensors.to_device(w)
         self.copies = max(1, math.ceil(rotate_bytes / w.nbytes)) if case.op != "gemm" else 1
         self.weights = [base] + [
@@ -92,10 +95,11 @@ class Launch:
                                   None if base.biases is None else base.biases.clone())
             for _ in range(self.copies - 1)]
         self.x = torch.from_numpy(x).cuda()
-        self.y = torch.empty(case.rows * case.M, dtype=torch.float32, device="cuda")
+        out_cols = case.K if case.op == "embed" else case.M
+        self.y = torch.empty(case.rows * out_cols, dtype=torch.float32, device="cuda")
         op = {"gemv": q.QG_OP_GEMV, "gemv_argmax": q.QG_OP_GEMV_ARGMAX, "greedy": q.QG_OP_GEMV_ARGMAX,
-              "gemm": q.QG_OP_GEMM}[case.op]
-        self.ws = tensors.workspace(op, case.fmt, case.M, case.K, case.rows)
+              "gemm": q.QG_OP_GEMM, "embed": None}[case.op]
+        self.ws = None if op is None else tensors.workspace(op, case.fmt, case.M, case.K, case.rows)
         self.ws_bytes = 0 if self.ws is None else self.ws.numel()
         self.idx = torch.empty(case.rows, dtype=torch.int32, device="cuda")
         self.lib = q._binding.lib()
@@ -115,6 +119,9 @@ class Launch:
             st = L.qgemv_argmax(case.fmt, c, s, b, self.x.data_ptr(), y,
                                 self.idx.data_ptr(), case.M, case.K, case.rows, ws,
                                 self.ws_bytes, stream)
+        elif case.op == "embed":
+            st = L.qembed(case.fmt, c, s, b, self.x.data_ptr(), self.y.data_ptr(), case.M, case.K,
+                          case.rows, stream)
         else:
             st = L.qgemm(case.fmt, c, s, b, self.x.data_ptr(), self.y.data_ptr(), case.M, case.K,
                          case.rows, ws, self.ws_bytes, stream)
@@ -123,7 +130,14 @@ class Launch:
 
     @property
     def weight_bytes(self):
-        return self.case.weight_bytes
+        """Algorithmic bytes of one call: the packed weights a product reads
+        once; for the gather, the ids, the packed rows of those ids (codes,
+        scales, biases) and the float32 rows written."""
+        c = self.case
+        if c.op == "embed":
+            row = c.weight_bytes // c.M
+            return c.rows * (4 + row + 4 * c.K)
+        return c.weight_bytes
 
 
 def per_launch_ms(torch, fn, stream, n, reps=5):
@@ -159,6 +173,8 @@ def cpu_baseline(launches, seconds):
             if c.op == "gemm":
                 # bounded sample: the first 8 token rows
                 orc.qgemv(c.fmt, w.codes, w.scales, w.biases, x[:8], c.M, c.K)
+            elif c.op == "embed":
+                orc.embed(w.codes, w.scales, w.biases, x, c.M, c.K)
             else:
                 orc.qgemv(c.fmt, w.codes, w.scales, w.biases, x, c.M, c.K)
         reps += 1
@@ -401,7 +417,8 @@ def main():
         per_case.append((L, avg, avg))
         unit = L.weight_bytes / (avg * 1e-3) / 1e9
         log(f"  {L.case.name}: {avg * 1e3:.2f} us per launch, {unit:.1f} GB/s weight"
-            + (f", {L.case.flops / (avg * 1e-3) / 1e12:.2f} TFLOP/s" if gemm or L.case.rows > 1 else ""))
+            + (f", {L.case.flops / (avg * 1e-3) / 1e12:.2f} TFLOP/s"
+               if gemm or (L.case.rows > 1 and L.case.op != "embed") else ""))
 
     src_hash = kernel_source_hash()
     traffic = load_traffic(args.workload, src_hash)
@@ -430,8 +447,9 @@ def main():
                 "kernel_calls": [L.case.name for L, _, _ in per_case]}
         dtype = "f32"
 
+    embed = cases[0].op == "embed"
     out = {
-        "metric": METRIC,
+        "metric": EMBED_METRIC if embed else METRIC,
         "value": round(value, 3),
         "unit": unit,
         "n_gpus": 1,
@@ -453,6 +471,7 @@ def main():
     }
     if not gemm:
         out["pct_of_hbm_peak"] = round(100 * value / HBM_PEAK_GBS, 2)
+    if not gemm and not embed:
         out["tok_s_equiv"] = round(value * 1e9 / BYTES_PER_TOKEN[cases[0].fmt], 1)
     if gemm and args.vendor:
         out["vendor_ceiling"] = vendor_ceiling(launches, torch, stream)

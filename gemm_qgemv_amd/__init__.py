@@ -1,5 +1,5 @@
-"""Dequantize-fused low-bit matrix-vector / matrix-matrix products and a fused
-greedy (argmax) head for AMD MI355X (gfx950).
+"""Dequantize-fused low-bit matrix-vector / matrix-matrix products, a fused
+greedy (argmax) head and the embedding-row gather for AMD MI355X (gfx950).
 
 The computation lives in ``libqg.so`` (HIP kernels behind the C ABI of
 ``include/qg.h``); this package is its thin ctypes binding, plus the seeded
@@ -10,4 +10,4 @@ from ._binding import (QG_B1_G128, QG_ERR_ALIAS, QG_ERR_ALIGN, QG_ERR_FORMAT,  #
                        QG_ERR_LAUNCH, QG_ERR_NULL, QG_ERR_SHAPE, QG_ERR_UNSUPPORTED,
                        QG_ERR_WORKSPACE, QG_I8_ROW, QG_MAX_ARGMAX_BATCH, QG_MAX_GEMV_BATCH, QG_OK, QG_OP_GEMM,
                        QG_OP_GEMV, QG_OP_GEMV_ARGMAX, QG_U4_G64, QG_WS_CONTROL_BYTES, QGError, qg_abi_version,
-                       qg_status_str, qg_workspace_bytes, qgemm, qgemv, qgemv_argmax)
+                       qg_status_str, qg_workspace_bytes, qembed, qgemm, qgemv, qgemv_argmax)

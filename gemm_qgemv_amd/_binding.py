@@ -22,8 +22,8 @@ QG_WS_CONTROL_BYTES = 4096
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqg.so")
 
-EXPORTS = ("qgemv", "qgemm", "qgemv_argmax", "qg_workspace_bytes", "qg_status_str",
-           "qg_abi_version")
+EXPORTS = ("qgemv", "qgemm", "qgemv_argmax", "qembed", "qg_workspace_bytes",
+           "qg_status_str", "qg_abi_version")
 
 _lib = None
 
@@ -47,12 +47,13 @@ def lib() -> ctypes.CDLL:
         L.qgemv.argtypes = [I32, P, P, P, P, P, I64, I64, I32, P, SZ, P]
         L.qgemm.argtypes = [I32, P, P, P, P, P, I64, I64, I64, P, SZ, P]
         L.qgemv_argmax.argtypes = [I32, P, P, P, P, P, P, I64, I64, I32, P, SZ, P]
+        L.qembed.argtypes = [I32, P, P, P, P, P, I64, I64, I64, P]
         L.qg_workspace_bytes.argtypes = [I32, I32, I64, I64, I64]
         L.qg_workspace_bytes.restype = SZ
         L.qg_status_str.argtypes = [I32]
         L.qg_status_str.restype = ctypes.c_char_p
         L.qg_abi_version.argtypes = []
-        for f in (L.qgemv, L.qgemm, L.qgemv_argmax, L.qg_abi_version):
+        for f in (L.qgemv, L.qgemm, L.qgemv_argmax, L.qembed, L.qg_abi_version):
             f.restype = I32
         _lib = L
     return _lib
@@ -103,6 +104,11 @@ def qgemv_argmax(fmt, codes, scales, biases, x, logits, idx, M, K, batch, ws=Non
     _check(lib().qgemv_argmax(fmt, _ptr(codes), _ptr(scales), _ptr(biases), _ptr(x),
                               _ptr(logits), _ptr(idx), M, K, batch, _ptr(ws),
                               _nbytes(ws, ws_bytes), _stream(stream)), "qgemv_argmax")
+
+
+def qembed(fmt, codes, scales, biases, ids, out, M, K, n, stream=None):
+    _check(lib().qembed(fmt, _ptr(codes), _ptr(scales), _ptr(biases), _ptr(ids), _ptr(out),
+                        M, K, n, _stream(stream)), "qembed")
 
 
 def qg_workspace_bytes(op, fmt, M, K, rows) -> int:

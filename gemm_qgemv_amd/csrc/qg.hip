@@ -11,6 +11,7 @@
 #include <algorithm>
 
 #include "../../include/qg.h"
+#include "embed.hpp"
 #include "gemm.hpp"
 #include "gemv.hpp"
 #include "gemv1.hpp"
@@ -631,6 +632,43 @@ int gemm_entry(int fmt, const void *codes, const void *scales, const void *biase
     return launch_status();
 }
 
+// Workgroups of the embedding gather: enough to fill the chip several times
+// over; more rows are taken by the grid-stride loop.
+constexpr int64_t kEmbedMaxGrid = 65536;
+
+int embed_entry(int fmt, const void *codes, const void *scales, const void *biases,
+                const int32_t *ids, float *out, int64_t M, int64_t K, int64_t n,
+                hipStream_t stream)
+{
+    if (fmt != QG_I8_ROW && fmt != QG_U4_G64 && fmt != QG_B1_G128) return QG_ERR_FORMAT;
+    if (!codes || !scales || !ids || !out) return QG_ERR_NULL;
+    if ((fmt == QG_U4_G64) != (biases != nullptr)) return QG_ERR_NULL;
+    if (fmt != QG_U4_G64) return QG_ERR_UNSUPPORTED;
+    if (M < 1 || M > kMaxM || K < 1 || K > kMaxK || K % k_unit(fmt) != 0 || n < 1 ||
+        n > kMaxN)
+        return QG_ERR_SHAPE;
+    if (!aligned(codes, kAlign) || !aligned(scales, kAlign) || !aligned(biases, kAlign) ||
+        !aligned(out, kAlign) || !aligned(ids, 4))
+        return QG_ERR_ALIGN;
+    Range all[5];
+    int nr = 0;
+    all[nr++] = range_of(codes, M * row_bytes(fmt, K));
+    all[nr++] = range_of(scales, scale_bytes(fmt, M, K));
+    all[nr++] = range_of(biases, bias_bytes(fmt, M, K));
+    all[nr++] = range_of(ids, n * 4);
+    Range wr[1];
+    wr[0] = all[nr++] = range_of(out, n * K * 4);
+    const int st = check_alias(all, nr, wr, 1);
+    if (st != QG_OK) return st;
+
+    (void)hipGetLastError();
+    qg::EmbedParams p{static_cast<const uint8_t *>(codes), static_cast<const uint16_t *>(scales),
+                      static_cast<const uint16_t *>(biases), ids, out, M, K, n};
+    const auto grid = static_cast<unsigned>(std::min(ceil_div(n, qg::kEmbedRows), kEmbedMaxGrid));
+    hipLaunchKernelGGL(qg::embed_u4_kernel, dim3(grid), dim3(qg::kEmbedThreads), 0, stream, p);
+    return launch_status();
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -665,6 +703,12 @@ int qgemm(int fmt, const void *codes, const void *scales, const void *biases,
     return gemm_entry(fmt, codes, scales, biases, x, y, M, K, N, ws, ws_bytes, stream);
 }
 
+int qembed(int fmt, const void *codes, const void *scales, const void *biases,
+           const int32_t *ids, float *out, int64_t M, int64_t K, int64_t n, hipStream_t stream)
+{
+    return embed_entry(fmt, codes, scales, biases, ids, out, M, K, n, stream);
+}
+
 size_t qg_workspace_bytes(int op, int fmt, int64_t M, int64_t K, int64_t rows)
 {
     if (fmt != QG_I8_ROW && fmt != QG_U4_G64 && fmt != QG_B1_G128) return 0;
@@ -693,7 +737,7 @@ const char *qg_status_str(int status)
     case QG_ERR_WORKSPACE: return "workspace missing or smaller than qg_workspace_bytes()";
     case QG_ERR_ALIAS: return "a written buffer overlaps another buffer";
     case QG_ERR_LAUNCH: return "kernel launch failed";
-    case QG_ERR_UNSUPPORTED: return "combination not implemented by this library (reserved)";
+    case QG_ERR_UNSUPPORTED: return "format not implemented by this entry point";
     default: return "unknown status";
     }
 }

@@ -103,6 +103,62 @@ def draw_x(rows: int, K: int, rng: np.random.Generator) -> np.ndarray:
     return rng.standard_normal(size=(rows, K), dtype=np.float32)
 
 
+def draw_ids(n: int, M: int, rng: np.random.Generator) -> np.ndarray:
+    """Token ids of a prompt: uniform over the vocabulary (int32)."""
+    return rng.integers(0, M, size=n, dtype=np.int32)
+
+
+# bf16 patterns of signed zeros and of the smallest and largest subnormals
+_BF16_EDGES = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x807F], np.uint16)
+
+
+def draw_embed_stress(M: int, K: int, rng: np.random.Generator) -> QWeights:
+    """A 4-bit table whose groups hit the corners of decoding a row: each
+    64-input group takes one of four recipes,
+      0  scale and bias any bf16 bit pattern (zeros, subnormals, huge values
+         whose products overflow, infinities, NaNs);
+      1  typical magnitudes of both signs;
+      2  a bias close to -scale * q0 and codes within one of q0, so that
+         scale * code + bias cancels to tiny values of either sign, zeros
+         and binary16 subnormals;
+      3  a signed zero or a bf16 subnormal as scale or bias, the other term
+         typical."""
+    if K % 64:
+        raise ValueError("K must be a multiple of 64")
+    G = K // 64
+    codes = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    mode = rng.integers(0, 4, size=(M, G))
+    sb = rng.integers(0, 1 << 16, size=(M, G)).astype(np.uint16)
+    bb = rng.integers(0, 1 << 16, size=(M, G)).astype(np.uint16)
+
+    s1 = to_bf16_bits(rng.uniform(-2e-2, 2e-2, size=(M, G)).astype(np.float32))
+    b1 = to_bf16_bits(rng.uniform(-0.1, 0.1, size=(M, G)).astype(np.float32))
+    sb = np.where(mode == 1, s1, sb)
+    bb = np.where(mode == 1, b1, bb)
+
+    sign = rng.choice([-1.0, 1.0], size=(M, G))
+    mag = rng.uniform(1.0, 2.0, size=(M, G)) * 2.0 ** rng.integers(-30, 6, size=(M, G))
+    s2 = to_bf16_bits((sign * mag).astype(np.float32))
+    sval = (s2.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    q0 = rng.integers(1, 15, size=(M, G))
+    b2 = to_bf16_bits((-(sval * q0)).astype(np.float32))
+    sb = np.where(mode == 2, s2, sb)
+    bb = np.where(mode == 2, b2, bb)
+    near = np.clip(q0[:, :, None] + rng.integers(-1, 2, size=(M, G, 64)), 0, 15)
+    near = near.reshape(M, K).astype(np.uint8)
+    packed = near[:, 0::2] | (near[:, 1::2] << 4)
+    in_mode2 = np.repeat(mode == 2, 32, axis=1)
+    codes = np.where(in_mode2, packed, codes).astype(np.uint8)
+
+    edge = _BF16_EDGES[rng.integers(0, len(_BF16_EDGES), size=(M, G))]
+    which = rng.integers(0, 2, size=(M, G))
+    sb = np.where((mode == 3) & (which == 0), edge, np.where(mode == 3, s1, sb))
+    bb = np.where((mode == 3) & (which == 1), edge, np.where(mode == 3, b1, bb))
+    return QWeights(U4_G64, M, K, np.ascontiguousarray(codes),
+                    np.ascontiguousarray(sb.astype(np.uint16)),
+                    np.ascontiguousarray(bb.astype(np.uint16)))
+
+
 # ---------------------------------------------------------------------------
 # The workloads: five configurations restated as thirteen concrete cases.
 # ---------------------------------------------------------------------------
@@ -110,7 +166,8 @@ def draw_x(rows: int, K: int, rng: np.random.Generator) -> np.ndarray:
 @dataclasses.dataclass(frozen=True)
 class Case:
     name: str
-    op: str          # "gemv", "gemv_argmax", "greedy" (argmax, no logits) or "gemm"
+    op: str          # "gemv", "gemv_argmax", "greedy" (argmax, no logits), "gemm"
+                     # or "embed" (rows = token ids gathered)
     fmt: int
     M: int
     K: int
@@ -145,7 +202,9 @@ CASES = [
 ]
 # Measurement cases of widened rows (not configurations): the 4-bit prefill
 # at the 4-bit matvec shapes, with a 2048-token prompt; the greedy head at 64
-# and 128 rows, with logits and without ("greedy": qgemv_argmax, logits NULL).
+# and 128 rows, with logits and without ("greedy": qgemv_argmax, logits NULL);
+# the embedding rows of a 2048-token prompt gathered from the same (tied)
+# head matrix.
 NEXT_CASES = [
     Case("n2a_u4_gemm_6144x2048_n2048", "gemm", U4_G64, 6144, 2048, 2048, 5, 0),
     Case("n2b_u4_gemm_2048x6144_n2048", "gemm", U4_G64, 2048, 6144, 2048, 5, 1),
@@ -153,16 +212,19 @@ NEXT_CASES = [
     Case("n1b_u4_head_151936x2048_b64_nologits", "greedy", U4_G64, 151936, 2048, 64, 2, 0, x_variant=6),
     Case("n1c_u4_head_151936x2048_b128", "gemv_argmax", U4_G64, 151936, 2048, 128, 2, 0, x_variant=7),
     Case("n1d_u4_head_151936x2048_b128_nologits", "greedy", U4_G64, 151936, 2048, 128, 2, 0, x_variant=7),
+    Case("n3_u4_embed_151936x2048_t2048", "embed", U4_G64, 151936, 2048, 2048, 2, 0, x_variant=8),
 ]
 CASES_BY_NAME = {c.name: c for c in CASES + NEXT_CASES}
 
 
 def case_inputs(c: Case) -> tuple[QWeights, np.ndarray]:
-    """Weights and activations of one case. Cases that share a (case,
-    variant) weight stream get the same weights; `x_variant` draws the
-    activations from a separate stream."""
+    """Weights and activations (token ids for "embed") of one case. Cases
+    that share a (case, variant) weight stream get the same weights;
+    `x_variant` draws the activations from a separate stream."""
     rng = rng_for(c.case, c.variant)
     w = draw_weights(c.fmt, c.M, c.K, rng)
+    if c.op == "embed":
+        return w, draw_ids(c.rows, c.M, rng_for(c.case, c.x_variant))
     if c.x_variant is None:
         x = draw_x(c.rows, c.K, rng)
     else:

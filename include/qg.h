@@ -1,7 +1,8 @@
 /*
  * qg.h -- C ABI of libqg: dequantize-fused low-bit weight matrix-vector
  * product (batch-1 LLM decode), its small-batch and prefill matrix-matrix
- * form, and a fused greedy (argmax) output head, for AMD MI355X (gfx950).
+ * form, a fused greedy (argmax) output head, and the embedding-row gather
+ * from the same 4-bit matrix, for AMD MI355X (gfx950).
  *
  * Notation. W is M x K (M outputs, K inputs). Activations x are float32
  * [rows][K], outputs y are float32 [rows][M]; every array is row-major and
@@ -51,9 +52,9 @@
  *               device, and nothing is allocated on the hot path.)
  *   Streams     Work is enqueued on `stream` (0 = the null stream) and the
  *               call returns without waiting for it.
- *   Alignment   codes, scales, biases, x, y / logits and ws must be 16-byte
- *               aligned; idx 4-byte aligned.
- *   Aliasing    The written buffers (y or logits, idx, ws) must not overlap
+ *   Alignment   codes, scales, biases, x, y / logits / out and ws must be
+ *               16-byte aligned; idx and ids 4-byte aligned.
+ *   Aliasing    The written buffers (y or logits, idx, out, ws) must not overlap
  *               each other or any input.
  *   Errors      Every argument error is detected on the host before
  *               anything is enqueued; the outputs are then left untouched
@@ -108,8 +109,8 @@ enum {
     QG_ERR_WORKSPACE = -5,   /* ws_bytes smaller than qg_workspace_bytes(...) */
     QG_ERR_ALIAS = -6,       /* a written buffer overlaps another buffer */
     QG_ERR_LAUNCH = -7,      /* the kernel launch failed */
-    QG_ERR_UNSUPPORTED = -8  /* reserved: a combination this library does not implement
-                                (no entry point returns it at this ABI version) */
+    QG_ERR_UNSUPPORTED = -8  /* a known format this entry point does not implement
+                                (only qembed returns it: 4-bit rows only) */
 };
 
 /* Control words at the start of every workspace (see Workspace above). */
@@ -173,6 +174,34 @@ int qgemv_argmax(int fmt, const void *codes, const void *scales,
                  const void *biases, const float *x, float *logits,
                  int32_t *idx, int64_t M, int64_t K, int batch,
                  void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * qembed -- embedding rows gathered from the (tied) 4-bit weight matrix.
+ *   out[t][k] = e(ids[t], k),  0 <= t < n, 0 <= k < K, where for a row m
+ *   inside the table e(m, k) is decoded as three rounded steps:
+ *     p = scales[m][k/64] * q        (float32; exact, 8 x 4 significant bits)
+ *     a = p + biases[m][k/64]        (float32, round to nearest even; the
+ *                                     product and the sum are not fused)
+ *     e = a rounded to IEEE binary16 (nearest even, subnormals kept,
+ *         overflow to infinity) and widened back to float32.
+ *   A zero sum is -0 only when both terms are -0 (IEEE 754 sums under
+ *   nearest-even), and a negative sum too small for binary16 becomes -0,
+ *   not +0. A row id outside [0, M) gives a row of quiet NaNs.
+ * (Pushing the limits of legacy hardware, "Half a billion values, and one
+ * negative zero": the row decoder keeps the separate affine operations and
+ * the inherited FP16 round-trip, and the lookup moved to the GPU had to get
+ * denormals, signed zero and round-to-nearest-even exactly right; I Built an
+ * LLM Inference Engine..., "Cost 1: the embedding lookup still runs on the
+ * CPU": the quantized rows are decoded on the device from token ids instead
+ * of crossing PCIe.)
+ *   fmt     QG_U4_G64 only; the other known formats give QG_ERR_UNSUPPORTED.
+ *   ids     int32 [n], device memory (4-byte aligned); any values.
+ *   out     float32 [n][K] (overwritten).
+ *   1 <= n <= 2^31-1; M and K as qgemv. No workspace.
+ */
+int qembed(int fmt, const void *codes, const void *scales, const void *biases,
+           const int32_t *ids, float *out, int64_t M, int64_t K, int64_t n,
+           hipStream_t stream);
 
 /* Bytes of device workspace the call (op, fmt, M, K, rows) needs; rows is
  * the batch for QG_OP_GEMV / QG_OP_GEMV_ARGMAX and N for QG_OP_GEMM.

@@ -145,3 +145,42 @@ def test_wide_greedy_head_checks():
                 ws=ws, ws_bytes=need) == q.QG_ERR_ALIAS
     # qgemv without an output
     assert _err(q.qgemv, q.QG_U4_G64, codes, scales, biases, x, None, M, K, 1) == q.QG_ERR_NULL
+
+
+def test_embed_checks():
+    """qembed: 4-bit rows only (the other known formats are not implemented
+    for the gather), ids and out required, out 16-byte and ids 4-byte
+    aligned, out overlapping nothing."""
+    M, K, n = 1000, 128, 8
+    codes, scales, biases = A, A + (1 << 20), A + (1 << 21)
+    ids, out = A + (1 << 22), A + (1 << 23)
+    ok = dict(fmt=q.QG_U4_G64, codes=codes, scales=scales, biases=biases, ids=ids, out=out,
+              M=M, K=K, n=n)
+
+    def err(**kw):
+        a = dict(ok, **kw)
+        with pytest.raises(q.QGError) as e:
+            q.qembed(a["fmt"], a["codes"], a["scales"], a["biases"], a["ids"], a["out"],
+                     a["M"], a["K"], a["n"], stream=0)
+        return e.value.status
+
+    assert err(fmt=9) == q.QG_ERR_FORMAT
+    assert err(fmt=q.QG_I8_ROW, biases=None) == q.QG_ERR_UNSUPPORTED
+    assert err(fmt=q.QG_B1_G128, biases=None) == q.QG_ERR_UNSUPPORTED
+    assert err(fmt=q.QG_I8_ROW) == q.QG_ERR_NULL            # biases where none belong
+    assert err(biases=None) == q.QG_ERR_NULL
+    assert err(ids=None) == q.QG_ERR_NULL
+    assert err(out=None) == q.QG_ERR_NULL
+    assert err(codes=None) == q.QG_ERR_NULL
+    assert err(K=96) == q.QG_ERR_SHAPE
+    assert err(K=0) == q.QG_ERR_SHAPE
+    assert err(M=0) == q.QG_ERR_SHAPE
+    assert err(n=0) == q.QG_ERR_SHAPE
+    assert err(n=-3) == q.QG_ERR_SHAPE
+    assert err(out=out + 4) == q.QG_ERR_ALIGN
+    assert err(ids=ids + 2) == q.QG_ERR_ALIGN
+    assert err(scales=scales + 8) == q.QG_ERR_ALIGN
+    assert err(out=codes + 4096) == q.QG_ERR_ALIAS          # inside the codes
+    assert err(out=ids - 16) == q.QG_ERR_ALIAS              # covers the ids
+    assert err(ids=out + 64) == q.QG_ERR_ALIAS              # ids inside out
+    assert "format" in q.qg_status_str(q.QG_ERR_UNSUPPORTED)
