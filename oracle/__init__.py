@@ -16,7 +16,7 @@ import subprocess
 
 import numpy as np
 
-I8_ROW, U4_G64, B1_G128 = 1, 2, 3
+I8_ROW, U4_G64, B1_G128, I8_G64 = 1, 2, 3, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qg_oracle.c")

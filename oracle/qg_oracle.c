@@ -45,6 +45,12 @@
  *     (A 27B model on two 4GB Maxwell GPUs, "Why this machine is awkward":
  *     binary weights with FP16 scales.)
  *
+ *  4  INT8 symmetric, group of 64 along k.  codes int8 [M][K],
+ *     scales fp32 [M][K/64].  w = scale[m][k/64] * q, q two's complement,
+ *     no clamping.  (MiniCPM-V-4.6 on a Tesla C2075, section 2.3
+ *     "Quantization and residency": symmetric 8-bit weights with one FP32
+ *     scale per group of 64.)
+ *
  * bf16 is the upper half of an IEEE binary32; fp16 is IEEE binary16
  * (subnormals included). Both are decoded here bit by bit, on purpose
  * without any half-precision type of the compiler.
@@ -76,7 +82,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_I8_ROW = 1, OR_U4_G64 = 2, OR_B1_G128 = 3 };
+enum { OR_I8_ROW = 1, OR_U4_G64 = 2, OR_B1_G128 = 3, OR_I8_G64 = 4 };
 enum { OR_OK = 0, OR_BAD_FORMAT = -1, OR_BAD_SHAPE = -2 };
 
 /* ---- scalar decoders ------------------------------------------------- */
@@ -168,7 +174,7 @@ static int shape_ok(int fmt, int64_t M, int64_t K)
 {
     if (M < 1 || K < 1)
         return 0;
-    if (fmt == OR_U4_G64)
+    if (fmt == OR_U4_G64 || fmt == OR_I8_G64)
         return K % 64 == 0;
     if (fmt == OR_B1_G128)
         return K % 128 == 0;
@@ -183,6 +189,11 @@ static double weight(const struct qmat *A, int64_t m, int64_t k)
         const int8_t *q = (const int8_t *)A->codes;
         const float *s = (const float *)A->scales;
         return (double)s[m] * (double)q[m * K + k];
+    }
+    if (A->fmt == OR_I8_G64) {
+        const int8_t *code = (const int8_t *)A->codes;
+        const float *gs = (const float *)A->scales;
+        return (double)gs[m * (K / 64) + k / 64] * (double)code[m * K + k];
     }
     if (A->fmt == OR_U4_G64) {
         const uint8_t *c = (const uint8_t *)A->codes;
@@ -224,7 +235,7 @@ static void dot_one(const struct qmat *A, const float *x, int64_t n, int64_t m,
 int oracle_decode(int fmt, const void *codes, const void *scales,
                   const void *biases, int64_t M, int64_t K, double *w)
 {
-    if (fmt < OR_I8_ROW || fmt > OR_B1_G128)
+    if (fmt < OR_I8_ROW || fmt > OR_I8_G64)
         return OR_BAD_FORMAT;
     if (!shape_ok(fmt, M, K))
         return OR_BAD_SHAPE;
@@ -241,7 +252,7 @@ int oracle_qgemv(int fmt, const void *codes, const void *scales,
                  const void *biases, const float *x, int64_t M, int64_t K,
                  int64_t N, double *y, double *a)
 {
-    if (fmt < OR_I8_ROW || fmt > OR_B1_G128)
+    if (fmt < OR_I8_ROW || fmt > OR_I8_G64)
         return OR_BAD_FORMAT;
     if (!shape_ok(fmt, M, K) || N < 1)
         return OR_BAD_SHAPE;
@@ -264,7 +275,7 @@ int oracle_qgemv_sample(int fmt, const void *codes, const void *scales,
                         const int64_t *m_idx, int64_t count, double *y,
                         double *a)
 {
-    if (fmt < OR_I8_ROW || fmt > OR_B1_G128)
+    if (fmt < OR_I8_ROW || fmt > OR_I8_G64)
         return OR_BAD_FORMAT;
     if (!shape_ok(fmt, M, K) || N < 1)
         return OR_BAD_SHAPE;

@@ -35,7 +35,7 @@ import os
 
 import numpy as np
 
-I8, U4, B1 = 1, 2, 3
+I8, U4, B1, I8G = 1, 2, 3, 4
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
@@ -48,9 +48,11 @@ def load_fixture(name):
         d = json.load(f)
     M, K = d["M"], d["K"]
     codes = np.frombuffer(bytes.fromhex(d["codes_hex"]), dtype=np.uint8).copy()
-    if d["fmt"] == I8:
+    if d["fmt"] in (I8, I8G):
         codes = codes.view(np.int8).reshape(M, K)
         scales = np.asarray(d["scales_f32"], np.float32)
+        if d["fmt"] == I8G:
+            scales = scales.reshape(M, K // 64)
     else:
         codes = codes.reshape(M, -1)
         scales = np.asarray(d["scales_bits"], np.uint16).reshape(M, -1)
@@ -71,6 +73,8 @@ def hand_fixtures():
 def numpy_weights(fmt, codes, scales, biases, M, K):
     if fmt == I8:
         return codes.astype(np.float64) * scales.astype(np.float64)[:, None]
+    if fmt == I8G:
+        return codes.astype(np.float64) * np.repeat(scales.astype(np.float64), 64, axis=1)
     if fmt == U4:
         q = np.empty((M, K), np.float64)
         q[:, 0::2] = codes & 0x0F
@@ -93,6 +97,12 @@ def random_tiny(fmt, M, K, rng, extremes=True):
         if extremes:
             codes.flat[0], codes.flat[-1] = -128, 127
         scales = rng.uniform(-2, 2, size=M).astype(np.float32)
+        return codes, scales, None
+    if fmt == I8G:
+        codes = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+        if extremes:
+            codes.flat[0], codes.flat[-1] = -128, 127
+        scales = rng.uniform(-2, 2, size=(M, K // 64)).astype(np.float32)
         return codes, scales, None
     if fmt == U4:
         codes = rng.integers(0, 256, size=(M, K // 2)).astype(np.uint8)
@@ -166,6 +176,17 @@ def pin_one_hot(orc):
     x = np.eye(K, dtype=np.float32)
     y, _ = orc.qgemv(I8, q, s, None, x, M, K)
     assert np.array_equal(y, (q.astype(np.float64) * s[:, None]).T), "i8 one-hot"
+    # I8 group-64: w = s[m][k/64]*q
+    K = 192
+    q = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+    sg = (2.0 ** rng.integers(-6, 3, size=(M, K // 64))).astype(np.float32)
+    x = np.eye(K, dtype=np.float32)
+    y, _ = orc.qgemv(I8G, q, sg, None, x, M, K)
+    want = np.zeros((M, K))
+    for m in range(M):
+        for k in range(K):
+            want[m, k] = float(q[m, k]) * float(sg[m, k // 64])
+    assert np.array_equal(y, want.T), "i8 group-64 one-hot"
     # U4: w = s*q + b with q packed low nibble = even k
     K = 128
     qu = rng.integers(0, 16, size=(M, K))
@@ -207,6 +228,13 @@ def pin_zero_and_sign_codes(orc):
     _close(y, xg64 @ bval.T, 1e-13, "u4 zero codes")
     y, _ = orc.qgemv(I8, np.zeros((M, K), np.int8), np.ones(M, np.float32), None, x, M, K)
     assert np.all(y == 0), "i8 zero codes"
+    y, _ = orc.qgemv(I8G, np.zeros((M, K), np.int8), np.ones((M, K // 64), np.float32), None,
+                     x, M, K)
+    assert np.all(y == 0), "i8 group-64 zero codes"
+    # constant code c in every group: y = c * Σ_g s_g Σ_{k∈g} x
+    sg = rng.uniform(0.01, 1, size=(M, K // 64)).astype(np.float32)
+    y, _ = orc.qgemv(I8G, np.full((M, K), -3, np.int8), sg, None, x, M, K)
+    _close(y, -3.0 * (xg64 @ sg.astype(np.float64).T), 1e-13, "i8 group-64 constant codes")
     K = 256
     x = rng.standard_normal((N, K)).astype(np.float32)
     xg128 = x.astype(np.float64).reshape(N, K // 128, 128).sum(-1)
@@ -231,6 +259,14 @@ def pin_exact_integer_arithmetic(orc):
     y, _ = orc.qgemv(I8, q.astype(np.int8), (2.0 ** -e).astype(np.float32), None, xf, M, K)
     num = x @ q.T                                        # int64
     assert np.array_equal(y * (2.0 ** e)[None, :], num.astype(np.float64)), "i8 exact"
+    # I8 group-64: y * 2^7 = Σ_g (q·x)_g * 2^(7-e_g)
+    eg = rng.integers(0, 8, size=(M, K // 64))
+    y, _ = orc.qgemv(I8G, q.astype(np.int8), (2.0 ** -eg).astype(np.float32), None, xf, M, K)
+    want = np.zeros((N, M), np.int64)
+    for g in range(K // 64):
+        sl = slice(64 * g, 64 * g + 64)
+        want += (x[:, sl] @ q[:, sl].T) * (2 ** (7 - eg[:, g]))[None, :]
+    assert np.array_equal(y * 2.0 ** 7, want.astype(np.float64)), "i8 group-64 exact"
     # U4: y * 2^8 * 2^7 = Σ_g (q·x)_g * 2^(15-e) + (b*2^8)_g * Σx_g * 2^7
     qu = rng.integers(0, 16, size=(M, K))
     packed = (qu[:, 0::2] | (qu[:, 1::2] << 4)).astype(np.uint8)
@@ -264,10 +300,11 @@ def pin_exact_integer_arithmetic(orc):
 
 
 def pin_numpy_second_opinion(orc):
-    """Random tiny matrices over the full code range, all three formats,
+    """Random tiny matrices over the full code range, all four formats,
     K <= 256, against numpy's float16 / bit unpacking and a float64 matmul."""
     rng = np.random.default_rng(14)
-    for fmt, K in ((I8, 48), (I8, 256), (U4, 64), (U4, 256), (B1, 128), (B1, 256)):
+    for fmt, K in ((I8, 48), (I8, 256), (I8G, 64), (I8G, 320), (U4, 64), (U4, 256), (B1, 128),
+                   (B1, 256)):
         for M in (1, 3, 17):
             codes, scales, biases = random_tiny(fmt, M, K, rng)
             x = rng.standard_normal((4, K)).astype(np.float32)
@@ -286,7 +323,7 @@ def pin_invariants(orc):
     """Linearity in x, permuted activation rows, duplicate weight rows, and
     the prefill product row n equal to the matvec of x[n]."""
     rng = np.random.default_rng(15)
-    for fmt, K in ((I8, 64), (U4, 128), (B1, 256)):
+    for fmt, K in ((I8, 64), (I8G, 192), (U4, 128), (B1, 256)):
         M = 9
         codes, scales, biases = random_tiny(fmt, M, K, rng)
         # activations on a 1/8 grid, so that 2*x1 - x2 is exact in float32

@@ -44,6 +44,13 @@ MUTANTS = [
     ("embed_bias_dropped", "const float a = prod + b;", "const float a = prod + 0.0f * b;"),
     ("embed_group_index", "biases[id * (K / 64) + k / 64]", "biases[id * (K / 64)]"),
     ("embed_out_of_range_zero", "            float v = NAN;", "            float v = 0.0f;"),
+    ("i8g_one_scale_per_row", "(double)gs[m * (K / 64) + k / 64]", "(double)gs[m * (K / 64)]"),
+    ("i8g_scales_transposed", "(double)gs[m * (K / 64) + k / 64]", "(double)gs[(k / 64) * A->M + m]"),
+    ("i8g_group_of_128", "(double)gs[m * (K / 64) + k / 64]", "(double)gs[m * (K / 64) + k / 128]"),
+    ("i8g_read_unsigned", "const int8_t *code = (const int8_t *)A->codes;",
+     "const uint8_t *code = (const uint8_t *)A->codes;"),
+    ("i8g_scale_dropped", "return (double)gs[m * (K / 64) + k / 64] * (double)code[m * K + k];",
+     "(void)gs; return (double)code[m * K + k];"),
 ]
 
 
