@@ -20,7 +20,7 @@ Reported (one JSON line):
 
 Other workloads (--workload): any case name of gemm_qgemv_amd.synth.CASES, or
 a config prefix (c0, c1, c2b1, c2b8, c3, c4gemv, c4gemm), or one of the widened
-rows (u4gemm, head64, head128, embed). GEMM workloads report TFLOP/s; the
+rows (u4gemm, head64, head128, embed, i8g, i8ggemm). GEMM workloads report TFLOP/s; the
 embedding gather reports the GB/s of its ids, packed rows and float32 rows.
 
 The timed region replays a HIP graph of the steps (captured once) so that the
@@ -45,9 +45,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_MATRIX_PEAK_TFLOPS = 157.3
 BF16_MATRIX_PEAK_TFLOPS = 2500.0
 # bytes of weights per decoded token implied by the pages' measurements
-# (effective GB/s divided by tok/s): 8-bit 0.8B backbone, 4-bit 2B model,
-# 1-bit 27B model
-BYTES_PER_TOKEN = {1: 0.99e9, 2: 1.10e9, 3: 3.9e9}
+# (effective GB/s divided by tok/s): 8-bit 0.8B backbone (either scale
+# layout), 4-bit 2B model, 1-bit 27B model
+BYTES_PER_TOKEN = {1: 0.99e9, 2: 1.10e9, 3: 3.9e9, 4: 0.99e9}
 
 WORKLOADS = {
     "c0": ["c0_i8_gemv_1024x1024"],
@@ -62,6 +62,8 @@ WORKLOADS = {
     "head64": ["n1a_u4_head_151936x2048_b64", "n1b_u4_head_151936x2048_b64_nologits"],
     "head128": ["n1c_u4_head_151936x2048_b128", "n1d_u4_head_151936x2048_b128_nologits"],
     "embed": ["n3_u4_embed_151936x2048_t2048"],
+    "i8g": ["n2c_i8g_gemv_3584x1024", "n2d_i8g_gemv_1024x3584"],
+    "i8ggemm": ["n2e_i8g_gemm_3584x1024_n2048", "n2f_i8g_gemm_1024x3584_n2048"],
 }
 METRIC = "effective weight GB/s and % of HBM peak, batch-1 qgemv; prefill qgemm TFLOP/s"
 EMBED_METRIC = "embedding gather GB/s (ids + packed rows read + float32 rows written)"
@@ -211,6 +213,8 @@ def vendor_ceiling(launches, torch, stream):
         def dequant():
             if c.fmt == 1:      # 8-bit, per-row fp32 scale
                 return codes.float() * wd.scales[:, None]
+            if c.fmt == 4:      # 8-bit, fp32 scale per 64 inputs
+                return codes.float() * wd.scales.repeat_interleave(64, dim=1)
             if c.fmt == 2:      # 4-bit, bf16 scale and bias per 64 inputs (int16 bits)
                 b = codes.view(torch.uint8).int()
                 q4 = torch.stack((b & 15, b >> 4), dim=-1).reshape(c.M, c.K).float()

@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-QG_I8_ROW, QG_U4_G64, QG_B1_G128 = 1, 2, 3
+QG_I8_ROW, QG_U4_G64, QG_B1_G128, QG_I8_G64 = 1, 2, 3, 4
 QG_OP_GEMV, QG_OP_GEMM, QG_OP_GEMV_ARGMAX = 1, 2, 3
 QG_OK = 0
 QG_ERR_NULL, QG_ERR_FORMAT, QG_ERR_SHAPE, QG_ERR_ALIGN = -1, -2, -3, -4

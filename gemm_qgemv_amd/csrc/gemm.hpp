@@ -6,9 +6,10 @@
 // exactly into three bf16 pieces, X = hi + mid + lo (truncation: hi takes the
 // top 8 significant bits, mid the next 8, lo the last 8), and the product runs
 // as three bf16 MFMAs accumulating in float32. The weight operand is exact in
-// bf16 for both formats: int8 codes (|q| <= 128 needs 8 bits) and the signs
-// +-1 of the 1-bit format. Per-row (int8) and per-group (1-bit, 128 k) scales
-// are applied in float32 outside the MFMA.
+// bf16 for every format: int8 codes (|q| <= 128 needs 8 bits), 4-bit codes
+// and the signs +-1 of the 1-bit format. Per-row (int8) and per-group (int8
+// and 4-bit: 64 k, 1-bit: 128 k) scales are applied in float32 outside the
+// MFMA.
 // (MiniCPM-V-4.6 on a Tesla C2075, academ.us 2607.14568, section 3.1:
 // prefill projections are genuine matrix-matrix products; this kernel keeps
 // the weights packed instead of dequantizing them to a float scratch first.)
@@ -100,8 +101,11 @@ __device__ __forceinline__ uint32_t signpair_to_bf16x2(uint32_t nbits2)
 
 constexpr int GT_K = 32;    // k per step
 constexpr int kGemmThreads = 256;
-// k-steps of loads in flight (register sets); the 1-bit format also holds
-// its per-group accumulators, so it keeps fewer sets
+// k-steps of loads in flight (register sets), per format, as measured. For
+// the 64-input groups a depth of 2 (one group) puts the group close at the
+// same place of every unrolled pass of the pipeline loop, which is cheaper
+// than deeper prefetch (8-bit group-64 at 3584 x 1024, N = 2048: 99 us at
+// depth 2, 105 us at depth 3).
 #ifndef QG_GEMM_DEPTH_I8
 #define QG_GEMM_DEPTH_I8 3
 #endif
@@ -110,6 +114,9 @@ constexpr int kGemmThreads = 256;
 #endif
 #ifndef QG_GEMM_DEPTH_U4
 #define QG_GEMM_DEPTH_U4 2
+#endif
+#ifndef QG_GEMM_DEPTH_I8G
+#define QG_GEMM_DEPTH_I8G 2
 #endif
 #ifndef QG_GEMM_INTERLEAVE
 #define QG_GEMM_INTERLEAVE 6   // staging VALU instructions issued after each MFMA
@@ -163,7 +170,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
     const bool xst = 2 * BN >= kGemmThreads || sr < BN;
     const int64_t wrow = m0 + sr, xrow = n0 + sr;
     const bool wvalid = wst && wrow < p.M, xvalid = xst && xrow < p.N;
-    const int64_t row_bytes = FMT == FMT_I8_ROW ? p.K : FMT == FMT_U4_G64 ? p.K / 2 : p.K / 8;
+    constexpr bool I8 = FMT == FMT_I8_ROW || FMT == FMT_I8_G64;   // int8 codes
+    const int64_t row_bytes = I8 ? p.K : FMT == FMT_U4_G64 ? p.K / 2 : p.K / 8;
     const uint8_t *wsrc = p.codes + (wvalid ? wrow : 0) * row_bytes;
     const float *xsrc = p.x + (xvalid ? xrow : 0) * p.K;
     const int nk = static_cast<int>((p.K + GT_K - 1) / GT_K);   // K is a multiple of 16
@@ -180,7 +188,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
     auto load = [&](Regs &R, int kt) {
         const int64_t k = static_cast<int64_t>(kt) * GT_K + 16 * sh;
         const bool kin = k < p.K;   // the last step of an odd number of 16-k halves
-        if (FMT == FMT_I8_ROW) {
+        if (I8) {
             R.w = (wvalid && kin) ? *reinterpret_cast<const uint4 *>(wsrc + k) : make_uint4(0, 0, 0, 0);
         } else if (FMT == FMT_U4_G64) {
             const uint2 v = (wvalid && kin) ? *reinterpret_cast<const uint2 *>(wsrc + k / 2) : make_uint2(0, 0);
@@ -195,7 +203,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
                                      : make_float4(0.f, 0.f, 0.f, 0.f);
         if (GROUPED && kt % GSTEPS == 0 && tid < BM) {
             const int64_t gi = (m0 + tid) * groups + kt / GSTEPS;
-            R.s = m0 + tid < p.M ? ssrc[gi] : 0u;
+            if (FMT == FMT_I8_G64)
+                R.s = m0 + tid < p.M ? __float_as_uint(static_cast<const float *>(p.scales)[gi]) : 0u;
+            else
+                R.s = m0 + tid < p.M ? ssrc[gi] : 0u;
             if (FMT == FMT_U4_G64) R.b = m0 + tid < p.M ? p.biases[gi] : 0u;
         }
     };
@@ -203,7 +214,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
     auto stage = [&](const Regs &R, int kt, int b) {
         if (wst) {
             uint32_t wv[8];
-            if (FMT == FMT_I8_ROW) {
+            if (I8) {
                 const uint32_t d[4] = {R.w.x, R.w.y, R.w.z, R.w.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -269,6 +280,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
             const int gb = (kt / GSTEPS) & 1;
             if (FMT == FMT_B1_G128) {
                 ls[gb][tid] = fp16_bits_to_f32(static_cast<uint16_t>(R.s));
+            } else if (FMT == FMT_I8_G64) {
+                ls[gb][tid] = __uint_as_float(R.s);
             } else {
                 ls[gb][tid] = bf16_bits_to_f32(R.s);
                 lb[gb][tid] = bf16_bits_to_f32(R.b);
@@ -341,7 +354,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
     // pipeline: LDS buffer kt & 1 holds step kt; register set s % D holds
     // step s from its load (D steps before it is staged) until it is staged
     // (one step before it is computed)
-    constexpr int D = FMT == FMT_I8_ROW ? QG_GEMM_DEPTH_I8 : FMT == FMT_U4_G64 ? QG_GEMM_DEPTH_U4 : QG_GEMM_DEPTH_B1;
+    constexpr int D = FMT == FMT_I8_ROW   ? QG_GEMM_DEPTH_I8
+                      : FMT == FMT_I8_G64 ? QG_GEMM_DEPTH_I8G
+                      : FMT == FMT_U4_G64 ? QG_GEMM_DEPTH_U4
+                                          : QG_GEMM_DEPTH_B1;
     Regs R[D];
 #pragma unroll
     for (int u = 0; u < D; ++u)

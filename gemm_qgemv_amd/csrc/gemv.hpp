@@ -29,12 +29,13 @@
 
 namespace qg {
 
-enum { FMT_I8_ROW = 1, FMT_U4_G64 = 2, FMT_B1_G128 = 3 };
+enum { FMT_I8_ROW = 1, FMT_U4_G64 = 2, FMT_B1_G128 = 3, FMT_I8_G64 = 4 };
 
 template <int FMT> struct Fmt;
 template <> struct Fmt<FMT_I8_ROW>  { static constexpr int KPS = 16;  static constexpr bool kXsum = false; };
 template <> struct Fmt<FMT_U4_G64>  { static constexpr int KPS = 32;  static constexpr bool kXsum = true; };
 template <> struct Fmt<FMT_B1_G128> { static constexpr int KPS = 128; static constexpr bool kXsum = true; };
+template <> struct Fmt<FMT_I8_G64>  { static constexpr int KPS = 16;  static constexpr bool kXsum = false; };
 
 struct GemvParams {
     const uint8_t *codes;
@@ -329,7 +330,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int S = kc / KPS;                       // slices in this split
-    const int64_t row_bytes = FMT == FMT_I8_ROW ? p.K : FMT == FMT_U4_G64 ? p.K / 2 : p.K / 8;
+    const int64_t row_bytes =
+        (FMT == FMT_I8_ROW || FMT == FMT_I8_G64) ? p.K : FMT == FMT_U4_G64 ? p.K / 2 : p.K / 8;
     const int64_t slice0 = k0 / KPS;              // first global slice of this split
     const int64_t m_begin = static_cast<int64_t>(blockIdx.x) * p.rows_per_wg;
     const int64_t m_end = min(p.M, m_begin + p.rows_per_wg);
@@ -387,6 +389,51 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
                         }
                     }
                 }
+            } else if constexpr (FMT == FMT_I8_G64) {
+                // a 16-input slice lies inside one 64-input group: its dot
+                // products are scaled by the group's float32 scale
+                float sc[R];
+                const float *sp = static_cast<const float *>(p.scales);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int64_t m = rb + r;
+                    sc[r] = sp[(m < m_end ? m : m_begin) * (p.K / 64) + gslice / 4];
+                }
+                float dot[R][B];
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int b = 0; b < B; ++b) dot[r][b] = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float qv[R][4];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const uint32_t d = word_of(c[r], j);
+                        qv[r][0] = static_cast<float>(static_cast<int8_t>(d & 0xff));
+                        qv[r][1] = static_cast<float>(static_cast<int8_t>((d >> 8) & 0xff));
+                        qv[r][2] = static_cast<float>(static_cast<int8_t>((d >> 16) & 0xff));
+                        qv[r][3] = static_cast<float>(static_cast<int8_t>(d >> 24));
+                    }
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        const float4 xv = xl[b * pc + swz<CPS>(t * CPS + j)];
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            float a = dot[r][b];
+                            a = fmaf(qv[r][0], xv.x, a);
+                            a = fmaf(qv[r][1], xv.y, a);
+                            a = fmaf(qv[r][2], xv.z, a);
+                            a = fmaf(qv[r][3], xv.w, a);
+                            dot[r][b] = a;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        acc[r * B + b] = fmaf(sc[r], dot[r][b], acc[r * B + b]);
             } else if constexpr (FMT == FMT_U4_G64) {
                 float sc[R], bi[R];
                 const uint16_t *sp = static_cast<const uint16_t *>(p.scales);

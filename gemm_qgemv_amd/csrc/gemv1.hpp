@@ -1,4 +1,5 @@
-// gemv1.hpp -- batch-1 matrix-vector kernel for the 8-bit and 4-bit formats.
+// gemv1.hpp -- batch-1 matrix-vector kernel for the 8-bit (per-row and
+// group-64 scales) and 4-bit formats.
 //
 // Workgroups of 4 independent waves; no LDS and no barrier on the hot path.
 // Lane l owns the 16-byte slices t = l + 64 j (j < NS) of every row, so it
@@ -51,7 +52,7 @@ __device__ __forceinline__ uint4 load_codes(const uint8_t *p)
 template <int NS, int R>
 struct Gemv1Block {
     uint4 c[R][NS];
-    uint32_t s[R][NS];   // 4-bit: bf16 bits of the scale
+    uint32_t s[R][NS];   // 4-bit: bf16 bits of the scale; 8-bit group-64: fp32 bits
     uint32_t b[R][NS];   // 4-bit: bf16 bits of the bias
     float rs;            // 8-bit: scale of the row this lane writes
 };
@@ -63,6 +64,7 @@ struct Gemv1Cursor {
     const uint16_t *s;
     const uint16_t *b;
     const float *rs;
+    const float *gs;     // 8-bit group-64: this lane's first group scale
 };
 
 // Load the next block of R rows and advance the cursor. CHECK: rows at or
@@ -82,6 +84,9 @@ __device__ __forceinline__ void gemv1_load(Gemv1Cursor &cur, int64_t row_bytes, 
             if constexpr (FMT == FMT_U4_G64) {
                 blk.s[r][j] = v ? cur.s[r * groups + 32 * j] : 0u;
                 blk.b[r][j] = v ? cur.b[r * groups + 32 * j] : 0u;
+            } else if constexpr (FMT == FMT_I8_G64) {
+                // slice t = lane + 64 j covers inputs 16 t .. 16 t + 15, in group t / 4
+                blk.s[r][j] = v ? __float_as_uint(cur.gs[r * groups + 16 * j]) : 0u;
             }
         }
     }
@@ -90,19 +95,21 @@ __device__ __forceinline__ void gemv1_load(Gemv1Cursor &cur, int64_t row_bytes, 
     cur.s += R * groups;
     cur.b += R * groups;
     cur.rs += R;
+    cur.gs += R * groups;
 }
 
 template <int FMT, int NS, int R, bool FULL, bool NT>
 __global__ __launch_bounds__(256) void gemv1_kernel(Gemv1Params p)
 {
-    constexpr int KPS = Fmt<FMT>::KPS;   // 16 (I8) or 32 (U4)
+    constexpr int KPS = Fmt<FMT>::KPS;   // 16 (8-bit) or 32 (4-bit)
     constexpr int CPS = KPS / 4;         // float4 chunks per slice
-    static_assert(FMT == FMT_I8_ROW || FMT == FMT_U4_G64, "8-bit and 4-bit formats only");
+    static_assert(FMT == FMT_I8_ROW || FMT == FMT_U4_G64 || FMT == FMT_I8_G64,
+                  "8-bit and 4-bit formats only");
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int S = static_cast<int>(p.K / KPS);
-    const int64_t row_bytes = FMT == FMT_I8_ROW ? p.K : p.K / 2;
+    const int64_t row_bytes = FMT == FMT_U4_G64 ? p.K / 2 : p.K;
     const int64_t groups = p.K / 64;
     const int64_t m_begin = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * p.rows_per_wave;
     const int64_t m_end = min(p.M, m_begin + p.rows_per_wave);
@@ -118,6 +125,7 @@ __global__ __launch_bounds__(256) void gemv1_kernel(Gemv1Params p)
     cur.b = static_cast<const uint16_t *>(FMT == FMT_U4_G64 ? p.biases : p.scales) +
             (FMT == FMT_U4_G64 ? m_begin * groups + lane / 2 : 0);
     cur.rs = static_cast<const float *>(p.scales) + (FMT == FMT_I8_ROW ? m_begin + own : 0);
+    cur.gs = static_cast<const float *>(p.scales) + (FMT == FMT_I8_G64 ? m_begin * groups + lane / 4 : 0);
 
     Gemv1Block<NS, R> A, B;
     if (nfull > 0) gemv1_load<FMT, NS, R, FULL, NT, false>(cur, row_bytes, groups, lane, S, own, R, A);
@@ -160,6 +168,13 @@ __global__ __launch_bounds__(256) void gemv1_kernel(Gemv1Params p)
                     a = dot_i8x4(c.y, xv[j][1], a);
                     a = dot_i8x4(c.z, xv[j][2], a);
                     a = dot_i8x4(c.w, xv[j][3], a);
+                } else if constexpr (FMT == FMT_I8_G64) {
+                    float d = 0.f;
+                    d = dot_i8x4(c.x, xv[j][0], d);
+                    d = dot_i8x4(c.y, xv[j][1], d);
+                    d = dot_i8x4(c.z, xv[j][2], d);
+                    d = dot_i8x4(c.w, xv[j][3], d);
+                    a = fmaf(__uint_as_float(blk.s[r][j]), d, a);
                 } else {
                     float d = 0.f;
                     d = dot_u4x8(c.x, xv[j][0], xv[j][1], d);

@@ -38,16 +38,29 @@ constexpr int64_t kComputeUnits = 256;
 constexpr int64_t kAlign = 16;
 constexpr int kThreads = 256;
 
-int k_unit(int fmt) { return fmt == QG_I8_ROW ? 16 : fmt == QG_U4_G64 ? 64 : 128; }
-int k_per_slice(int fmt) { return fmt == QG_I8_ROW ? 16 : fmt == QG_U4_G64 ? 32 : 128; }
+bool known_format(int fmt)
+{
+    return fmt == QG_I8_ROW || fmt == QG_U4_G64 || fmt == QG_B1_G128 || fmt == QG_I8_G64;
+}
+int k_unit(int fmt)
+{
+    return fmt == QG_I8_ROW ? 16 : (fmt == QG_U4_G64 || fmt == QG_I8_G64) ? 64 : 128;
+}
+int k_per_slice(int fmt)
+{
+    return (fmt == QG_I8_ROW || fmt == QG_I8_G64) ? 16 : fmt == QG_U4_G64 ? 32 : 128;
+}
 
 int64_t row_bytes(int fmt, int64_t K)
 {
-    return fmt == QG_I8_ROW ? K : fmt == QG_U4_G64 ? K / 2 : K / 8;
+    return (fmt == QG_I8_ROW || fmt == QG_I8_G64) ? K : fmt == QG_U4_G64 ? K / 2 : K / 8;
 }
 int64_t scale_bytes(int fmt, int64_t M, int64_t K)
 {
-    return fmt == QG_I8_ROW ? 4 * M : fmt == QG_U4_G64 ? 2 * M * (K / 64) : 2 * M * (K / 128);
+    return fmt == QG_I8_ROW    ? 4 * M
+           : fmt == QG_I8_G64  ? 4 * M * (K / 64)
+           : fmt == QG_U4_G64  ? 2 * M * (K / 64)
+                               : 2 * M * (K / 128);
 }
 int64_t bias_bytes(int fmt, int64_t M, int64_t K)
 {
@@ -67,7 +80,7 @@ size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 int check_weights(int fmt, const void *codes, const void *scales, const void *biases,
                   const float *x, int64_t M, int64_t K)
 {
-    if (fmt != QG_I8_ROW && fmt != QG_U4_G64 && fmt != QG_B1_G128) return QG_ERR_FORMAT;
+    if (!known_format(fmt)) return QG_ERR_FORMAT;
     if (!codes || !scales || !x) return QG_ERR_NULL;
     if ((fmt == QG_U4_G64) != (biases != nullptr)) return QG_ERR_NULL;
     if (M < 1 || M > kMaxM || K < 1 || K > kMaxK || K % k_unit(fmt) != 0) return QG_ERR_SHAPE;
@@ -220,7 +233,7 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
     }
     pl.B = nb <= 1 ? 1 : nb <= 2 ? 2 : nb <= 4 ? 4 : nb <= 8 ? 8 : 16;
     const int kps = k_per_slice(fmt);
-    const bool xsum = fmt != QG_I8_ROW;
+    const bool xsum = fmt == QG_U4_G64 || fmt == QG_B1_G128;   // per-slice activation sums
     // activation planes (+ per-slice sums) must fit the LDS budget
     const double bytes_per_k = pl.B * 4.0 * (1.0 + (xsum ? 1.0 / kps : 0.0));
     int64_t kc_max = static_cast<int64_t>((kLdsBudget - 64 * pl.B) / bytes_per_k);
@@ -371,6 +384,7 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         q.K = K;
         q.rows_per_wave = pl.rows_per_wave;
         if (fmt == QG_I8_ROW) launch_gemv1_fmt<qg::FMT_I8_ROW>(pl, q, s);
+        else if (fmt == QG_I8_G64) launch_gemv1_fmt<qg::FMT_I8_G64>(pl, q, s);
         else launch_gemv1_fmt<qg::FMT_U4_G64>(pl, q, s);
         return;
     }
@@ -425,6 +439,7 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
     p.nsplit = pl.nsplit;
     p.nkeys = pl.nkeys;
     if (fmt == QG_I8_ROW) launch_gemv_fmt<qg::FMT_I8_ROW>(pl, p, s);
+    else if (fmt == QG_I8_G64) launch_gemv_fmt<qg::FMT_I8_G64>(pl, p, s);
     else if (fmt == QG_U4_G64) launch_gemv_fmt<qg::FMT_U4_G64>(pl, p, s);
     else launch_gemv_fmt<qg::FMT_B1_G128>(pl, p, s);
     if (pl.nsplit > 1) {
@@ -501,6 +516,8 @@ void gemm_tile(int fmt, int64_t M, int64_t N, int &bm, int &bn)
     // (64 token rows with 128-row tiles would halve the useful MFMA work)
     const bool n128 = N % 128 == 0 || N % 128 > 64;
     if (!n128) return;
+    // 128 x 128 only for the per-row 8-bit format: the grouped formats keep a
+    // second set of accumulators, which would not fit in registers
     if (fmt == QG_I8_ROW && tiles(128, 128) >= kComputeUnits) bm = 128, bn = 128;
     else if (tiles(64, 128) >= kComputeUnits) bn = 128;
 }
@@ -531,6 +548,9 @@ void launch_gemm(int fmt, const void *codes, const void *scales, const void *bia
         if (bm == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_ROW, 128, 128>), grid, block, 0, s, p);
         else if (bn == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_ROW, 64, 128>), grid, block, 0, s, p);
         else hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_ROW, 64, 64>), grid, block, 0, s, p);
+    } else if (fmt == QG_I8_G64) {
+        if (bn == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_G64, 64, 128>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_G64, 64, 64>), grid, block, 0, s, p);
     } else if (fmt == QG_U4_G64) {
         if (bn == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_U4_G64, 64, 128>), grid, block, 0, s, p);
         else hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_U4_G64, 64, 64>), grid, block, 0, s, p);
@@ -640,7 +660,7 @@ int embed_entry(int fmt, const void *codes, const void *scales, const void *bias
                 const int32_t *ids, float *out, int64_t M, int64_t K, int64_t n,
                 hipStream_t stream)
 {
-    if (fmt != QG_I8_ROW && fmt != QG_U4_G64 && fmt != QG_B1_G128) return QG_ERR_FORMAT;
+    if (!known_format(fmt)) return QG_ERR_FORMAT;
     if (!codes || !scales || !ids || !out) return QG_ERR_NULL;
     if ((fmt == QG_U4_G64) != (biases != nullptr)) return QG_ERR_NULL;
     if (fmt != QG_U4_G64) return QG_ERR_UNSUPPORTED;
@@ -711,7 +731,7 @@ int qembed(int fmt, const void *codes, const void *scales, const void *biases,
 
 size_t qg_workspace_bytes(int op, int fmt, int64_t M, int64_t K, int64_t rows)
 {
-    if (fmt != QG_I8_ROW && fmt != QG_U4_G64 && fmt != QG_B1_G128) return 0;
+    if (!known_format(fmt)) return 0;
     if (M < 1 || M > kMaxM || K < 1 || K > kMaxK || K % k_unit(fmt) != 0) return 0;
     if (op == QG_OP_GEMV_ARGMAX && rows > QG_MAX_GEMV_BATCH && rows <= QG_MAX_ARGMAX_BATCH)
         return wide_argmax_workspace(fmt, M, rows);

@@ -31,9 +31,9 @@ import dataclasses
 
 import numpy as np
 
-I8_ROW, U4_G64, B1_G128 = 1, 2, 3
-FORMAT_NAMES = {I8_ROW: "i8_row", U4_G64: "u4_g64", B1_G128: "b1_g128"}
-K_UNIT = {I8_ROW: 16, U4_G64: 64, B1_G128: 128}
+I8_ROW, U4_G64, B1_G128, I8_G64 = 1, 2, 3, 4
+FORMAT_NAMES = {I8_ROW: "i8_row", U4_G64: "u4_g64", B1_G128: "b1_g128", I8_G64: "i8_g64"}
+K_UNIT = {I8_ROW: 16, U4_G64: 64, B1_G128: 128, I8_G64: 64}
 
 
 def rng_for(case: int, variant: int) -> np.random.Generator:
@@ -73,6 +73,8 @@ def weight_bytes(fmt: int, M: int, K: int) -> int:
     """Bytes of codes + scales (+ biases) of an M x K matrix in `fmt`."""
     if fmt == I8_ROW:
         return M * K + 4 * M
+    if fmt == I8_G64:
+        return M * K + 4 * M * (K // 64)
     if fmt == U4_G64:
         return M * K // 2 + 2 * 2 * M * (K // 64)
     if fmt == B1_G128:
@@ -86,6 +88,10 @@ def draw_weights(fmt: int, M: int, K: int, rng: np.random.Generator) -> QWeights
     if fmt == I8_ROW:
         codes = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
         scales = rng.uniform(1e-3, 1e-2, size=M).astype(np.float32)
+        return QWeights(fmt, M, K, codes, scales, None)
+    if fmt == I8_G64:
+        codes = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+        scales = rng.uniform(1e-3, 1e-2, size=(M, K // 64)).astype(np.float32)
         return QWeights(fmt, M, K, codes, scales, None)
     if fmt == U4_G64:
         codes = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
@@ -204,7 +210,8 @@ CASES = [
 # at the 4-bit matvec shapes, with a 2048-token prompt; the greedy head at 64
 # and 128 rows, with logits and without ("greedy": qgemv_argmax, logits NULL);
 # the embedding rows of a 2048-token prompt gathered from the same (tied)
-# head matrix.
+# head matrix; the 8-bit format with one scale per 64 inputs at the 8-bit
+# projection shapes, batch 1 and a 2048-token prompt.
 NEXT_CASES = [
     Case("n2a_u4_gemm_6144x2048_n2048", "gemm", U4_G64, 6144, 2048, 2048, 5, 0),
     Case("n2b_u4_gemm_2048x6144_n2048", "gemm", U4_G64, 2048, 6144, 2048, 5, 1),
@@ -213,6 +220,10 @@ NEXT_CASES = [
     Case("n1c_u4_head_151936x2048_b128", "gemv_argmax", U4_G64, 151936, 2048, 128, 2, 0, x_variant=7),
     Case("n1d_u4_head_151936x2048_b128_nologits", "greedy", U4_G64, 151936, 2048, 128, 2, 0, x_variant=7),
     Case("n3_u4_embed_151936x2048_t2048", "embed", U4_G64, 151936, 2048, 2048, 2, 0, x_variant=8),
+    Case("n2c_i8g_gemv_3584x1024", "gemv", I8_G64, 3584, 1024, 1, 6, 0),
+    Case("n2d_i8g_gemv_1024x3584", "gemv", I8_G64, 1024, 3584, 1, 6, 1),
+    Case("n2e_i8g_gemm_3584x1024_n2048", "gemm", I8_G64, 3584, 1024, 2048, 6, 2),
+    Case("n2f_i8g_gemm_1024x3584_n2048", "gemm", I8_G64, 1024, 3584, 2048, 6, 3),
 ]
 CASES_BY_NAME = {c.name: c for c in CASES + NEXT_CASES}
 

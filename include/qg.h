@@ -24,6 +24,12 @@
  *     is slower": symmetric 8-bit weights with an FP32 scale, read without
  *     unpacking; here the scale is per row.)
  *
+ *   QG_I8_G64   codes  int8  [M][K]      two's complement, any value
+ *               scales fp32  [M][K/64]   w = scales[m][k/64] * q
+ *               biases must be NULL.  K must be a multiple of 64.
+ *     (MiniCPM-V-4.6 on a Tesla C2075, section 2.3: one FP32 scale per
+ *     group of 64 symmetric 8-bit weights, the format that backbone ships.)
+ *
  *   QG_U4_G64   codes  uint8 [M][K/2]    byte j of a row: k=2j in bits 0..3,
  *                                        k=2j+1 in bits 4..7, q in 0..15
  *               scales bf16  [M][K/64]   (uint16 bit patterns)
@@ -91,7 +97,8 @@ extern "C" {
 typedef enum {
     QG_I8_ROW = 1,
     QG_U4_G64 = 2,
-    QG_B1_G128 = 3
+    QG_B1_G128 = 3,
+    QG_I8_G64 = 4
 } qg_format;
 
 typedef enum {
@@ -145,7 +152,7 @@ int qgemv(int fmt, const void *codes, const void *scales, const void *biases,
  * 4GB Maxwell GPUs, "A packed Q1 prefill kernel with a narrow dispatch
  * window": the weights may be consumed packed.)
  *   X  float32 [N][K];  Y  float32 [N][M] (overwritten).  1 <= N <= 2^31-1.
- *   All three formats; for QG_U4_G64 the bias term sum_g b[m][g] * (sum of
+ *   All four formats; for QG_U4_G64 the bias term sum_g b[m][g] * (sum of
  *   X[n][k] over group g) is added per group beside the scaled code sums.
  */
 int qgemm(int fmt, const void *codes, const void *scales, const void *biases,

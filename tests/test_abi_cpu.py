@@ -184,3 +184,22 @@ def test_embed_checks():
     assert err(out=ids - 16) == q.QG_ERR_ALIAS              # covers the ids
     assert err(ids=out + 64) == q.QG_ERR_ALIAS              # ids inside out
     assert "format" in q.qg_status_str(q.QG_ERR_UNSUPPORTED)
+
+
+def test_i8_group64_format_checks():
+    """8-bit weights with a float32 scale per 64 inputs: K a multiple of 64,
+    no biases; the workspace rules are those of the other formats."""
+    assert _err(q.qgemv, q.QG_I8_G64, A, A + 4096, None, A + 8192, A + 65536, 4, 48, 1) == \
+        q.QG_ERR_SHAPE
+    assert _err(q.qgemv, q.QG_I8_G64, A, A + 4096, A + 12288, A + 8192, A + 65536, 4, 64, 1) == \
+        q.QG_ERR_NULL
+    assert _err(q.qgemm, q.QG_I8_G64, A, A + 4096, None, A + 8192, A + 65536, 4, 96, 32) == \
+        q.QG_ERR_SHAPE
+    # y overlapping the scales ([M][K/64] floats = 4 * 2 * 4 bytes here)
+    assert _err(q.qgemv, q.QG_I8_G64, A, A + 4096, None, A + 8192, A + 4096, 4, 128, 1) == \
+        q.QG_ERR_ALIAS
+    assert q.qg_workspace_bytes(q.QG_OP_GEMV, q.QG_I8_G64, 10, 96, 1) == 0
+    assert q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_I8_G64, 3584, 1024, 1) >= \
+        q.QG_WS_CONTROL_BYTES
+    assert q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_I8_G64, 3584, 1024, 64) >= \
+        q.QG_WS_CONTROL_BYTES + 64 * (3584 // 64) * 8

@@ -146,6 +146,10 @@ def exact_inputs(fmt, M, K, N, rng):
         codes = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
         scales = (2.0 ** -rng.integers(4, 8, size=M)).astype(np.float32)
         return synth.QWeights(fmt, M, K, codes, scales, None), x
+    if fmt == synth.I8_G64:
+        codes = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+        scales = (2.0 ** -rng.integers(4, 8, size=(M, K // 64))).astype(np.float32)
+        return synth.QWeights(fmt, M, K, codes, scales, None), x
     if fmt == synth.U4_G64:
         codes = rng.integers(0, 256, size=(M, K // 2)).astype(np.uint8)
         s = (2.0 ** -rng.integers(4, 8, size=(M, K // 64))).astype(np.float32)
@@ -160,6 +164,8 @@ def exact_inputs(fmt, M, K, N, rng):
     (synth.I8_ROW, 129, 1024, 1), (synth.I8_ROW, 70, 528, 5), (synth.I8_ROW, 33, 1024, 16),
     (synth.U4_G64, 129, 1024, 1), (synth.U4_G64, 65, 576, 3), (synth.U4_G64, 300, 1024, 8),
     (synth.B1_G128, 129, 1024, 1), (synth.B1_G128, 17, 1152, 6), (synth.B1_G128, 257, 1024, 16),
+    (synth.I8_G64, 129, 1024, 1), (synth.I8_G64, 70, 576, 5), (synth.I8_G64, 33, 1024, 16),
+    (synth.I8_G64, 100, 4160, 1),
 ])
 def test_exact_arithmetic_bit_exact(torch, orc, fmt, M, K, N):
     say(f"exact fmt={fmt} M={M} K={K} N={N}")
@@ -179,6 +185,8 @@ def test_exact_arithmetic_bit_exact(torch, orc, fmt, M, K, N):
     (synth.I8_ROW, 1024, 3584, 64), (synth.B1_G128, 129, 1024, 17), (synth.B1_G128, 260, 640, 300),
     (synth.B1_G128, 5, 128, 129), (synth.U4_G64, 129, 1024, 17), (synth.U4_G64, 300, 1088, 130),
     (synth.U4_G64, 7, 64, 257), (synth.U4_G64, 1024, 2048, 64), (synth.U4_G64, 4001, 192, 1503),
+    (synth.I8_G64, 129, 1024, 17), (synth.I8_G64, 300, 1088, 130), (synth.I8_G64, 7, 64, 257),
+    (synth.I8_G64, 4001, 192, 1503), (synth.I8_G64, 1024, 3584, 64),
 ])
 def test_exact_arithmetic_prefill_bit_exact(torch, orc, fmt, M, K, N):
     """The matrix-core prefill path (more than 16 token rows) on exact inputs."""
@@ -212,6 +220,8 @@ def test_exact_arithmetic_prefill_large_grid(torch, orc, M, K, N):
     (synth.I8_ROW, 130, 3584, 33), (synth.B1_G128, 1, 128, 40), (synth.B1_G128, 250, 5120, 131),
     (synth.B1_G128, 129, 1152, 256), (synth.U4_G64, 1, 64, 40), (synth.U4_G64, 1000, 2048, 300),
     (synth.U4_G64, 127, 6144, 129), (synth.U4_G64, 6144, 2048, 2048),
+    (synth.I8_G64, 1, 64, 40), (synth.I8_G64, 1000, 1024, 300), (synth.I8_G64, 127, 3584, 129),
+    (synth.I8_G64, 3584, 1024, 2048),
 ])
 def test_random_prefill_small(torch, orc, fmt, M, K, N):
     say(f"random prefill fmt={fmt} M={M} K={K} N={N}")
@@ -234,6 +244,9 @@ SMALL = [
     (synth.U4_G64, 129, 6144, 5), (synth.U4_G64, 64, 8192, 16), (synth.U4_G64, 31, 18048, 7),
     (synth.B1_G128, 1, 128, 1), (synth.B1_G128, 129, 5120, 1), (synth.B1_G128, 1000, 1152, 2),
     (synth.B1_G128, 63, 17408, 1), (synth.B1_G128, 33, 2048, 16), (synth.B1_G128, 8, 640, 9),
+    (synth.I8_G64, 1, 64, 1), (synth.I8_G64, 127, 1088, 1), (synth.I8_G64, 1000, 1024, 3),
+    (synth.I8_G64, 129, 16384, 1), (synth.I8_G64, 45, 20032, 2), (synth.I8_G64, 64, 4096, 16),
+    (synth.I8_G64, 3584, 1024, 1), (synth.I8_G64, 1024, 3584, 1),
 ]
 
 
@@ -432,8 +445,10 @@ def test_wide_greedy_head_ties():
 # the configurations at full size
 # ---------------------------------------------------------------------------
 
-GEMV_CASES = [c for c in synth.CASES if c.op != "gemm"]
-GEMM_CASES = [c for c in synth.CASES if c.op == "gemm"]
+# the configurations, and the measured cases of the 8-bit group-64 format
+MEASURED = synth.CASES + [c for c in synth.NEXT_CASES if c.fmt == synth.I8_G64]
+GEMV_CASES = [c for c in MEASURED if c.op != "gemm"]
+GEMM_CASES = [c for c in MEASURED if c.op == "gemm"]
 
 
 @pytest.mark.parametrize("case", GEMV_CASES, ids=lambda c: c.name)
