@@ -222,6 +222,25 @@ __device__ __forceinline__ float splitk_get(const float *src)
     return __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Sum of the nsplit partials part[s * stride], s = 0 .. nsplit-1, added in
+// split order. The device-scope loads go out in batches of 8 before any of
+// them is used (a plain loop would wait for each one in turn); a batch
+// past the last split re-reads the last partial and drops it.
+__device__ __forceinline__ float splitk_sum(const float *part, int64_t stride, int nsplit)
+{
+    constexpr int kBatch = 8;
+    float acc = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+        float v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) v[i] = splitk_get(part + min(s0 + i, nsplit - 1) * stride);
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            if (s0 + i < nsplit) acc += v[i];
+    }
+    return acc;
+}
+
 __device__ __forceinline__ bool splitk_arrive(unsigned *counter, int nsplit)
 {
     __shared__ unsigned s_last;

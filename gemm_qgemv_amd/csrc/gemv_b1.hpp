@@ -9,25 +9,31 @@
 // kernel with a narrow dispatch window": the weights stay packed and
 // LUT-based products over low-bit weights are the related method).
 //
-// Mapping. A workgroup of 4 waves covers 256 rows (one row per lane) and one
-// chunk of KC inputs; its tables (KC/4 positions x 16 floats = 16 KiB for
-// KC = 1024) are built once in LDS by the workgroup and shared by all its
-// rows. At any instant all 64 lanes of a wave read the same 64-byte table
-// (same position, different rows), so every lookup is served without bank
-// conflicts (same-address lanes are broadcast, distinct entries sit in
-// distinct banks). The tile's codes are read with coalesced 16-byte loads
-// (8 consecutive threads per 128-byte row segment), issued before the
-// tables are built, and passed through padded LDS rows to the lane that
-// owns the row. Per 16-byte group (128 weights, one fp16 scale): 32 nibble
-// lookups and no cross-lane reduction. Chunks of K go to different
-// workgroups; their partial sums are combined in split order by the last
-// workgroup of each row tile (splitk_arrive), or by gemv_combine_kernel when
-// there are more row tiles than counters.
+// Mapping. A workgroup covers 64 rows (one row per lane) and one chunk of KC
+// inputs; its 4 waves split the chunk four ways, so all four run the same
+// rows over different quarters of the tables, and their partial sums meet
+// in LDS. The chunk's tables (KC/4 positions x 16 floats = 16 KiB for
+// KC = 1024) are built once by the workgroup. At any instant the 64 lanes
+// of a wave read the same 64-byte table (same position, different rows), so
+// every lookup is served without bank conflicts (same-address lanes are
+// broadcast, distinct entries sit in distinct banks). The tile's codes are
+// read with coalesced 16-byte loads (8 consecutive threads per 128-byte row
+// segment), issued before the tables are built, and passed through padded
+// LDS rows to the lane that owns the row. Small 64-row tiles give many
+// workgroups (several per compute unit at once), which spreads the lookups
+// evenly over the SIMDs and lets one workgroup's lookups overlap another's
+// loads. Chunks of K go to different workgroups; their partial sums are
+// combined in split order by the last workgroup of each row tile
+// (splitk_arrive), or by gemv_combine_kernel when there are more row tiles
+// than counters.
 #pragma once
 
 #include "gemv.hpp"
 
 namespace qg {
+
+// Rows per workgroup of the lookup kernel (one per lane of each wave).
+constexpr int kB1Rows = 64;
 
 struct B1LutParams {
     const uint8_t *codes;
@@ -58,26 +64,29 @@ template <int KC>
 __global__ __launch_bounds__(256) void gemv_b1_lut_kernel(B1LutParams p)
 {
     constexpr int NG = KC / 128;          // 16-byte groups per row and chunk
+    constexpr int GPW = NG / 4;           // groups per wave
     constexpr int NQ = KC / 4;            // nibble positions per chunk
-    constexpr int ROWS = 256;             // rows per workgroup (one per lane)
+    constexpr int ROWS = kB1Rows;
     constexpr int CROW = 16 * NG + 16;    // padded LDS row of codes (bytes)
     constexpr int NLD = ROWS * NG / 256;  // 16-byte code loads per thread
-    static_assert(NQ <= 256, "one table per thread");
+    static_assert(NG % 4 == 0 && NLD >= 1 && ROWS * NG % 256 == 0, "chunk shape");
     __shared__ __attribute__((aligned(16))) float lut[NQ * 16];
     __shared__ __attribute__((aligned(16))) uint8_t codes_l[ROWS * CROW];
+    __shared__ float red[4][ROWS];
 
     const int split = blockIdx.y;
     const int64_t k0 = static_cast<int64_t>(split) * KC;
     const int ng = static_cast<int>(min(static_cast<int64_t>(NG), (p.K - k0) / 128));
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t row0 = static_cast<int64_t>(blockIdx.x) * ROWS;
-    const int64_t m = row0 + tid;
+    const int64_t m = row0 + lane;
     const bool mv = m < p.M;
     const int64_t row_bytes = p.K / 8;
     const int64_t groups = p.K / 128;
 
     // 1. request the tile's codes, coalesced: 8 consecutive threads read one
-    //    row's 128 contiguous bytes; also this thread's row scales
+    //    row's 128 contiguous bytes; also the scales of this wave's groups
     uint4 st[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
@@ -86,10 +95,10 @@ __global__ __launch_bounds__(256) void gemv_b1_lut_kernel(B1LutParams p)
         st[i] = v ? *reinterpret_cast<const uint4 *>(p.codes + (row0 + r) * row_bytes + k0 / 8 + 16 * g)
                   : make_uint4(0, 0, 0, 0);
     }
-    uint32_t sc[NG];
-    const uint16_t *sp = p.scales + (mv ? m : 0) * groups + k0 / 128;
+    uint32_t sc[GPW];
+    const uint16_t *sp = p.scales + (mv ? m : 0) * groups + k0 / 128 + wave * GPW;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) sc[g] = (mv && g < ng) ? sp[g] : 0u;
+    for (int j = 0; j < GPW; ++j) sc[j] = (mv && wave * GPW + j < ng) ? sp[j] : 0u;
 
     // 2. tables of this chunk: thread q builds position q (16 signed sums)
     for (int q = tid; q < NQ; q += blockDim.x) {
@@ -120,13 +129,14 @@ __global__ __launch_bounds__(256) void gemv_b1_lut_kernel(B1LutParams p)
     }
     __syncthreads();
 
-    // 4. lookups: this thread's row
+    // 4. lookups: this lane's row, this wave's groups
     const char *lb = reinterpret_cast<const char *>(lut);
     float acc = 0.f;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
+    for (int j = 0; j < GPW; ++j) {
+        const int g = wave * GPW + j;
         if (g < ng) {
-            const uint4 cg = *reinterpret_cast<const uint4 *>(codes_l + tid * CROW + 16 * g);
+            const uint4 cg = *reinterpret_cast<const uint4 *>(codes_l + lane * CROW + 16 * g);
             const uint32_t dw[4] = {cg.x, cg.y, cg.z, cg.w};
             // two batches of 16 independent lookups (the LDS counter tracks
             // at most 15 in flight), each summed as a tree
@@ -136,12 +146,12 @@ __global__ __launch_bounds__(256) void gemv_b1_lut_kernel(B1LutParams p)
                 float v[16];
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj) {
-                    const int j = 2 * h + jj;
+                    const int d = 2 * h + jj;
                     uint32_t lo4, hi4;
-                    nibble_offsets(dw[j], lo4, hi4);
+                    nibble_offsets(dw[d], lo4, hi4);
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
-                        const int q = 32 * g + 8 * j + 2 * b;    // position of the low nibble of byte b
+                        const int q = 32 * g + 8 * d + 2 * b;    // position of the low nibble of byte b
                         const uint32_t ol = (lo4 >> (8 * b)) & 0xffu;
                         const uint32_t oh = (hi4 >> (8 * b)) & 0xffu;
                         v[8 * jj + 2 * b] = *reinterpret_cast<const float *>(lb + 64 * q + ol);
@@ -154,35 +164,44 @@ __global__ __launch_bounds__(256) void gemv_b1_lut_kernel(B1LutParams p)
                     for (int i = 0; i < w; ++i) v[i] += v[i + w];
                 half[h] = v[0];
             }
-            acc = fmaf(fp16_bits_to_f32(static_cast<uint16_t>(sc[g])), half[0] + half[1], acc);
+            acc = fmaf(fp16_bits_to_f32(static_cast<uint16_t>(sc[j])), half[0] + half[1], acc);
         }
     }
+    // the four quarters of the chunk, summed in wave order
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) {
+        // only wave 0 carries the rows from here; the others still take part
+        // in the workgroup-wide steps below
+        acc = 0.f;
+    } else {
+        acc = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    }
+    const bool own = wave == 0 && mv;
 
     // 5. several chunks: fused combine, finished by the tile's last workgroup
     if (p.nsplit > 1) {
         if (p.fused) {
-            if (mv) splitk_put(&p.part[static_cast<int64_t>(split) * p.M + m], acc);
+            if (own) splitk_put(&p.part[static_cast<int64_t>(split) * p.M + m], acc);
             if (!splitk_arrive(&tile_counters(p.ctl)[blockIdx.x], p.nsplit)) return;
-            acc = 0.f;
-            if (mv)
-                for (int s = 0; s < p.nsplit; ++s) acc += splitk_get(&p.part[static_cast<int64_t>(s) * p.M + m]);
+            acc = own ? splitk_sum(p.part + m, p.M, p.nsplit) : 0.f;
         } else {
-            if (mv) p.part[static_cast<int64_t>(split) * p.M + m] = acc;
+            if (own) p.part[static_cast<int64_t>(split) * p.M + m] = acc;
             return;
         }
     }
-    if (mv && p.y) p.y[m] = acc;
+    if (own && p.y) p.y[m] = acc;
     if (p.idx != nullptr) {
         __shared__ unsigned long long s_key;
         if (tid == 0) s_key = 0ull;
         __syncthreads();
-        uint64_t key = mv ? argmax_key(acc, static_cast<uint32_t>(m)) : 0ull;
+        uint64_t key = own ? argmax_key(acc, static_cast<uint32_t>(m)) : 0ull;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) {
             const uint64_t other = shfl_xor_u64(key, o);
             key = other > key ? other : key;
         }
-        if ((tid & 63) == 0) atomicMax(&s_key, static_cast<unsigned long long>(key));
+        if (lane == 0) atomicMax(&s_key, static_cast<unsigned long long>(key));
         __syncthreads();
         greedy_finish(&s_key, 1, p.ctl, p.idx, static_cast<int>(gridDim.x));
     }

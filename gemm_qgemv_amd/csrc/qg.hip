@@ -147,7 +147,15 @@ constexpr size_t kCtlBytes = qg::kCtlBytes;
 static_assert(kCtlBytes == QG_WS_CONTROL_BYTES, "control area and header disagree");
 static_assert(sizeof(qg::GreedyCtl) <= qg::kCtlTileOffset, "greedy control words exceed their area");
 
-constexpr int kB1Chunk = 1024;  // K per workgroup of the 1-bit lookup kernel
+// K per workgroup of the 1-bit lookup kernel: 1024 (26 KiB of LDS, six
+// workgroups per compute unit) or 2048 (50 KiB, three). The larger chunk
+// halves the partial sums to combine, and is taken when K is long and its
+// grid still fits in one round of resident workgroups (5120 x 17408: 11.2
+// against 13.7 us; 17408 x 5120 would need 816 workgroups and stays at
+// 1024: 10.2 against 13.1 us).
+constexpr int kB1Chunk = 1024;
+constexpr int kB1ChunkLong = 2048;
+constexpr int64_t kB1LongResident = 3;   // workgroups per compute unit at the long chunk
 
 struct GemvPlan {
     bool mfma;           // small-batch 4-bit kernel on the matrix cores
@@ -190,13 +198,15 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
         return pl;
     }
     if (nb == 1 && fmt == QG_B1_G128) {
-        // batch 1, 1-bit: 256 rows x 1024 inputs per workgroup, partial sums
-        // of the K chunks combined in order
+        // batch 1, 1-bit: 64 rows x 1024 (or 2048) inputs per workgroup,
+        // partial sums of the K chunks combined in order
         pl.lut = true;
         pl.B = 1;
-        pl.kc = kB1Chunk;
-        pl.nsplit = static_cast<int>(ceil_div(K, kB1Chunk));
-        pl.grid_x = ceil_div(M, 256);
+        pl.grid_x = ceil_div(M, qg::kB1Rows);
+        const bool long_chunk = K >= 2 * kB1ChunkLong &&
+                                pl.grid_x * ceil_div(K, kB1ChunkLong) <= kB1LongResident * kComputeUnits;
+        pl.kc = long_chunk ? kB1ChunkLong : kB1Chunk;
+        pl.nsplit = static_cast<int>(ceil_div(K, pl.kc));
         pl.fused = pl.nsplit > 1 && pl.grid_x <= qg::kCtlTileCounters;
         size_t off = kCtlBytes;
         if (pl.nsplit > 1) {
@@ -401,9 +411,11 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         q.K = K;
         q.nsplit = pl.nsplit;
         q.fused = pl.fused;
-        hipLaunchKernelGGL(qg::gemv_b1_lut_kernel<kB1Chunk>,
-                           dim3(static_cast<unsigned>(pl.grid_x), static_cast<unsigned>(pl.nsplit)),
-                           dim3(256), 0, s, q);
+        const dim3 grid(static_cast<unsigned>(pl.grid_x), static_cast<unsigned>(pl.nsplit));
+        if (pl.kc == kB1ChunkLong)
+            hipLaunchKernelGGL(qg::gemv_b1_lut_kernel<kB1ChunkLong>, grid, dim3(256), 0, s, q);
+        else
+            hipLaunchKernelGGL(qg::gemv_b1_lut_kernel<kB1Chunk>, grid, dim3(256), 0, s, q);
         if (pl.nsplit > 1 && !pl.fused) {
             GemvParams c{};
             c.y = y;
