@@ -119,8 +119,32 @@ constexpr int kGemmThreads = 256;
 #define QG_GEMM_DEPTH_I8G 2
 #endif
 #ifndef QG_GEMM_INTERLEAVE
-#define QG_GEMM_INTERLEAVE 6   // staging VALU instructions issued after each MFMA
+#define QG_GEMM_INTERLEAVE 3   // VALU instructions issued after each MFMA
 #endif
+
+// Largest K of the matrix-core prefill: the buffer loads below address a
+// tile's activation rows (128 rows of 4 K bytes) with 32-bit offsets, and
+// every range stays below 2^30 bytes.
+constexpr int64_t kGemmMaxK = int64_t(1) << 21;
+
+// Raw buffer resource over [base, base + bytes) (gfx9 family descriptor
+// word 3: 32-bit data format, untyped). A load whose offset lies outside
+// the range returns zeros, so tile edges need no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0,
+                                             static_cast<int>(bytes), 0x00020000);
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;   // above every range used here
+
+// `off`, or an offset out of range when i >= n, by arithmetic only: a select
+// here would be turned into a branch around the load.
+__device__ __forceinline__ uint32_t in_range_or_out(uint32_t off, int64_t i, int64_t n)
+{
+    uint32_t out = static_cast<uint32_t>(static_cast<uint64_t>(n - 1 - i) >> 63) << 31;
+    asm("" : "+v"(out));
+    return off | out;
+}
 
 // Physical 16-byte chunk of logical chunk c (0..3) in LDS row r (rows of
 // 64 bytes). Under this XOR swizzle any 16 consecutive rows read at one
@@ -138,18 +162,15 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
 {
     constexpr int TI = BM / 16;   // 16-row weight blocks per wave
     constexpr int TJ = BN / 64;   // 16-token blocks per wave
-    static_assert(TI >= 1 && TJ >= 1 && BM * 2 <= kGemmThreads && BN * 2 <= kGemmThreads,
-                  "one staging item per thread");
-    // double-buffered stages: [buffer][row][4 chunks of 8 bf16]
+    static_assert(TI >= 1 && TJ >= 1 && BM * 2 <= kGemmThreads, "one staging item per thread");
+    // double-buffered weight stages: [buffer][row][4 chunks of 8 bf16]
     __shared__ uint4 lw[2][BM * 4];
-    __shared__ uint4 lx[2][3][BN * 4];
-    // per-group coefficients of the current and next group: scales (1-bit
-    // and 4-bit), biases and activation group sums (4-bit)
+    // per-group coefficients of the current and next group: scales (grouped
+    // formats) and biases (4-bit)
     constexpr bool GROUPED = FMT != FMT_I8_ROW;
     constexpr int GSTEPS = FMT == FMT_B1_G128 ? 4 : 2;   // 32-k steps per group
     __shared__ float ls[2][BM];
     __shared__ float lb[2][FMT == FMT_U4_G64 ? BM : 1];
-    __shared__ float lxs[2][FMT == FMT_U4_G64 ? BN : 1];
 
     // XCD-aware order: consecutive workgroup ids go round-robin to the 8
     // XCDs; give each XCD a contiguous run of tiles (m fastest) so the tiles
@@ -164,50 +185,81 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
     const int wn = wave * (BN / 4);
     const int fr = lane & 15, fq = lane >> 4;
 
-    // staging assignment: thread -> (row, half of the 32-k step)
+    // weight staging assignment: thread -> (row, half of the 32-k step)
     const int sr = tid >> 1, sh = tid & 1;
     const bool wst = 2 * BM >= kGemmThreads || sr < BM;   // constant when every thread stages
-    const bool xst = 2 * BN >= kGemmThreads || sr < BN;
-    const int64_t wrow = m0 + sr, xrow = n0 + sr;
-    const bool wvalid = wst && wrow < p.M, xvalid = xst && xrow < p.N;
     constexpr bool I8 = FMT == FMT_I8_ROW || FMT == FMT_I8_G64;   // int8 codes
     const int64_t row_bytes = I8 ? p.K : FMT == FMT_U4_G64 ? p.K / 2 : p.K / 8;
-    const uint8_t *wsrc = p.codes + (wvalid ? wrow : 0) * row_bytes;
-    const float *xsrc = p.x + (xvalid ? xrow : 0) * p.K;
+    const int64_t wrows = min(static_cast<int64_t>(BM), p.M - m0);    // valid rows of the tile
+    const int64_t xrows = min(static_cast<int64_t>(BN), p.N - n0);    // valid tokens of the tile
+    // Buffer views of the tile's weight rows and activation rows: a row
+    // beyond M or N lies outside its view and reads as zero. Offsets of
+    // inputs beyond K (the last step of an odd number of 16-k halves) are
+    // moved out of range explicitly.
+    const auto wbuf = buffer_rsrc(p.codes + m0 * row_bytes, wrows * row_bytes);
+    const auto xbuf = buffer_rsrc(p.x + n0 * p.K, xrows * p.K * 4);
+    const uint32_t woff = wst ? static_cast<uint32_t>(sr * row_bytes) : kOutOfRange;
+    // activation fragments: this lane feeds the MFMA operand of token
+    // n0 + wn + 16 j + fr with inputs 8 fq .. 8 fq + 7 of each step; each
+    // token row is used by this wave only, so it goes straight from global
+    // memory to registers (no LDS stage)
+    uint32_t xoff[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+        xoff[j] = static_cast<uint32_t>(((wn + 16 * j + fr) * p.K + 8 * fq) * 4);
     const int nk = static_cast<int>((p.K + GT_K - 1) / GT_K);   // K is a multiple of 16
     const int64_t groups = p.K / (32 * GSTEPS);
-    const uint16_t *ssrc = static_cast<const uint16_t *>(p.scales);
-    float xsum = 0.f;   // 4-bit format: this thread's part of its activation row's group sum
+    constexpr int SBYTES = FMT == FMT_I8_G64 ? 4 : 2;   // bytes per group coefficient
+    const auto sbuf = buffer_rsrc(static_cast<const uint8_t *>(p.scales) + m0 * groups * SBYTES,
+                                  wrows * groups * SBYTES);
+    const auto bbuf = buffer_rsrc(reinterpret_cast<const uint8_t *>(p.biases) + m0 * groups * 2,
+                                  FMT == FMT_U4_G64 ? wrows * groups * 2 : 0);
+    const uint32_t soff = tid < BM ? static_cast<uint32_t>(tid * groups * SBYTES) : kOutOfRange;
+    const uint32_t boff = tid < BM ? static_cast<uint32_t>(tid * groups * 2) : kOutOfRange;
 
     struct Regs {
         uint4 w;          // I8: 16 codes; U4: w.x, w.y = 16 nibbles; B1: low 16 bits = 16 sign bits
-        float4 x[4];
         uint32_t s, b;    // grouped formats, first step of a group: scale (and bias) bits of row m0 + tid
+        float4 x[TJ][2];  // this lane's activations of the step (8 consecutive inputs per block)
     };
 
-    auto load = [&](Regs &R, int kt) {
+    // Every load is issued unconditionally (edges read zeros through the
+    // buffer range checks), so the compiler can count the loads in flight
+    // exactly and waits only for the step it needs.
+    auto load_w = [&](Regs &R, int kt) {
         const int64_t k = static_cast<int64_t>(kt) * GT_K + 16 * sh;
-        const bool kin = k < p.K;   // the last step of an odd number of 16-k halves
+        constexpr int KSHIFT = I8 ? 0 : FMT == FMT_U4_G64 ? 1 : 3;   // input index -> byte in the row
+        const uint32_t off = in_range_or_out(woff + static_cast<uint32_t>(k >> KSHIFT), k, p.K);
         if (I8) {
-            R.w = (wvalid && kin) ? *reinterpret_cast<const uint4 *>(wsrc + k) : make_uint4(0, 0, 0, 0);
+            R.w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wbuf, off, 0, 0));
         } else if (FMT == FMT_U4_G64) {
-            const uint2 v = (wvalid && kin) ? *reinterpret_cast<const uint2 *>(wsrc + k / 2) : make_uint2(0, 0);
+            const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wbuf, off, 0, 0));
             R.w.x = v.x;
             R.w.y = v.y;
         } else {
-            R.w.x = (wvalid && kin) ? *reinterpret_cast<const uint16_t *>(wsrc + k / 8) : 0u;
+            R.w.x = __builtin_amdgcn_raw_buffer_load_b16(wbuf, off, 0, 0);
         }
+        if (GROUPED && kt % GSTEPS == 0) {
+            const uint32_t o = soff + static_cast<uint32_t>((kt / GSTEPS) * SBYTES);
+            if (FMT == FMT_I8_G64) {
+                R.s = __builtin_amdgcn_raw_buffer_load_b32(sbuf, o, 0, 0);
+            } else {
+                R.s = __builtin_amdgcn_raw_buffer_load_b16(sbuf, o, 0, 0);
+                if (FMT == FMT_U4_G64)
+                    R.b = __builtin_amdgcn_raw_buffer_load_b16(
+                        bbuf, boff + static_cast<uint32_t>((kt / GSTEPS) * 2), 0, 0);
+            }
+        }
+    };
+
+    auto load_x = [&](Regs &R, int kt) {
+        const int64_t k = static_cast<int64_t>(kt) * GT_K;
+        // K is a multiple of 16: a block of 8 inputs is all in or all out
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            R.x[j] = (xvalid && kin) ? *reinterpret_cast<const float4 *>(xsrc + k + 4 * j)
-                                     : make_float4(0.f, 0.f, 0.f, 0.f);
-        if (GROUPED && kt % GSTEPS == 0 && tid < BM) {
-            const int64_t gi = (m0 + tid) * groups + kt / GSTEPS;
-            if (FMT == FMT_I8_G64)
-                R.s = m0 + tid < p.M ? __float_as_uint(static_cast<const float *>(p.scales)[gi]) : 0u;
-            else
-                R.s = m0 + tid < p.M ? ssrc[gi] : 0u;
-            if (FMT == FMT_U4_G64) R.b = m0 + tid < p.M ? p.biases[gi] : 0u;
+        for (int j = 0; j < TJ; ++j) {
+            const uint32_t off = in_range_or_out(xoff[j] + static_cast<uint32_t>(k * 4), k + 8 * fq, p.K);
+            R.x[j][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xbuf, off, 0, 0));
+            R.x[j][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xbuf, off + 16, 0, 0));
         }
     };
 
@@ -236,46 +288,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
             lw[b][sr * 4 + swz_chunk(sr, 2 * sh)] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
             lw[b][sr * 4 + swz_chunk(sr, 2 * sh + 1)] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
         }
-        if (xst) {
-            uint32_t h[8], md[8], lo[8];
-            if (FMT == FMT_U4_G64) {
-                // the weight operand's order: k = 0, 2, 4, 6, 1, 3, 5, 7 of each 8
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const float4 a = R.x[2 * c], e = R.x[2 * c + 1];
-                    split3_pair(a.x, a.z, h[4 * c], md[4 * c], lo[4 * c]);
-                    split3_pair(e.x, e.z, h[4 * c + 1], md[4 * c + 1], lo[4 * c + 1]);
-                    split3_pair(a.y, a.w, h[4 * c + 2], md[4 * c + 2], lo[4 * c + 2]);
-                    split3_pair(e.y, e.w, h[4 * c + 3], md[4 * c + 3], lo[4 * c + 3]);
-                }
-                // group sums of the activations, for the bias term: this
-                // thread's 16 inputs per step, two steps per group, and the
-                // other half of the row from the neighbouring lane
-                float part = 0.f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) part += (R.x[j].x + R.x[j].y) + (R.x[j].z + R.x[j].w);
-                if (kt % GSTEPS == 0) {
-                    xsum = part;
-                } else {
-                    xsum += part;
-                    const float total = xsum + __shfl_xor(xsum, 1);
-                    if (sh == 0) lxs[(kt / GSTEPS) & 1][sr] = total;
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    split3_pair(R.x[j].x, R.x[j].y, h[2 * j], md[2 * j], lo[2 * j]);
-                    split3_pair(R.x[j].z, R.x[j].w, h[2 * j + 1], md[2 * j + 1], lo[2 * j + 1]);
-                }
-            }
-            const int c0 = sr * 4 + swz_chunk(sr, 2 * sh), c1 = sr * 4 + swz_chunk(sr, 2 * sh + 1);
-            lx[b][0][c0] = make_uint4(h[0], h[1], h[2], h[3]);
-            lx[b][0][c1] = make_uint4(h[4], h[5], h[6], h[7]);
-            lx[b][1][c0] = make_uint4(md[0], md[1], md[2], md[3]);
-            lx[b][1][c1] = make_uint4(md[4], md[5], md[6], md[7]);
-            lx[b][2][c0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-            lx[b][2][c1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
-        }
         if (GROUPED && kt % GSTEPS == 0 && tid < BM) {
             const int gb = (kt / GSTEPS) & 1;
             if (FMT == FMT_B1_G128) {
@@ -290,7 +302,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
     };
 
     floatx4_t acc[TI][TJ];
-    floatx4_t gacc[TI][TJ];  // 1-bit format: sums of the current 128-k group
+    floatx4_t gacc[TI][TJ];  // grouped formats: sums of the current group
+    float xs[TJ];            // 4-bit format: this lane's token's activation sum over the group
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -298,8 +311,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
             acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
             gacc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
         }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) xs[j] = 0.f;
 
-    auto compute = [&](int kt) {
+    auto compute = [&](int kt, const Regs &R) {
         const int b = kt & 1;
         bf16x8_t a[TI];
 #pragma unroll
@@ -307,18 +322,44 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
             const int r = 16 * i + fr;
             a[i] = __builtin_bit_cast(bf16x8_t, lw[b][r * 4 + swz_chunk(r, fq)]);
         }
+        // exact three-piece split of this lane's activations (the 4-bit
+        // operand order k = 0, 2, 4, 6, 1, 3, 5, 7 for the 4-bit format)
+        bf16x8_t bx[TJ][3];
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+            const float4 u = R.x[j][0], v = R.x[j][1];
+            uint32_t h[4], md[4], lo[4];
+            if (FMT == FMT_U4_G64) {
+                split3_pair(u.x, u.z, h[0], md[0], lo[0]);
+                split3_pair(v.x, v.z, h[1], md[1], lo[1]);
+                split3_pair(u.y, u.w, h[2], md[2], lo[2]);
+                split3_pair(v.y, v.w, h[3], md[3], lo[3]);
+                // group sum of the activations for the bias term: this
+                // lane's 8 inputs, then the other three blocks of the step
+                float t = ((u.x + u.y) + (u.z + u.w)) + ((v.x + v.y) + (v.z + v.w));
+                t += __shfl_xor(t, 16);
+                t += __shfl_xor(t, 32);
+                xs[j] = kt % GSTEPS == 0 ? t : xs[j] + t;
+            } else {
+                split3_pair(u.x, u.y, h[0], md[0], lo[0]);
+                split3_pair(u.z, u.w, h[1], md[1], lo[1]);
+                split3_pair(v.x, v.y, h[2], md[2], lo[2]);
+                split3_pair(v.z, v.w, h[3], md[3], lo[3]);
+            }
+            bx[j][0] = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+            bx[j][1] = __builtin_bit_cast(bf16x8_t, make_uint4(md[0], md[1], md[2], md[3]));
+            bx[j][2] = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+        }
 #pragma unroll
         for (int pc = 0; pc < 3; ++pc) {
 #pragma unroll
             for (int j = 0; j < TJ; ++j) {
-                const int r = wn + 16 * j + fr;
-                const bf16x8_t bx = __builtin_bit_cast(bf16x8_t, lx[b][pc][r * 4 + swz_chunk(r, fq)]);
 #pragma unroll
                 for (int i = 0; i < TI; ++i) {
                     if (FMT == FMT_I8_ROW)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bx, acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bx[j][pc], acc[i][j], 0, 0, 0);
                     else
-                        gacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bx, gacc[i][j], 0, 0, 0);
+                        gacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bx[j][pc], gacc[i][j], 0, 0, 0);
                 }
             }
         }
@@ -326,9 +367,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
             // close the group: acc += scale[m][g] * (sum of code * x over the
             // group) [+ bias[m][g] * (sum of x over the group), 4-bit]
             const int gb = (kt / GSTEPS) & 1;
-            float xs[TJ];
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) xs[j] = FMT == FMT_U4_G64 ? lxs[gb][wn + 16 * j + fr] : 0.f;
 #pragma unroll
             for (int i = 0; i < TI; ++i) {
                 const float4 s4 = *reinterpret_cast<const float4 *>(&ls[gb][16 * i + 4 * fq]);
@@ -351,9 +389,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
         }
     };
 
-    // pipeline: LDS buffer kt & 1 holds step kt; register set s % D holds
-    // step s from its load (D steps before it is staged) until it is staged
-    // (one step before it is computed)
+    // pipeline: LDS buffer kt & 1 holds the weights of step kt; register set
+    // s % D holds the weights of step s from their load (D steps before they
+    // are staged) until they are staged (one step before they are used), and
+    // the activations of step s from their load (D steps before) until step
+    // s is computed
     constexpr int D = FMT == FMT_I8_ROW   ? QG_GEMM_DEPTH_I8
                       : FMT == FMT_I8_G64 ? QG_GEMM_DEPTH_I8G
                       : FMT == FMT_U4_G64 ? QG_GEMM_DEPTH_U4
@@ -361,24 +401,29 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
     Regs R[D];
 #pragma unroll
     for (int u = 0; u < D; ++u)
-        if (u < nk) load(R[u], u);
+        if (u < nk) {
+            load_w(R[u], u);
+            load_x(R[u], u);
+        }
     stage(R[0], 0, 0);
-    if (D < nk) load(R[0], D);
+    if (D < nk) load_w(R[0], D);
     __syncthreads();
     int kt0 = 0;
-    // steady state: every step stages the next one and loads D ahead
+    // steady state: every step computes, stages the next step's weights and
+    // loads the weights of D + 1 and the activations of D steps ahead
     for (; kt0 + 2 * D < nk; kt0 += D) {
 #pragma unroll
         for (int u = 0; u < D; ++u) {
             const int kt = kt0 + u;
-            compute(kt);
+            compute(kt, R[u]);
+            load_x(R[u], kt + D);
             stage(R[(u + 1) % D], kt + 1, (kt + 1) & 1);
-            load(R[(u + 1) % D], kt + 1 + D);
+            load_w(R[(u + 1) % D], kt + 1 + D);
 #if QG_GEMM_INTERLEAVE
             // issue order: the fragment reads, then each MFMA followed by a
-            // few staging VALU instructions, so that the conversion of the
-            // next step runs while the matrix pipe is busy
-            __builtin_amdgcn_sched_group_barrier(0x100, TI + 3 * TJ, 0);
+            // few VALU instructions, so that the conversion work runs while
+            // the matrix pipe is busy
+            __builtin_amdgcn_sched_group_barrier(0x100, TI, 0);
 #pragma unroll
             for (int i = 0; i < 3 * TI * TJ; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -394,10 +439,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
         for (int u = 0; u < D; ++u) {
             const int kt = kt0 + u;
             if (kt < nk) {
-                compute(kt);
+                compute(kt, R[u]);
+                if (kt + D < nk) load_x(R[u], kt + D);
                 if (kt + 1 < nk) {
                     stage(R[(u + 1) % D], kt + 1, (kt + 1) & 1);
-                    if (kt + 1 + D < nk) load(R[(u + 1) % D], kt + 1 + D);
+                    if (kt + 1 + D < nk) load_w(R[(u + 1) % D], kt + 1 + D);
                 }
                 __syncthreads();
             }

@@ -510,10 +510,10 @@ size_t gemm_workspace(int fmt, int64_t M, int64_t K, int64_t N)
     return 0;
 }
 
-bool gemm_shape_ok(int64_t M, int64_t N)
+bool gemm_shape_ok(int64_t M, int64_t K, int64_t N)
 {
     if (N <= kGemmViaGemv) return true;
-    return ceil_div(M, 64) * ceil_div(N, 64) <= 0x7fffffffLL;   // smallest tile
+    return K <= qg::kGemmMaxK && ceil_div(M, 64) * ceil_div(N, 64) <= 0x7fffffffLL;   // smallest tile
 }
 
 // The largest tile that still gives every compute unit a workgroup
@@ -603,7 +603,7 @@ int wide_argmax_entry(int fmt, const void *codes, const void *scales, const void
 {
     int st = check_weights(fmt, codes, scales, biases, x, M, K);
     if (st != QG_OK) return st;
-    if (N < 1 || N > QG_MAX_ARGMAX_BATCH) return QG_ERR_SHAPE;
+    if (N < 1 || N > QG_MAX_ARGMAX_BATCH || K > qg::kGemmMaxK) return QG_ERR_SHAPE;
     if ((y && !aligned(y, kAlign)) || !aligned(idx, 4)) return QG_ERR_ALIGN;
     const size_t need = wide_argmax_workspace(fmt, M, N);
     if (!ws || ws_bytes < need) return QG_ERR_WORKSPACE;
@@ -639,7 +639,7 @@ int gemm_entry(int fmt, const void *codes, const void *scales, const void *biase
     int st = check_weights(fmt, codes, scales, biases, x, M, K);
     if (st != QG_OK) return st;
     if (!y) return QG_ERR_NULL;
-    if (N < 1 || N > kMaxN || !gemm_shape_ok(M, N)) return QG_ERR_SHAPE;
+    if (N < 1 || N > kMaxN || !gemm_shape_ok(M, K, N)) return QG_ERR_SHAPE;
     if (!aligned(y, kAlign)) return QG_ERR_ALIGN;
     const size_t need = gemm_workspace(fmt, M, K, N);
     if (need > 0) {
@@ -746,13 +746,13 @@ size_t qg_workspace_bytes(int op, int fmt, int64_t M, int64_t K, int64_t rows)
     if (!known_format(fmt)) return 0;
     if (M < 1 || M > kMaxM || K < 1 || K > kMaxK || K % k_unit(fmt) != 0) return 0;
     if (op == QG_OP_GEMV_ARGMAX && rows > QG_MAX_GEMV_BATCH && rows <= QG_MAX_ARGMAX_BATCH)
-        return wide_argmax_workspace(fmt, M, rows);
+        return K <= qg::kGemmMaxK ? wide_argmax_workspace(fmt, M, rows) : 0;
     if (op == QG_OP_GEMV || op == QG_OP_GEMV_ARGMAX) {
         if (rows < 1 || rows > QG_MAX_GEMV_BATCH) return 0;
         return plan_gemv(fmt, M, K, static_cast<int>(rows), op == QG_OP_GEMV_ARGMAX).ws_bytes;
     }
     if (op == QG_OP_GEMM) {
-        if (rows < 1 || rows > kMaxN) return 0;
+        if (rows < 1 || rows > kMaxN || !gemm_shape_ok(M, K, rows)) return 0;
         return gemm_workspace(fmt, M, K, rows);
     }
     return 0;

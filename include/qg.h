@@ -151,7 +151,8 @@ int qgemv(int fmt, const void *codes, const void *scales, const void *biases,
  * prefill projection is a genuine matrix-matrix product; A 27B model on two
  * 4GB Maxwell GPUs, "A packed Q1 prefill kernel with a narrow dispatch
  * window": the weights may be consumed packed.)
- *   X  float32 [N][K];  Y  float32 [N][M] (overwritten).  1 <= N <= 2^31-1.
+ *   X  float32 [N][K];  Y  float32 [N][M] (overwritten).  1 <= N <= 2^31-1;
+ *   above QG_MAX_GEMV_BATCH rows (the matrix-core kernel) K <= 2^21.
  *   All four formats; for QG_U4_G64 the bias term sum_g b[m][g] * (sum of
  *   X[n][k] over group g) is added per group beside the scaled code sums.
  */
@@ -171,7 +172,8 @@ int qgemm(int fmt, const void *codes, const void *scales, const void *biases,
  *           greedy-only head; the maxima still come from the same float32
  *           values a non-NULL call writes).
  *   idx     int32 [batch].
- *   1 <= batch <= QG_MAX_ARGMAX_BATCH; other limits as qgemv. Up to
+ *   1 <= batch <= QG_MAX_ARGMAX_BATCH; other limits as qgemv, and K <= 2^21
+ *   above QG_MAX_GEMV_BATCH rows. Up to
  *   QG_MAX_GEMV_BATCH rows use the matrix-vector kernels; more rows use the
  *   prefill kernels, which keep one (value, index) key per 64- or 128-row
  *   tile and token row in the workspace and reduce them in a second launch

@@ -203,3 +203,16 @@ def test_i8_group64_format_checks():
         q.QG_WS_CONTROL_BYTES
     assert q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_I8_G64, 3584, 1024, 64) >= \
         q.QG_WS_CONTROL_BYTES + 64 * (3584 // 64) * 8
+
+
+def test_prefill_k_limit():
+    """Above 16 token rows the matrix-core kernels take K up to 2^21 (their
+    buffer loads use 32-bit offsets within a tile); the matrix-vector path
+    below that keeps the full range."""
+    K = (1 << 21) + 64
+    assert _err(q.qgemm, q.QG_U4_G64, A, A + (1 << 32), A + (1 << 33), A + (1 << 34),
+                A + (1 << 36), 4, K, 17) == q.QG_ERR_SHAPE
+    assert q.qg_workspace_bytes(q.QG_OP_GEMM, q.QG_U4_G64, 4, K, 17) == 0
+    assert q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_U4_G64, 4, K, 64) == 0
+    assert _err(q.qgemv_argmax, q.QG_U4_G64, A, A + (1 << 32), A + (1 << 33), A + (1 << 34),
+                None, A + (1 << 36), 4, K, 64, ws=A + (1 << 37), ws_bytes=1 << 20) == q.QG_ERR_SHAPE
