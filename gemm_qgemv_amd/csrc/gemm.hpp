@@ -101,13 +101,15 @@ __device__ __forceinline__ uint32_t signpair_to_bf16x2(uint32_t nbits2)
 
 constexpr int GT_K = 32;    // k per step
 constexpr int kGemmThreads = 256;
-// k-steps of loads in flight (register sets), per format, as measured. For
-// the 64-input groups a depth of 2 (one group) puts the group close at the
-// same place of every unrolled pass of the pipeline loop, which is cheaper
-// than deeper prefetch (8-bit group-64 at 3584 x 1024, N = 2048: 99 us at
-// depth 2, 105 us at depth 3).
+// k-steps of loads in flight (register sets), per format, as measured. With
+// every load issued unconditionally two steps cover the latency for the
+// byte formats (8-bit 3584 x 1024, N = 10240: 252 us at depth 2, 266 at 3);
+// for the grouped formats a depth equal to the steps of one group also puts
+// the group close at the same place of every unrolled pass. The 1-bit
+// format keeps 4 (one 128-input group; 514 us at depth 2, 461 at 4 for
+// 17408 x 5120, N = 512).
 #ifndef QG_GEMM_DEPTH_I8
-#define QG_GEMM_DEPTH_I8 3
+#define QG_GEMM_DEPTH_I8 2
 #endif
 #ifndef QG_GEMM_DEPTH_B1
 #define QG_GEMM_DEPTH_B1 4
@@ -119,7 +121,7 @@ constexpr int kGemmThreads = 256;
 #define QG_GEMM_DEPTH_I8G 2
 #endif
 #ifndef QG_GEMM_INTERLEAVE
-#define QG_GEMM_INTERLEAVE 3   // VALU instructions issued after each MFMA
+#define QG_GEMM_INTERLEAVE 5   // VALU instructions issued after each MFMA
 #endif
 
 // Largest K of the matrix-core prefill: the buffer loads below address a
@@ -314,17 +316,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) xs[j] = 0.f;
 
-    auto compute = [&](int kt, const Regs &R) {
-        const int b = kt & 1;
-        bf16x8_t a[TI];
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-            const int r = 16 * i + fr;
-            a[i] = __builtin_bit_cast(bf16x8_t, lw[b][r * 4 + swz_chunk(r, fq)]);
-        }
-        // exact three-piece split of this lane's activations (the 4-bit
-        // operand order k = 0, 2, 4, 6, 1, 3, 5, 7 for the 4-bit format)
-        bf16x8_t bx[TJ][3];
+    // exact three-piece split of this lane's activations of step kt (the
+    // 4-bit operand order k = 0, 2, 4, 6, 1, 3, 5, 7 for the 4-bit format),
+    // and for the 4-bit format the running group sum of the activations
+    auto split = [&](int kt, const Regs &R, bf16x8_t (&bx)[TJ][3]) {
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
             const float4 u = R.x[j][0], v = R.x[j][1];
@@ -334,8 +329,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
                 split3_pair(v.x, v.z, h[1], md[1], lo[1]);
                 split3_pair(u.y, u.w, h[2], md[2], lo[2]);
                 split3_pair(v.y, v.w, h[3], md[3], lo[3]);
-                // group sum of the activations for the bias term: this
-                // lane's 8 inputs, then the other three blocks of the step
+                // this lane's 8 inputs, then the other three blocks of the step
                 float t = ((u.x + u.y) + (u.z + u.w)) + ((v.x + v.y) + (v.z + v.w));
                 t += __shfl_xor(t, 16);
                 t += __shfl_xor(t, 32);
@@ -349,6 +343,18 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
             bx[j][0] = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
             bx[j][1] = __builtin_bit_cast(bf16x8_t, make_uint4(md[0], md[1], md[2], md[3]));
             bx[j][2] = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+        }
+    };
+
+    // the MFMAs of step kt on its weights (LDS buffer kt & 1) and its
+    // activation pieces bx, then the group close
+    auto compute = [&](int kt, const bf16x8_t (&bx)[TJ][3]) {
+        const int b = kt & 1;
+        bf16x8_t a[TI];
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+            const int r = 16 * i + fr;
+            a[i] = __builtin_bit_cast(bf16x8_t, lw[b][r * 4 + swz_chunk(r, fq)]);
         }
 #pragma unroll
         for (int pc = 0; pc < 3; ++pc) {
@@ -390,10 +396,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
     };
 
     // pipeline: LDS buffer kt & 1 holds the weights of step kt; register set
-    // s % D holds the weights of step s from their load (D steps before they
-    // are staged) until they are staged (one step before they are used), and
-    // the activations of step s from their load (D steps before) until step
-    // s is computed
+    // s % D holds the weights and activations of step s from their load (D
+    // steps ahead) until the step before s, when the weights are staged and
+    // the activations split; the split pieces of the step being computed
+    // stay in registers (bx), so a step's MFMAs never wait for its own
+    // VALU work, which runs beside the previous step's MFMAs
     constexpr int D = FMT == FMT_I8_ROW   ? QG_GEMM_DEPTH_I8
                       : FMT == FMT_I8_G64 ? QG_GEMM_DEPTH_I8G
                       : FMT == FMT_U4_G64 ? QG_GEMM_DEPTH_U4
@@ -405,24 +412,36 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
             load_w(R[u], u);
             load_x(R[u], u);
         }
+    bf16x8_t bx[TJ][3];
+    split(0, R[0], bx);
     stage(R[0], 0, 0);
-    if (D < nk) load_w(R[0], D);
+    if (D < nk) {
+        load_x(R[0], D);
+        load_w(R[0], D);
+    }
     __syncthreads();
     int kt0 = 0;
-    // steady state: every step computes, stages the next step's weights and
-    // loads the weights of D + 1 and the activations of D steps ahead
+    // steady state: every step computes, splits and stages the next step
+    // and loads D + 1 steps ahead
     for (; kt0 + 2 * D < nk; kt0 += D) {
 #pragma unroll
         for (int u = 0; u < D; ++u) {
             const int kt = kt0 + u;
-            compute(kt, R[u]);
-            load_x(R[u], kt + D);
-            stage(R[(u + 1) % D], kt + 1, (kt + 1) & 1);
-            load_w(R[(u + 1) % D], kt + 1 + D);
+            Regs &N = R[(u + 1) % D];
+            compute(kt, bx);
+            bf16x8_t bn[TJ][3];
+            split(kt + 1, N, bn);
+            load_x(N, kt + 1 + D);
+            stage(N, kt + 1, (kt + 1) & 1);
+            load_w(N, kt + 1 + D);
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                for (int c = 0; c < 3; ++c) bx[j][c] = bn[j][c];
 #if QG_GEMM_INTERLEAVE
             // issue order: the fragment reads, then each MFMA followed by a
-            // few VALU instructions, so that the conversion work runs while
-            // the matrix pipe is busy
+            // few VALU instructions (the next step's split and staging), so
+            // that they run while the matrix pipe is busy
             __builtin_amdgcn_sched_group_barrier(0x100, TI, 0);
 #pragma unroll
             for (int i = 0; i < 3 * TI * TJ; ++i) {
@@ -439,11 +458,18 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
         for (int u = 0; u < D; ++u) {
             const int kt = kt0 + u;
             if (kt < nk) {
-                compute(kt, R[u]);
-                if (kt + D < nk) load_x(R[u], kt + D);
+                Regs &N = R[(u + 1) % D];
+                compute(kt, bx);
                 if (kt + 1 < nk) {
-                    stage(R[(u + 1) % D], kt + 1, (kt + 1) & 1);
-                    if (kt + 1 + D < nk) load_w(R[(u + 1) % D], kt + 1 + D);
+                    bf16x8_t bn[TJ][3];
+                    split(kt + 1, N, bn);
+                    if (kt + 1 + D < nk) load_x(N, kt + 1 + D);
+                    stage(N, kt + 1, (kt + 1) & 1);
+                    if (kt + 1 + D < nk) load_w(N, kt + 1 + D);
+#pragma unroll
+                    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                        for (int c = 0; c < 3; ++c) bx[j][c] = bn[j][c];
                 }
                 __syncthreads();
             }
