@@ -528,10 +528,14 @@ void gemm_tile(int fmt, int64_t M, int64_t N, int &bm, int &bn)
     // (64 token rows with 128-row tiles would halve the useful MFMA work)
     const bool n128 = N % 128 == 0 || N % 128 > 64;
     if (!n128) return;
-    // 128 x 128 only for the per-row 8-bit format: the grouped formats keep a
-    // second set of accumulators, which would not fit in registers
+    // 128 x 128 only for the per-row 8-bit format (the grouped formats keep a
+    // second set of accumulators, which would not fit in registers), once
+    // every compute unit gets a tile; 64 x 128 only once every compute unit
+    // gets two, since a single workgroup per compute unit leaves one wave
+    // per SIMD, which cannot keep the matrix pipe busy (1024 x 3584, N =
+    // 2048: 99 us on 256 tiles of 64 x 128, 80 us on 512 of 64 x 64)
     if (fmt == QG_I8_ROW && tiles(128, 128) >= kComputeUnits) bm = 128, bn = 128;
-    else if (tiles(64, 128) >= kComputeUnits) bn = 128;
+    else if (tiles(64, 128) >= 2 * kComputeUnits) bn = 128;
 }
 
 // Enqueue the matrix-core prefill kernel; with `keys`, the greedy head's
