@@ -356,6 +356,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
             const int r = 16 * i + fr;
             a[i] = __builtin_bit_cast(bf16x8_t, lw[b][r * 4 + swz_chunk(r, fq)]);
         }
+        // the first MFMA of a group starts its sum from zero (the group's
+        // position is known at compile time in the unrolled pipeline)
+        const bool first = GROUPED && kt % GSTEPS == 0;
+        const floatx4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int pc = 0; pc < 3; ++pc) {
 #pragma unroll
@@ -365,7 +369,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
                     if (FMT == FMT_I8_ROW)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bx[j][pc], acc[i][j], 0, 0, 0);
                     else
-                        gacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bx[j][pc], gacc[i][j], 0, 0, 0);
+                        gacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            a[i], bx[j][pc], first && pc == 0 ? zero : gacc[i][j], 0, 0, 0);
                 }
             }
         }
@@ -389,7 +394,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
                         float a = acc[i][j][r];
                         if (FMT == FMT_U4_G64) a = fmaf(bv[r], xs[j], a);
                         acc[i][j][r] = fmaf(sv[r], gacc[i][j][r], a);
-                        gacc[i][j][r] = 0.f;
                     }
             }
         }
