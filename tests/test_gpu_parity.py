@@ -569,3 +569,67 @@ def test_graph_replay_matches_eager(torch, orc):
         work(s)
         torch.cuda.synchronize()
     assert not ws[:q.QG_WS_CONTROL_BYTES].cpu().numpy().any()
+
+
+def test_graph_replay_counters_and_gather(torch, orc):
+    """The paths that keep counters in the workspace, and the gather, in one
+    HIP graph: the batch-8 matrix-core head (per-workgroup key rows), the
+    64-row greedy head without logits (tile keys and their reduction), the
+    1-bit batch-1 product with its K chunks combined in the kernel (row-tile
+    counters), and qembed of the chosen tokens. Each replay, with eager calls
+    between replays, equals the eager result bit for bit, and the control
+    words are back at zero after each."""
+    say("graph replay: counters and gather")
+    rng = synth.rng_for(302, 0)
+    M, K = 30000, 2048
+    wu = synth.draw_weights(synth.U4_G64, M, K, rng)
+    wb = synth.draw_weights(synth.B1_G128, 5000, 5120, rng)
+    du, db = dev(wu), dev(wb)
+    x8 = torch.from_numpy(synth.draw_x(8, K, rng)).cuda()
+    x64 = torch.from_numpy(synth.draw_x(64, K, rng)).cuda()
+    xb = torch.from_numpy(synth.draw_x(1, 5120, rng)).cuda()
+    logits8 = torch.empty(8 * M, device="cuda")
+    idx8 = torch.empty(8, dtype=torch.int32, device="cuda")
+    idx64 = torch.empty(64, dtype=torch.int32, device="cuda")
+    yb = torch.empty(5000, device="cuda")
+    rows = torch.empty(8 * K, device="cuda")
+    ws8 = tensors.workspace(q.QG_OP_GEMV_ARGMAX, wu.fmt, M, K, 8)
+    ws64 = tensors.workspace(q.QG_OP_GEMV_ARGMAX, wu.fmt, M, K, 64)
+    wsb = tensors.workspace(q.QG_OP_GEMV, wb.fmt, 5000, 5120, 1)
+    assert wsb is not None, "the 1-bit product at this K combines chunks in a workspace"
+    s = torch.cuda.Stream()
+
+    def work(stream):
+        q.qgemv_argmax(wu.fmt, du.codes, du.scales, du.biases, x8, logits8, idx8, M, K, 8, ws8,
+                       stream=stream)
+        q.qgemv_argmax(wu.fmt, du.codes, du.scales, du.biases, x64, None, idx64, M, K, 64, ws64,
+                       stream=stream)
+        q.qgemv(wb.fmt, db.codes, db.scales, None, xb, yb, 5000, 5120, 1, wsb, stream=stream)
+        q.qembed(wu.fmt, du.codes, du.scales, du.biases, idx8, rows, M, K, 8, stream=stream)
+
+    work(s)
+    torch.cuda.synchronize()
+    outs = (logits8, idx8, idx64, yb, rows)
+    want = [t.clone() for t in outs]
+    # the eager results themselves are right
+    ref8, _ = orc.qgemv(wu.fmt, wu.codes, wu.scales, wu.biases, x8.cpu().numpy(), M, K)
+    assert np.array_equal(idx8.cpu().numpy(), orc.argmax(ref8)[0])
+    e = orc.embed(wu.codes, wu.scales, wu.biases, idx8.cpu().numpy(), M, K)
+    assert np.array_equal(rows.cpu().numpy().reshape(8, K).view(np.uint32), e.view(np.uint32))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        work(s)
+    for rep in range(4):
+        for t in (logits8, yb, rows):
+            t.fill_(float("nan"))
+        idx8.fill_(-1)
+        idx64.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, want):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager result"
+        for w in (ws8, ws64, wsb):
+            assert not w[:q.QG_WS_CONTROL_BYTES].cpu().numpy().any(), "control words not back at zero"
+        work(s)
+        torch.cuda.synchronize()
