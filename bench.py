@@ -19,8 +19,8 @@ Reported (one JSON line):
   cpu_baseline   the CPU oracle on the same workload, on this host's cores
 
 Other workloads (--workload): any case name of gemm_qgemv_amd.synth.CASES, or
-a config prefix (c0, c1, c2b1, c2b8, c3, c4gemv, c4gemm), or one of the widened
-rows (u4gemm, head64, head128, embed, i8g, i8ggemm). GEMM workloads report TFLOP/s; the
+a config prefix (c0, c1, c2b1, c2b8, c3, c4gemv, c4gemm), or one of the extensions
+(u4gemm, head64, head128, embed, i8g, i8ggemm). GEMM workloads report TFLOP/s; the
 embedding gather reports the GB/s of its ids, packed rows and float32 rows.
 
 The timed region replays a HIP graph of the steps (captured once) so that the

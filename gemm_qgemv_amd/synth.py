@@ -206,7 +206,7 @@ CASES = [
     Case("c4c_b1_gemm_17408x5120_n512", "gemm", B1_G128, 17408, 5120, 512, 4, 2),
     Case("c4d_b1_gemm_5120x17408_n512", "gemm", B1_G128, 5120, 17408, 512, 4, 3),
 ]
-# Measurement cases of widened rows (not configurations): the 4-bit prefill
+# Measurement cases beyond the configurations: the 4-bit prefill
 # at the 4-bit matvec shapes, with a 2048-token prompt; the greedy head at 64
 # and 128 rows, with logits and without ("greedy": qgemv_argmax, logits NULL);
 # the embedding rows of a 2048-token prompt gathered from the same (tied)
