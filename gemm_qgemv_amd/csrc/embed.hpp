@@ -5,10 +5,10 @@
 // bits) plus the bias, one float32 rounding to nearest even, then a
 // round-trip through IEEE binary16 (nearest even, subnormals and the sign of
 // zero kept). (Pushing the limits of legacy hardware, "Half a billion
-// values, and one negative zero": the decoder kept the separate affine
-// operations and the inherited FP16 round-trip, and moving the lookup to the
-// GPU needed exact denormal, signed-zero and round-to-nearest-even
-// behaviour.) On gfx950 the default floating-point mode already rounds to
+// values, and one negative zero": that decoder multiplies and adds in two
+// steps and passes each value through FP16 on its way to FP32, and the
+// lookup on the GPU had to reproduce denormals, the sign of zero and
+// round-to-nearest-even exactly.) On gfx950 the default floating-point mode already rounds to
 // nearest even and keeps binary16 denormals; this library is built without
 // float32 denormal flushing. The product and the sum stay two operations:
 // the product is exact unless it overflows, and there a fused multiply-add

@@ -166,8 +166,9 @@ int qgemm(int fmt, const void *codes, const void *scales, const void *biases,
  *   idx[n]       = the lowest m whose logits[n][m] is the maximum of row n
  *                  (ties go to the lowest index; -0 equals +0).
  * (Pushing the limits of legacy hardware, "Build the execution path, then
- * share the weights": the head keeps per-tile maxima with their original
- * indices, and greedy selection stays on the device.)
+ * share the weights": for greedy decoding the head only has to report, per
+ * tile of logits, the largest value and where it sits, and the choice of
+ * token is made on the device.)
  *   logits  float32 [batch][M], or NULL: then no logits are written (the
  *           greedy-only head; the maxima still come from the same float32
  *           values a non-NULL call writes).
@@ -177,7 +178,7 @@ int qgemm(int fmt, const void *codes, const void *scales, const void *biases,
  *   QG_MAX_GEMV_BATCH rows use the matrix-vector kernels; more rows use the
  *   prefill kernels, which keep one (value, index) key per 64- or 128-row
  *   tile and token row in the workspace and reduce them in a second launch
- *   (the head's "tile maxima" of the page above). Needs a workspace.
+ *   (the per-tile reduction of the page above). Needs a workspace.
  */
 int qgemv_argmax(int fmt, const void *codes, const void *scales,
                  const void *biases, const float *x, float *logits,
@@ -197,9 +198,10 @@ int qgemv_argmax(int fmt, const void *codes, const void *scales,
  *   nearest-even), and a negative sum too small for binary16 becomes -0,
  *   not +0. A row id outside [0, M) gives a row of quiet NaNs.
  * (Pushing the limits of legacy hardware, "Half a billion values, and one
- * negative zero": the row decoder keeps the separate affine operations and
- * the inherited FP16 round-trip, and the lookup moved to the GPU had to get
- * denormals, signed zero and round-to-nearest-even exactly right; I Built an
+ * negative zero": that row decoder multiplies and adds in two steps and
+ * passes each value through FP16 on its way to FP32, and the lookup on the
+ * GPU had to reproduce denormals, the sign of zero and round-to-nearest-even
+ * exactly; I Built an
  * LLM Inference Engine..., "Cost 1: the embedding lookup still runs on the
  * CPU": the quantized rows are decoded on the device from token ids instead
  * of crossing PCIe.)

@@ -65,9 +65,10 @@
  * + bias, rounded to nearest even), the result rounded to an IEEE binary16
  * (nearest even, subnormals and signed zero kept) and widened back to
  * float32. (Pushing the limits of legacy hardware, "Half a billion values,
- * and one negative zero": the direct decoder kept the separate affine
- * operations and the inherited FP16 round-trip, and the GPU lookup needed
- * exact denormal, signed-zero and round-to-nearest-even behaviour.) Rows of
+ * and one negative zero": that decoder multiplies and adds in two steps and
+ * passes each value through FP16 on its way to FP32, and its GPU version had
+ * to reproduce denormals, the sign of zero and round-to-nearest-even
+ * exactly.) Rows of
  * ids outside [0, M) come out as quiet NaN. The float32 operations are
  * plain C float arithmetic (IEEE binary32 on this host; ISO C mode, so no
  * contraction); the binary16 rounding is written out bit by bit below.
