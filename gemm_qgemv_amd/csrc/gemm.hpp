@@ -11,7 +11,7 @@
 // and 4-bit: 64 k, 1-bit: 128 k) scales are applied in float32 outside the
 // MFMA.
 // (MiniCPM-V-4.6 on a Tesla C2075, academ.us 2607.14568, section 3.1:
-// prefill projections are genuine matrix-matrix products; this kernel keeps
+// the prompt's projections contract whole matrices, not vectors; this kernel keeps
 // the weights packed instead of dequantizing them to a float scratch first.)
 //
 // Tiling. A workgroup of 4 waves computes a BM (m) x BN (n) tile of Y

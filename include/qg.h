@@ -27,8 +27,8 @@
  *   QG_I8_G64   codes  int8  [M][K]      two's complement, any value
  *               scales fp32  [M][K/64]   w = scales[m][k/64] * q
  *               biases must be NULL.  K must be a multiple of 64.
- *     (MiniCPM-V-4.6 on a Tesla C2075, section 2.3: one FP32 scale per
- *     group of 64 symmetric 8-bit weights, the format that backbone ships.)
+ *     (MiniCPM-V-4.6 on a Tesla C2075, section 2.3: symmetric 8-bit codes,
+ *     each run of 64 sharing an FP32 factor, as that backbone ships them.)
  *
  *   QG_U4_G64   codes  uint8 [M][K/2]    byte j of a row: k=2j in bits 0..3,
  *                                        k=2j+1 in bits 4..7, q in 0..15
@@ -148,7 +148,7 @@ int qgemv(int fmt, const void *codes, const void *scales, const void *biases,
  * qgemm -- prefill form: the same product over N token rows.
  *   Y[n][m] = sum_k w[m][k] * X[n][k],  0 <= n < N.
  * (MiniCPM-V-4.6 on a Tesla C2075, section 3.1 "Prefill projections": the
- * prefill projection is a genuine matrix-matrix product; A 27B model on two
+ * prompt's projections contract whole matrices, not vectors; A 27B model on two
  * 4GB Maxwell GPUs, "A packed Q1 prefill kernel with a narrow dispatch
  * window": the weights may be consumed packed.)
  *   X  float32 [N][K];  Y  float32 [N][M] (overwritten).  1 <= N <= 2^31-1;

@@ -48,8 +48,8 @@
  *  4  INT8 symmetric, group of 64 along k.  codes int8 [M][K],
  *     scales fp32 [M][K/64].  w = scale[m][k/64] * q, q two's complement,
  *     no clamping.  (MiniCPM-V-4.6 on a Tesla C2075, section 2.3
- *     "Quantization and residency": symmetric 8-bit weights with one FP32
- *     scale per group of 64.)
+ *     "Quantization and residency": symmetric 8-bit weights, each run of 64
+ *     sharing an FP32 factor.)
  *
  * bf16 is the upper half of an IEEE binary32; fp16 is IEEE binary16
  * (subnormals included). Both are decoded here bit by bit, on purpose
