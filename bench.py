@@ -20,7 +20,7 @@ Reported (one JSON line):
 
 Other workloads (--workload): any case name of gemm_qgemv_amd.synth.CASES, or
 a config prefix (c0, c1, c2b1, c2b8, c3, c4gemv, c4gemm), or one of the extensions
-(u4gemm, head64, head128, embed, i8g, i8ggemm). GEMM workloads report TFLOP/s; the
+(u4gemm, head16, head64, head128, embed, i8g, i8ggemm). GEMM workloads report TFLOP/s; the
 embedding gather reports the GB/s of its ids, packed rows and float32 rows.
 
 The timed region replays a HIP graph of the steps (captured once) so that the
@@ -62,6 +62,7 @@ WORKLOADS = {
     "head64": ["n1a_u4_head_151936x2048_b64", "n1b_u4_head_151936x2048_b64_nologits"],
     "head128": ["n1c_u4_head_151936x2048_b128", "n1d_u4_head_151936x2048_b128_nologits"],
     "embed": ["n3_u4_embed_151936x2048_t2048"],
+    "head16": ["n4_u4_head_151936x2048_b16"],
     "i8g": ["n2c_i8g_gemv_3584x1024", "n2d_i8g_gemv_1024x3584"],
     "i8ggemm": ["n2e_i8g_gemm_3584x1024_n2048", "n2f_i8g_gemm_1024x3584_n2048"],
 }

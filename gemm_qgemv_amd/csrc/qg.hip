@@ -159,6 +159,7 @@ constexpr int64_t kB1LongResident = 3;   // workgroups per compute unit at the l
 
 struct GemvPlan {
     bool mfma;           // small-batch 4-bit kernel on the matrix cores
+    int passes;          // small-batch kernel: launches of up to 8 activation rows each
     bool lut;            // batch-1 1-bit kernel (table lookup, lanes along rows)
     bool fused;          // split-K combined inside the kernel (per-tile counters);
                          // small-batch kernel: outputs staged in LDS
@@ -219,12 +220,16 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
         pl.ws_bytes = (off > kCtlBytes || argmax) ? off : 0;
         return pl;
     }
-    if (fmt == QG_U4_G64 && nb >= 2 && nb <= 8 && K % (64 * qg::kMfmaChunk) == 0 &&
+    if (fmt == QG_U4_G64 && nb >= 2 && K % (64 * qg::kMfmaChunk) == 0 &&
         K <= static_cast<int64_t>(qg::kStageItems) * qg::kMfmaThreads &&
         static_cast<int64_t>(qg::gemv_mfma_lds_bytes(K)) + kLdsStaticReserve <= kLdsMax) {
-        // 2..8 rows, 4-bit: matrix cores, one workgroup of 8 waves per
-        // compute unit, at least one 16-row tile per wave
+        // 2..16 rows, 4-bit: matrix cores, one workgroup of 8 waves per
+        // compute unit, at least one 16-row tile per wave; a launch takes up
+        // to 8 activation rows (9..16 rows: two launches, each reading the
+        // weights once, which is far cheaper than the vector-ALU kernel at
+        // 16 rows: 151936 x 2048 at 16 rows took 761 us there)
         pl.mfma = true;
+        pl.passes = static_cast<int>(ceil_div(nb, 8));
         const int64_t ntiles = ceil_div(M, 16);
         pl.grid_x = std::min<int64_t>(kComputeUnits, ceil_div(ntiles, qg::kMfmaWaves));
         pl.lds_bytes = qg::gemv_mfma_lds_bytes(K);
@@ -366,7 +371,6 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         q.idx = idx;
         q.M = M;
         q.K = K;
-        q.nb = nb;
         q.stage_out = pl.fused;
         // dynamic LDS up to the plan's limit (the kernel's few static bytes
         // come on top, within the compute unit's 160 KiB)
@@ -377,8 +381,17 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
             return true;
         }();
         (void)lds_set;
-        hipLaunchKernelGGL(qg::gemv_mfma_u4_kernel, dim3(static_cast<unsigned>(pl.grid_x)),
-                           dim3(64 * qg::kMfmaWaves), pl.lds_bytes, s, q);
+        // rows 8 h .. 8 h + 7 in pass h; the passes share the workspace in
+        // stream order (each leaves the control words at zero)
+        for (int h = 0; h < pl.passes; ++h) {
+            qg::GemvMfmaParams qh = q;
+            qh.x = x + static_cast<int64_t>(8) * h * K;
+            qh.y = y ? y + static_cast<int64_t>(8) * h * M : nullptr;
+            qh.idx = idx ? idx + 8 * h : nullptr;
+            qh.nb = std::min(8, nb - 8 * h);
+            hipLaunchKernelGGL(qg::gemv_mfma_u4_kernel, dim3(static_cast<unsigned>(pl.grid_x)),
+                               dim3(64 * qg::kMfmaWaves), pl.lds_bytes, s, qh);
+        }
         return;
     }
     if (pl.one) {

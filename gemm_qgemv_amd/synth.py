@@ -210,8 +210,9 @@ CASES = [
 # at the 4-bit matvec shapes, with a 2048-token prompt; the greedy head at 64
 # and 128 rows, with logits and without ("greedy": qgemv_argmax, logits NULL);
 # the embedding rows of a 2048-token prompt gathered from the same (tied)
-# head matrix; the 8-bit format with one scale per 64 inputs at the 8-bit
-# projection shapes, batch 1 and a 2048-token prompt.
+# head matrix; the greedy head at the largest matrix-vector batch (16); the
+# 8-bit format with one scale per 64 inputs at the 8-bit projection shapes,
+# batch 1 and a 2048-token prompt.
 NEXT_CASES = [
     Case("n2a_u4_gemm_6144x2048_n2048", "gemm", U4_G64, 6144, 2048, 2048, 5, 0),
     Case("n2b_u4_gemm_2048x6144_n2048", "gemm", U4_G64, 2048, 6144, 2048, 5, 1),
@@ -220,6 +221,7 @@ NEXT_CASES = [
     Case("n1c_u4_head_151936x2048_b128", "gemv_argmax", U4_G64, 151936, 2048, 128, 2, 0, x_variant=7),
     Case("n1d_u4_head_151936x2048_b128_nologits", "greedy", U4_G64, 151936, 2048, 128, 2, 0, x_variant=7),
     Case("n3_u4_embed_151936x2048_t2048", "embed", U4_G64, 151936, 2048, 2048, 2, 0, x_variant=8),
+    Case("n4_u4_head_151936x2048_b16", "gemv_argmax", U4_G64, 151936, 2048, 16, 2, 0, x_variant=9),
     Case("n2c_i8g_gemv_3584x1024", "gemv", I8_G64, 3584, 1024, 1, 6, 0),
     Case("n2d_i8g_gemv_1024x3584", "gemv", I8_G64, 1024, 3584, 1, 6, 1),
     Case("n2e_i8g_gemm_3584x1024_n2048", "gemm", I8_G64, 3584, 1024, 2048, 6, 2),

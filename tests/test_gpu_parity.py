@@ -319,6 +319,7 @@ def test_zero_codes_give_bias_times_sum(torch, orc):
 MFMA_SHAPES = [
     (16, 512, 8), (17, 1024, 5), (300, 1536, 2), (40007, 512, 3), (70001, 2048, 8),
     (5000, 3072, 2), (9001, 3072, 7), (1000, 3584, 4), (2049, 2048, 9),
+    (70001, 2048, 16), (3000, 3072, 12), (40007, 512, 10),
 ]
 
 
@@ -401,6 +402,7 @@ def gpu_greedy(torch, w, x, logits=True):
     (synth.U4_G64, 40007, 512, 3), (synth.I8_ROW, 777, 1040, 5), (synth.B1_G128, 1000, 6144, 9),
     (synth.U4_G64, 30001, 2048, 64), (synth.I8_ROW, 9000, 1024, 100), (synth.B1_G128, 5000, 1280, 17),
     (synth.U4_G64, 20000, 2048, 128), (synth.U4_G64, 4099, 1024, 256),
+    (synth.U4_G64, 30001, 2048, 16), (synth.U4_G64, 9000, 1024, 11),
 ])
 def test_greedy_head_with_and_without_logits(torch, orc, fmt, M, K, N):
     say(f"greedy fmt={fmt} M={M} K={K} N={N}")
