@@ -155,6 +155,7 @@ static_assert(sizeof(qg::GreedyCtl) <= qg::kCtlTileOffset, "greedy control words
 // 1024: 10.2 against 13.1 us).
 constexpr int kB1Chunk = 1024;
 constexpr int kB1ChunkLong = 2048;
+constexpr int kB1ChunkWide = 512;        // chunk of the 8-row tables (64 KiB of LDS)
 constexpr int64_t kB1LongResident = 3;   // workgroups per compute unit at the long chunk
 
 struct GemvPlan {
@@ -198,15 +199,24 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
         }
         return pl;
     }
-    if (nb == 1 && fmt == QG_B1_G128) {
-        // batch 1, 1-bit: 64 rows x 1024 (or 2048) inputs per workgroup,
-        // partial sums of the K chunks combined in order
+    if (fmt == QG_B1_G128) {
+        // 1-bit, 1..16 activation rows: 64 weight rows x one K chunk per
+        // workgroup, a lookup table per activation row, partial sums of the
+        // K chunks combined in order. Launches take up to 8 activation rows
+        // (tables for 1, 2, 4 or 8 rows); one chunk size for all launches of
+        // a call: 512 inputs when a launch has 8-row tables (64 KiB of LDS),
+        // else 1024, or 2048 for one row and long K.
         pl.lut = true;
-        pl.B = 1;
+        pl.B = nb == 1 ? 1 : nb <= 2 ? 2 : nb <= 4 ? 4 : 8;   // tables of the widest launch
+        pl.passes = static_cast<int>(ceil_div(nb, 8));
         pl.grid_x = ceil_div(M, qg::kB1Rows);
-        const bool long_chunk = K >= 2 * kB1ChunkLong &&
-                                pl.grid_x * ceil_div(K, kB1ChunkLong) <= kB1LongResident * kComputeUnits;
-        pl.kc = long_chunk ? kB1ChunkLong : kB1Chunk;
+        if (pl.B == 1) {
+            const bool long_chunk = K >= 2 * kB1ChunkLong &&
+                                    pl.grid_x * ceil_div(K, kB1ChunkLong) <= kB1LongResident * kComputeUnits;
+            pl.kc = long_chunk ? kB1ChunkLong : kB1Chunk;
+        } else {
+            pl.kc = pl.B == 8 ? kB1ChunkWide : kB1Chunk;
+        }
         pl.nsplit = static_cast<int>(ceil_div(K, pl.kc));
         pl.fused = pl.nsplit > 1 && pl.grid_x <= qg::kCtlTileCounters;
         size_t off = kCtlBytes;
@@ -214,7 +224,7 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
             pl.comb_rows_per_wg = round_up(ceil_div(M, 1024), 256);
             pl.comb_grid = ceil_div(M, pl.comb_rows_per_wg);
             pl.part_off = off;
-            off = align256(off + static_cast<size_t>(pl.nsplit) * M * 4);
+            off = align256(off + static_cast<size_t>(pl.nsplit) * std::min(nb, 8) * M * 4);
         }
         if (argmax) pl.nkeys = static_cast<int>(pl.nsplit > 1 && !pl.fused ? pl.comb_grid : pl.grid_x);
         pl.ws_bytes = (off > kCtlBytes || argmax) ? off : 0;
@@ -412,37 +422,54 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         return;
     }
     if (pl.lut) {
-        qg::B1LutParams q{};
-        q.codes = static_cast<const uint8_t *>(codes);
-        q.scales = static_cast<const uint16_t *>(scales);
-        q.x = x;
-        q.y = y;
-        q.part = pl.nsplit > 1 ? reinterpret_cast<float *>(static_cast<char *>(ws) + pl.part_off) : nullptr;
-        q.ctl = static_cast<qg::GreedyCtl *>(ws);
-        q.idx = (pl.nsplit == 1 || pl.fused) ? idx : nullptr;
-        q.M = M;
-        q.K = K;
-        q.nsplit = pl.nsplit;
-        q.fused = pl.fused;
-        const dim3 grid(static_cast<unsigned>(pl.grid_x), static_cast<unsigned>(pl.nsplit));
-        if (pl.kc == kB1ChunkLong)
-            hipLaunchKernelGGL(qg::gemv_b1_lut_kernel<kB1ChunkLong>, grid, dim3(256), 0, s, q);
-        else
-            hipLaunchKernelGGL(qg::gemv_b1_lut_kernel<kB1Chunk>, grid, dim3(256), 0, s, q);
-        if (pl.nsplit > 1 && !pl.fused) {
-            GemvParams c{};
-            c.y = y;
-            c.part = q.part;
-            c.ctl = idx ? static_cast<qg::GreedyCtl *>(ws) : nullptr;
-            c.idx = idx;
-            c.M = M;
-            c.K = K;
-            c.rows_per_wg = pl.comb_rows_per_wg;
-            c.nb = 1;
-            c.nsplit = pl.nsplit;
-            c.nkeys = pl.nkeys;
-            hipLaunchKernelGGL(qg::gemv_combine_kernel, dim3(static_cast<unsigned>(pl.comb_grid)),
-                               dim3(kThreads), 0, s, c);
+        // activation rows 8 h .. 8 h + 7 in pass h; the passes share the
+        // workspace in stream order (each leaves the control words at zero)
+        for (int h = 0; h < pl.passes; ++h) {
+            const int rows = std::min(8, nb - 8 * h);
+            float *yh = y ? y + static_cast<int64_t>(8) * h * M : nullptr;
+            int32_t *ih = idx ? idx + 8 * h : nullptr;
+            qg::B1LutParams q{};
+            q.codes = static_cast<const uint8_t *>(codes);
+            q.scales = static_cast<const uint16_t *>(scales);
+            q.x = x + static_cast<int64_t>(8) * h * K;
+            q.y = yh;
+            q.part = pl.nsplit > 1 ? reinterpret_cast<float *>(static_cast<char *>(ws) + pl.part_off) : nullptr;
+            q.ctl = static_cast<qg::GreedyCtl *>(ws);
+            q.idx = (pl.nsplit == 1 || pl.fused) ? ih : nullptr;
+            q.M = M;
+            q.K = K;
+            q.nb = rows;
+            q.nsplit = pl.nsplit;
+            q.fused = pl.fused;
+            const dim3 grid(static_cast<unsigned>(pl.grid_x), static_cast<unsigned>(pl.nsplit));
+            const int tb = rows == 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : 8;   // this launch's tables
+            if (pl.kc == kB1ChunkWide) {
+                if (tb == 8) hipLaunchKernelGGL((qg::gemv_b1_lut_kernel<kB1ChunkWide, 8>), grid, dim3(256), 0, s, q);
+                else if (tb == 4) hipLaunchKernelGGL((qg::gemv_b1_lut_kernel<kB1ChunkWide, 4>), grid, dim3(256), 0, s, q);
+                else if (tb == 2) hipLaunchKernelGGL((qg::gemv_b1_lut_kernel<kB1ChunkWide, 2>), grid, dim3(256), 0, s, q);
+                else hipLaunchKernelGGL((qg::gemv_b1_lut_kernel<kB1ChunkWide, 1>), grid, dim3(256), 0, s, q);
+            } else if (pl.kc == kB1ChunkLong) {
+                hipLaunchKernelGGL((qg::gemv_b1_lut_kernel<kB1ChunkLong, 1>), grid, dim3(256), 0, s, q);
+            } else {
+                if (tb == 4) hipLaunchKernelGGL((qg::gemv_b1_lut_kernel<kB1Chunk, 4>), grid, dim3(256), 0, s, q);
+                else if (tb == 2) hipLaunchKernelGGL((qg::gemv_b1_lut_kernel<kB1Chunk, 2>), grid, dim3(256), 0, s, q);
+                else hipLaunchKernelGGL((qg::gemv_b1_lut_kernel<kB1Chunk, 1>), grid, dim3(256), 0, s, q);
+            }
+            if (pl.nsplit > 1 && !pl.fused) {
+                GemvParams c{};
+                c.y = yh;
+                c.part = q.part;
+                c.ctl = idx ? static_cast<qg::GreedyCtl *>(ws) : nullptr;
+                c.idx = ih;
+                c.M = M;
+                c.K = K;
+                c.rows_per_wg = pl.comb_rows_per_wg;
+                c.nb = rows;
+                c.nsplit = pl.nsplit;
+                c.nkeys = pl.nkeys;
+                hipLaunchKernelGGL(qg::gemv_combine_kernel, dim3(static_cast<unsigned>(pl.comb_grid)),
+                                   dim3(kThreads), 0, s, c);
+            }
         }
         return;
     }

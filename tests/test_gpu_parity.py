@@ -244,6 +244,8 @@ SMALL = [
     (synth.U4_G64, 129, 6144, 5), (synth.U4_G64, 64, 8192, 16), (synth.U4_G64, 31, 18048, 7),
     (synth.B1_G128, 1, 128, 1), (synth.B1_G128, 129, 5120, 1), (synth.B1_G128, 1000, 1152, 2),
     (synth.B1_G128, 63, 17408, 1), (synth.B1_G128, 33, 2048, 16), (synth.B1_G128, 8, 640, 9),
+    (synth.B1_G128, 3000, 5120, 5), (synth.B1_G128, 700, 17408, 12), (synth.B1_G128, 129, 1536, 3),
+    (synth.B1_G128, 65, 4096, 7),
     (synth.I8_G64, 1, 64, 1), (synth.I8_G64, 127, 1088, 1), (synth.I8_G64, 1000, 1024, 3),
     (synth.I8_G64, 129, 16384, 1), (synth.I8_G64, 45, 20032, 2), (synth.I8_G64, 64, 4096, 16),
     (synth.I8_G64, 3584, 1024, 1), (synth.I8_G64, 1024, 3584, 1),
