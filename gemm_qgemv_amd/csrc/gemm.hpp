@@ -48,8 +48,10 @@ struct GemmParams {
     const float *x;   // [N][K]
     float *y;         // [N][M], or nullptr (greedy head without logits)
     unsigned long long *keys;  // greedy head: [N][tiles_m] tile keys, or nullptr
+    float *part;      // split K: [nsplit][N][M] partial products (y and keys unused)
     int64_t M, K, N;
     int tiles_m, tiles_n;
+    int kt_split;     // 32-input steps per split of K (a multiple of 4), or 0: no split
 };
 
 // 8 nibbles of one dword (8 consecutive inputs, even k in the low nibbles)
@@ -209,7 +211,12 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
         xoff[j] = static_cast<uint32_t>(((wn + 16 * j + fr) * p.K + 8 * fq) * 4);
-    const int nk = static_cast<int>((p.K + GT_K - 1) / GT_K);   // K is a multiple of 16
+    // steps of this workgroup: all of K, or split blockIdx.y of it (kt
+    // counts local steps below; loads add ktb; ktb is a multiple of every
+    // group's step count, so group boundaries stay where they are)
+    const int nk_all = static_cast<int>((p.K + GT_K - 1) / GT_K);   // K is a multiple of 16
+    const int ktb = p.kt_split > 0 ? static_cast<int>(blockIdx.y) * p.kt_split : 0;
+    const int nk = p.kt_split > 0 ? min(p.kt_split, nk_all - ktb) : nk_all;
     const int64_t groups = p.K / (32 * GSTEPS);
     constexpr int SBYTES = FMT == FMT_I8_G64 ? 4 : 2;   // bytes per group coefficient
     const auto sbuf = buffer_rsrc(static_cast<const uint8_t *>(p.scales) + m0 * groups * SBYTES,
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
     // buffer range checks), so the compiler can count the loads in flight
     // exactly and waits only for the step it needs.
     auto load_w = [&](Regs &R, int kt) {
-        const int64_t k = static_cast<int64_t>(kt) * GT_K + 16 * sh;
+        const int64_t k = static_cast<int64_t>(kt + ktb) * GT_K + 16 * sh;
         constexpr int KSHIFT = I8 ? 0 : FMT == FMT_U4_G64 ? 1 : 3;   // input index -> byte in the row
         const uint32_t off = in_range_or_out(woff + static_cast<uint32_t>(k >> KSHIFT), k, p.K);
         if (I8) {
@@ -242,20 +249,20 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
             R.w.x = __builtin_amdgcn_raw_buffer_load_b16(wbuf, off, 0, 0);
         }
         if (GROUPED && kt % GSTEPS == 0) {
-            const uint32_t o = soff + static_cast<uint32_t>((kt / GSTEPS) * SBYTES);
+            const uint32_t o = soff + static_cast<uint32_t>(((kt + ktb) / GSTEPS) * SBYTES);
             if (FMT == FMT_I8_G64) {
                 R.s = __builtin_amdgcn_raw_buffer_load_b32(sbuf, o, 0, 0);
             } else {
                 R.s = __builtin_amdgcn_raw_buffer_load_b16(sbuf, o, 0, 0);
                 if (FMT == FMT_U4_G64)
                     R.b = __builtin_amdgcn_raw_buffer_load_b16(
-                        bbuf, boff + static_cast<uint32_t>((kt / GSTEPS) * 2), 0, 0);
+                        bbuf, boff + static_cast<uint32_t>(((kt + ktb) / GSTEPS) * 2), 0, 0);
             }
         }
     };
 
     auto load_x = [&](Regs &R, int kt) {
-        const int64_t k = static_cast<int64_t>(kt) * GT_K;
+        const int64_t k = static_cast<int64_t>(kt + ktb) * GT_K;
         // K is a multiple of 16: a block of 8 inputs is all in or all out
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
@@ -509,8 +516,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
                         best[j] = k > best[j] ? k : best[j];
                     }
             }
-            if (p.y == nullptr) continue;
-            float *dst = p.y + n * p.M + mb;
+            float *out = p.kt_split > 0 ? p.part + static_cast<int64_t>(blockIdx.y) * p.N * p.M : p.y;
+            if (out == nullptr) continue;
+            float *dst = out + n * p.M + mb;
             if (vec && mb + 3 < p.M) {
                 *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
             } else {
@@ -532,6 +540,33 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
             k = o > k ? o : k;
             const int64_t n = n0 + wn + 16 * j + fr;
             if (fq == 0 && n < p.N) p.keys[n * p.tiles_m + tm] = k;
+        }
+    }
+}
+
+// Split K: y[n][m] = sum over splits s of part[s][n][m], added in split
+// order (one thread per 4 outputs; M a multiple of 4 takes 16-byte accesses).
+__global__ __launch_bounds__(256) void gemm_splitk_combine_kernel(const float *part, float *y,
+                                                                  int64_t M, int64_t N, int nsplit)
+{
+    const int64_t total = M * N;
+    const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+    if (i >= total) return;
+    if ((M & 3) == 0) {
+        float4 a = *reinterpret_cast<const float4 *>(part + i);
+        for (int s = 1; s < nsplit; ++s) {
+            const float4 b = *reinterpret_cast<const float4 *>(part + s * total + i);
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+        }
+        *reinterpret_cast<float4 *>(y + i) = a;
+    } else {
+        for (int64_t e = i; e < min(i + 4, total); ++e) {
+            float a = part[e];
+            for (int s = 1; s < nsplit; ++s) a += part[s * total + e];
+            y[e] = a;
         }
     }
 }

@@ -544,10 +544,37 @@ int gemv_entry(int fmt, const void *codes, const void *scales, const void *biase
 
 constexpr int kGemmViaGemv = 16;
 
+void gemm_tile(int fmt, int64_t M, int64_t N, int &bm, int &bn);
+
+// Split of K for prefill grids too small for the chip: with fewer tiles than
+// compute units, each tile's K range is cut into nsplit pieces of kt_split
+// steps (a multiple of 4, so that group boundaries do not move) to give
+// about two workgroups per compute unit; the partial products go to the
+// workspace and a second launch adds them in split order. kt_split = 0: no
+// split.
+void gemm_split(int fmt, int64_t M, int64_t K, int64_t N, int &kt_split, int &nsplit)
+{
+    kt_split = 0;
+    nsplit = 1;
+    int bm, bn;
+    gemm_tile(fmt, M, N, bm, bn);
+    const int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
+    const int64_t nk = ceil_div(K, 32);
+    if (tiles >= kComputeUnits || nk < 8) return;
+    const int64_t want = std::min(ceil_div(2 * kComputeUnits, tiles), nk / 4);
+    if (want < 2) return;
+    kt_split = static_cast<int>(round_up(ceil_div(nk, want), 4));
+    nsplit = static_cast<int>(ceil_div(nk, kt_split));
+    if (nsplit < 2) kt_split = 0, nsplit = 1;
+}
+
 size_t gemm_workspace(int fmt, int64_t M, int64_t K, int64_t N)
 {
     if (N <= kGemmViaGemv) return plan_gemv(fmt, M, K, static_cast<int>(N), false).ws_bytes;
-    return 0;
+    int kt_split, nsplit;
+    gemm_split(fmt, M, K, N, kt_split, nsplit);
+    // partial products after the control words, which every call leaves zero
+    return nsplit > 1 ? align256(kCtlBytes + static_cast<size_t>(nsplit) * N * M * 4) : 0;
 }
 
 bool gemm_shape_ok(int64_t M, int64_t K, int64_t N)
@@ -582,9 +609,11 @@ void gemm_tile(int fmt, int64_t M, int64_t N, int &bm, int &bn)
 // tile keys [N][tiles_m] as well (y may then be nullptr).
 void launch_gemm(int fmt, const void *codes, const void *scales, const void *biases,
                  const float *x, float *y, unsigned long long *keys, int64_t M, int64_t K,
-                 int64_t N, hipStream_t s)
+                 int64_t N, hipStream_t s, float *part = nullptr, int kt_split = 0, int nsplit = 1)
 {
     qg::GemmParams p{};
+    p.part = part;
+    p.kt_split = kt_split;
     p.codes = static_cast<const uint8_t *>(codes);
     p.scales = scales;
     p.biases = static_cast<const uint16_t *>(biases);
@@ -598,7 +627,7 @@ void launch_gemm(int fmt, const void *codes, const void *scales, const void *bia
     gemm_tile(fmt, M, N, bm, bn);
     p.tiles_m = static_cast<int>(ceil_div(M, bm));
     p.tiles_n = static_cast<int>(ceil_div(N, bn));
-    const dim3 grid(static_cast<unsigned>(int64_t(p.tiles_m) * p.tiles_n));
+    const dim3 grid(static_cast<unsigned>(int64_t(p.tiles_m) * p.tiles_n), static_cast<unsigned>(nsplit));
     const dim3 block(qg::kGemmThreads);
     if (fmt == QG_I8_ROW) {
         if (bm == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_ROW, 128, 128>), grid, block, 0, s, p);
@@ -625,7 +654,17 @@ void run_gemm(int fmt, const void *codes, const void *scales, const void *biases
         run_gemv(fmt, pl, codes, scales, biases, x, y, nullptr, M, K, nb, ws, s);
         return;
     }
-    launch_gemm(fmt, codes, scales, biases, x, y, nullptr, M, K, N, s);
+    int kt_split, nsplit;
+    gemm_split(fmt, M, K, N, kt_split, nsplit);
+    if (nsplit == 1) {
+        launch_gemm(fmt, codes, scales, biases, x, y, nullptr, M, K, N, s);
+        return;
+    }
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + kCtlBytes);
+    launch_gemm(fmt, codes, scales, biases, x, nullptr, nullptr, M, K, N, s, part, kt_split, nsplit);
+    const int64_t quads = ceil_div(M * N, 4);
+    hipLaunchKernelGGL(qg::gemm_splitk_combine_kernel, dim3(static_cast<unsigned>(ceil_div(quads, 256))),
+                       dim3(256), 0, s, part, y, M, N, nsplit);
 }
 
 // ---------------------------------------------------------------------------

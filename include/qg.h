@@ -155,6 +155,12 @@ int qgemv(int fmt, const void *codes, const void *scales, const void *biases,
  *   above QG_MAX_GEMV_BATCH rows (the matrix-core kernel) K <= 2^21.
  *   All four formats; for QG_U4_G64 the bias term sum_g b[m][g] * (sum of
  *   X[n][k] over group g) is added per group beside the scaled code sums.
+ *   Needs a workspace when qg_workspace_bytes(QG_OP_GEMM, ...) is nonzero:
+ *   up to QG_MAX_GEMV_BATCH rows as qgemv, and above that whenever the
+ *   output has fewer tiles than the chip has compute units, since K is then
+ *   cut into pieces whose float32 partial products are added in a fixed
+ *   order by a second launch (the result does not depend on the stream or
+ *   the schedule).
  */
 int qgemm(int fmt, const void *codes, const void *scales, const void *biases,
           const float *x, float *y, int64_t M, int64_t K, int64_t N,

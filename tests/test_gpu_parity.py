@@ -505,15 +505,21 @@ def test_config_gemm_sampled(torch, orc, case):
 
 def test_shared_workspace_sequence(torch, orc):
     """One zero-filled workspace (sized for the largest call) serves a
-    sequence of greedy-head calls of different shapes and batches; the
-    control words return to zero after each."""
+    sequence of greedy-head calls of different shapes and batches and
+    prefill calls that split K (their partial products live after the
+    control words); the control words return to zero after each."""
     say("shared workspace")
-    shapes = [(synth.U4_G64, 5000, 2048, 1), (synth.U4_G64, 3000, 1024, 8),
-              (synth.I8_ROW, 7000, 1024, 1), (synth.B1_G128, 2000, 1280, 3),
-              (synth.U4_G64, 5000, 2048, 1)]
-    need = max(q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, f, M, K, n) for f, M, K, n in shapes)
+    calls = [(q.QG_OP_GEMV_ARGMAX, synth.U4_G64, 5000, 2048, 1),
+             (q.QG_OP_GEMV_ARGMAX, synth.U4_G64, 3000, 1024, 8),
+             (q.QG_OP_GEMM, synth.I8_ROW, 1024, 3584, 40),
+             (q.QG_OP_GEMV_ARGMAX, synth.I8_ROW, 7000, 1024, 1),
+             (q.QG_OP_GEMV_ARGMAX, synth.B1_G128, 2000, 1280, 3),
+             (q.QG_OP_GEMM, synth.U4_G64, 500, 2048, 100),
+             (q.QG_OP_GEMV_ARGMAX, synth.U4_G64, 5000, 2048, 1)]
+    assert q.qg_workspace_bytes(q.QG_OP_GEMM, synth.I8_ROW, 1024, 3584, 40) > q.QG_WS_CONTROL_BYTES
+    need = max(q.qg_workspace_bytes(op, f, M, K, n) for op, f, M, K, n in calls)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
-    for i, (fmt, M, K, n) in enumerate(shapes):
+    for i, (op, fmt, M, K, n) in enumerate(calls):
         rng = synth.rng_for(300, i)
         w = synth.draw_weights(fmt, M, K, rng)
         x = synth.draw_x(n, K, rng)
@@ -521,12 +527,16 @@ def test_shared_workspace_sequence(torch, orc):
         xd = torch.from_numpy(x).cuda()
         y = torch.empty(n * M, device="cuda")
         idx = torch.empty(n, dtype=torch.int32, device="cuda")
-        q.qgemv_argmax(fmt, wd.codes, wd.scales, wd.biases, xd, y, idx, M, K, n, ws)
+        if op == q.QG_OP_GEMM:
+            q.qgemm(fmt, wd.codes, wd.scales, wd.biases, xd, y, M, K, n, ws)
+        else:
+            q.qgemv_argmax(fmt, wd.codes, wd.scales, wd.biases, xd, y, idx, M, K, n, ws)
         torch.cuda.synchronize()
         ref, a = orc.qgemv(fmt, w.codes, w.scales, w.biases, x, M, K)
         yh = y.cpu().numpy().reshape(n, M)
         check_bound(yh, ref, a, f"call {i}")
-        check_argmax(idx.cpu().numpy(), yh, ref, a, orc, f"call {i}")
+        if op != q.QG_OP_GEMM:
+            check_argmax(idx.cpu().numpy(), yh, ref, a, orc, f"call {i}")
         assert not ws[:q.QG_WS_CONTROL_BYTES].cpu().numpy().any()
 
 
@@ -546,13 +556,17 @@ def test_graph_replay_matches_eager(torch, orc):
     yv = torch.empty(3000, device="cuda")
     yg = torch.empty(200 * 3000, device="cuda")
     ws = tensors.workspace(q.QG_OP_GEMV_ARGMAX, wu.fmt, 20000, 2048, 1)
+    # the prefill call at this size splits K (too few tiles for the chip):
+    # partial products in a workspace of its own size
+    wsg = tensors.workspace(q.QG_OP_GEMM, wi.fmt, 3000, 1024, 200)
+    assert wsg is not None
     s = torch.cuda.Stream()
 
     def work(stream):
         q.qgemv_argmax(wu.fmt, du.codes, du.scales, du.biases, xu, logits, idx, 20000, 2048, 1, ws,
                        stream=stream)
         q.qgemv(wi.fmt, di.codes, di.scales, None, xi[:1], yv, 3000, 1024, 1, stream=stream)
-        q.qgemm(wi.fmt, di.codes, di.scales, None, xi, yg, 3000, 1024, 200, stream=stream)
+        q.qgemm(wi.fmt, di.codes, di.scales, None, xi, yg, 3000, 1024, 200, wsg, stream=stream)
 
     work(s)
     torch.cuda.synchronize()
@@ -573,6 +587,7 @@ def test_graph_replay_matches_eager(torch, orc):
         work(s)
         torch.cuda.synchronize()
     assert not ws[:q.QG_WS_CONTROL_BYTES].cpu().numpy().any()
+    assert not wsg[:q.QG_WS_CONTROL_BYTES].cpu().numpy().any()
 
 
 def test_graph_replay_counters_and_gather(torch, orc):
