@@ -18,7 +18,9 @@
 // (128 x 128, 64 x 128 or 64 x 64, chosen by the host so that the grid fills
 // the 256 compute units); the waves sit side by side along n, each covering
 // all BM weight rows, so a wave reads BM / 16 weight fragments and 3 * BN / 64
-// activation fragments per k-step for 3 * BM * BN / 1024 MFMAs. A k-step
+// activation fragments per k-step for 3 * BM * BN / 1024 MFMAs. For up to 32
+// token rows the tile is 16 or 32 tokens wide and the waves split the
+// weight rows instead (see gemm_kernel). A k-step
 // stages 32 k of W (converted to bf16) and X (split into 3 bf16 planes) in
 // LDS, double-buffered: the step after the current one is staged from
 // registers while the current MFMAs run, and the loads of the step after
@@ -47,10 +49,11 @@ struct GemmParams {
     const uint16_t *biases;   // 4-bit format: bf16 [M][K/64]
     const float *x;   // [N][K]
     float *y;         // [N][M], or nullptr (greedy head without logits)
-    unsigned long long *keys;  // greedy head: [N][tiles_m] tile keys, or nullptr
+    unsigned long long *keys;  // greedy head: [N][keys_m] keys of the waves' row blocks, or nullptr
     float *part;      // split K: [nsplit][N][M] partial products (y and keys unused)
     int64_t M, K, N;
     int tiles_m, tiles_n;
+    int keys_m;       // greedy head: keys per token row (tiles_m x waves along m)
     int kt_split;     // 32-input steps per split of K (a multiple of 4), or 0: no split
 };
 
@@ -159,13 +162,19 @@ __device__ __forceinline__ int swz_chunk(int r, int c)
     return c ^ (((r >> 1) ^ (r >> 3)) & 3);
 }
 
-// Workgroup tile BM (weight rows m) x BN (token rows n); 4 waves side by
-// side along n, each covering all BM rows and BN / 4 tokens.
-template <int FMT, int BM, int BN>
+// Workgroup tile BM (weight rows m) x BN (token rows n); the 4 waves form a
+// WM x WN grid: WN side by side along n, each covering BM / WM rows and
+// BN / WN tokens. Wide tiles put all 4 along n (every wave reads all BM
+// weight rows from LDS); the narrow tiles of a few token rows (BN = 16 or
+// 32) put 4 or 2 along m, so that no MFMA works on more padding than the
+// last 16-token block holds.
+template <int FMT, int BM, int BN, int WN = 4>
 __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
 {
-    constexpr int TI = BM / 16;   // 16-row weight blocks per wave
-    constexpr int TJ = BN / 64;   // 16-token blocks per wave
+    static_assert(WN == 1 || WN == 2 || WN == 4, "4 waves in a WM x WN grid");
+    constexpr int WM = 4 / WN;
+    constexpr int TI = BM / (16 * WM);   // 16-row weight blocks per wave
+    constexpr int TJ = BN / (16 * WN);   // 16-token blocks per wave
     static_assert(TI >= 1 && TJ >= 1 && BM * 2 <= kGemmThreads, "one staging item per thread");
     // double-buffered weight stages: [buffer][row][4 chunks of 8 bf16]
     __shared__ uint4 lw[2][BM * 4];
@@ -186,7 +195,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
     const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave * (BN / 4);
+    const int wn = (wave % WN) * (BN / WN), wm = (wave / WN) * (BM / WM);
     const int fr = lane & 15, fq = lane >> 4;
 
     // weight staging assignment: thread -> (row, half of the 32-k step)
@@ -360,7 +369,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
         bf16x8_t a[TI];
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
-            const int r = 16 * i + fr;
+            const int r = wm + 16 * i + fr;
             a[i] = __builtin_bit_cast(bf16x8_t, lw[b][r * 4 + swz_chunk(r, fq)]);
         }
         // the first MFMA of a group starts its sum from zero (the group's
@@ -387,11 +396,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
             const int gb = (kt / GSTEPS) & 1;
 #pragma unroll
             for (int i = 0; i < TI; ++i) {
-                const float4 s4 = *reinterpret_cast<const float4 *>(&ls[gb][16 * i + 4 * fq]);
+                const float4 s4 = *reinterpret_cast<const float4 *>(&ls[gb][wm + 16 * i + 4 * fq]);
                 const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
                 float bv[4] = {0.f, 0.f, 0.f, 0.f};
                 if (FMT == FMT_U4_G64) {
-                    const float4 b4 = *reinterpret_cast<const float4 *>(&lb[gb][16 * i + 4 * fq]);
+                    const float4 b4 = *reinterpret_cast<const float4 *>(&lb[gb][wm + 16 * i + 4 * fq]);
                     bv[0] = b4.x; bv[1] = b4.y; bv[2] = b4.z; bv[3] = b4.w;
                 }
 #pragma unroll
@@ -488,14 +497,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
     }
 
     // epilogue: row scale (int8), store Y[n][m .. m+3]; greedy head: the
-    // tile's best (value, lowest index) key per token row
+    // best (value, lowest index) key of the wave's rows per token row
     const bool vec = (p.M & 3) == 0;
     uint64_t best[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j) best[j] = 0ull;
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
-        const int64_t mb = m0 + 16 * i + 4 * fq;
+        const int64_t mb = m0 + wm + 16 * i + 4 * fq;
         float s[4] = {1.f, 1.f, 1.f, 1.f};
         if (FMT == FMT_I8_ROW) {
             const float *sp = static_cast<const float *>(p.scales);
@@ -539,7 +548,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
             o = shfl_xor_u64(k, 32);
             k = o > k ? o : k;
             const int64_t n = n0 + wn + 16 * j + fr;
-            if (fq == 0 && n < p.N) p.keys[n * p.tiles_m + tm] = k;
+            if (fq == 0 && n < p.N) p.keys[n * p.keys_m + tm * WM + wave / WN] = k;
         }
     }
 }
@@ -571,17 +580,17 @@ __global__ __launch_bounds__(256) void gemm_splitk_combine_kernel(const float *p
     }
 }
 
-// Greedy selection over the tile keys of the prefill-shaped head: one
-// workgroup per token row n reduces keys[n][0 .. tiles_m) and writes idx[n]
-// (the key order makes the result the lowest index of the maximum).
-__global__ __launch_bounds__(256) void argmax_keys_kernel(const unsigned long long *keys, int tiles_m,
+// Greedy selection over the keys of the prefill-shaped head: one workgroup
+// per token row n reduces keys[n][0 .. nkeys) and writes idx[n] (the key
+// order makes the result the lowest index of the maximum).
+__global__ __launch_bounds__(256) void argmax_keys_kernel(const unsigned long long *keys, int nkeys,
                                                           int32_t *idx)
 {
     __shared__ unsigned long long s_best[4];
     const int64_t n = blockIdx.x;
     uint64_t best = 0ull;
-    for (int t = threadIdx.x; t < tiles_m; t += blockDim.x) {
-        const uint64_t k = keys[n * tiles_m + t];
+    for (int t = threadIdx.x; t < nkeys; t += blockDim.x) {
+        const uint64_t k = keys[n * nkeys + t];
         best = k > best ? k : best;
     }
 #pragma unroll

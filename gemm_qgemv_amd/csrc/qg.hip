@@ -159,6 +159,7 @@ constexpr int kB1ChunkWide = 512;        // chunk of the 8-row tables (64 KiB of
 constexpr int64_t kB1LongResident = 3;   // workgroups per compute unit at the long chunk
 
 struct GemvPlan {
+    bool gemm;           // small batch run as the prefill product on narrow tiles
     bool mfma;           // small-batch 4-bit kernel on the matrix cores
     int passes;          // small-batch kernel: launches of up to 8 activation rows each
     bool lut;            // batch-1 1-bit kernel (table lookup, lanes along rows)
@@ -178,9 +179,55 @@ struct GemvPlan {
     size_t part_off, ws_bytes;
 };
 
+// The matrix-core prefill product over N token rows, K split when its grid
+// is small (defined below), and the workspace that needs.
+size_t gemm_mfma_workspace(int fmt, int64_t M, int64_t K, int64_t N);
+void run_gemm_mfma(int fmt, const void *codes, const void *scales, const void *biases,
+                   const float *x, float *y, int64_t M, int64_t K, int64_t N, void *ws,
+                   hipStream_t s);
+
+// The 4-bit small-batch matrix-core kernel stages all of K in LDS.
+bool u4_mfma_ok(int fmt, int64_t K)
+{
+    return fmt == QG_U4_G64 && K % (64 * qg::kMfmaChunk) == 0 &&
+           K <= static_cast<int64_t>(qg::kStageItems) * qg::kMfmaThreads &&
+           static_cast<int64_t>(qg::gemv_mfma_lds_bytes(K)) + kLdsStaticReserve <= kLdsMax;
+}
+
+// Whether nb (2..16) activation rows run faster as the prefill product on
+// narrow tiles (weights read once, 16 token rows of matrix-core work) than
+// on the matrix-vector kernels. Estimates in microseconds, fitted to
+// MI355X measurements (8-bit 3584 x 1024 and 1024 x 3584, 4-bit 6144 x 2048,
+// 2048 x 6144 and 151936 x 2048, 1-bit 17408 x 5120 and 5120 x 17408):
+//   prefill, narrow tiles     10 + 96 M K / R, R = 220e6 flop/us (1-bit, on
+//                             128-row tiles with K split four ways per
+//                             compute unit: 280e6)
+//   4-bit matrix-core matvec  per launch of up to 8 rows the weight bytes at
+//                             4.4 TB/s, at least 14
+//   1-bit lookup kernel       8 + nb M K / 14e6
+// and the vector-ALU and lookup kernels lose from 6 rows on matrices wider
+// than tall, whose few rows leave their grids small.
+bool batch_on_gemm(int fmt, int64_t M, int64_t K, int nb)
+{
+    if (nb < 2 || K > qg::kGemmMaxK) return false;
+    const double w = static_cast<double>(M) * static_cast<double>(K);
+    const double t_gemm = 10.0 + 96.0 * w / (fmt == QG_B1_G128 ? 280e6 : 220e6);
+    if (u4_mfma_ok(fmt, K)) {
+        const double bytes = static_cast<double>(M) * (row_bytes(fmt, K) + 4 * (K / 64));
+        return t_gemm < static_cast<double>(ceil_div(nb, 8)) * std::max(14.0, bytes / 4.4e6);
+    }
+    if (M < K && nb >= 6) return true;
+    return fmt == QG_B1_G128 && t_gemm < 8.0 + nb * w / 14e6;
+}
+
 GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
 {
     GemvPlan pl{};
+    if (!argmax && nb >= 2 && batch_on_gemm(fmt, M, K, nb)) {
+        pl.gemm = true;
+        pl.ws_bytes = gemm_mfma_workspace(fmt, M, K, nb);
+        return pl;
+    }
     const int64_t S = K / k_per_slice(fmt);
     if (nb == 1 && fmt != QG_B1_G128 && ceil_div(S, 64) <= 4) {
         // batch 1: workgroups of 4 independent waves, each wave a
@@ -230,9 +277,7 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
         pl.ws_bytes = (off > kCtlBytes || argmax) ? off : 0;
         return pl;
     }
-    if (fmt == QG_U4_G64 && nb >= 2 && K % (64 * qg::kMfmaChunk) == 0 &&
-        K <= static_cast<int64_t>(qg::kStageItems) * qg::kMfmaThreads &&
-        static_cast<int64_t>(qg::gemv_mfma_lds_bytes(K)) + kLdsStaticReserve <= kLdsMax) {
+    if (nb >= 2 && u4_mfma_ok(fmt, K)) {
         // 2..16 rows, 4-bit: matrix cores, one workgroup of 8 waves per
         // compute unit, at least one 16-row tile per wave; a launch takes up
         // to 8 activation rows (9..16 rows: two launches, each reading the
@@ -369,6 +414,10 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
               const void *biases, const float *x, float *y, int32_t *idx, int64_t M,
               int64_t K, int nb, void *ws, hipStream_t s)
 {
+    if (pl.gemm) {
+        run_gemm_mfma(fmt, codes, scales, biases, x, y, M, K, nb, ws, s);
+        return;
+    }
     if (pl.mfma) {
         qg::GemvMfmaParams q{};
         q.codes = static_cast<const uint8_t *>(codes);
@@ -544,37 +593,48 @@ int gemv_entry(int fmt, const void *codes, const void *scales, const void *biase
 
 constexpr int kGemmViaGemv = 16;
 
-void gemm_tile(int fmt, int64_t M, int64_t N, int &bm, int &bn);
+void gemm_tile(int fmt, int64_t M, int64_t N, int &bm, int &bn, int &wn);
 
 // Split of K for prefill grids too small for the chip: with fewer tiles than
 // compute units, each tile's K range is cut into nsplit pieces of kt_split
 // steps (a multiple of 4, so that group boundaries do not move) to give
 // about two workgroups per compute unit; the partial products go to the
-// workspace and a second launch adds them in split order. kt_split = 0: no
-// split.
+// workspace and a second launch adds them in split order. The 1-bit format
+// does the most work per k-step beside its MFMAs (sign unpacking and a
+// barrier for few MFMAs), so it splits grids of up to four tiles per
+// compute unit, into about four workgroups per compute unit (17408 x 5120,
+// 128 token rows: 148 -> 131 us; 64 rows: 101 -> 75 us); the other formats
+// lose from such splits (8-bit 3584 x 1024, 128 rows: 16.7 -> 21.6 us).
+// kt_split = 0: no split.
 void gemm_split(int fmt, int64_t M, int64_t K, int64_t N, int &kt_split, int &nsplit)
 {
     kt_split = 0;
     nsplit = 1;
-    int bm, bn;
-    gemm_tile(fmt, M, N, bm, bn);
+    int bm, bn, wn;
+    gemm_tile(fmt, M, N, bm, bn, wn);
     const int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
     const int64_t nk = ceil_div(K, 32);
-    if (tiles >= kComputeUnits || nk < 8) return;
-    const int64_t want = std::min(ceil_div(2 * kComputeUnits, tiles), nk / 4);
+    const int below = fmt == QG_B1_G128 ? 4 : 1, per_cu = fmt == QG_B1_G128 ? 4 : 2;
+    if (tiles >= below * kComputeUnits || nk < 8) return;
+    const int64_t want = std::min(ceil_div(per_cu * kComputeUnits, tiles), nk / 4);
     if (want < 2) return;
     kt_split = static_cast<int>(round_up(ceil_div(nk, want), 4));
     nsplit = static_cast<int>(ceil_div(nk, kt_split));
     if (nsplit < 2) kt_split = 0, nsplit = 1;
 }
 
-size_t gemm_workspace(int fmt, int64_t M, int64_t K, int64_t N)
+size_t gemm_mfma_workspace(int fmt, int64_t M, int64_t K, int64_t N)
 {
-    if (N <= kGemmViaGemv) return plan_gemv(fmt, M, K, static_cast<int>(N), false).ws_bytes;
     int kt_split, nsplit;
     gemm_split(fmt, M, K, N, kt_split, nsplit);
     // partial products after the control words, which every call leaves zero
     return nsplit > 1 ? align256(kCtlBytes + static_cast<size_t>(nsplit) * N * M * 4) : 0;
+}
+
+size_t gemm_workspace(int fmt, int64_t M, int64_t K, int64_t N)
+{
+    if (N <= kGemmViaGemv) return plan_gemv(fmt, M, K, static_cast<int>(N), false).ws_bytes;
+    return gemm_mfma_workspace(fmt, M, K, N);
 }
 
 bool gemm_shape_ok(int64_t M, int64_t K, int64_t N)
@@ -585,12 +645,25 @@ bool gemm_shape_ok(int64_t M, int64_t K, int64_t N)
 
 // The largest tile that still gives every compute unit a workgroup
 // (4-bit and 1-bit: at most 64 x 128, their per-group accumulators double
-// the accumulator registers).
-void gemm_tile(int fmt, int64_t M, int64_t N, int &bm, int &bn)
+// the accumulator registers). wn: waves along n (4, or 2 and 1 for the
+// narrow tiles of up to 32 token rows).
+void gemm_tile(int fmt, int64_t M, int64_t N, int &bm, int &bn, int &wn)
 {
     auto tiles = [&](int tm, int tn) { return ceil_div(M, tm) * ceil_div(N, tn); };
     bm = 64;
     bn = 64;
+    wn = 4;
+    if (N <= 32) {
+        // a few token rows: 16 or 32 tokens wide (a 64-wide tile would spend
+        // most of its MFMAs on padding), the waves split the weight rows;
+        // 128 rows once every compute unit still gets two tiles, and always
+        // for the 1-bit format, whose k-steps cost the most beside the MFMAs
+        // (K is split to fill the chip; 17408 x 5120, 17 rows: 54 -> 44 us)
+        bn = N <= 16 ? 16 : 32;
+        wn = bn / 16;
+        if (fmt == QG_B1_G128 || tiles(128, bn) >= 2 * kComputeUnits) bm = 128;
+        return;
+    }
     // 128 token rows per tile only where that pads no more than 64 would
     // (64 token rows with 128-row tiles would halve the useful MFMA work)
     const bool n128 = N % 128 == 0 || N % 128 > 64;
@@ -605,8 +678,28 @@ void gemm_tile(int fmt, int64_t M, int64_t N, int &bm, int &bn)
     else if (tiles(64, 128) >= 2 * kComputeUnits) bn = 128;
 }
 
+template <int FMT>
+void launch_gemm_fmt(int bm, int bn, dim3 grid, hipStream_t s, const qg::GemmParams &p)
+{
+    const dim3 block(qg::kGemmThreads);
+    if (bn == 16) {
+        if (bm == 128) hipLaunchKernelGGL((qg::gemm_kernel<FMT, 128, 16, 1>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((qg::gemm_kernel<FMT, 64, 16, 1>), grid, block, 0, s, p);
+    } else if (bn == 32) {
+        if (bm == 128) hipLaunchKernelGGL((qg::gemm_kernel<FMT, 128, 32, 2>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((qg::gemm_kernel<FMT, 64, 32, 2>), grid, block, 0, s, p);
+    } else if (bn == 64) {
+        hipLaunchKernelGGL((qg::gemm_kernel<FMT, 64, 64>), grid, block, 0, s, p);
+    } else if constexpr (FMT == qg::FMT_I8_ROW) {
+        if (bm == 128) hipLaunchKernelGGL((qg::gemm_kernel<FMT, 128, 128>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((qg::gemm_kernel<FMT, 64, 128>), grid, block, 0, s, p);
+    } else {
+        hipLaunchKernelGGL((qg::gemm_kernel<FMT, 64, 128>), grid, block, 0, s, p);
+    }
+}
+
 // Enqueue the matrix-core prefill kernel; with `keys`, the greedy head's
-// tile keys [N][tiles_m] as well (y may then be nullptr).
+// keys [N][tiles_m x waves along m] as well (y may then be nullptr).
 void launch_gemm(int fmt, const void *codes, const void *scales, const void *biases,
                  const float *x, float *y, unsigned long long *keys, int64_t M, int64_t K,
                  int64_t N, hipStream_t s, float *part = nullptr, int kt_split = 0, int nsplit = 1)
@@ -623,37 +716,22 @@ void launch_gemm(int fmt, const void *codes, const void *scales, const void *bia
     p.M = M;
     p.K = K;
     p.N = N;
-    int bm, bn;
-    gemm_tile(fmt, M, N, bm, bn);
+    int bm, bn, wn;
+    gemm_tile(fmt, M, N, bm, bn, wn);
     p.tiles_m = static_cast<int>(ceil_div(M, bm));
     p.tiles_n = static_cast<int>(ceil_div(N, bn));
+    p.keys_m = p.tiles_m * (4 / wn);
     const dim3 grid(static_cast<unsigned>(int64_t(p.tiles_m) * p.tiles_n), static_cast<unsigned>(nsplit));
-    const dim3 block(qg::kGemmThreads);
-    if (fmt == QG_I8_ROW) {
-        if (bm == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_ROW, 128, 128>), grid, block, 0, s, p);
-        else if (bn == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_ROW, 64, 128>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_ROW, 64, 64>), grid, block, 0, s, p);
-    } else if (fmt == QG_I8_G64) {
-        if (bn == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_G64, 64, 128>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_I8_G64, 64, 64>), grid, block, 0, s, p);
-    } else if (fmt == QG_U4_G64) {
-        if (bn == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_U4_G64, 64, 128>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_U4_G64, 64, 64>), grid, block, 0, s, p);
-    } else {
-        if (bn == 128) hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_B1_G128, 64, 128>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((qg::gemm_kernel<qg::FMT_B1_G128, 64, 64>), grid, block, 0, s, p);
-    }
+    if (fmt == QG_I8_ROW) launch_gemm_fmt<qg::FMT_I8_ROW>(bm, bn, grid, s, p);
+    else if (fmt == QG_I8_G64) launch_gemm_fmt<qg::FMT_I8_G64>(bm, bn, grid, s, p);
+    else if (fmt == QG_U4_G64) launch_gemm_fmt<qg::FMT_U4_G64>(bm, bn, grid, s, p);
+    else launch_gemm_fmt<qg::FMT_B1_G128>(bm, bn, grid, s, p);
 }
 
-void run_gemm(int fmt, const void *codes, const void *scales, const void *biases, const float *x,
-              float *y, int64_t M, int64_t K, int64_t N, void *ws, hipStream_t s)
+void run_gemm_mfma(int fmt, const void *codes, const void *scales, const void *biases,
+                   const float *x, float *y, int64_t M, int64_t K, int64_t N, void *ws,
+                   hipStream_t s)
 {
-    if (N <= kGemmViaGemv) {
-        const int nb = static_cast<int>(N);
-        const GemvPlan pl = plan_gemv(fmt, M, K, nb, false);
-        run_gemv(fmt, pl, codes, scales, biases, x, y, nullptr, M, K, nb, ws, s);
-        return;
-    }
     int kt_split, nsplit;
     gemm_split(fmt, M, K, N, kt_split, nsplit);
     if (nsplit == 1) {
@@ -667,17 +745,35 @@ void run_gemm(int fmt, const void *codes, const void *scales, const void *biases
                        dim3(256), 0, s, part, y, M, N, nsplit);
 }
 
+void run_gemm(int fmt, const void *codes, const void *scales, const void *biases, const float *x,
+              float *y, int64_t M, int64_t K, int64_t N, void *ws, hipStream_t s)
+{
+    if (N <= kGemmViaGemv) {
+        const int nb = static_cast<int>(N);
+        const GemvPlan pl = plan_gemv(fmt, M, K, nb, false);
+        run_gemv(fmt, pl, codes, scales, biases, x, y, nullptr, M, K, nb, ws, s);
+        return;
+    }
+    run_gemm_mfma(fmt, codes, scales, biases, x, y, M, K, N, ws, s);
+}
+
 // ---------------------------------------------------------------------------
 // Greedy head over more than QG_MAX_GEMV_BATCH rows: the prefill kernel with
 // tile keys in the workspace (after the control words), then one workgroup
 // per row reduces its keys. The logits may be skipped (y == nullptr).
 // ---------------------------------------------------------------------------
 
+// Greedy-head keys per token row: one per tile and wave along m.
+int64_t wide_argmax_keys(int fmt, int64_t M, int64_t N)
+{
+    int bm, bn, wn;
+    gemm_tile(fmt, M, N, bm, bn, wn);
+    return ceil_div(M, bm) * (4 / wn);
+}
+
 size_t wide_argmax_workspace(int fmt, int64_t M, int64_t N)
 {
-    int bm, bn;
-    gemm_tile(fmt, M, N, bm, bn);
-    return align256(kCtlBytes + static_cast<size_t>(N) * ceil_div(M, bm) * 8);
+    return align256(kCtlBytes + static_cast<size_t>(N) * wide_argmax_keys(fmt, M, N) * 8);
 }
 
 int wide_argmax_entry(int fmt, const void *codes, const void *scales, const void *biases,
@@ -708,10 +804,8 @@ int wide_argmax_entry(int fmt, const void *codes, const void *scales, const void
     (void)hipGetLastError();
     auto *keys = reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + kCtlBytes);
     launch_gemm(fmt, codes, scales, biases, x, y, keys, M, K, N, stream);
-    int bm, bn;
-    gemm_tile(fmt, M, N, bm, bn);
     hipLaunchKernelGGL(qg::argmax_keys_kernel, dim3(static_cast<unsigned>(N)), dim3(256), 0, stream,
-                       keys, static_cast<int>(ceil_div(M, bm)), idx);
+                       keys, static_cast<int>(wide_argmax_keys(fmt, M, N)), idx);
     return launch_status();
 }
 

@@ -222,6 +222,11 @@ def test_exact_arithmetic_prefill_large_grid(torch, orc, M, K, N):
     (synth.U4_G64, 127, 6144, 129), (synth.U4_G64, 6144, 2048, 2048),
     (synth.I8_G64, 1, 64, 40), (synth.I8_G64, 1000, 1024, 300), (synth.I8_G64, 127, 3584, 129),
     (synth.I8_G64, 3584, 1024, 2048),
+    # narrow tiles: 16 or 32 token rows wide, waves along the weight rows;
+    # 128-row tiles once M gives every compute unit two of them
+    (synth.I8_ROW, 66001, 256, 24), (synth.U4_G64, 70001, 512, 20), (synth.B1_G128, 66000, 256, 32),
+    (synth.I8_G64, 66001, 192, 29), (synth.U4_G64, 3000, 2048, 32), (synth.I8_ROW, 2049, 3584, 25),
+    (synth.B1_G128, 700, 5120, 21), (synth.I8_G64, 1000, 3584, 18),
 ])
 def test_random_prefill_small(torch, orc, fmt, M, K, N):
     say(f"random prefill fmt={fmt} M={M} K={K} N={N}")
@@ -249,6 +254,10 @@ SMALL = [
     (synth.I8_G64, 1, 64, 1), (synth.I8_G64, 127, 1088, 1), (synth.I8_G64, 1000, 1024, 3),
     (synth.I8_G64, 129, 16384, 1), (synth.I8_G64, 45, 20032, 2), (synth.I8_G64, 64, 4096, 16),
     (synth.I8_G64, 3584, 1024, 1), (synth.I8_G64, 1024, 3584, 1),
+    # batches that the host routes to the prefill kernel's narrow tiles
+    (synth.U4_G64, 6144, 2048, 12), (synth.U4_G64, 2048, 6144, 6), (synth.I8_ROW, 1024, 3584, 8),
+    (synth.B1_G128, 17408, 5120, 16), (synth.I8_G64, 1024, 3584, 11), (synth.B1_G128, 5120, 17408, 6),
+    (synth.B1_G128, 17408, 5120, 7),
 ]
 
 
@@ -405,6 +414,8 @@ def gpu_greedy(torch, w, x, logits=True):
     (synth.U4_G64, 30001, 2048, 64), (synth.I8_ROW, 9000, 1024, 100), (synth.B1_G128, 5000, 1280, 17),
     (synth.U4_G64, 20000, 2048, 128), (synth.U4_G64, 4099, 1024, 256),
     (synth.U4_G64, 30001, 2048, 16), (synth.U4_G64, 9000, 1024, 11),
+    (synth.U4_G64, 30001, 2048, 24), (synth.I8_ROW, 70001, 256, 32), (synth.I8_G64, 70001, 192, 19),
+    (synth.B1_G128, 66001, 256, 30),
 ])
 def test_greedy_head_with_and_without_logits(torch, orc, fmt, M, K, N):
     say(f"greedy fmt={fmt} M={M} K={K} N={N}")
@@ -420,19 +431,21 @@ def test_greedy_head_with_and_without_logits(torch, orc, fmt, M, K, N):
     assert np.array_equal(idx, idx2), "logits-free call chose other rows"
 
 
-def test_wide_greedy_head_ties():
+@pytest.mark.parametrize("N", [64, 20])
+def test_wide_greedy_head_ties(N):
     """Equal maxima in different 64-row tiles (first row, last row, the
-    middle) with 64 rows of activations."""
+    middle), and in the two halves of one tile (20 rows of activations:
+    32-token tiles whose two waves each cover 32 of the 64 weight rows)."""
     import torch as t
     orc = oracle.get()
-    say("wide greedy ties")
+    say(f"wide greedy ties N={N}")
     rng = np.random.default_rng(12)
-    M, K, N = 20000, 1024, 64
+    M, K = 20000, 1024
     w = synth.draw_weights(synth.U4_G64, M, K, rng)
     x = synth.draw_x(N, K, rng)
     ref, _ = orc.qgemv(synth.U4_G64, w.codes, w.scales, w.biases, x, M, K)
     top = int(np.argmax(ref[0]))
-    for dst in (0, M - 1, 10000, 10063):
+    for dst in (0, M - 1, 10000, 10040, 10063):
         if dst != top:
             for arr in (w.codes, w.scales, w.biases):
                 arr[dst] = arr[top]
