@@ -459,6 +459,48 @@ def test_wide_greedy_head_ties(N):
 
 
 # ---------------------------------------------------------------------------
+# seeded random shapes: every entry point on shapes drawn across the host's
+# kernel choices (batch-1 kernels, small-batch kernels, the prefill kernel's
+# narrow and wide tiles, split K, routed batches, the wide greedy head)
+# ---------------------------------------------------------------------------
+
+ROWS_DRAWN = [1, 2, 3, 4, 5, 6, 7, 8, 9, 11, 12, 13, 15, 16, 17, 19, 24, 31, 32, 33, 47, 64, 65, 100, 129]
+
+
+def drawn_shapes(fmt, count, seed):
+    """(M, K, N) with M and K log-uniform (K a multiple of the format's
+    unit, up to 8192) and N from ROWS_DRAWN, at most 12e6 multiply-adds."""
+    rng = np.random.default_rng([seed, fmt])
+    unit = synth.K_UNIT[fmt]
+    shapes = []
+    while len(shapes) < count:
+        M = int(np.exp(rng.uniform(0.0, np.log(40000.0))))
+        K = unit * max(1, int(round(np.exp(rng.uniform(0.0, np.log(8192 / unit))))))
+        N = int(rng.choice(ROWS_DRAWN))
+        if M * K * N <= 12e6:
+            shapes.append((M, K, N))
+    return shapes
+
+
+@pytest.mark.parametrize("fmt", [synth.I8_ROW, synth.U4_G64, synth.B1_G128, synth.I8_G64])
+def test_drawn_shapes_all_entry_points(torch, orc, fmt):
+    for i, (M, K, N) in enumerate(drawn_shapes(fmt, 32, 77)):
+        say(f"drawn fmt={fmt} #{i} M={M} K={K} N={N}")
+        rng = synth.rng_for(700 + fmt, i)
+        w = synth.draw_weights(fmt, M, K, rng)
+        x = synth.draw_x(N, K, rng)
+        ref, a = orc.qgemv(fmt, w.codes, w.scales, w.biases, x, M, K)
+        wd = dev(w)
+        check_bound(gpu_gemm(torch, wd, x), ref, a, f"qgemm {M}x{K} n{N}")
+        if N <= q.QG_MAX_GEMV_BATCH:
+            y, _ = gpu_gemv(torch, wd, x, ws_fill=0x77)
+            check_bound(y, ref, a, f"qgemv {M}x{K} b{N}")
+        y, idx = gpu_greedy(torch, wd, x, logits=True)
+        check_bound(y, ref, a, f"greedy {M}x{K} b{N}")
+        check_argmax(idx, y, ref, a, orc, "greedy")
+
+
+# ---------------------------------------------------------------------------
 # the configurations at full size
 # ---------------------------------------------------------------------------
 
