@@ -208,15 +208,10 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_u4_kernel(GemvMfmaPara
         }
     };
 
-    MfmaChunk buf[kMfmaBufs];
-    point(tb);
-#pragma unroll
-    for (int u = 0; u < kMfmaBufs - 1; ++u)
-        if (u < total) load(buf[u]);
-
-    // 1a. activation pieces in operand order. Item (n, g, qq, s)
-    //     covers 8 inputs of activation row n; a thread's items (at most
-    //     kStageItems) load first, then split and store.
+    // 1. activation pieces in operand order. Item (n, g, qq, s) covers 8
+    //    inputs of activation row n; a thread's items (at most kStageItems)
+    //    are requested before the first weight chunks, so that waiting for
+    //    them (memory counters count in order) does not wait for the weights.
     const int nitems = 8 * G * 8;
     float4 xa[kStageItems], xb[kStageItems];
 #pragma unroll
@@ -232,44 +227,58 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_u4_kernel(GemvMfmaPara
             xb[u] = src[1];
         }
     }
+
+    MfmaChunk buf[kMfmaBufs];
+    point(tb);
+#pragma unroll
+    for (int u = 0; u < kMfmaBufs - 1; ++u)
+        if (u < total) load(buf[u]);
+
+    // split and store the pieces; the 8 items of one group of one row sit
+    // in 8 consecutive lanes, which add their sums into the group sum X[n][g]
+    // (the bias-contraction operand: group g is input k = g % 32 of bias
+    // step g / 32, quarter (g / 8) % 4, element g % 8)
 #pragma unroll
     for (int u = 0; u < kStageItems; ++u) {
         const int it = tid + u * kMfmaThreads;
-        if (it < nitems) {
+        if (u * kMfmaThreads < nitems) {   // uniform over the workgroup
             const int n = it / (G * 8), rem = it - n * (G * 8);
             const int g = rem >> 3, qq = (rem >> 1) & 3, s = rem & 1;
             const float4 a = xa[u], b = xb[u];
-            // operand order k0 + {0, 2, 4, 6, 1, 3, 5, 7}
-            const float v[8] = {a.x, a.z, b.x, b.z, a.y, a.w, b.y, b.w};
-            uint32_t h[4], md[4], lo[4];
+            float sum = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+            sum += __shfl_xor(sum, 1);
+            sum += __shfl_xor(sum, 2);
+            sum += __shfl_xor(sum, 4);
+            if (it < nitems) {
+                // operand order k0 + {0, 2, 4, 6, 1, 3, 5, 7}
+                const float v[8] = {a.x, a.z, b.x, b.z, a.y, a.w, b.y, b.w};
+                uint32_t h[4], md[4], lo[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) split3h_pair(v[2 * j], v[2 * j + 1], h[j], md[j], lo[j]);
-            uint8_t *blk = lds + static_cast<size_t>(g) * kMfmaGroupBytes + s * kMfmaBlockBytes;
-            *reinterpret_cast<uint4 *>(blk + (qq * 16 + n) * 16) = make_uint4(h[0], h[1], h[2], h[3]);
-            *reinterpret_cast<uint4 *>(blk + (qq * 16 + 8 + n) * 16) = make_uint4(md[0], md[1], md[2], md[3]);
-            *reinterpret_cast<uint4 *>(blk + 1024 + (qq * 8 + n) * 16) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        }
-    }
-    // 1b. group sums X[n][g] as bias-contraction operand: group g is input
-    //     k = g % 32 of bias step g / 32 (quarter (g / 8) % 4, element g % 8)
-    for (int it = tid; it < NBS * 32 * 8; it += blockDim.x) {
-        const int n = it & 7, g = it >> 3;
-        float sum = 0.f;
-        if (n < p.nb && g < G) {
-            const float4 *src = reinterpret_cast<const float4 *>(p.x + static_cast<int64_t>(n) * p.K + 64 * g);
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float4 v = src[j];
-                sum += (v.x + v.y) + (v.z + v.w);
+                for (int j = 0; j < 4; ++j) split3h_pair(v[2 * j], v[2 * j + 1], h[j], md[j], lo[j]);
+                uint8_t *blk = lds + static_cast<size_t>(g) * kMfmaGroupBytes + s * kMfmaBlockBytes;
+                *reinterpret_cast<uint4 *>(blk + (qq * 16 + n) * 16) = make_uint4(h[0], h[1], h[2], h[3]);
+                *reinterpret_cast<uint4 *>(blk + (qq * 16 + 8 + n) * 16) = make_uint4(md[0], md[1], md[2], md[3]);
+                *reinterpret_cast<uint4 *>(blk + 1024 + (qq * 8 + n) * 16) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+                if ((rem & 7) == 0) {
+                    uint32_t sh, sm, sl;
+                    split3h(sum, sh, sm, sl);
+                    uint8_t *bb = bias_blocks + static_cast<size_t>(g >> 5) * kMfmaBlockBytes;
+                    const int bq = (g >> 3) & 3, e = g & 7;
+                    *reinterpret_cast<uint16_t *>(bb + (bq * 16 + n) * 16 + 2 * e) = static_cast<uint16_t>(sh);
+                    *reinterpret_cast<uint16_t *>(bb + (bq * 16 + 8 + n) * 16 + 2 * e) = static_cast<uint16_t>(sm);
+                    *reinterpret_cast<uint16_t *>(bb + 1024 + (bq * 8 + n) * 16 + 2 * e) = static_cast<uint16_t>(sl);
+                }
             }
         }
-        uint32_t h, md, lo;
-        split3h(sum, h, md, lo);
-        uint8_t *blk = bias_blocks + static_cast<size_t>(g >> 5) * kMfmaBlockBytes;
-        const int qq = (g >> 3) & 3, e = g & 7;
-        *reinterpret_cast<uint16_t *>(blk + (qq * 16 + n) * 16 + 2 * e) = static_cast<uint16_t>(h);
-        *reinterpret_cast<uint16_t *>(blk + (qq * 16 + 8 + n) * 16 + 2 * e) = static_cast<uint16_t>(md);
-        *reinterpret_cast<uint16_t *>(blk + 1024 + (qq * 8 + n) * 16 + 2 * e) = static_cast<uint16_t>(lo);
+    }
+    // the last bias step's groups beyond G contribute zero
+    for (int it = tid; it < (NBS * 32 - G) * 8; it += blockDim.x) {
+        const int n = it & 7, g = G + (it >> 3);
+        uint8_t *bb = bias_blocks + static_cast<size_t>(g >> 5) * kMfmaBlockBytes;
+        const int bq = (g >> 3) & 3, e = g & 7;
+        *reinterpret_cast<uint16_t *>(bb + (bq * 16 + n) * 16 + 2 * e) = 0;
+        *reinterpret_cast<uint16_t *>(bb + (bq * 16 + 8 + n) * 16 + 2 * e) = 0;
+        *reinterpret_cast<uint16_t *>(bb + 1024 + (bq * 8 + n) * 16 + 2 * e) = 0;
     }
     __syncthreads();
 
