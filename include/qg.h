@@ -132,11 +132,14 @@ enum {
 /*
  * qgemv -- batch-1 (up to QG_MAX_GEMV_BATCH) quantized matrix-vector product.
  *   y[n][m] = sum_k w[m][k] * x[n][k],  0 <= n < batch, 0 <= m < M.
- * Every packed weight is read once per call, dequantized in registers and
- * never written out. (MiniCPM-V-4.6 on a Tesla C2075, section 3.3: decode
- * reads each weight once and is bandwidth-bound; I Built an LLM Inference
- * Engine..., "Optimization 4: Quantized Kernels": dequantization is fused
- * into the product.)
+ * Every packed weight is read once per call (4-bit, 9 to 16 rows on the
+ * small-batch matrix-core kernel: once per launch of up to 8 rows),
+ * dequantized in registers and never written out. Batches of 2 to 16 rows
+ * may run on the prefill kernel (see qgemm) where that is expected to be
+ * faster; the result contract is the same. (MiniCPM-V-4.6 on a Tesla
+ * C2075, section 3.3: decode reads each weight once and is bandwidth-bound;
+ * I Built an LLM Inference Engine..., "Optimization 4: Quantized Kernels":
+ * dequantization is fused into the product.)
  *   x  float32 [batch][K];  y  float32 [batch][M] (overwritten).
  *   1 <= M <= 2^31-1, 1 <= K <= 2^30, 1 <= batch <= QG_MAX_GEMV_BATCH.
  */
@@ -207,10 +210,9 @@ int qgemv_argmax(int fmt, const void *codes, const void *scales,
  * negative zero": that row decoder multiplies and adds in two steps and
  * passes each value through FP16 on its way to FP32, and the lookup on the
  * GPU had to reproduce denormals, the sign of zero and round-to-nearest-even
- * exactly; I Built an
- * LLM Inference Engine..., "Cost 1: the embedding lookup still runs on the
- * CPU": the quantized rows are decoded on the device from token ids instead
- * of crossing PCIe.)
+ * exactly; I Built an LLM Inference Engine..., "Cost 1: the embedding lookup
+ * still runs on the CPU": the quantized rows are decoded on the device from
+ * token ids instead of crossing PCIe.)
  *   fmt     QG_U4_G64 only; the other known formats give QG_ERR_UNSUPPORTED.
  *   ids     int32 [n], device memory (4-byte aligned); any values.
  *   out     float32 [n][K] (overwritten).
