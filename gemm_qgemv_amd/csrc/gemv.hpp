@@ -285,21 +285,23 @@ __device__ __forceinline__ void greedy_finish(const unsigned long long *wg_key, 
 // Greedy finish for grids whose workgroups all end at about the same time:
 // rather than folding its keys into shared slots (contended atomics on one
 // line, serialized at the coherence point), each workgroup parks its nb
-// keys in its own row of `keys` ([workgroups][8], any initial contents)
+// keys in its own row of `keys` ([workgroups][KS], KS >= nb, any initial
+// contents)
 // with returning device-scope exchanges, then counts itself in once. The
 // last workgroup reads every row back with device-scope atomic loads,
 // reduces them, writes the indices and puts the counter back to zero.
+template <int KS>
 __device__ __forceinline__ void greedy_finish_rows(const unsigned long long *wg_key, int nb,
                                                    GreedyCtl *ctl, unsigned long long *keys,
                                                    int32_t *idx, int nwg)
 {
     __shared__ unsigned s_last;
-    __shared__ unsigned long long s_best[8];
+    __shared__ unsigned long long s_best[KS];
     if (threadIdx.x == 0) {
         uint32_t dep = 0;
         for (int b = 0; b < nb; ++b) {
             const unsigned long long old = __hip_atomic_exchange(
-                &keys[static_cast<int64_t>(blockIdx.x) * 8 + b], wg_key[b], __ATOMIC_RELAXED,
+                &keys[static_cast<int64_t>(blockIdx.x) * KS + b], wg_key[b], __ATOMIC_RELAXED,
                 __HIP_MEMORY_SCOPE_AGENT);
             dep |= static_cast<uint32_t>(old) | static_cast<uint32_t>(old >> 32);
         }
@@ -309,12 +311,12 @@ __device__ __forceinline__ void greedy_finish_rows(const unsigned long long *wg_
                                                   __HIP_MEMORY_SCOPE_AGENT);
         s_last = (t == static_cast<unsigned>(nwg) - 1u);
     }
-    if (threadIdx.x < 8) s_best[threadIdx.x] = 0ull;
+    if (threadIdx.x < KS) s_best[threadIdx.x] = 0ull;
     __syncthreads();
     if (!s_last) return;
     for (int i = threadIdx.x; i < nwg * nb; i += blockDim.x) {
         const int w = i / nb, b = i - w * nb;
-        const unsigned long long k = __hip_atomic_load(&keys[static_cast<int64_t>(w) * 8 + b],
+        const unsigned long long k = __hip_atomic_load(&keys[static_cast<int64_t>(w) * KS + b],
                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         atomicMax(&s_best[b], k);
     }

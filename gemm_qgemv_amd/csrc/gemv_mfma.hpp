@@ -408,7 +408,7 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_u4_kernel(GemvMfmaPara
             if (r == 0 && q < 2 && n < p.nb) atomicMax(&wg_key[n], static_cast<unsigned long long>(key));
         }
         __syncthreads();
-        greedy_finish_rows(wg_key, p.nb, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x));
+        greedy_finish_rows<8>(wg_key, p.nb, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x));
     }
 }
 

@@ -1,0 +1,258 @@
+// gemv_mfma16.hpp -- 9..16 activation rows of the 4-bit group-64 format in
+// one pass over the weights, on the gfx950 matrix cores.
+//
+// The 8-row kernel (gemv_mfma.hpp) stages the activation pieces of all K in
+// LDS; 16 rows of them would not fit, so 9..16 rows there take two launches
+// that each read the weights. Here K is cut across the workgroup's 8 waves
+// instead: wave w owns groups 2 PAIRS w .. 2 PAIRS (w + 1) - 1 (K = 1024
+// PAIRS) and keeps the exact bf16 pieces of all 16 activation rows for
+// those inputs in registers for the whole kernel; all 8 waves stream the
+// same 16-row weight tiles, each reading its part of every row, so the
+// weights are read once. Per k-step a tile takes three MFMAs, one per piece
+// (top, middle, bottom of the three-way split; 16 operand rows = 16
+// activation rows), each group's sum is folded with its scale, and the bias
+// term sum_g b[m][g] X[n][g] is added on the vector ALUs (the wave's group
+// sums of the activations sit in registers). The 8 partial sums of a tile
+// meet in LDS and are added in wave order after a barrier, every k16Tiles
+// tiles, so the result does not depend on timing.
+//
+// Operand order as in gemv_mfma.hpp: lane l is operand row r = l % 16 and
+// quarter q = l / 16; its 16-byte code load covers a pair of groups, and one
+// permlane32 swap per dword pair gives it, at k-step s of group g, inputs
+//     k = 64 g + 32 (q & 1) + 16 (q >> 1) + 8 s + {0, 2, 4, 6, 1, 3, 5, 7}.
+// The same lane holds activation row r at those inputs. D: lane (r, q) holds
+// weight row r of the tile for activation rows 4 q .. 4 q + 3.
+#pragma once
+
+#include "gemv_mfma.hpp"
+
+namespace qg {
+
+constexpr int k16Tiles = 4;   // tiles between two barriers (and code loads in flight per wave)
+// LDS: partial sums [2][k16Tiles][8 waves][16 x 16] floats, then staged
+// outputs [tiles][16 activation rows][16 weight rows] floats
+constexpr int k16RedFloats = 2 * k16Tiles * 8 * 256;
+constexpr int k16TileOutBytes = 16 * 16 * 4;
+
+__host__ __device__ constexpr size_t gemv_mfma16_lds_bytes() { return k16RedFloats * 4; }
+
+template <int PAIRS>
+__global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_u4_kernel(GemvMfmaParams p)
+{
+    static_assert(kMfmaWaves == 8, "K is cut into 8 slices");
+    extern __shared__ float4 lds_f4[];
+    float *red = reinterpret_cast<float *>(lds_f4);
+    float *out_stage = red + k16RedFloats;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, q = lane >> 4;
+    const int64_t row_bytes = p.K / 2;
+    const int64_t G = p.K / 64;
+    const int gw = wave * 2 * PAIRS;   // this wave's first group
+
+    // the workgroup's run of 16-row tiles; every wave takes every tile
+    const int64_t ntiles = (p.M + 15) / 16;
+    const int64_t tb = static_cast<int64_t>(blockIdx.x) * ntiles / gridDim.x;
+    const int64_t te = static_cast<int64_t>(blockIdx.x + 1) * ntiles / gridDim.x;
+    const int64_t nt = te - tb;
+
+    // 1a. this lane's activations (row r, its inputs of the wave's groups),
+    //     requested before the first code loads (the memory counters count
+    //     in order)
+    float4 xa[PAIRS][2][2][2];
+#pragma unroll
+    for (int pp = 0; pp < PAIRS; ++pp)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int64_t k0 = 64 * (gw + 2 * pp + h) + 32 * (q & 1) + 16 * (q >> 1) + 8 * s;
+                xa[pp][h][s][0] = xa[pp][h][s][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (r < p.nb) {
+                    const float4 *src = reinterpret_cast<const float4 *>(p.x + r * p.K + k0);
+                    xa[pp][h][s][0] = src[0];
+                    xa[pp][h][s][1] = src[1];
+                }
+            }
+
+    // code ring: tile t's codes (PAIRS x 16 bytes), scales and biases of
+    // this lane's weight row for the wave's groups (rows past M read row
+    // M - 1; their outputs are not written)
+    struct Tile16 {
+        uint4 c[PAIRS];
+        uint32_t s[PAIRS], b[PAIRS];
+    };
+    auto load = [&](Tile16 &T, int64_t t) {
+        const int64_t m = min(t * 16 + r, p.M - 1);
+        const uint8_t *c = p.codes + m * row_bytes + 32 * gw + 16 * q;
+#pragma unroll
+        for (int pp = 0; pp < PAIRS; ++pp) {
+#if QG_MFMA_NT
+            const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(c + 64 * pp));
+            T.c[pp] = make_uint4(v.x, v.y, v.z, v.w);
+#else
+            T.c[pp] = *reinterpret_cast<const uint4 *>(c + 64 * pp);
+#endif
+        }
+        const uint32_t *sc = reinterpret_cast<const uint32_t *>(p.scales + m * G + gw);
+        const uint32_t *bi = reinterpret_cast<const uint32_t *>(p.biases + m * G + gw);
+#pragma unroll
+        for (int pp = 0; pp < PAIRS; ++pp) {
+            T.s[pp] = sc[pp];
+            T.b[pp] = bi[pp];
+        }
+    };
+    constexpr int NB = k16Tiles;
+    Tile16 ring[NB];
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u)
+        if (u < nt) load(ring[u], tb + u);
+
+    // 1b. exact three-way split into operand pieces; the group sums
+    //     X[n][g] of the activations for the bias term, gathered to the
+    //     lanes that hold D rows n = 4 q .. 4 q + 3
+    bf16x8_t at[PAIRS][2][2][3];
+    float xg[PAIRS][2][4];
+#pragma unroll
+    for (int pp = 0; pp < PAIRS; ++pp)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float sum = 0.f;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const float4 a = xa[pp][h][s][0], b = xa[pp][h][s][1];
+                sum += ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+                const float v[8] = {a.x, a.z, b.x, b.z, a.y, a.w, b.y, b.w};
+                uint32_t hi[4], md[4], lo[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) split3_pair(v[2 * j], v[2 * j + 1], hi[j], md[j], lo[j]);
+                at[pp][h][s][0] = __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+                at[pp][h][s][1] = __builtin_bit_cast(bf16x8_t, make_uint4(md[0], md[1], md[2], md[3]));
+                at[pp][h][s][2] = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+            }
+            sum += __shfl_xor(sum, 16);
+            sum += __shfl_xor(sum, 32);   // X[r][g] in every lane of row r
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xg[pp][h][i] = __shfl(sum, 4 * q + i);
+        }
+
+    auto mfma = [](bf16x8_t a, bf16x8_t b, floatx4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    };
+    // one tile's partial product over the wave's groups, into LDS slot u of
+    // buffer buf
+    auto reduce = [&](const Tile16 &T, int buf, int u) {
+        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int pp = 0; pp < PAIRS; ++pp) {
+            const auto s0 = __builtin_amdgcn_permlane32_swap(T.c[pp].x, T.c[pp].z, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(T.c[pp].y, T.c[pp].w, false, false);
+            const uint32_t dw[2][2] = {{s0[0], s1[0]}, {s0[1], s1[1]}};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bf16x8_t w0 = nibbles_to_bf16(dw[h][0]), w1 = nibbles_to_bf16(dw[h][1]);
+                floatx4_t t = {0.f, 0.f, 0.f, 0.f};
+                t = mfma(at[pp][h][0][0], w0, t);
+                t = mfma(at[pp][h][0][1], w0, t);
+                t = mfma(at[pp][h][0][2], w0, t);
+                t = mfma(at[pp][h][1][0], w1, t);
+                t = mfma(at[pp][h][1][1], w1, t);
+                t = mfma(at[pp][h][1][2], w1, t);
+                const float sc = h ? __uint_as_float(T.s[pp] & 0xFFFF0000u) : __uint_as_float(T.s[pp] << 16);
+                const float bv = h ? __uint_as_float(T.b[pp] & 0xFFFF0000u) : __uint_as_float(T.b[pp] << 16);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = fmaf(bv, xg[pp][h][i], fmaf(sc, t[i], acc[i]));
+            }
+        }
+        float *dst = red + ((buf * NB + u) * 8 + wave) * 256;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(4 * q + i) * 16 + r] = acc[i];
+    };
+
+    // 2. after each batch of NB tiles: thread t adds the 8 partials of
+    //    output (n, tile row rr) of batch slots (t >> 8) and (t >> 8) + 2 in
+    //    wave order; n and rr are fixed per thread, so its rows arrive in
+    //    increasing order for the greedy head
+    const int sn = (tid & 255) >> 4, srr = tid & 15, su0 = tid >> 8;
+    const int64_t tb_wg = tb;
+    float best_v = 0.f;
+    int64_t best_m = -1;
+    auto finish = [&](int buf, int64_t t0) {
+#pragma unroll
+        for (int j = 0; j < NB / 2; ++j) {
+            const int u = su0 + 2 * j;
+            const int64_t tile = t0 + u;
+            if (tile < te) {
+                const float *src = red + (buf * NB + u) * 8 * 256 + sn * 16 + srr;
+                float v = src[0];
+#pragma unroll
+                for (int w = 1; w < 8; ++w) v += src[w * 256];
+                const int64_t m = tile * 16 + srr;
+                if (sn < p.nb && m < p.M) {
+                    if (p.stage_out)
+                        out_stage[((tile - tb_wg) * 16 + sn) * 16 + srr] = v;
+                    else if (p.y)
+                        p.y[static_cast<int64_t>(sn) * p.M + m] = v;
+                    if (best_m < 0 || v > best_v) {
+                        best_v = v;
+                        best_m = m;
+                    }
+                }
+            }
+        }
+    };
+
+    // steady state: batches whose code loads (NB - 1 tiles ahead) all lie
+    // in the run, so every load is issued unconditionally
+    int buf = 0;
+    int64_t t0 = 0;
+    for (; t0 + 2 * NB - 1 <= nt; t0 += NB) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            load(ring[(u + NB - 1) % NB], tb + t0 + u + NB - 1);
+            reduce(ring[u], buf, u);
+        }
+        __syncthreads();
+        finish(buf, tb + t0);
+        buf ^= 1;
+    }
+    // drain: fewer than 2 NB - 1 tiles left (uniform conditions)
+    for (; t0 < nt; t0 += NB) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            if (t0 + u < nt) {
+                if (t0 + u + NB - 1 < nt) load(ring[(u + NB - 1) % NB], tb + t0 + u + NB - 1);
+                reduce(ring[u], buf, u);
+            }
+        }
+        __syncthreads();
+        finish(buf, tb + t0);
+        buf ^= 1;
+    }
+
+    if (p.stage_out && p.y) {
+        __syncthreads();
+        const int64_t m0 = tb * 16, rows = min(te * 16, p.M) - m0;
+        for (int n = 0; n < p.nb; ++n)
+            for (int64_t j = tid; j < rows; j += blockDim.x)
+                p.y[static_cast<int64_t>(n) * p.M + m0 + j] = out_stage[((j >> 4) * 16 + n) * 16 + (j & 15)];
+    }
+
+    if (p.ctl != nullptr) {
+        __shared__ unsigned long long wg_key[16];
+        if (tid < 16) wg_key[tid] = 0ull;
+        __syncthreads();
+        uint64_t key = best_m >= 0 ? argmax_key(best_v, static_cast<uint32_t>(best_m)) : 0ull;
+        // the 16 lanes srr = 0..15 of a 16-lane group share n
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) {
+            const uint64_t other = shfl_xor_u64(key, o);
+            key = other > key ? other : key;
+        }
+        if (srr == 0 && sn < p.nb) atomicMax(&wg_key[sn], static_cast<unsigned long long>(key));
+        __syncthreads();
+        greedy_finish_rows<16>(wg_key, p.nb, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x));
+    }
+}
+
+}  // namespace qg

@@ -17,6 +17,7 @@
 #include "gemv1.hpp"
 #include "gemv_b1.hpp"
 #include "gemv_mfma.hpp"
+#include "gemv_mfma16.hpp"
 
 namespace {
 
@@ -161,6 +162,8 @@ constexpr int64_t kB1LongResident = 3;   // workgroups per compute unit at the l
 struct GemvPlan {
     bool gemm;           // small batch run as the prefill product on narrow tiles
     bool mfma;           // small-batch 4-bit kernel on the matrix cores
+    bool mfma16;         // 9..16 rows of the 4-bit format in one pass (K cut across waves)
+    int pairs;           // mfma16: group pairs per wave (K / 1024)
     int passes;          // small-batch kernel: launches of up to 8 activation rows each
     bool lut;            // batch-1 1-bit kernel (table lookup, lanes along rows)
     bool fused;          // split-K combined inside the kernel (per-tile counters);
@@ -194,6 +197,23 @@ bool u4_mfma_ok(int fmt, int64_t K)
            static_cast<int64_t>(qg::gemv_mfma_lds_bytes(K)) + kLdsStaticReserve <= kLdsMax;
 }
 
+// The one-pass kernel for up to 16 rows keeps each wave's share of K (a
+// multiple of 128 inputs) for all 16 rows in registers: K = 1024 or 2048.
+bool u4_mfma16_ok(int fmt, int64_t K)
+{
+    return fmt == QG_U4_G64 && (K == 1024 || K == 2048);
+}
+
+// It takes 9..16 rows (one pass instead of two launches of 8), and 2..8
+// rows when the 8-row kernel (each wave its own run of tiles) would leave
+// compute units without a workgroup: 6144 x 2048 at 2..8 rows 15.2-15.8 ->
+// 7.7-8.8 us; on the 151936 x 2048 head the 8-row kernel stays ~6% ahead.
+bool u4_one_pass(int fmt, int64_t M, int64_t K, int nb)
+{
+    if (nb < 2 || !u4_mfma16_ok(fmt, K)) return false;
+    return nb > 8 || ceil_div(ceil_div(M, 16), qg::kMfmaWaves) < kComputeUnits;
+}
+
 // Whether nb (2..16) activation rows run faster as the prefill product on
 // narrow tiles (weights read once, 16 token rows of matrix-core work) than
 // on the matrix-vector kernels. Estimates in microseconds, fitted to
@@ -202,8 +222,10 @@ bool u4_mfma_ok(int fmt, int64_t K)
 //   prefill, narrow tiles     10 + 96 M K / R, R = 220e6 flop/us (1-bit, on
 //                             128-row tiles with K split four ways per
 //                             compute unit: 280e6)
-//   4-bit matrix-core matvec  per launch of up to 8 rows the weight bytes at
-//                             4.4 TB/s, at least 14
+//   4-bit matrix-core matvec  one pass (K = 1024 or 2048): the weight bytes
+//                             at 3.4 TB/s, at least 8; else per launch of up
+//                             to 8 rows the weight bytes at 4.4 TB/s, at
+//                             least 14
 //   1-bit lookup kernel       8 + nb M K / 14e6
 // and the vector-ALU and lookup kernels lose from 6 rows on matrices wider
 // than tall, whose few rows leave their grids small.
@@ -214,6 +236,7 @@ bool batch_on_gemm(int fmt, int64_t M, int64_t K, int nb)
     const double t_gemm = 10.0 + 96.0 * w / (fmt == QG_B1_G128 ? 280e6 : 220e6);
     if (u4_mfma_ok(fmt, K)) {
         const double bytes = static_cast<double>(M) * (row_bytes(fmt, K) + 4 * (K / 64));
+        if (u4_one_pass(fmt, M, K, nb)) return t_gemm < std::max(8.0, bytes / 3.4e6);
         return t_gemm < static_cast<double>(ceil_div(nb, 8)) * std::max(14.0, bytes / 4.4e6);
     }
     if (M < K && nb >= 6) return true;
@@ -275,6 +298,26 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
         }
         if (argmax) pl.nkeys = static_cast<int>(pl.nsplit > 1 && !pl.fused ? pl.comb_grid : pl.grid_x);
         pl.ws_bytes = (off > kCtlBytes || argmax) ? off : 0;
+        return pl;
+    }
+    if (u4_one_pass(fmt, M, K, nb)) {
+        // 4-bit, one pass over the weights with K cut across the 8 waves of
+        // a workgroup per compute unit, each workgroup a run of 16-row tiles
+        pl.mfma16 = true;
+        pl.pairs = static_cast<int>(K / 1024);
+        const int64_t ntiles = ceil_div(M, 16);
+        pl.grid_x = std::min<int64_t>(kComputeUnits, ntiles);
+        pl.lds_bytes = qg::gemv_mfma16_lds_bytes();
+        const size_t out_bytes = static_cast<size_t>(ceil_div(ntiles, pl.grid_x)) * qg::k16TileOutBytes;
+        pl.fused = static_cast<int64_t>(pl.lds_bytes + out_bytes) + kLdsStaticReserve <= kLdsMax;
+        if (pl.fused) pl.lds_bytes += out_bytes;
+        pl.nsplit = 1;
+        if (argmax) {
+            // per-workgroup greedy keys (16 per workgroup) after the control words
+            pl.nkeys = static_cast<int>(pl.grid_x);
+            pl.part_off = kCtlBytes;
+            pl.ws_bytes = align256(kCtlBytes + static_cast<size_t>(pl.grid_x) * 16 * 8);
+        }
         return pl;
     }
     if (nb >= 2 && u4_mfma_ok(fmt, K)) {
@@ -416,6 +459,33 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
 {
     if (pl.gemm) {
         run_gemm_mfma(fmt, codes, scales, biases, x, y, M, K, nb, ws, s);
+        return;
+    }
+    if (pl.mfma16) {
+        qg::GemvMfmaParams q{};
+        q.codes = static_cast<const uint8_t *>(codes);
+        q.scales = static_cast<const uint16_t *>(scales);
+        q.biases = static_cast<const uint16_t *>(biases);
+        q.x = x;
+        q.y = y;
+        q.ctl = idx ? static_cast<qg::GreedyCtl *>(ws) : nullptr;
+        q.keys = idx ? reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + pl.part_off) : nullptr;
+        q.idx = idx;
+        q.M = M;
+        q.K = K;
+        q.nb = nb;
+        q.stage_out = pl.fused;
+        static const bool lds_set = [] {
+            for (const void *f : {reinterpret_cast<const void *>(qg::gemv_mfma16_u4_kernel<1>),
+                                  reinterpret_cast<const void *>(qg::gemv_mfma16_u4_kernel<2>)})
+                (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                          static_cast<int>(kLdsMax - kLdsStaticReserve));
+            return true;
+        }();
+        (void)lds_set;
+        const dim3 grid(static_cast<unsigned>(pl.grid_x)), block(64 * qg::kMfmaWaves);
+        if (pl.pairs == 1) hipLaunchKernelGGL(qg::gemv_mfma16_u4_kernel<1>, grid, block, pl.lds_bytes, s, q);
+        else hipLaunchKernelGGL(qg::gemv_mfma16_u4_kernel<2>, grid, block, pl.lds_bytes, s, q);
         return;
     }
     if (pl.mfma) {

@@ -322,15 +322,17 @@ def test_zero_codes_give_bias_times_sum(torch, orc):
 
 
 # ---------------------------------------------------------------------------
-# the small-batch 4-bit matrix-core path: 2..8 rows, K a multiple of 512 up
-# to 3072 (16-row tiles, up to several per wave, chunks of 512 inputs);
-# K = 3584 and 9 rows take the vector path and are checked alongside
+# the small-batch 4-bit matrix-core paths: 2..8 rows, K a multiple of 512 up
+# to 3072 (16-row tiles, up to several per wave, chunks of 512 inputs); 9..16
+# rows in one pass for K = 1024 and 2048 (K cut across the waves), in two
+# launches of up to 8 rows for other K; K = 3584 takes the vector path
 # ---------------------------------------------------------------------------
 
 MFMA_SHAPES = [
     (16, 512, 8), (17, 1024, 5), (300, 1536, 2), (40007, 512, 3), (70001, 2048, 8),
     (5000, 3072, 2), (9001, 3072, 7), (1000, 3584, 4), (2049, 2048, 9),
     (70001, 2048, 16), (3000, 3072, 12), (40007, 512, 10),
+    (16, 1024, 9), (1000, 1024, 16), (17, 2048, 13), (70001, 1024, 11), (4097, 2048, 15),
 ]
 
 
@@ -505,7 +507,8 @@ def test_drawn_shapes_all_entry_points(torch, orc, fmt):
 # ---------------------------------------------------------------------------
 
 # the configurations, and the measured cases of the 8-bit group-64 format
-MEASURED = synth.CASES + [c for c in synth.NEXT_CASES if c.fmt == synth.I8_G64]
+MEASURED = synth.CASES + [c for c in synth.NEXT_CASES
+                          if c.fmt == synth.I8_G64 or c.name == "n4_u4_head_151936x2048_b16"]
 GEMV_CASES = [c for c in MEASURED if c.op != "gemm"]
 GEMM_CASES = [c for c in MEASURED if c.op == "gemm"]
 
