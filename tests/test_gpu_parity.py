@@ -333,6 +333,8 @@ MFMA_SHAPES = [
     (5000, 3072, 2), (9001, 3072, 7), (1000, 3584, 4), (2049, 2048, 9),
     (70001, 2048, 16), (3000, 3072, 12), (40007, 512, 10),
     (16, 1024, 9), (1000, 1024, 16), (17, 2048, 13), (70001, 1024, 11), (4097, 2048, 15),
+    # more 16-row tiles per workgroup than LDS can stage: outputs stored directly
+    (400003, 1024, 12),
 ]
 
 
