@@ -1,9 +1,11 @@
-// gemv_mfma16.hpp -- 9..16 activation rows of the 4-bit group-64 format in
-// one pass over the weights, on the gfx950 matrix cores.
+// gemv_mfma16.hpp -- up to 16 activation rows of the 4-bit group-64 format
+// in one pass over the weights, on the gfx950 matrix cores.
 //
 // The 8-row kernel (gemv_mfma.hpp) stages the activation pieces of all K in
 // LDS; 16 rows of them would not fit, so 9..16 rows there take two launches
-// that each read the weights. Here K is cut across the workgroup's 8 waves
+// that each read the weights, and its waves each take their own tiles, which
+// leaves compute units idle when M is small. Here K is cut across the
+// workgroup's 8 waves
 // instead: wave w owns groups 2 PAIRS w .. 2 PAIRS (w + 1) - 1 (K = 1024
 // PAIRS) and keeps the exact bf16 pieces of all 16 activation rows for
 // those inputs in registers for the whole kernel; all 8 waves stream the
