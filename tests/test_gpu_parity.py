@@ -335,6 +335,8 @@ MFMA_SHAPES = [
     (16, 1024, 9), (1000, 1024, 16), (17, 2048, 13), (70001, 1024, 11), (4097, 2048, 15),
     # more 16-row tiles per workgroup than LDS can stage: outputs stored directly
     (400003, 1024, 12),
+    # a single weight row (every tile row but the first clamps to it)
+    (1, 2048, 16), (1, 1024, 3), (5, 2048, 2),
 ]
 
 
