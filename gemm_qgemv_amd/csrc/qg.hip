@@ -701,9 +701,51 @@ size_t gemm_mfma_workspace(int fmt, int64_t M, int64_t K, int64_t N)
     return nsplit > 1 ? align256(kCtlBytes + static_cast<size_t>(nsplit) * N * M * 4) : 0;
 }
 
+// 17..48 rows of the 4-bit format at K = 1024 or 2048 as launches of up to
+// 16 rows each (the one-pass matrix-vector kernel, or the batch-1 kernel for
+// a last single row), where reading the weights once per 16 rows costs less
+// than the prefill kernel's matrix-core work on rows padded to a multiple
+// of 32 (an estimate fitted to the 151936 x 2048 head: 10 us + 6 M K
+// round_up(N, 32) flop at 560 TFLOP/s, against ~51.5 us per launch of 16
+// rows). Returns the number of launches, or 0 for the prefill kernel.
+int u4_row_launches(int fmt, int64_t M, int64_t K, int64_t N)
+{
+    if (N <= kGemmViaGemv || N > 48 || !u4_mfma16_ok(fmt, K)) return 0;
+    const int n = static_cast<int>(ceil_div(N, 16));
+    const double w = static_cast<double>(M) * static_cast<double>(K);
+    const double bytes = static_cast<double>(M) * (row_bytes(fmt, K) + 4 * (K / 64));
+    const double t_gemm = 10.0 + 6.0 * w * static_cast<double>(round_up(N, 32)) / 560e6;
+    return n * std::max(8.0, bytes / 3.4e6) < t_gemm ? n : 0;
+}
+
+// Workspace of those launches: the largest of their plans (they run in
+// stream order, and each leaves the control words at zero).
+size_t row_launches_workspace(int fmt, int64_t M, int64_t K, int64_t N, bool argmax)
+{
+    size_t ws = 0;
+    for (int64_t r0 = 0; r0 < N; r0 += kGemmViaGemv) {
+        const int nb = static_cast<int>(std::min<int64_t>(kGemmViaGemv, N - r0));
+        ws = std::max(ws, plan_gemv(fmt, M, K, nb, argmax).ws_bytes);
+    }
+    return ws;
+}
+
+void run_row_launches(int fmt, const void *codes, const void *scales, const void *biases,
+                      const float *x, float *y, int32_t *idx, int64_t M, int64_t K, int64_t N,
+                      void *ws, hipStream_t s)
+{
+    for (int64_t r0 = 0; r0 < N; r0 += kGemmViaGemv) {
+        const int nb = static_cast<int>(std::min<int64_t>(kGemmViaGemv, N - r0));
+        const GemvPlan pl = plan_gemv(fmt, M, K, nb, idx != nullptr);
+        run_gemv(fmt, pl, codes, scales, biases, x + r0 * K, y ? y + r0 * M : nullptr,
+                 idx ? idx + r0 : nullptr, M, K, nb, ws, s);
+    }
+}
+
 size_t gemm_workspace(int fmt, int64_t M, int64_t K, int64_t N)
 {
     if (N <= kGemmViaGemv) return plan_gemv(fmt, M, K, static_cast<int>(N), false).ws_bytes;
+    if (u4_row_launches(fmt, M, K, N)) return row_launches_workspace(fmt, M, K, N, false);
     return gemm_mfma_workspace(fmt, M, K, N);
 }
 
@@ -824,6 +866,10 @@ void run_gemm(int fmt, const void *codes, const void *scales, const void *biases
         run_gemv(fmt, pl, codes, scales, biases, x, y, nullptr, M, K, nb, ws, s);
         return;
     }
+    if (u4_row_launches(fmt, M, K, N)) {
+        run_row_launches(fmt, codes, scales, biases, x, y, nullptr, M, K, N, ws, s);
+        return;
+    }
     run_gemm_mfma(fmt, codes, scales, biases, x, y, M, K, N, ws, s);
 }
 
@@ -841,8 +887,9 @@ int64_t wide_argmax_keys(int fmt, int64_t M, int64_t N)
     return ceil_div(M, bm) * (4 / wn);
 }
 
-size_t wide_argmax_workspace(int fmt, int64_t M, int64_t N)
+size_t wide_argmax_workspace(int fmt, int64_t M, int64_t K, int64_t N)
 {
+    if (u4_row_launches(fmt, M, K, N)) return row_launches_workspace(fmt, M, K, N, true);
     return align256(kCtlBytes + static_cast<size_t>(N) * wide_argmax_keys(fmt, M, N) * 8);
 }
 
@@ -854,7 +901,7 @@ int wide_argmax_entry(int fmt, const void *codes, const void *scales, const void
     if (st != QG_OK) return st;
     if (N < 1 || N > QG_MAX_ARGMAX_BATCH || K > qg::kGemmMaxK) return QG_ERR_SHAPE;
     if ((y && !aligned(y, kAlign)) || !aligned(idx, 4)) return QG_ERR_ALIGN;
-    const size_t need = wide_argmax_workspace(fmt, M, N);
+    const size_t need = wide_argmax_workspace(fmt, M, K, N);
     if (!ws || ws_bytes < need) return QG_ERR_WORKSPACE;
     if (!aligned(ws, kAlign)) return QG_ERR_ALIGN;
     Range all[8];
@@ -872,6 +919,10 @@ int wide_argmax_entry(int fmt, const void *codes, const void *scales, const void
     if (st != QG_OK) return st;
 
     (void)hipGetLastError();
+    if (u4_row_launches(fmt, M, K, N)) {
+        run_row_launches(fmt, codes, scales, biases, x, y, idx, M, K, N, ws, stream);
+        return launch_status();
+    }
     auto *keys = reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + kCtlBytes);
     launch_gemm(fmt, codes, scales, biases, x, y, keys, M, K, N, stream);
     hipLaunchKernelGGL(qg::argmax_keys_kernel, dim3(static_cast<unsigned>(N)), dim3(256), 0, stream,
@@ -993,7 +1044,7 @@ size_t qg_workspace_bytes(int op, int fmt, int64_t M, int64_t K, int64_t rows)
     if (!known_format(fmt)) return 0;
     if (M < 1 || M > kMaxM || K < 1 || K > kMaxK || K % k_unit(fmt) != 0) return 0;
     if (op == QG_OP_GEMV_ARGMAX && rows > QG_MAX_GEMV_BATCH && rows <= QG_MAX_ARGMAX_BATCH)
-        return K <= qg::kGemmMaxK ? wide_argmax_workspace(fmt, M, rows) : 0;
+        return K <= qg::kGemmMaxK ? wide_argmax_workspace(fmt, M, K, rows) : 0;
     if (op == QG_OP_GEMV || op == QG_OP_GEMV_ARGMAX) {
         if (rows < 1 || rows > QG_MAX_GEMV_BATCH) return 0;
         return plan_gemv(fmt, M, K, static_cast<int>(rows), op == QG_OP_GEMV_ARGMAX).ws_bytes;

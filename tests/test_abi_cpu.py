@@ -128,16 +128,23 @@ def test_wide_greedy_head_checks():
     hdr = open(HEADER).read()
     assert f"#define QG_MAX_ARGMAX_BATCH {q.QG_MAX_ARGMAX_BATCH}" in hdr
     M, K = 151936, 2048
-    for n in (17, 64, 128, q.QG_MAX_ARGMAX_BATCH):
+    for n in (64, 128, q.QG_MAX_ARGMAX_BATCH):
         need = q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_U4_G64, M, K, n)
         assert need >= q.QG_WS_CONTROL_BYTES + n * (M // 64) * 8
+    # 17..48 rows of this 4-bit head run as launches of up to 16 rows of the
+    # matrix-vector kernels: control words plus 16 keys per workgroup
+    for n in (17, 33, 48):
+        need = q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_U4_G64, M, K, n)
+        assert need >= q.QG_WS_CONTROL_BYTES + 16 * 8
     assert q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_U4_G64, M, K,
                                 q.QG_MAX_ARGMAX_BATCH + 1) == 0
     codes, scales, biases = A, A + (1 << 28), A + (1 << 29)
     x, idx, ws = A + (1 << 30), A + (1 << 32), A + (1 << 33)
+    for n in (17, 64):
+        need = q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_U4_G64, M, K, n)
+        assert _err(q.qgemv_argmax, q.QG_U4_G64, codes, scales, biases, x, None, idx, M, K, n,
+                    ws=ws, ws_bytes=need - 1) == q.QG_ERR_WORKSPACE
     need = q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_U4_G64, M, K, 64)
-    assert _err(q.qgemv_argmax, q.QG_U4_G64, codes, scales, biases, x, None, idx, M, K, 64,
-                ws=ws, ws_bytes=need - 1) == q.QG_ERR_WORKSPACE
     assert _err(q.qgemv_argmax, q.QG_U4_G64, codes, scales, biases, x, None, idx, M, K,
                 q.QG_MAX_ARGMAX_BATCH + 1, ws=ws, ws_bytes=1 << 30) == q.QG_ERR_SHAPE
     # idx inside the keys area of the workspace

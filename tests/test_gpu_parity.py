@@ -227,6 +227,9 @@ def test_exact_arithmetic_prefill_large_grid(torch, orc, M, K, N):
     (synth.I8_ROW, 66001, 256, 24), (synth.U4_G64, 70001, 512, 20), (synth.B1_G128, 66000, 256, 32),
     (synth.I8_G64, 66001, 192, 29), (synth.U4_G64, 3000, 2048, 32), (synth.I8_ROW, 2049, 3584, 25),
     (synth.B1_G128, 700, 5120, 21), (synth.I8_G64, 1000, 3584, 18),
+    # 4-bit rows run as launches of 16 on the one-pass kernel (the last one
+    # a single row on the batch-1 kernel, or 8 rows on the 8-row kernel)
+    (synth.U4_G64, 30001, 2048, 17), (synth.U4_G64, 40000, 1024, 40),
 ])
 def test_random_prefill_small(torch, orc, fmt, M, K, N):
     say(f"random prefill fmt={fmt} M={M} K={K} N={N}")
@@ -422,6 +425,7 @@ def gpu_greedy(torch, w, x, logits=True):
     (synth.U4_G64, 30001, 2048, 16), (synth.U4_G64, 9000, 1024, 11),
     (synth.U4_G64, 30001, 2048, 24), (synth.I8_ROW, 70001, 256, 32), (synth.I8_G64, 70001, 192, 19),
     (synth.B1_G128, 66001, 256, 30),
+    (synth.U4_G64, 40000, 1024, 33), (synth.U4_G64, 60000, 2048, 48),
 ])
 def test_greedy_head_with_and_without_logits(torch, orc, fmt, M, K, N):
     say(f"greedy fmt={fmt} M={M} K={K} N={N}")
