@@ -163,7 +163,10 @@ int qgemv(int fmt, const void *codes, const void *scales, const void *biases,
  *   output has fewer tiles than the chip has compute units, since K is then
  *   cut into pieces whose float32 partial products are added in a fixed
  *   order by a second launch (the result does not depend on the stream or
- *   the schedule).
+ *   the schedule). 17..48 rows of the 4-bit format at K = 1024 or 2048 may
+ *   run as launches of up to QG_MAX_GEMV_BATCH rows of the matrix-vector
+ *   product where that reads the weights for less than the prefill kernel's
+ *   padded work costs.
  */
 int qgemm(int fmt, const void *codes, const void *scales, const void *biases,
           const float *x, float *y, int64_t M, int64_t K, int64_t N,
@@ -185,9 +188,11 @@ int qgemm(int fmt, const void *codes, const void *scales, const void *biases,
  *   1 <= batch <= QG_MAX_ARGMAX_BATCH; other limits as qgemv, and K <= 2^21
  *   above QG_MAX_GEMV_BATCH rows. Up to
  *   QG_MAX_GEMV_BATCH rows use the matrix-vector kernels; more rows use the
- *   prefill kernels, which keep one (value, index) key per 64- or 128-row
- *   tile and token row in the workspace and reduce them in a second launch
- *   (the per-tile reduction of the page above). Needs a workspace.
+ *   prefill kernels, which keep one (value, index) key per tile (or part of
+ *   one) and token row in the workspace and reduce them in a second launch
+ *   (the per-tile reduction of the page above), except 17..48 rows of the
+ *   4-bit format at K = 1024 or 2048, which may run as launches of up to
+ *   QG_MAX_GEMV_BATCH rows on the matrix-vector kernels. Needs a workspace.
  */
 int qgemv_argmax(int fmt, const void *codes, const void *scales,
                  const void *biases, const float *x, float *logits,
