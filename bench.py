@@ -4,9 +4,8 @@
 Default workload: the fused greedy output head -- 4-bit group-64 affine
 matrix-vector product of the 151936x2048 tied output matrix at batch 1,
 returning the float32 logits and the argmax index (one step = one call).
-This is the configuration the headline weight-bandwidth figure is quoted on:
-the only matrix-vector product large enough (175 MB) to get past launch and
-ramp latency. Weights are cache-cold: every step reads a different copy, from
+It is the headline weight-bandwidth workload: the only matrix-vector
+product large enough (175 MB) to get past launch and ramp latency. Weights are cache-cold: every step reads a different copy, from
 a rotation of distinct copies that together exceed 512 MiB, so each read
 comes from HBM rather than from the L2 or the 256 MB Infinity Cache.
 

@@ -166,7 +166,9 @@ def draw_embed_stress(M: int, K: int, rng: np.random.Generator) -> QWeights:
 
 
 # ---------------------------------------------------------------------------
-# The workloads: five configurations restated as thirteen concrete cases.
+# The measured workloads: thirteen concrete cases in five families (8-bit
+# 1024x1024 matvec, 4-bit 2B-model matvecs, the 151936x2048 greedy head at 1
+# and 8 rows, 8-bit prefill, 1-bit matvec and prefill).
 # ---------------------------------------------------------------------------
 
 @dataclasses.dataclass(frozen=True)
@@ -178,7 +180,7 @@ class Case:
     M: int
     K: int
     rows: int        # batch (gemv) or tokens N (gemm)
-    case: int        # seed component: configuration index
+    case: int        # seed component: workload family
     variant: int     # seed component: variant within it
     x_variant: int | None = None  # draw x from another variant's stream
 
@@ -206,7 +208,7 @@ CASES = [
     Case("c4c_b1_gemm_17408x5120_n512", "gemm", B1_G128, 17408, 5120, 512, 4, 2),
     Case("c4d_b1_gemm_5120x17408_n512", "gemm", B1_G128, 5120, 17408, 512, 4, 3),
 ]
-# Measurement cases beyond the configurations: the 4-bit prefill
+# Measurement cases beyond those thirteen: the 4-bit prefill
 # at the 4-bit matvec shapes, with a 2048-token prompt; the greedy head at 64
 # and 128 rows, with logits and without ("greedy": qgemv_argmax, logits NULL);
 # the embedding rows of a 2048-token prompt gathered from the same (tied)

@@ -511,10 +511,11 @@ def test_drawn_shapes_all_entry_points(torch, orc, fmt):
 
 
 # ---------------------------------------------------------------------------
-# the configurations at full size
+# the thirteen measured workloads at full size
 # ---------------------------------------------------------------------------
 
-# the configurations, and the measured cases of the 8-bit group-64 format
+# those workloads, the measured cases of the 8-bit group-64 format and the
+# 16-row head
 MEASURED = synth.CASES + [c for c in synth.NEXT_CASES
                           if c.fmt == synth.I8_G64 or c.name == "n4_u4_head_151936x2048_b16"]
 GEMV_CASES = [c for c in MEASURED if c.op != "gemm"]
