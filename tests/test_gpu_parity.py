@@ -477,26 +477,41 @@ def test_wide_greedy_head_ties(N):
 ROWS_DRAWN = [1, 2, 3, 4, 5, 6, 7, 8, 9, 11, 12, 13, 15, 16, 17, 19, 24, 31, 32, 33, 47, 64, 65, 100, 129]
 
 
-def drawn_shapes(fmt, count, seed):
+def drawn_shapes(fmt, count, seed, budget=12e6, min_m=1.0, max_m=40000.0, ks=None):
     """(M, K, N) with M and K log-uniform (K a multiple of the format's
-    unit, up to 8192) and N from ROWS_DRAWN, at most 12e6 multiply-adds."""
+    unit, up to 8192, or drawn from `ks`) and N from ROWS_DRAWN, at most
+    `budget` multiply-adds."""
     rng = np.random.default_rng([seed, fmt])
     unit = synth.K_UNIT[fmt]
     shapes = []
     while len(shapes) < count:
-        M = int(np.exp(rng.uniform(0.0, np.log(40000.0))))
-        K = unit * max(1, int(round(np.exp(rng.uniform(0.0, np.log(8192 / unit))))))
+        M = int(np.exp(rng.uniform(np.log(min_m), np.log(max_m))))
+        if ks is None:
+            K = unit * max(1, int(round(np.exp(rng.uniform(0.0, np.log(8192 / unit))))))
+        else:
+            K = int(rng.choice(ks))
         N = int(rng.choice(ROWS_DRAWN))
-        if M * K * N <= 12e6:
+        if M * K * N <= budget:
             shapes.append((M, K, N))
     return shapes
 
 
+# the drawn sets: small shapes of any K, and larger ones at the K values
+# where the host has the most kernel choices (the one-pass 4-bit kernel at
+# K = 1024 and 2048, the batch-8 kernel up to 3072, long-K 1-bit tables)
+DRAWN_SETS = {
+    "small": dict(count=32, seed=77),
+    "large": dict(count=12, seed=78, budget=2.5e8, min_m=2000.0, max_m=200000.0,
+                  ks=[512, 1024, 2048, 3072, 4096, 5120]),
+}
+
+
 @pytest.mark.parametrize("fmt", [synth.I8_ROW, synth.U4_G64, synth.B1_G128, synth.I8_G64])
-def test_drawn_shapes_all_entry_points(torch, orc, fmt):
-    for i, (M, K, N) in enumerate(drawn_shapes(fmt, 32, 77)):
-        say(f"drawn fmt={fmt} #{i} M={M} K={K} N={N}")
-        rng = synth.rng_for(700 + fmt, i)
+@pytest.mark.parametrize("drawn", sorted(DRAWN_SETS))
+def test_drawn_shapes_all_entry_points(torch, orc, fmt, drawn):
+    for i, (M, K, N) in enumerate(drawn_shapes(fmt, **DRAWN_SETS[drawn])):
+        say(f"drawn {drawn} fmt={fmt} #{i} M={M} K={K} N={N}")
+        rng = synth.rng_for(700 + fmt + (0 if drawn == "small" else 10), i)
         w = synth.draw_weights(fmt, M, K, rng)
         x = synth.draw_x(N, K, rng)
         ref, a = orc.qgemv(fmt, w.codes, w.scales, w.biases, x, M, K)
