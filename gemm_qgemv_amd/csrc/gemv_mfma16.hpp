@@ -1,5 +1,6 @@
-// gemv_mfma16.hpp -- up to 16 activation rows of the 4-bit group-64 format
-// in one pass over the weights, on the gfx950 matrix cores.
+// gemv_mfma16.hpp -- up to 16 activation rows of the 4-bit group-64 format,
+// and of the two 8-bit formats, in one pass over the weights, on the gfx950
+// matrix cores.
 //
 // The 8-row kernel (gemv_mfma.hpp) stages the activation pieces of all K in
 // LDS; 16 rows of them would not fit, so 9..16 rows there take two launches
@@ -24,6 +25,12 @@
 //     k = 64 g + 32 (q & 1) + 16 (q >> 1) + 8 s + {0, 2, 4, 6, 1, 3, 5, 7}.
 // The same lane holds activation row r at those inputs. D: lane (r, q) holds
 // weight row r of the tile for activation rows 4 q .. 4 q + 3.
+//
+// 8-bit codes (exact in bf16) use the same inputs in natural order: lane
+// (r, q) loads the 16 bytes 64 g + 32 (q & 1) + 16 (q >> 1) of group g and
+// takes its first 8 at k-step 0, the other 8 at k-step 1. The per-row scale
+// multiplies the finished sum; the per-group scales (8-bit group-64) fold
+// each group's sum as for the 4-bit format; there is no bias term.
 #pragma once
 
 #include "gemv_mfma.hpp"
@@ -38,19 +45,24 @@ constexpr int k16TileOutBytes = 16 * 16 * 4;
 
 __host__ __device__ constexpr size_t gemv_mfma16_lds_bytes() { return k16RedFloats * 4; }
 
-template <int PAIRS>
-__global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_u4_kernel(GemvMfmaParams p)
+// GW: groups of 64 inputs per wave (K = 512 GW).
+template <int FMT, int GW>
+__global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParams p)
 {
     static_assert(kMfmaWaves == 8, "K is cut into 8 slices");
+    static_assert(FMT == FMT_U4_G64 || FMT == FMT_I8_ROW || FMT == FMT_I8_G64, "4-bit or 8-bit");
+    static_assert(GW % 2 == 0, "whole pairs of groups");
+    constexpr bool U4 = FMT == FMT_U4_G64;
+    constexpr int PAIRS = GW / 2;
     extern __shared__ float4 lds_f4[];
     float *red = reinterpret_cast<float *>(lds_f4);
     float *out_stage = red + k16RedFloats;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, q = lane >> 4;
-    const int64_t row_bytes = p.K / 2;
+    const int64_t row_bytes = U4 ? p.K / 2 : p.K;
     const int64_t G = p.K / 64;
-    const int gw = wave * 2 * PAIRS;   // this wave's first group
+    const int gw = wave * GW;   // this wave's first group
 
     // the workgroup's run of 16-row tiles; every wave takes every tile
     const int64_t ntiles = (p.M + 15) / 16;
@@ -61,47 +73,56 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_u4_kernel(GemvMfmaPa
     // 1a. this lane's activations (row r, its inputs of the wave's groups),
     //     requested before the first code loads (the memory counters count
     //     in order)
-    float4 xa[PAIRS][2][2][2];
+    float4 xa[GW][2][2];
 #pragma unroll
-    for (int pp = 0; pp < PAIRS; ++pp)
+    for (int gi = 0; gi < GW; ++gi)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int64_t k0 = 64 * (gw + 2 * pp + h) + 32 * (q & 1) + 16 * (q >> 1) + 8 * s;
-                xa[pp][h][s][0] = xa[pp][h][s][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (r < p.nb) {
-                    const float4 *src = reinterpret_cast<const float4 *>(p.x + r * p.K + k0);
-                    xa[pp][h][s][0] = src[0];
-                    xa[pp][h][s][1] = src[1];
-                }
+        for (int s = 0; s < 2; ++s) {
+            const int64_t k0 = 64 * (gw + gi) + 32 * (q & 1) + 16 * (q >> 1) + 8 * s;
+            xa[gi][s][0] = xa[gi][s][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (r < p.nb) {
+                const float4 *src = reinterpret_cast<const float4 *>(p.x + r * p.K + k0);
+                xa[gi][s][0] = src[0];
+                xa[gi][s][1] = src[1];
             }
+        }
 
     // code ring: tile t's codes (PAIRS x 16 bytes), scales and biases of
     // this lane's weight row for the wave's groups (rows past M read row
     // M - 1; their outputs are not written)
+    // 4-bit: one 16-byte load per pair of groups, bf16 scale and bias pairs;
+    // 8-bit: one per group, fp32 group scales (group-64 format)
+    constexpr int NC = U4 ? PAIRS : GW;
+    constexpr int NS = FMT == FMT_I8_ROW ? 1 : U4 ? PAIRS : GW;
     struct Tile16 {
-        uint4 c[PAIRS];
-        uint32_t s[PAIRS], b[PAIRS];
+        uint4 c[NC];
+        uint32_t s[NS], b[U4 ? PAIRS : 1];
     };
     auto load = [&](Tile16 &T, int64_t t) {
         const int64_t m = min(t * 16 + r, p.M - 1);
-        const uint8_t *c = p.codes + m * row_bytes + 32 * gw + 16 * q;
+        const uint8_t *c = p.codes + m * row_bytes + (U4 ? 32 * gw + 16 * q
+                                                          : 64 * gw + 32 * (q & 1) + 16 * (q >> 1));
 #pragma unroll
-        for (int pp = 0; pp < PAIRS; ++pp) {
+        for (int j = 0; j < NC; ++j) {
 #if QG_MFMA_NT
-            const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(c + 64 * pp));
-            T.c[pp] = make_uint4(v.x, v.y, v.z, v.w);
+            const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(c + 64 * j));
+            T.c[j] = make_uint4(v.x, v.y, v.z, v.w);
 #else
-            T.c[pp] = *reinterpret_cast<const uint4 *>(c + 64 * pp);
+            T.c[j] = *reinterpret_cast<const uint4 *>(c + 64 * j);
 #endif
         }
-        const uint32_t *sc = reinterpret_cast<const uint32_t *>(p.scales + m * G + gw);
-        const uint32_t *bi = reinterpret_cast<const uint32_t *>(p.biases + m * G + gw);
+        if constexpr (U4) {
+            const uint32_t *sc = reinterpret_cast<const uint32_t *>(p.scales + m * G + gw);
+            const uint32_t *bi = reinterpret_cast<const uint32_t *>(p.biases + m * G + gw);
 #pragma unroll
-        for (int pp = 0; pp < PAIRS; ++pp) {
-            T.s[pp] = sc[pp];
-            T.b[pp] = bi[pp];
+            for (int pp = 0; pp < PAIRS; ++pp) {
+                T.s[pp] = sc[pp];
+                T.b[pp] = bi[pp];
+            }
+        } else if constexpr (FMT == FMT_I8_G64) {
+            const uint32_t *sc = reinterpret_cast<const uint32_t *>(p.scales) + m * G + gw;
+#pragma unroll
+            for (int gi = 0; gi < GW; ++gi) T.s[gi] = sc[gi];
         }
     };
     constexpr int NB = k16Tiles;
@@ -113,57 +134,88 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_u4_kernel(GemvMfmaPa
     // 1b. exact three-way split into operand pieces; the group sums
     //     X[n][g] of the activations for the bias term, gathered to the
     //     lanes that hold D rows n = 4 q .. 4 q + 3
-    bf16x8_t at[PAIRS][2][2][3];
-    float xg[PAIRS][2][4];
+    bf16x8_t at[GW][2][3];
+    float xg[U4 ? GW : 1][4];
 #pragma unroll
-    for (int pp = 0; pp < PAIRS; ++pp)
+    for (int gi = 0; gi < GW; ++gi) {
+        float sum = 0.f;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float sum = 0.f;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const float4 a = xa[pp][h][s][0], b = xa[pp][h][s][1];
-                sum += ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
-                const float v[8] = {a.x, a.z, b.x, b.z, a.y, a.w, b.y, b.w};
-                uint32_t hi[4], md[4], lo[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) split3_pair(v[2 * j], v[2 * j + 1], hi[j], md[j], lo[j]);
-                at[pp][h][s][0] = __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
-                at[pp][h][s][1] = __builtin_bit_cast(bf16x8_t, make_uint4(md[0], md[1], md[2], md[3]));
-                at[pp][h][s][2] = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+        for (int s = 0; s < 2; ++s) {
+            const float4 a = xa[gi][s][0], b = xa[gi][s][1];
+            // 4-bit operand order k = 0, 2, 4, 6, 1, 3, 5, 7; 8-bit natural
+            float v[8];
+            if constexpr (U4) {
+                v[0] = a.x; v[1] = a.z; v[2] = b.x; v[3] = b.z;
+                v[4] = a.y; v[5] = a.w; v[6] = b.y; v[7] = b.w;
+            } else {
+                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+                v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
             }
+            uint32_t hi[4], md[4], lo[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) split3_pair(v[2 * j], v[2 * j + 1], hi[j], md[j], lo[j]);
+            at[gi][s][0] = __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+            at[gi][s][1] = __builtin_bit_cast(bf16x8_t, make_uint4(md[0], md[1], md[2], md[3]));
+            at[gi][s][2] = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+            if constexpr (U4) sum += ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+        }
+        if constexpr (U4) {
             sum += __shfl_xor(sum, 16);
             sum += __shfl_xor(sum, 32);   // X[r][g] in every lane of row r
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xg[pp][h][i] = __shfl(sum, 4 * q + i);
+            for (int i = 0; i < 4; ++i) xg[gi][i] = __shfl(sum, 4 * q + i);
         }
+    }
 
     auto mfma = [](bf16x8_t a, bf16x8_t b, floatx4_t c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     };
     // one tile's partial product over the wave's groups, into LDS slot u of
     // buffer buf
+    auto group = [&](int gi, bf16x8_t w0, bf16x8_t w1) {
+        floatx4_t t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int f = 0; f < 3; ++f) t = mfma(at[gi][0][f], w0, t);
+#pragma unroll
+        for (int f = 0; f < 3; ++f) t = mfma(at[gi][1][f], w1, t);
+        return t;
+    };
     auto reduce = [&](const Tile16 &T, int buf, int u) {
         floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (U4) {
 #pragma unroll
-        for (int pp = 0; pp < PAIRS; ++pp) {
-            const auto s0 = __builtin_amdgcn_permlane32_swap(T.c[pp].x, T.c[pp].z, false, false);
-            const auto s1 = __builtin_amdgcn_permlane32_swap(T.c[pp].y, T.c[pp].w, false, false);
-            const uint32_t dw[2][2] = {{s0[0], s1[0]}, {s0[1], s1[1]}};
+            for (int pp = 0; pp < PAIRS; ++pp) {
+                const auto s0 = __builtin_amdgcn_permlane32_swap(T.c[pp].x, T.c[pp].z, false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(T.c[pp].y, T.c[pp].w, false, false);
+                const uint32_t dw[2][2] = {{s0[0], s1[0]}, {s0[1], s1[1]}};
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bf16x8_t w0 = nibbles_to_bf16(dw[h][0]), w1 = nibbles_to_bf16(dw[h][1]);
-                floatx4_t t = {0.f, 0.f, 0.f, 0.f};
-                t = mfma(at[pp][h][0][0], w0, t);
-                t = mfma(at[pp][h][0][1], w0, t);
-                t = mfma(at[pp][h][0][2], w0, t);
-                t = mfma(at[pp][h][1][0], w1, t);
-                t = mfma(at[pp][h][1][1], w1, t);
-                t = mfma(at[pp][h][1][2], w1, t);
-                const float sc = h ? __uint_as_float(T.s[pp] & 0xFFFF0000u) : __uint_as_float(T.s[pp] << 16);
-                const float bv = h ? __uint_as_float(T.b[pp] & 0xFFFF0000u) : __uint_as_float(T.b[pp] << 16);
+                for (int h = 0; h < 2; ++h) {
+                    const floatx4_t t = group(2 * pp + h, nibbles_to_bf16(dw[h][0]), nibbles_to_bf16(dw[h][1]));
+                    const float sc = h ? __uint_as_float(T.s[pp] & 0xFFFF0000u) : __uint_as_float(T.s[pp] << 16);
+                    const float bv = h ? __uint_as_float(T.b[pp] & 0xFFFF0000u) : __uint_as_float(T.b[pp] << 16);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = fmaf(bv, xg[pp][h][i], fmaf(sc, t[i], acc[i]));
+                    for (int i = 0; i < 4; ++i) acc[i] = fmaf(bv, xg[2 * pp + h][i], fmaf(sc, t[i], acc[i]));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int gi = 0; gi < GW; ++gi) {
+                const uint4 c = T.c[gi];   // bytes 0..7: k-step 0, 8..15: k-step 1
+                const bf16x8_t w0 = __builtin_bit_cast(
+                    bf16x8_t, make_uint4(i8pair_to_bf16x2(c.x, 0), i8pair_to_bf16x2(c.x, 2),
+                                         i8pair_to_bf16x2(c.y, 0), i8pair_to_bf16x2(c.y, 2)));
+                const bf16x8_t w1 = __builtin_bit_cast(
+                    bf16x8_t, make_uint4(i8pair_to_bf16x2(c.z, 0), i8pair_to_bf16x2(c.z, 2),
+                                         i8pair_to_bf16x2(c.w, 0), i8pair_to_bf16x2(c.w, 2)));
+                const floatx4_t t = group(gi, w0, w1);
+                if constexpr (FMT == FMT_I8_G64) {
+                    const float sc = __uint_as_float(T.s[gi]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, t[i], acc[i]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[i] += t[i];
+                }
             }
         }
         float *dst = red + ((buf * NB + u) * 8 + wave) * 256;
@@ -191,6 +243,7 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_u4_kernel(GemvMfmaPa
                 for (int w = 1; w < 8; ++w) v += src[w * 256];
                 const int64_t m = tile * 16 + srr;
                 if (sn < p.nb && m < p.M) {
+                    if constexpr (FMT == FMT_I8_ROW) v *= reinterpret_cast<const float *>(p.scales)[m];
                     if (p.stage_out)
                         out_stage[((tile - tb_wg) * 16 + sn) * 16 + srr] = v;
                     else if (p.y)

@@ -163,7 +163,7 @@ struct GemvPlan {
     bool gemm;           // small batch run as the prefill product on narrow tiles
     bool mfma;           // small-batch 4-bit kernel on the matrix cores
     bool mfma16;         // 9..16 rows of the 4-bit format in one pass (K cut across waves)
-    int pairs;           // mfma16: group pairs per wave (K / 1024)
+    int gw;              // mfma16: groups of 64 inputs per wave (K / 512)
     int passes;          // small-batch kernel: launches of up to 8 activation rows each
     bool lut;            // batch-1 1-bit kernel (table lookup, lanes along rows)
     bool fused;          // split-K combined inside the kernel (per-tile counters);
@@ -198,19 +198,24 @@ bool u4_mfma_ok(int fmt, int64_t K)
 }
 
 // The one-pass kernel for up to 16 rows keeps each wave's share of K (a
-// multiple of 128 inputs) for all 16 rows in registers: K = 1024 or 2048.
-bool u4_mfma16_ok(int fmt, int64_t K)
+// multiple of 128 inputs) for all 16 rows in registers: K = 1024 or 2048,
+// 4-bit and both 8-bit formats.
+bool mfma16_ok(int fmt, int64_t K)
 {
-    return fmt == QG_U4_G64 && (K == 1024 || K == 2048);
+    return (fmt == QG_U4_G64 || fmt == QG_I8_ROW || fmt == QG_I8_G64) && (K == 1024 || K == 2048);
 }
 
-// It takes 9..16 rows (one pass instead of two launches of 8), and 2..8
-// rows when the 8-row kernel (each wave its own run of tiles) would leave
-// compute units without a workgroup: 6144 x 2048 at 2..8 rows 15.2-15.8 ->
-// 7.7-8.8 us; on the 151936 x 2048 head the 8-row kernel stays ~6% ahead.
-bool u4_one_pass(int fmt, int64_t M, int64_t K, int nb)
+// 4-bit: it takes 9..16 rows (one pass instead of two launches of 8), and
+// 2..8 rows when the 8-row kernel (each wave its own run of tiles) would
+// leave compute units without a workgroup: 6144 x 2048 at 2..8 rows
+// 15.2-15.8 -> 7.7-8.8 us; on the 151936 x 2048 head the 8-row kernel stays
+// ~6% ahead. 8-bit: 3..16 rows, in place of the vector-ALU kernel (3584 x
+// 1024 at 16 rows 9.5 -> 6.8 us, 4096 x 2048 25.6 -> 9.6 us, 151936 x 1024
+// 123 -> 46 us); at 2 rows that kernel is as fast or faster.
+bool one_pass(int fmt, int64_t M, int64_t K, int nb)
 {
-    if (nb < 2 || !u4_mfma16_ok(fmt, K)) return false;
+    if (nb < 2 || !mfma16_ok(fmt, K)) return false;
+    if (fmt != QG_U4_G64) return nb >= 3;
     return nb > 8 || ceil_div(ceil_div(M, 16), qg::kMfmaWaves) < kComputeUnits;
 }
 
@@ -234,9 +239,12 @@ bool batch_on_gemm(int fmt, int64_t M, int64_t K, int nb)
     if (nb < 2 || K > qg::kGemmMaxK) return false;
     const double w = static_cast<double>(M) * static_cast<double>(K);
     const double t_gemm = 10.0 + 96.0 * w / (fmt == QG_B1_G128 ? 280e6 : 220e6);
+    if (one_pass(fmt, M, K, nb)) {
+        const double bytes = static_cast<double>(M) * (row_bytes(fmt, K) + 4 * (K / 64));
+        return t_gemm < std::max(8.0, bytes / 3.4e6);
+    }
     if (u4_mfma_ok(fmt, K)) {
         const double bytes = static_cast<double>(M) * (row_bytes(fmt, K) + 4 * (K / 64));
-        if (u4_one_pass(fmt, M, K, nb)) return t_gemm < std::max(8.0, bytes / 3.4e6);
         return t_gemm < static_cast<double>(ceil_div(nb, 8)) * std::max(14.0, bytes / 4.4e6);
     }
     if (M < K && nb >= 6) return true;
@@ -300,11 +308,11 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
         pl.ws_bytes = (off > kCtlBytes || argmax) ? off : 0;
         return pl;
     }
-    if (u4_one_pass(fmt, M, K, nb)) {
-        // 4-bit, one pass over the weights with K cut across the 8 waves of
-        // a workgroup per compute unit, each workgroup a run of 16-row tiles
+    if (one_pass(fmt, M, K, nb)) {
+        // one pass over the weights with K cut across the 8 waves of a
+        // workgroup per compute unit, each workgroup a run of 16-row tiles
         pl.mfma16 = true;
-        pl.pairs = static_cast<int>(K / 1024);
+        pl.gw = static_cast<int>(K / 512);
         const int64_t ntiles = ceil_div(M, 16);
         pl.grid_x = std::min<int64_t>(kComputeUnits, ntiles);
         pl.lds_bytes = qg::gemv_mfma16_lds_bytes();
@@ -476,16 +484,29 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         q.nb = nb;
         q.stage_out = pl.fused;
         static const bool lds_set = [] {
-            for (const void *f : {reinterpret_cast<const void *>(qg::gemv_mfma16_u4_kernel<1>),
-                                  reinterpret_cast<const void *>(qg::gemv_mfma16_u4_kernel<2>)})
+            for (const void *f : {reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_U4_G64, 2>),
+                                  reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_U4_G64, 4>),
+                                  reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_I8_ROW, 2>),
+                                  reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_I8_ROW, 4>),
+                                  reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_I8_G64, 2>),
+                                  reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_I8_G64, 4>)})
                 (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                                           static_cast<int>(kLdsMax - kLdsStaticReserve));
             return true;
         }();
         (void)lds_set;
         const dim3 grid(static_cast<unsigned>(pl.grid_x)), block(64 * qg::kMfmaWaves);
-        if (pl.pairs == 1) hipLaunchKernelGGL(qg::gemv_mfma16_u4_kernel<1>, grid, block, pl.lds_bytes, s, q);
-        else hipLaunchKernelGGL(qg::gemv_mfma16_u4_kernel<2>, grid, block, pl.lds_bytes, s, q);
+        const bool g2 = pl.gw == 2;
+        if (fmt == QG_U4_G64) {
+            if (g2) hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_U4_G64, 2>), grid, block, pl.lds_bytes, s, q);
+            else hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_U4_G64, 4>), grid, block, pl.lds_bytes, s, q);
+        } else if (fmt == QG_I8_ROW) {
+            if (g2) hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_I8_ROW, 2>), grid, block, pl.lds_bytes, s, q);
+            else hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_I8_ROW, 4>), grid, block, pl.lds_bytes, s, q);
+        } else {
+            if (g2) hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_I8_G64, 2>), grid, block, pl.lds_bytes, s, q);
+            else hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_I8_G64, 4>), grid, block, pl.lds_bytes, s, q);
+        }
         return;
     }
     if (pl.mfma) {
@@ -710,7 +731,7 @@ size_t gemm_mfma_workspace(int fmt, int64_t M, int64_t K, int64_t N)
 // rows). Returns the number of launches, or 0 for the prefill kernel.
 int u4_row_launches(int fmt, int64_t M, int64_t K, int64_t N)
 {
-    if (N <= kGemmViaGemv || N > 48 || !u4_mfma16_ok(fmt, K)) return 0;
+    if (N <= kGemmViaGemv || N > 48 || fmt != QG_U4_G64 || !mfma16_ok(fmt, K)) return 0;
     const int n = static_cast<int>(ceil_div(N, 16));
     const double w = static_cast<double>(M) * static_cast<double>(K);
     const double bytes = static_cast<double>(M) * (row_bytes(fmt, K) + 4 * (K / 64));

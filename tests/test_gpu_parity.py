@@ -165,7 +165,7 @@ def exact_inputs(fmt, M, K, N, rng):
     (synth.U4_G64, 129, 1024, 1), (synth.U4_G64, 65, 576, 3), (synth.U4_G64, 300, 1024, 8),
     (synth.B1_G128, 129, 1024, 1), (synth.B1_G128, 17, 1152, 6), (synth.B1_G128, 257, 1024, 16),
     (synth.I8_G64, 129, 1024, 1), (synth.I8_G64, 70, 576, 5), (synth.I8_G64, 33, 1024, 16),
-    (synth.I8_G64, 100, 4160, 1),
+    (synth.I8_G64, 100, 4160, 1), (synth.I8_ROW, 300, 2048, 7), (synth.I8_G64, 4099, 2048, 13),
 ])
 def test_exact_arithmetic_bit_exact(torch, orc, fmt, M, K, N):
     say(f"exact fmt={fmt} M={M} K={K} N={N}")
@@ -261,6 +261,9 @@ SMALL = [
     (synth.U4_G64, 6144, 2048, 12), (synth.U4_G64, 2048, 6144, 6), (synth.I8_ROW, 1024, 3584, 8),
     (synth.B1_G128, 17408, 5120, 16), (synth.I8_G64, 1024, 3584, 11), (synth.B1_G128, 5120, 17408, 6),
     (synth.B1_G128, 17408, 5120, 7),
+    # 8-bit batches on the one-pass matrix-core kernel (K = 1024 or 2048)
+    (synth.I8_ROW, 3000, 2048, 12), (synth.I8_G64, 70001, 2048, 5), (synth.I8_ROW, 1, 1024, 2),
+    (synth.I8_G64, 17, 1024, 16), (synth.I8_ROW, 3584, 1024, 9),
 ]
 
 
