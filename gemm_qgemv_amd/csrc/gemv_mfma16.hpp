@@ -6,10 +6,9 @@
 // LDS; 16 rows of them would not fit, so 9..16 rows there take two launches
 // that each read the weights, and its waves each take their own tiles, which
 // leaves compute units idle when M is small. Here K is cut across the
-// workgroup's 8 waves
-// instead: wave w owns groups 2 PAIRS w .. 2 PAIRS (w + 1) - 1 (K = 1024
-// PAIRS) and keeps the exact bf16 pieces of all 16 activation rows for
-// those inputs in registers for the whole kernel; all 8 waves stream the
+// workgroup's 8 waves instead: wave w owns groups GW w .. GW (w + 1) - 1
+// (K = 512 GW) and keeps the exact bf16 pieces of all 16 activation rows
+// for those inputs in registers for the whole kernel; all 8 waves stream the
 // same 16-row weight tiles, each reading its part of every row, so the
 // weights are read once. Per k-step a tile takes three MFMAs, one per piece
 // (top, middle, bottom of the three-way split; 16 operand rows = 16
@@ -87,11 +86,10 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
             }
         }
 
-    // code ring: tile t's codes (PAIRS x 16 bytes), scales and biases of
-    // this lane's weight row for the wave's groups (rows past M read row
-    // M - 1; their outputs are not written)
-    // 4-bit: one 16-byte load per pair of groups, bf16 scale and bias pairs;
-    // 8-bit: one per group, fp32 group scales (group-64 format)
+    // code ring: tile t's codes, scales and biases of this lane's weight row
+    // for the wave's groups (rows past M read row M - 1; their outputs are
+    // not written). 4-bit: one 16-byte load per pair of groups, bf16 scale
+    // and bias pairs; 8-bit: one per group, fp32 group scales (group-64)
     constexpr int NC = U4 ? PAIRS : GW;
     constexpr int NS = FMT == FMT_I8_ROW ? 1 : U4 ? PAIRS : GW;
     struct Tile16 {
