@@ -58,8 +58,11 @@ struct GemvMfmaParams {
     unsigned long long *keys;   // greedy head: [workgroups][8] scratch
     int32_t *idx;          // [nb] greedy indices, or nullptr
     int64_t M, K;
-    int nb;                // 1..8
+    int nb;                // 1..8 (one-pass kernel: 1..16)
     int stage_out;         // outputs staged in LDS, written at the end
+    float *part;           // one-pass kernel with K split over blockIdx.y:
+                           // partial outputs [splits][nb][M] (y and the
+                           // greedy head unused), else nullptr
 };
 
 #ifndef QG_MFMA_WAVES

@@ -30,6 +30,10 @@
 // takes its first 8 at k-step 0, the other 8 at k-step 1. The per-row scale
 // multiplies the finished sum; the per-group scales (8-bit group-64) fold
 // each group's sum as for the 4-bit format; there is no bias term.
+//
+// Longer K: the grid's second dimension cuts K into slices of 8 GW groups;
+// each slice writes its partial outputs to p.part, and the split-K combine
+// kernel adds them in slice order (matrix-vector calls only).
 #pragma once
 
 #include "gemv_mfma.hpp"
@@ -51,6 +55,8 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
     static_assert(kMfmaWaves == 8, "K is cut into 8 slices");
     static_assert(FMT == FMT_U4_G64 || FMT == FMT_I8_ROW || FMT == FMT_I8_G64, "4-bit or 8-bit");
     static_assert(GW % 2 == 0, "whole pairs of groups");
+    // K may be split over blockIdx.y into slices of 8 GW groups; each slice
+    // writes its partial outputs to p.part
     constexpr bool U4 = FMT == FMT_U4_G64;
     constexpr int PAIRS = GW / 2;
     extern __shared__ float4 lds_f4[];
@@ -61,7 +67,8 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
     const int r = lane & 15, q = lane >> 4;
     const int64_t row_bytes = U4 ? p.K / 2 : p.K;
     const int64_t G = p.K / 64;
-    const int gw = wave * GW;   // this wave's first group
+    const int gw = (static_cast<int>(blockIdx.y) * 8 + wave) * GW;   // this wave's first group
+    float *const out = p.part ? p.part + static_cast<int64_t>(blockIdx.y) * p.nb * p.M : p.y;
 
     // the workgroup's run of 16-row tiles; every wave takes every tile
     const int64_t ntiles = (p.M + 15) / 16;
@@ -244,8 +251,8 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
                     if constexpr (FMT == FMT_I8_ROW) v *= reinterpret_cast<const float *>(p.scales)[m];
                     if (p.stage_out)
                         out_stage[((tile - tb_wg) * 16 + sn) * 16 + srr] = v;
-                    else if (p.y)
-                        p.y[static_cast<int64_t>(sn) * p.M + m] = v;
+                    else if (out)
+                        out[static_cast<int64_t>(sn) * p.M + m] = v;
                     if (best_m < 0 || v > best_v) {
                         best_v = v;
                         best_m = m;
@@ -283,12 +290,12 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
         buf ^= 1;
     }
 
-    if (p.stage_out && p.y) {
+    if (p.stage_out && out) {
         __syncthreads();
         const int64_t m0 = tb * 16, rows = min(te * 16, p.M) - m0;
         for (int n = 0; n < p.nb; ++n)
             for (int64_t j = tid; j < rows; j += blockDim.x)
-                p.y[static_cast<int64_t>(n) * p.M + m0 + j] = out_stage[((j >> 4) * 16 + n) * 16 + (j & 15)];
+                out[static_cast<int64_t>(n) * p.M + m0 + j] = out_stage[((j >> 4) * 16 + n) * 16 + (j & 15)];
     }
 
     if (p.ctl != nullptr) {

@@ -219,6 +219,26 @@ bool one_pass(int fmt, int64_t M, int64_t K, int nb)
     return nb > 8 || ceil_div(ceil_div(M, 16), qg::kMfmaWaves) < kComputeUnits;
 }
 
+// Longer K for the one-pass kernel: slices of 2048 (or 1024) inputs over a
+// second grid dimension, each writing partial outputs to the workspace,
+// which the split-K combine kernel adds in slice order. 0: not available.
+// Matrix-vector calls only (the greedy head keeps its own kernels).
+int64_t one_pass_slice(int fmt, int64_t K)
+{
+    if (!(fmt == QG_U4_G64 || fmt == QG_I8_ROW || fmt == QG_I8_G64) || K <= 2048) return 0;
+    if (K % 2048 == 0 && K / 2048 <= 8) return 2048;
+    if (K % 1024 == 0 && K / 1024 <= 8) return 1024;
+    return 0;
+}
+
+// From 3 rows (at 2 the vector-ALU kernel is as fast or faster): 4-bit
+// 4096 x 4096 at 16 rows 69 -> 20.6 us, 17408 x 16384 484 -> 122 us, 8-bit
+// 4096 x 4096 63 -> 20 us.
+bool split_pass(int fmt, int64_t K, int nb, bool argmax)
+{
+    return !argmax && nb >= 3 && one_pass_slice(fmt, K) > 0;
+}
+
 // Whether nb (2..16) activation rows run faster as the prefill product on
 // narrow tiles (weights read once, 16 token rows of matrix-core work) than
 // on the matrix-vector kernels. Estimates in microseconds, fitted to
@@ -242,6 +262,10 @@ bool batch_on_gemm(int fmt, int64_t M, int64_t K, int nb)
     if (one_pass(fmt, M, K, nb)) {
         const double bytes = static_cast<double>(M) * (row_bytes(fmt, K) + 4 * (K / 64));
         return t_gemm < std::max(8.0, bytes / 3.4e6);
+    }
+    if (split_pass(fmt, K, nb, false)) {
+        const double bytes = static_cast<double>(M) * (row_bytes(fmt, K) + 4 * (K / 64));
+        return t_gemm < std::max(8.0, bytes / 3.4e6) + 2.0;
     }
     if (u4_mfma_ok(fmt, K)) {
         const double bytes = static_cast<double>(M) * (row_bytes(fmt, K) + 4 * (K / 64));
@@ -308,18 +332,26 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
         pl.ws_bytes = (off > kCtlBytes || argmax) ? off : 0;
         return pl;
     }
-    if (one_pass(fmt, M, K, nb)) {
+    const bool split = split_pass(fmt, K, nb, argmax);
+    if (split || one_pass(fmt, M, K, nb)) {
         // one pass over the weights with K cut across the 8 waves of a
-        // workgroup per compute unit, each workgroup a run of 16-row tiles
+        // workgroup per compute unit, each workgroup a run of 16-row tiles;
+        // longer K in slices over the second grid dimension
         pl.mfma16 = true;
-        pl.gw = static_cast<int>(K / 512);
+        const int64_t slice = split ? one_pass_slice(fmt, K) : K;
+        pl.gw = static_cast<int>(slice / 512);
+        pl.nsplit = static_cast<int>(K / slice);
         const int64_t ntiles = ceil_div(M, 16);
         pl.grid_x = std::min<int64_t>(kComputeUnits, ntiles);
         pl.lds_bytes = qg::gemv_mfma16_lds_bytes();
         const size_t out_bytes = static_cast<size_t>(ceil_div(ntiles, pl.grid_x)) * qg::k16TileOutBytes;
         pl.fused = static_cast<int64_t>(pl.lds_bytes + out_bytes) + kLdsStaticReserve <= kLdsMax;
         if (pl.fused) pl.lds_bytes += out_bytes;
-        pl.nsplit = 1;
+        if (pl.nsplit > 1) {
+            // partial outputs after the control words
+            pl.part_off = kCtlBytes;
+            pl.ws_bytes = align256(kCtlBytes + static_cast<size_t>(pl.nsplit) * nb * M * 4);
+        }
         if (argmax) {
             // per-workgroup greedy keys (16 per workgroup) after the control words
             pl.nkeys = static_cast<int>(pl.grid_x);
@@ -483,6 +515,7 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         q.K = K;
         q.nb = nb;
         q.stage_out = pl.fused;
+        q.part = pl.nsplit > 1 ? reinterpret_cast<float *>(static_cast<char *>(ws) + pl.part_off) : nullptr;
         static const bool lds_set = [] {
             for (const void *f : {reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_U4_G64, 2>),
                                   reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_U4_G64, 4>),
@@ -495,7 +528,8 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
             return true;
         }();
         (void)lds_set;
-        const dim3 grid(static_cast<unsigned>(pl.grid_x)), block(64 * qg::kMfmaWaves);
+        const dim3 grid(static_cast<unsigned>(pl.grid_x), static_cast<unsigned>(pl.nsplit));
+        const dim3 block(64 * qg::kMfmaWaves);
         const bool g2 = pl.gw == 2;
         if (fmt == QG_U4_G64) {
             if (g2) hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_U4_G64, 2>), grid, block, pl.lds_bytes, s, q);
@@ -506,6 +540,11 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         } else {
             if (g2) hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_I8_G64, 2>), grid, block, pl.lds_bytes, s, q);
             else hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_I8_G64, 4>), grid, block, pl.lds_bytes, s, q);
+        }
+        if (pl.nsplit > 1) {
+            const int64_t quads = ceil_div(M * nb, 4);
+            hipLaunchKernelGGL(qg::gemm_splitk_combine_kernel, dim3(static_cast<unsigned>(ceil_div(quads, 256))),
+                               dim3(256), 0, s, q.part, y, M, static_cast<int64_t>(nb), pl.nsplit);
         }
         return;
     }

@@ -166,6 +166,7 @@ def exact_inputs(fmt, M, K, N, rng):
     (synth.B1_G128, 129, 1024, 1), (synth.B1_G128, 17, 1152, 6), (synth.B1_G128, 257, 1024, 16),
     (synth.I8_G64, 129, 1024, 1), (synth.I8_G64, 70, 576, 5), (synth.I8_G64, 33, 1024, 16),
     (synth.I8_G64, 100, 4160, 1), (synth.I8_ROW, 300, 2048, 7), (synth.I8_G64, 4099, 2048, 13),
+    (synth.U4_G64, 300, 6144, 5), (synth.I8_ROW, 129, 4096, 11), (synth.I8_G64, 40, 3072, 16),
 ])
 def test_exact_arithmetic_bit_exact(torch, orc, fmt, M, K, N):
     say(f"exact fmt={fmt} M={M} K={K} N={N}")
@@ -264,6 +265,9 @@ SMALL = [
     # 8-bit batches on the one-pass matrix-core kernel (K = 1024 or 2048)
     (synth.I8_ROW, 3000, 2048, 12), (synth.I8_G64, 70001, 2048, 5), (synth.I8_ROW, 1, 1024, 2),
     (synth.I8_G64, 17, 1024, 16), (synth.I8_ROW, 3584, 1024, 9),
+    # longer K on the one-pass kernel in slices of 2048 or 1024 inputs
+    (synth.U4_G64, 5000, 3072, 2), (synth.U4_G64, 2048, 6144, 16), (synth.I8_ROW, 4096, 4096, 9),
+    (synth.I8_G64, 1000, 3072, 4), (synth.U4_G64, 70001, 16384, 3), (synth.I8_ROW, 7, 8192, 2),
 ]
 
 
