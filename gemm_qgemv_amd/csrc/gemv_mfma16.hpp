@@ -1,6 +1,6 @@
 // gemv_mfma16.hpp -- up to 16 activation rows of the 4-bit group-64 format,
-// and of the two 8-bit formats, in one pass over the weights, on the gfx950
-// matrix cores.
+// the two 8-bit formats and the 1-bit format, in one pass over the weights,
+// on the gfx950 matrix cores.
 //
 // The 8-row kernel (gemv_mfma.hpp) stages the activation pieces of all K in
 // LDS; 16 rows of them would not fit, so 9..16 rows there take two launches
@@ -31,6 +31,10 @@
 // multiplies the finished sum; the per-group scales (8-bit group-64) fold
 // each group's sum as for the 4-bit format; there is no bias term.
 //
+// 1-bit signs (exactly +-1 in bf16): lane (r, q) holds inputs 32 q .. 32 q
+// + 31 of each 128-input group (one 4-byte load), byte b at k-step b; the
+// fp16 scale folds the group's sum.
+//
 // Longer K: the grid's second dimension cuts K into slices of 8 GW groups;
 // each slice writes its partial outputs to p.part, and the split-K combine
 // kernel adds them in slice order (matrix-vector calls only).
@@ -53,19 +57,21 @@ template <int FMT, int GW>
 __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParams p)
 {
     static_assert(kMfmaWaves == 8, "K is cut into 8 slices");
-    static_assert(FMT == FMT_U4_G64 || FMT == FMT_I8_ROW || FMT == FMT_I8_G64, "4-bit or 8-bit");
+    static_assert(FMT == FMT_U4_G64 || FMT == FMT_I8_ROW || FMT == FMT_I8_G64 || FMT == FMT_B1_G128,
+                  "4-bit, 8-bit or 1-bit");
     static_assert(GW % 2 == 0, "whole pairs of groups");
     // K may be split over blockIdx.y into slices of 8 GW groups; each slice
     // writes its partial outputs to p.part
     constexpr bool U4 = FMT == FMT_U4_G64;
-    constexpr int PAIRS = GW / 2;
+    constexpr bool B1 = FMT == FMT_B1_G128;
+    constexpr int PAIRS = GW / 2;   // 1-bit: groups of 128 inputs per wave
     extern __shared__ float4 lds_f4[];
     float *red = reinterpret_cast<float *>(lds_f4);
     float *out_stage = red + k16RedFloats;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, q = lane >> 4;
-    const int64_t row_bytes = U4 ? p.K / 2 : p.K;
+    const int64_t row_bytes = U4 ? p.K / 2 : B1 ? p.K / 8 : p.K;
     const int64_t G = p.K / 64;
     const int gw = (static_cast<int>(blockIdx.y) * 8 + wave) * GW;   // this wave's first group
     float *const out = p.part ? p.part + static_cast<int64_t>(blockIdx.y) * p.nb * p.M : p.y;
@@ -84,7 +90,10 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
     for (int gi = 0; gi < GW; ++gi)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const int64_t k0 = 64 * (gw + gi) + 32 * (q & 1) + 16 * (q >> 1) + 8 * s;
+            // 1-bit: lane q holds 32 consecutive inputs of each 128-input
+            // group (one 4-byte code load), k-steps in 8-input blocks
+            const int64_t k0 = B1 ? 64 * gw + 128 * (gi >> 1) + 32 * q + 16 * (gi & 1) + 8 * s
+                                  : 64 * (gw + gi) + 32 * (q & 1) + 16 * (q >> 1) + 8 * s;
             xa[gi][s][0] = xa[gi][s][1] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (r < p.nb) {
                 const float4 *src = reinterpret_cast<const float4 *>(p.x + r * p.K + k0);
@@ -96,15 +105,26 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
     // code ring: tile t's codes, scales and biases of this lane's weight row
     // for the wave's groups (rows past M read row M - 1; their outputs are
     // not written). 4-bit: one 16-byte load per pair of groups, bf16 scale
-    // and bias pairs; 8-bit: one per group, fp32 group scales (group-64)
-    constexpr int NC = U4 ? PAIRS : GW;
-    constexpr int NS = FMT == FMT_I8_ROW ? 1 : U4 ? PAIRS : GW;
+    // and bias pairs; 8-bit: one per group, fp32 group scales (group-64);
+    // 1-bit: 4 bytes (in .x) and the fp16 scale per 128-input group
+    constexpr int NC = U4 || B1 ? PAIRS : GW;
+    constexpr int NS = FMT == FMT_I8_ROW ? 1 : U4 || B1 ? PAIRS : GW;
     struct Tile16 {
         uint4 c[NC];
         uint32_t s[NS], b[U4 ? PAIRS : 1];
     };
     auto load = [&](Tile16 &T, int64_t t) {
         const int64_t m = min(t * 16 + r, p.M - 1);
+        if constexpr (B1) {
+            const uint8_t *c = p.codes + m * row_bytes + 8 * gw + 4 * q;
+            const uint16_t *sc = p.scales + m * (p.K / 128) + gw / 2;
+#pragma unroll
+            for (int j = 0; j < PAIRS; ++j) {
+                T.c[j].x = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(c + 16 * j));
+                T.s[j] = sc[j];
+            }
+            return;
+        }
         const uint8_t *c = p.codes + m * row_bytes + (U4 ? 32 * gw + 16 * q
                                                           : 64 * gw + 32 * (q & 1) + 16 * (q >> 1));
 #pragma unroll
@@ -149,7 +169,7 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
             const float4 a = xa[gi][s][0], b = xa[gi][s][1];
             // 4-bit operand order k = 0, 2, 4, 6, 1, 3, 5, 7; 8-bit natural
             float v[8];
-            if constexpr (U4) {
+            if constexpr (U4) {   // (1-bit and 8-bit: natural order)
                 v[0] = a.x; v[1] = a.z; v[2] = b.x; v[3] = b.z;
                 v[4] = a.y; v[5] = a.w; v[6] = b.y; v[7] = b.w;
             } else {
@@ -201,6 +221,26 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[i] = fmaf(bv, xg[2 * pp + h][i], fmaf(sc, t[i], acc[i]));
                 }
+            }
+        } else if constexpr (B1) {
+#pragma unroll
+            for (int gb = 0; gb < PAIRS; ++gb) {
+                // byte b of the lane's 4 is k-step b of the group: 8 signs
+                // -> 8 bf16 +-1 (the conversion takes inverted bits)
+                const uint32_t nbits = ~T.c[gb].x;
+                bf16x8_t w[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const uint32_t nb8 = nbits >> (8 * b);
+                    w[b] = __builtin_bit_cast(
+                        bf16x8_t, make_uint4(signpair_to_bf16x2(nb8 & 3u), signpair_to_bf16x2((nb8 >> 2) & 3u),
+                                             signpair_to_bf16x2((nb8 >> 4) & 3u),
+                                             signpair_to_bf16x2((nb8 >> 6) & 3u)));
+                }
+                const floatx4_t t0 = group(2 * gb, w[0], w[1]), t1 = group(2 * gb + 1, w[2], w[3]);
+                const float sc = fp16_bits_to_f32(static_cast<uint16_t>(T.s[gb]));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, t0[i] + t1[i], acc[i]);
             }
         } else {
 #pragma unroll

@@ -202,7 +202,15 @@ bool u4_mfma_ok(int fmt, int64_t K)
 // 4-bit and both 8-bit formats.
 bool mfma16_ok(int fmt, int64_t K)
 {
-    return (fmt == QG_U4_G64 || fmt == QG_I8_ROW || fmt == QG_I8_G64) && (K == 1024 || K == 2048);
+    return known_format(fmt) && (K == 1024 || K == 2048);
+}
+
+// Fewest rows for the one-pass kernel: 8-bit and 1-bit 3 (the vector-ALU
+// and lookup kernels are as fast at 2; 1-bit 4096 x 2048 at 3 / 16 rows
+// 9.5 / 14.3 -> 6.3 / 9.6 us), 4-bit 2.
+int one_pass_min_rows(int fmt)
+{
+    return fmt == QG_U4_G64 ? 2 : 3;
 }
 
 // 4-bit: it takes 9..16 rows (one pass instead of two launches of 8), and
@@ -214,8 +222,8 @@ bool mfma16_ok(int fmt, int64_t K)
 // 123 -> 46 us); at 2 rows that kernel is as fast or faster.
 bool one_pass(int fmt, int64_t M, int64_t K, int nb)
 {
-    if (nb < 2 || !mfma16_ok(fmt, K)) return false;
-    if (fmt != QG_U4_G64) return nb >= 3;
+    if (nb < one_pass_min_rows(fmt) || !mfma16_ok(fmt, K)) return false;
+    if (fmt != QG_U4_G64) return true;
     return nb > 8 || ceil_div(ceil_div(M, 16), qg::kMfmaWaves) < kComputeUnits;
 }
 
@@ -225,7 +233,7 @@ bool one_pass(int fmt, int64_t M, int64_t K, int nb)
 // Matrix-vector calls only (the greedy head keeps its own kernels).
 int64_t one_pass_slice(int fmt, int64_t K)
 {
-    if (!(fmt == QG_U4_G64 || fmt == QG_I8_ROW || fmt == QG_I8_G64) || K <= 2048) return 0;
+    if (!known_format(fmt) || K <= 2048) return 0;
     if (K % 2048 == 0 && K / 2048 <= 8) return 2048;
     if (K % 1024 == 0 && K / 1024 <= 8) return 1024;
     return 0;
@@ -233,10 +241,14 @@ int64_t one_pass_slice(int fmt, int64_t K)
 
 // From 3 rows (at 2 the vector-ALU kernel is as fast or faster): 4-bit
 // 4096 x 4096 at 16 rows 69 -> 20.6 us, 17408 x 16384 484 -> 122 us, 8-bit
-// 4096 x 4096 63 -> 20 us.
+// 4096 x 4096 63 -> 20 us. 1-bit from 6 rows (the lookup kernel is faster
+// at 3..4): 17408 x 5120 at 6 / 16 rows 37.2 / 47.9 -> 29.3 / 38.8 us. At
+// most 8 slices (17 slices of 5120 x 17408 ran at half the lookup kernel's
+// speed).
 bool split_pass(int fmt, int64_t K, int nb, bool argmax)
 {
-    return !argmax && nb >= 3 && one_pass_slice(fmt, K) > 0;
+    const int min_rows = fmt == QG_B1_G128 ? 6 : 3;
+    return !argmax && nb >= min_rows && one_pass_slice(fmt, K) > 0;
 }
 
 // Whether nb (2..16) activation rows run faster as the prefill product on
@@ -301,6 +313,34 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
         }
         return pl;
     }
+    const bool split = split_pass(fmt, K, nb, argmax);
+    if (split || one_pass(fmt, M, K, nb)) {
+        // one pass over the weights with K cut across the 8 waves of a
+        // workgroup per compute unit, each workgroup a run of 16-row tiles;
+        // longer K in slices over the second grid dimension
+        pl.mfma16 = true;
+        const int64_t slice = split ? one_pass_slice(fmt, K) : K;
+        pl.gw = static_cast<int>(slice / 512);
+        pl.nsplit = static_cast<int>(K / slice);
+        const int64_t ntiles = ceil_div(M, 16);
+        pl.grid_x = std::min<int64_t>(kComputeUnits, ntiles);
+        pl.lds_bytes = qg::gemv_mfma16_lds_bytes();
+        const size_t out_bytes = static_cast<size_t>(ceil_div(ntiles, pl.grid_x)) * qg::k16TileOutBytes;
+        pl.fused = static_cast<int64_t>(pl.lds_bytes + out_bytes) + kLdsStaticReserve <= kLdsMax;
+        if (pl.fused) pl.lds_bytes += out_bytes;
+        if (pl.nsplit > 1) {
+            // partial outputs after the control words
+            pl.part_off = kCtlBytes;
+            pl.ws_bytes = align256(kCtlBytes + static_cast<size_t>(pl.nsplit) * nb * M * 4);
+        }
+        if (argmax) {
+            // per-workgroup greedy keys (16 per workgroup) after the control words
+            pl.nkeys = static_cast<int>(pl.grid_x);
+            pl.part_off = kCtlBytes;
+            pl.ws_bytes = align256(kCtlBytes + static_cast<size_t>(pl.grid_x) * 16 * 8);
+        }
+        return pl;
+    }
     if (fmt == QG_B1_G128) {
         // 1-bit, 1..16 activation rows: 64 weight rows x one K chunk per
         // workgroup, a lookup table per activation row, partial sums of the
@@ -330,34 +370,6 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
         }
         if (argmax) pl.nkeys = static_cast<int>(pl.nsplit > 1 && !pl.fused ? pl.comb_grid : pl.grid_x);
         pl.ws_bytes = (off > kCtlBytes || argmax) ? off : 0;
-        return pl;
-    }
-    const bool split = split_pass(fmt, K, nb, argmax);
-    if (split || one_pass(fmt, M, K, nb)) {
-        // one pass over the weights with K cut across the 8 waves of a
-        // workgroup per compute unit, each workgroup a run of 16-row tiles;
-        // longer K in slices over the second grid dimension
-        pl.mfma16 = true;
-        const int64_t slice = split ? one_pass_slice(fmt, K) : K;
-        pl.gw = static_cast<int>(slice / 512);
-        pl.nsplit = static_cast<int>(K / slice);
-        const int64_t ntiles = ceil_div(M, 16);
-        pl.grid_x = std::min<int64_t>(kComputeUnits, ntiles);
-        pl.lds_bytes = qg::gemv_mfma16_lds_bytes();
-        const size_t out_bytes = static_cast<size_t>(ceil_div(ntiles, pl.grid_x)) * qg::k16TileOutBytes;
-        pl.fused = static_cast<int64_t>(pl.lds_bytes + out_bytes) + kLdsStaticReserve <= kLdsMax;
-        if (pl.fused) pl.lds_bytes += out_bytes;
-        if (pl.nsplit > 1) {
-            // partial outputs after the control words
-            pl.part_off = kCtlBytes;
-            pl.ws_bytes = align256(kCtlBytes + static_cast<size_t>(pl.nsplit) * nb * M * 4);
-        }
-        if (argmax) {
-            // per-workgroup greedy keys (16 per workgroup) after the control words
-            pl.nkeys = static_cast<int>(pl.grid_x);
-            pl.part_off = kCtlBytes;
-            pl.ws_bytes = align256(kCtlBytes + static_cast<size_t>(pl.grid_x) * 16 * 8);
-        }
         return pl;
     }
     if (nb >= 2 && u4_mfma_ok(fmt, K)) {
@@ -522,7 +534,9 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
                                   reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_I8_ROW, 2>),
                                   reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_I8_ROW, 4>),
                                   reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_I8_G64, 2>),
-                                  reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_I8_G64, 4>)})
+                                  reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_I8_G64, 4>),
+                                  reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_B1_G128, 2>),
+                                  reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_B1_G128, 4>)})
                 (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                                           static_cast<int>(kLdsMax - kLdsStaticReserve));
             return true;
@@ -537,9 +551,12 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         } else if (fmt == QG_I8_ROW) {
             if (g2) hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_I8_ROW, 2>), grid, block, pl.lds_bytes, s, q);
             else hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_I8_ROW, 4>), grid, block, pl.lds_bytes, s, q);
-        } else {
+        } else if (fmt == QG_I8_G64) {
             if (g2) hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_I8_G64, 2>), grid, block, pl.lds_bytes, s, q);
             else hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_I8_G64, 4>), grid, block, pl.lds_bytes, s, q);
+        } else {
+            if (g2) hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_B1_G128, 2>), grid, block, pl.lds_bytes, s, q);
+            else hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_B1_G128, 4>), grid, block, pl.lds_bytes, s, q);
         }
         if (pl.nsplit > 1) {
             const int64_t quads = ceil_div(M * nb, 4);

@@ -167,6 +167,7 @@ def exact_inputs(fmt, M, K, N, rng):
     (synth.I8_G64, 129, 1024, 1), (synth.I8_G64, 70, 576, 5), (synth.I8_G64, 33, 1024, 16),
     (synth.I8_G64, 100, 4160, 1), (synth.I8_ROW, 300, 2048, 7), (synth.I8_G64, 4099, 2048, 13),
     (synth.U4_G64, 300, 6144, 5), (synth.I8_ROW, 129, 4096, 11), (synth.I8_G64, 40, 3072, 16),
+    (synth.B1_G128, 300, 5120, 5), (synth.B1_G128, 33, 2048, 3),
 ])
 def test_exact_arithmetic_bit_exact(torch, orc, fmt, M, K, N):
     say(f"exact fmt={fmt} M={M} K={K} N={N}")
@@ -268,6 +269,8 @@ SMALL = [
     # longer K on the one-pass kernel in slices of 2048 or 1024 inputs
     (synth.U4_G64, 5000, 3072, 2), (synth.U4_G64, 2048, 6144, 16), (synth.I8_ROW, 4096, 4096, 9),
     (synth.I8_G64, 1000, 3072, 4), (synth.U4_G64, 70001, 16384, 3), (synth.I8_ROW, 7, 8192, 2),
+    # 1-bit batches on the one-pass kernel (4-byte code loads per 128 inputs)
+    (synth.B1_G128, 4096, 2048, 8), (synth.B1_G128, 1000, 1024, 3), (synth.B1_G128, 2000, 16384, 13),
 ]
 
 
@@ -433,6 +436,7 @@ def gpu_greedy(torch, w, x, logits=True):
     (synth.U4_G64, 30001, 2048, 24), (synth.I8_ROW, 70001, 256, 32), (synth.I8_G64, 70001, 192, 19),
     (synth.B1_G128, 66001, 256, 30),
     (synth.U4_G64, 40000, 1024, 33), (synth.U4_G64, 60000, 2048, 48),
+    (synth.B1_G128, 3000, 2048, 7), (synth.I8_ROW, 20000, 1024, 12),
 ])
 def test_greedy_head_with_and_without_logits(torch, orc, fmt, M, K, N):
     say(f"greedy fmt={fmt} M={M} K={K} N={N}")
