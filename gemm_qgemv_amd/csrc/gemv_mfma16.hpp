@@ -59,7 +59,8 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
     static_assert(kMfmaWaves == 8, "K is cut into 8 slices");
     static_assert(FMT == FMT_U4_G64 || FMT == FMT_I8_ROW || FMT == FMT_I8_G64 || FMT == FMT_B1_G128,
                   "4-bit, 8-bit or 1-bit");
-    static_assert(GW % 2 == 0, "whole pairs of groups");
+    static_assert(GW % 2 == 0 || FMT == FMT_I8_ROW || FMT == FMT_I8_G64,
+                  "whole pairs of groups (4-bit loads, 1-bit 128-input groups)");
     // K may be split over blockIdx.y into slices of 8 GW groups; each slice
     // writes its partial outputs to p.part
     constexpr bool U4 = FMT == FMT_U4_G64;

@@ -227,15 +227,17 @@ bool one_pass(int fmt, int64_t M, int64_t K, int nb)
     return nb > 8 || ceil_div(ceil_div(M, 16), qg::kMfmaWaves) < kComputeUnits;
 }
 
-// Longer K for the one-pass kernel: slices of 2048 (or 1024) inputs over a
+// Other K for the one-pass kernel: slices of 2048 (or 1024, or 512) inputs over a
 // second grid dimension, each writing partial outputs to the workspace,
 // which the split-K combine kernel adds in slice order. 0: not available.
 // Matrix-vector calls only (the greedy head keeps its own kernels).
 int64_t one_pass_slice(int fmt, int64_t K)
 {
-    if (!known_format(fmt) || K <= 2048) return 0;
+    if (!known_format(fmt) || mfma16_ok(fmt, K)) return 0;
     if (K % 2048 == 0 && K / 2048 <= 8) return 2048;
     if (K % 1024 == 0 && K / 1024 <= 8) return 1024;
+    // 8-bit: slices of 512 (one group per wave; 1024 x 3584 in 7)
+    if ((fmt == QG_I8_ROW || fmt == QG_I8_G64) && K % 512 == 0 && K / 512 <= 8) return 512;
     return 0;
 }
 
@@ -245,10 +247,14 @@ int64_t one_pass_slice(int fmt, int64_t K)
 // at 3..4): 17408 x 5120 at 6 / 16 rows 37.2 / 47.9 -> 29.3 / 38.8 us. At
 // most 8 slices (17 slices of 5120 x 17408 ran at half the lookup kernel's
 // speed).
+// 8-bit in several slices of 512 from 6 rows as well (4096 x 1536 and
+// 14336 x 2560 at 3..4 rows: 7.4 -> 9.1 and 18.8 -> 20.8 us, at 16 rows
+// 24.4 -> 12.8 and 97.8 -> 27.2 us; 1024 x 3584 at 16 rows 15.4 -> 10.1).
 bool split_pass(int fmt, int64_t K, int nb, bool argmax)
 {
-    const int min_rows = fmt == QG_B1_G128 ? 6 : 3;
-    return !argmax && nb >= min_rows && one_pass_slice(fmt, K) > 0;
+    const int64_t slice = one_pass_slice(fmt, K);
+    const int min_rows = fmt == QG_B1_G128 || (slice == 512 && K > 512) ? 6 : 3;
+    return !argmax && slice > 0 && nb >= min_rows;
 }
 
 // Whether nb (2..16) activation rows run faster as the prefill product on
@@ -505,6 +511,33 @@ void launch_gemv1_fmt(const GemvPlan &pl, const qg::Gemv1Params &p, hipStream_t 
 
 // Enqueue one planned GEMV (+ split-K combine). The greedy selection
 // finishes inside the last kernel.
+// Launch the one-pass kernel for GW groups of 64 inputs per wave (8-bit: 1,
+// 2 or 4; 4-bit and 1-bit: 2 or 4), with dynamic LDS above the default.
+template <int FMT, int GW>
+void launch_mfma16_gw(dim3 grid, size_t lds, hipStream_t s, const qg::GemvMfmaParams &q)
+{
+    static const bool lds_set = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<FMT, GW>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  static_cast<int>(kLdsMax - kLdsStaticReserve));
+        return true;
+    }();
+    (void)lds_set;
+    hipLaunchKernelGGL((qg::gemv_mfma16_kernel<FMT, GW>), grid, dim3(64 * qg::kMfmaWaves), lds, s, q);
+}
+
+template <int FMT>
+void launch_mfma16(int gw, dim3 grid, size_t lds, hipStream_t s, const qg::GemvMfmaParams &q)
+{
+    if (gw == 2) {
+        launch_mfma16_gw<FMT, 2>(grid, lds, s, q);
+    } else if (gw == 4) {
+        launch_mfma16_gw<FMT, 4>(grid, lds, s, q);
+    } else if constexpr (FMT == qg::FMT_I8_ROW || FMT == qg::FMT_I8_G64) {
+        launch_mfma16_gw<FMT, 1>(grid, lds, s, q);
+    }
+}
+
 void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales,
               const void *biases, const float *x, float *y, int32_t *idx, int64_t M,
               int64_t K, int nb, void *ws, hipStream_t s)
@@ -528,36 +561,11 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         q.nb = nb;
         q.stage_out = pl.fused;
         q.part = pl.nsplit > 1 ? reinterpret_cast<float *>(static_cast<char *>(ws) + pl.part_off) : nullptr;
-        static const bool lds_set = [] {
-            for (const void *f : {reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_U4_G64, 2>),
-                                  reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_U4_G64, 4>),
-                                  reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_I8_ROW, 2>),
-                                  reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_I8_ROW, 4>),
-                                  reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_I8_G64, 2>),
-                                  reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_I8_G64, 4>),
-                                  reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_B1_G128, 2>),
-                                  reinterpret_cast<const void *>(qg::gemv_mfma16_kernel<qg::FMT_B1_G128, 4>)})
-                (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                          static_cast<int>(kLdsMax - kLdsStaticReserve));
-            return true;
-        }();
-        (void)lds_set;
         const dim3 grid(static_cast<unsigned>(pl.grid_x), static_cast<unsigned>(pl.nsplit));
-        const dim3 block(64 * qg::kMfmaWaves);
-        const bool g2 = pl.gw == 2;
-        if (fmt == QG_U4_G64) {
-            if (g2) hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_U4_G64, 2>), grid, block, pl.lds_bytes, s, q);
-            else hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_U4_G64, 4>), grid, block, pl.lds_bytes, s, q);
-        } else if (fmt == QG_I8_ROW) {
-            if (g2) hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_I8_ROW, 2>), grid, block, pl.lds_bytes, s, q);
-            else hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_I8_ROW, 4>), grid, block, pl.lds_bytes, s, q);
-        } else if (fmt == QG_I8_G64) {
-            if (g2) hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_I8_G64, 2>), grid, block, pl.lds_bytes, s, q);
-            else hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_I8_G64, 4>), grid, block, pl.lds_bytes, s, q);
-        } else {
-            if (g2) hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_B1_G128, 2>), grid, block, pl.lds_bytes, s, q);
-            else hipLaunchKernelGGL((qg::gemv_mfma16_kernel<qg::FMT_B1_G128, 4>), grid, block, pl.lds_bytes, s, q);
-        }
+        if (fmt == QG_U4_G64) launch_mfma16<qg::FMT_U4_G64>(pl.gw, grid, pl.lds_bytes, s, q);
+        else if (fmt == QG_I8_ROW) launch_mfma16<qg::FMT_I8_ROW>(pl.gw, grid, pl.lds_bytes, s, q);
+        else if (fmt == QG_I8_G64) launch_mfma16<qg::FMT_I8_G64>(pl.gw, grid, pl.lds_bytes, s, q);
+        else launch_mfma16<qg::FMT_B1_G128>(pl.gw, grid, pl.lds_bytes, s, q);
         if (pl.nsplit > 1) {
             const int64_t quads = ceil_div(M * nb, 4);
             hipLaunchKernelGGL(qg::gemm_splitk_combine_kernel, dim3(static_cast<unsigned>(ceil_div(quads, 256))),

@@ -168,6 +168,7 @@ def exact_inputs(fmt, M, K, N, rng):
     (synth.I8_G64, 100, 4160, 1), (synth.I8_ROW, 300, 2048, 7), (synth.I8_G64, 4099, 2048, 13),
     (synth.U4_G64, 300, 6144, 5), (synth.I8_ROW, 129, 4096, 11), (synth.I8_G64, 40, 3072, 16),
     (synth.B1_G128, 300, 5120, 5), (synth.B1_G128, 33, 2048, 3),
+    (synth.I8_ROW, 77, 3584, 9), (synth.I8_G64, 1000, 2560, 7), (synth.I8_G64, 99, 512, 4),
 ])
 def test_exact_arithmetic_bit_exact(torch, orc, fmt, M, K, N):
     say(f"exact fmt={fmt} M={M} K={K} N={N}")
@@ -271,6 +272,8 @@ SMALL = [
     (synth.I8_G64, 1000, 3072, 4), (synth.U4_G64, 70001, 16384, 3), (synth.I8_ROW, 7, 8192, 2),
     # 1-bit batches on the one-pass kernel (4-byte code loads per 128 inputs)
     (synth.B1_G128, 4096, 2048, 8), (synth.B1_G128, 1000, 1024, 3), (synth.B1_G128, 2000, 16384, 13),
+    # 8-bit in slices of 512 inputs (one group per wave)
+    (synth.I8_ROW, 1024, 3584, 12), (synth.I8_G64, 1024, 3584, 5), (synth.I8_ROW, 33, 1536, 16),
 ]
 
 
