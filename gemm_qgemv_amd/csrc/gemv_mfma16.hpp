@@ -157,8 +157,8 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
     for (int u = 0; u < NB - 1; ++u)
         if (u < nt) load(ring[u], tb + u);
 
-    // 1b. exact three-way split into operand pieces; the group sums
-    //     X[n][g] of the activations for the bias term, gathered to the
+    // 1b. exact three-way split into operand pieces; for the 4-bit bias
+    //     term the group sums X[n][g] of the activations, gathered to the
     //     lanes that hold D rows n = 4 q .. 4 q + 3
     bf16x8_t at[GW][2][3];
     float xg[U4 ? GW : 1][4];
@@ -196,8 +196,7 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
     auto mfma = [](bf16x8_t a, bf16x8_t b, floatx4_t c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     };
-    // one tile's partial product over the wave's groups, into LDS slot u of
-    // buffer buf
+    // the two k-steps of 64-input unit gi against codes w0, w1 (bf16)
     auto group = [&](int gi, bf16x8_t w0, bf16x8_t w1) {
         floatx4_t t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -206,6 +205,8 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
         for (int f = 0; f < 3; ++f) t = mfma(at[gi][1][f], w1, t);
         return t;
     };
+    // one tile's partial product over the wave's groups, into LDS slot u of
+    // buffer buf
     auto reduce = [&](const Tile16 &T, int buf, int u) {
         floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
         if constexpr (U4) {
