@@ -169,6 +169,7 @@ def exact_inputs(fmt, M, K, N, rng):
     (synth.U4_G64, 300, 6144, 5), (synth.I8_ROW, 129, 4096, 11), (synth.I8_G64, 40, 3072, 16),
     (synth.B1_G128, 300, 5120, 5), (synth.B1_G128, 33, 2048, 3),
     (synth.I8_ROW, 77, 3584, 9), (synth.I8_G64, 1000, 2560, 7), (synth.I8_G64, 99, 512, 4),
+    (synth.U4_G64, 1003, 2048, 1), (synth.U4_G64, 259, 6144, 1), (synth.U4_G64, 70, 8192, 1),
 ])
 def test_exact_arithmetic_bit_exact(torch, orc, fmt, M, K, N):
     say(f"exact fmt={fmt} M={M} K={K} N={N}")
@@ -253,6 +254,8 @@ SMALL = [
     (synth.I8_ROW, 127, 3072, 3), (synth.I8_ROW, 129, 16384, 1), (synth.I8_ROW, 45, 20000, 2),
     (synth.U4_G64, 1, 64, 1), (synth.U4_G64, 127, 2112, 1), (synth.U4_G64, 1187, 2048, 4),
     (synth.U4_G64, 129, 6144, 5), (synth.U4_G64, 64, 8192, 16), (synth.U4_G64, 31, 18048, 7),
+    (synth.U4_G64, 5, 2048, 1), (synth.U4_G64, 1003, 2048, 1), (synth.U4_G64, 333, 4096, 1),
+    (synth.U4_G64, 130, 6144, 1), (synth.U4_G64, 77, 8192, 1), (synth.U4_G64, 4099, 4096, 1),
     (synth.B1_G128, 1, 128, 1), (synth.B1_G128, 129, 5120, 1), (synth.B1_G128, 1000, 1152, 2),
     (synth.B1_G128, 63, 17408, 1), (synth.B1_G128, 33, 2048, 16), (synth.B1_G128, 8, 640, 9),
     (synth.B1_G128, 3000, 5120, 5), (synth.B1_G128, 700, 17408, 12), (synth.B1_G128, 129, 1536, 3),
@@ -323,6 +326,29 @@ def test_argmax_ties_and_signed_zero(torch, orc):
     y, idx = gpu_gemv(torch, dev(wi), np.ones((1, K), np.float32), argmax=True)
     assert np.signbit(y[0, 3]) and y[0, 3] == 0 and y[0, 7] == 0 and not np.signbit(y[0, 7])
     assert idx[0] == 3
+
+
+@pytest.mark.parametrize("M,K", [(9001, 2048), (3003, 6144)])
+def test_batch1_argmax_ties(torch, orc, M, K):
+    """One activation row: the maximum row duplicated at the first row, the
+    last row, across waves and in a wave's final, partial block; the lowest
+    index wins."""
+    say(f"batch-1 ties M={M} K={K}")
+    rng = np.random.default_rng([13, M, K])
+    w = synth.draw_weights(synth.U4_G64, M, K, rng)
+    x = synth.draw_x(1, K, rng)
+    ref, _ = orc.qgemv(synth.U4_G64, w.codes, w.scales, w.biases, x, M, K)
+    top = int(np.argmax(ref[0]))
+    dups = [d for d in (0, M - 1, M // 2, M // 2 + 9, M - 2) if d != top]
+    for dst in dups:
+        for arr in (w.codes, w.scales, w.biases):
+            arr[dst] = arr[top]
+    ref, a = orc.qgemv(synth.U4_G64, w.codes, w.scales, w.biases, x, M, K)
+    y, idx = gpu_gemv(torch, dev(w), x, argmax=True)
+    check_bound(y, ref, a, "batch-1 ties")
+    assert all(y[0, d] == y[0, top] for d in dups), "duplicate rows must give identical logits"
+    check_argmax(idx, y, ref, a, orc, "batch-1 ties")
+    assert idx[0] == 0
 
 
 def test_zero_codes_give_bias_times_sum(torch, orc):
@@ -432,6 +458,7 @@ def gpu_greedy(torch, w, x, logits=True):
 
 @pytest.mark.parametrize("fmt,M,K,N", [
     (synth.U4_G64, 9000, 2048, 1), (synth.I8_ROW, 5000, 1024, 1), (synth.B1_G128, 3000, 1280, 1),
+    (synth.U4_G64, 9001, 2048, 1), (synth.U4_G64, 4097, 4096, 1), (synth.U4_G64, 3001, 6144, 1),
     (synth.U4_G64, 40007, 512, 3), (synth.I8_ROW, 777, 1040, 5), (synth.B1_G128, 1000, 6144, 9),
     (synth.U4_G64, 30001, 2048, 64), (synth.I8_ROW, 9000, 1024, 100), (synth.B1_G128, 5000, 1280, 17),
     (synth.U4_G64, 20000, 2048, 128), (synth.U4_G64, 4099, 1024, 256),
