@@ -266,6 +266,8 @@ def run_probe(args, torch, synth):
     L.qg_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                                 ctypes.c_void_p]
     L.qg_probe_read_blocked.argtypes = L.qg_probe_read.argtypes
+    L.qg_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_void_p]
     s = torch.cuda.current_stream().cuda_stream
     if args.probe == "copy":
         n = 256 << 20
@@ -282,8 +284,17 @@ def run_probe(args, torch, synth):
     bufs = [torch.empty(size, dtype=torch.uint8, device="cuda") for _ in range(copies)]
     out = torch.empty(8192, dtype=torch.int32, device="cuda")
     best, best_cfg = None, None
-    for name, fn in (("grid-stride", L.qg_probe_read), ("blocked", L.qg_probe_read_blocked)):
-        for grid in (1024, 2048, 4096, 8192):
+    if args.probe == "stream":
+        modes = ("LDS-direct loads", "LDS-direct loads, read back", "LDS-direct, matrix-core work",
+                 "register loads, matrix-core work")
+        variants = [(modes[m], lambda p, n, o, g, st, m=m: L.qg_probe_stream(p, n, o, g, m, st)) for m in range(4)]
+        grids = (256, 512, 1024, 2048)
+    else:
+        variants = [("grid-stride", L.qg_probe_read), ("blocked", L.qg_probe_read_blocked)]
+        grids = (1024, 2048, 4096, 8192)
+    per = {}
+    for name, fn in variants:
+        for grid in grids:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for b in bufs:
@@ -299,11 +310,16 @@ def run_probe(args, torch, synth):
             e1.record()
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
-            log(f"  read probe {name} grid {grid}: {us:.2f} us, {size / us / 1e3:.1f} GB/s")
+            log(f"  {args.probe} probe {name} grid {grid}: {us:.2f} us, {size / us / 1e3:.1f} GB/s")
+            if name not in per or us < per[name][0]:
+                per[name] = (us, grid)
             if best is None or us < best:
                 best, best_cfg = us, f"{name}, grid {grid}"
-    print(json.dumps({"probe": "read", "bytes": size, "us": round(best, 3),
-                      "GB/s": round(size / best / 1e3, 1), "best": best_cfg}))
+    rec = {"probe": args.probe, "bytes": size, "us": round(best, 3),
+           "GB/s": round(size / best / 1e3, 1), "best": best_cfg}
+    if args.probe == "stream":
+        rec["per_variant_GB/s"] = {k: round(size / v[0] / 1e3, 1) for k, v in per.items()}
+    print(json.dumps(rec))
 
 
 def load_traffic(workload, src_hash):
@@ -333,11 +349,13 @@ def main():
     ap.add_argument("--vendor", action="store_true",
                     help="prefill workloads: also time the vendor FP32 GEMM on weights dequantized "
                          "once (benchmark-only comparison, reported as vendor_ceiling)")
-    ap.add_argument("--probe", choices=["copy", "read"],
+    ap.add_argument("--probe", choices=["copy", "read", "stream"],
                     help="run only a measurement probe: 'copy' copies 256 MiB 8 times (a kernel of "
                          "known traffic, to calibrate FETCH_SIZE / WRITE_SIZE); 'read' times cold "
                          "streaming reads of the workload's weight size (two read kernels, four "
-                         "grid sizes, best reported)")
+                         "grid sizes, best reported); 'stream' the same size through LDS-direct "
+                         "loads, with and without read-back, and with the arithmetic of a "
+                         "matrix-core batch-1 kernel on LDS-direct or register loads")
     args = ap.parse_args()
 
     if args.gpus != 1:
