@@ -31,6 +31,24 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, name), name
 
 
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """The measurement-only probe library loads and checks its arguments on
+    the host (these calls fail validation, so nothing is launched)."""
+    import ctypes
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "gemm_qgemv_amd", "libqgprobe.so")
+    if not os.path.exists(path):
+        pytest.skip("libqgprobe.so not built")
+    lib = ctypes.CDLL(path)
+    for name in ("qg_probe_read", "qg_probe_read_blocked", "qg_probe_copy", "qg_probe_stream"):
+        assert hasattr(lib, name), name
+    lib.qg_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_void_p]
+    assert lib.qg_probe_stream(A, 1024, A, 256, 4, None) == -1      # no such mode
+    assert lib.qg_probe_stream(A, 1000, A, 256, 0, None) == -1      # not a multiple of 16 bytes
+    assert lib.qg_probe_stream(None, 1024, A, 256, 0, None) == -1
+
+
 def test_version_and_status_strings():
     assert q.qg_abi_version() == 1
     for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
