@@ -1,7 +1,8 @@
 // gemv1.hpp -- batch-1 matrix-vector kernel for the 8-bit (per-row and
 // group-64 scales) and 4-bit formats.
 //
-// Workgroups of 4 independent waves; no LDS and no barrier on the hot path.
+// Workgroups of 4 (or 8) independent waves; no LDS and no barrier on the
+// hot path.
 // Lane l owns the 16-byte slices t = l + 64 j (j < NS) of every row, so it
 // keeps exactly the activations of those slices in registers for the whole
 // kernel (loaded once, straight from global memory) together with their
@@ -98,8 +99,10 @@ __device__ __forceinline__ void gemv1_load(Gemv1Cursor &cur, int64_t row_bytes, 
     cur.gs += R * groups;
 }
 
-template <int FMT, int NS, int R, bool FULL, bool NT>
-__global__ __launch_bounds__(256) void gemv1_kernel(Gemv1Params p)
+// WGW: waves per workgroup (4; 8 for greedy-head calls with K of one or two
+// slices per lane, which halves the workgroups folding keys at the end)
+template <int FMT, int NS, int R, bool FULL, bool NT, int WGW>
+__global__ __launch_bounds__(64 * WGW) void gemv1_kernel(Gemv1Params p)
 {
     constexpr int KPS = Fmt<FMT>::KPS;   // 16 (8-bit) or 32 (4-bit)
     constexpr int CPS = KPS / 4;         // float4 chunks per slice
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(256) void gemv1_kernel(Gemv1Params p)
     const int S = static_cast<int>(p.K / KPS);
     const int64_t row_bytes = FMT == FMT_U4_G64 ? p.K / 2 : p.K;
     const int64_t groups = p.K / 64;
-    const int64_t m_begin = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * p.rows_per_wave;
+    const int64_t m_begin = (static_cast<int64_t>(blockIdx.x) * WGW + wave) * p.rows_per_wave;
     const int64_t m_end = min(p.M, m_begin + p.rows_per_wave);
     const int64_t rows = m_end > m_begin ? m_end - m_begin : 0;
     const int nfull = static_cast<int>(rows / R);
