@@ -11,20 +11,29 @@ comes from HBM rather than from the L2 or the 256 MB Infinity Cache.
 
 Reported (one JSON line):
   value          effective weight GB/s = weight bytes read per step / step time
-  roofline       the dominant kernel's algorithmic bytes per launch over its
-                 average launch duration (HIP events on its own stream), vs
-                 the 8 TB/s HBM peak; `traffic` from rocprofv3 counters when a
-                 profile of the current kernel source is committed
-  cpu_baseline   the CPU oracle on the same workload, on this host's cores
+  roofline       the dominant call's algorithmic bytes (or FLOPs) over its
+                 time per call, vs the 8 TB/s HBM peak (2.5 PFLOP/s bf16 for
+                 the prefill product): for a step of one call, the timed
+                 region's step time itself; `traffic` from rocprofv3 counters
+                 and `trace` (median, p10, p90 of the kernel's duration) from
+                 the committed profiles when they were taken from the current
+                 kernel sources
+  read_ceiling   the best cold streaming read of the same byte count by the
+                 measurement-only read kernels, and the call's rate as a
+                 percentage of it
+  gpu_state      clocks, temperatures and power before and after the timed
+                 region (the driver's hwmon files)
+  cpu_baseline   the CPU oracle on the same workload, on all of this host's
+                 threads and on one (with the CPU model)
 
 Other workloads (--workload): any case name of gemm_qgemv_amd.synth.CASES, or
 a config prefix (c0, c1, c2b1, c2b8, c3, c4gemv, c4gemm), or one of the extensions
 (u4gemm, head16, head64, head128, embed, i8g, i8ggemm). GEMM workloads report TFLOP/s; the
 embedding gather reports the GB/s of its ids, packed rows and float32 rows.
 
-The timed region replays a HIP graph of the steps (captured once) so that the
-host's launch cost does not pace the GPU; inputs are resident in HBM before
-timing starts.
+The timed region replays one HIP graph holding all the timed steps (captured
+once) so that the host's launch cost does not pace the GPU; inputs are
+resident in HBM before timing starts.
 """
 from __future__ import annotations
 
@@ -143,56 +152,86 @@ class Launch:
 
 
 def per_launch_ms(torch, fn, stream, n, reps=5):
-    """Average duration of one launch of `fn`: a HIP graph of n back-to-back
-    launches (rotating weight copies) is replayed `reps` times between two
-    HIP events on the stream the kernels run on. Back-to-back graph launches
-    leave no idle gap between kernels, so this is the kernels' own time."""
+    """Average time per call of `fn` when it runs alone: one HIP graph of
+    n * reps back-to-back calls (rotating over n weight copies), replayed
+    once between two HIP events on the stream the kernels run on (the same
+    method as the timed region; it includes the short gaps between
+    consecutive kernels of the graph)."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
-        for i in range(n):
+        for i in range(n * reps):
             fn(i, stream.cuda_stream)
     torch.cuda.synchronize()
     g.replay()
+    torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         e0.record()
-        for _ in range(reps):
-            g.replay()
+        g.replay()
         e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / (reps * n)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(launches, seconds):
+    """The oracle as it stands, on a bounded sample of the step: timed once
+    with all the threads OpenMP gives it and once on one thread, each for
+    about `seconds` / 2. `value` is the all-threads rate."""
     import oracle
     orc = oracle.get()
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        for L in launches:
-            w, x = L.host_w, L.host_x
-            c = L.case
-            if c.op == "gemm":
-                # bounded sample: the first 8 token rows
-                orc.qgemv(c.fmt, w.codes, w.scales, w.biases, x[:8], c.M, c.K)
-            elif c.op == "embed":
-                orc.embed(w.codes, w.scales, w.biases, x, c.M, c.K)
-            else:
-                orc.qgemv(c.fmt, w.codes, w.scales, w.biases, x, c.M, c.K)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+    all_threads = orc.num_threads()
     gemm = launches[0].case.op == "gemm"
-    if gemm:
-        flops = sum(2 * L.case.M * L.case.K * 8 for L in launches) * reps
-        return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
-                "kind": "oracle",
-                "sample": f"first 8 token rows of each GEMM, {reps} repetitions, {el:.1f} s"}
-    wb = sum(L.weight_bytes for L in launches) * reps
-    return {"value": wb / el / 1e9, "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",
-            "sample": f"the whole step ({' + '.join(L.case.name for L in launches)}), "
-                      f"{reps} repetitions, {el:.1f} s"}
+
+    def run(budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            for L in launches:
+                w, x = L.host_w, L.host_x
+                c = L.case
+                if c.op == "gemm":
+                    # bounded sample: the first 8 token rows
+                    orc.qgemv(c.fmt, w.codes, w.scales, w.biases, x[:8], c.M, c.K)
+                elif c.op == "embed":
+                    orc.embed(w.codes, w.scales, w.biases, x, c.M, c.K)
+                else:
+                    orc.qgemv(c.fmt, w.codes, w.scales, w.biases, x, c.M, c.K)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return reps, el
+
+    def rate(reps, el):
+        if gemm:
+            return sum(2 * L.case.M * L.case.K * 8 for L in launches) * reps / el / 1e12
+        return sum(L.weight_bytes for L in launches) * reps / el / 1e9
+
+    reps_n, el_n = run(seconds / 2)
+    orc.set_threads(1)
+    try:
+        reps_1, el_1 = run(seconds / 2)
+    finally:
+        orc.set_threads(all_threads)
+    what = ("first 8 token rows of each GEMM" if gemm else
+            f"the whole step ({' + '.join(L.case.name for L in launches)})")
+    return {"value": rate(reps_n, el_n), "unit": "TFLOP/s" if gemm else "GB/s",
+            "cores": all_threads, "kind": "oracle",
+            "sample": f"{what}: {reps_n} repetitions in {el_n:.1f} s on {all_threads} threads, "
+                      f"{reps_1} in {el_1:.1f} s on 1 thread",
+            "value_1_thread": rate(reps_1, el_1),
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "cpus_allowed": len(os.sched_getaffinity(0))}
 
 
 def vendor_ceiling(launches, torch, stream):
@@ -322,6 +361,158 @@ def run_probe(args, torch, synth):
     print(json.dumps(rec))
 
 
+def gpu_state(torch):
+    """Clocks, temperatures and power of the GPU, read from the kernel
+    driver's hwmon files of its PCI device (plain file reads)."""
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        dev = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (pr.pci_domain_id, pr.pci_bus_id,
+                                                         pr.pci_device_id)
+    except Exception as e:   # noqa: BLE001 - older torch without the PCI ids
+        return {"error": f"no PCI id: {e}"}
+    out = {"pci": os.path.basename(dev)}
+    for hw in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*"))):
+        for f in sorted(glob.glob(os.path.join(hw, "*_input")) + glob.glob(os.path.join(hw, "power*_average"))):
+            name = os.path.basename(f)
+            base = name.rsplit("_", 1)[0]
+            label = base
+            try:
+                with open(os.path.join(hw, base + "_label")) as g:
+                    label = g.read().strip() or base
+            except OSError:
+                pass
+            try:
+                with open(f) as g:
+                    v = int(g.read().strip())
+            except (OSError, ValueError):
+                continue
+            if base.startswith("temp"):
+                out[f"temp_{label}_C"] = v / 1000.0
+            elif base.startswith("freq"):
+                out[f"freq_{label}_MHz"] = v / 1e6
+            elif base.startswith("power"):
+                out[f"power_{label}_W"] = v / 1e6
+    for clk in ("pp_dpm_sclk", "pp_dpm_mclk"):
+        try:
+            with open(os.path.join(dev, clk)) as g:
+                cur = [l.split(":", 1)[1].strip() for l in g if l.rstrip().endswith("*")]
+            if cur:
+                out[clk] = cur[0].rstrip("*").strip()
+        except OSError:
+            pass
+    return out
+
+
+def read_ceiling(torch, nbytes, rotate_mib):
+    """The best cold streaming-read rate over `nbytes` (the step's weight
+    bytes) of the measurement-only read kernels: both read kernels at four
+    grid sizes, over a rotation of copies, HIP graph replays timed with
+    events. Returns (GB/s, description)."""
+    import ctypes
+    path = os.path.join(ROOT, "gemm_qgemv_amd", "libqgprobe.so")
+    if not os.path.exists(path):
+        return None, "libqgprobe.so not built"
+    L = ctypes.CDLL(path)
+    for fn in (L.qg_probe_read, L.qg_probe_read_blocked):
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    size = nbytes // 16 * 16
+    copies = max(1, math.ceil((rotate_mib << 20) / size))
+    bufs = [torch.empty(size, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    out = torch.empty(8192, dtype=torch.int32, device="cuda")
+    best, cfg = None, None
+    for name, fn in (("grid-stride", L.qg_probe_read), ("blocked", L.qg_probe_read_blocked)):
+        for grid in (1024, 2048, 4096, 8192):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for b in bufs:
+                    assert fn(b.data_ptr(), size, out.data_ptr(), grid,
+                              torch.cuda.current_stream().cuda_stream) == 0
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(1, 200 // copies)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+            if best is None or us < best:
+                best, cfg = us, f"{name} read kernel, grid {grid}, {size} bytes x {copies} copies"
+    del bufs
+    return size / best / 1e3, cfg
+
+
+def trace_summary(csv_path, workload, src_hash, command):
+    """Markdown summary of a rocprofv3 kernel-trace CSV: per kernel the
+    number of dispatches, average, median, p10 and p90 duration, with the
+    dominant kernel's algorithmic rate, and a JSON line that bench.py reads
+    back (profiles/trace_<workload>.md)."""
+    import csv
+    import statistics
+    from gemm_qgemv_amd import synth
+    durs = {}
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name") or row.get("KernelName")
+            t = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+            durs.setdefault(name, []).append(t)
+    names = WORKLOADS.get(workload, [workload])
+    cases = [synth.CASES_BY_NAME[n] for n in names]
+    rows = []
+    for k, v in durs.items():
+        v = sorted(v)
+        q = statistics.quantiles(v, n=10) if len(v) >= 10 else [v[0]] * 9
+        rows.append({"kernel": k, "calls": len(v), "avg_us": statistics.fmean(v),
+                     "median_us": statistics.median(v), "p10_us": q[0], "p90_us": q[8],
+                     "total_us": sum(v)})
+    rows.sort(key=lambda r: -r["total_us"])
+    dom = rows[0]
+    gemm = cases[0].op == "gemm"
+    lines = [f"# Kernel trace: workload {workload} ({', '.join(names)})", "",
+             "Command (repository root, one MI355X):", "", "```", command, "```", "",
+             "| kernel | calls | average (us) | median (us) | p10 (us) | p90 (us) | % of GPU time |",
+             "|---|---|---|---|---|---|---|"]
+    tot = sum(r["total_us"] for r in rows)
+    for r in rows:
+        lines.append(f"| `{r['kernel']}` | {r['calls']} | {r['avg_us']:.2f} | {r['median_us']:.2f} | "
+                     f"{r['p10_us']:.2f} | {r['p90_us']:.2f} | {100 * r['total_us'] / tot:.1f} |")
+    rec = {"workload": workload, "kernel": dom["kernel"], "calls": dom["calls"],
+           "avg_us": round(dom["avg_us"], 3), "median_us": round(dom["median_us"], 3),
+           "p10_us": round(dom["p10_us"], 3), "p90_us": round(dom["p90_us"], 3),
+           "kernel_source_hash": src_hash}
+    if len(cases) == 1:
+        c = cases[0]
+        if gemm:
+            rec["tflops_at_median"] = round(c.flops / (dom["median_us"] * 1e-6) / 1e12, 2)
+            rec["frac_of_bf16_peak_at_median"] = round(rec["tflops_at_median"] / BF16_MATRIX_PEAK_TFLOPS, 4)
+        else:
+            b = c.weight_bytes
+            rec["algorithmic_bytes"] = b
+            rec["GBs_at_average"] = round(b / (dom["avg_us"] * 1e-6) / 1e9, 1)
+            rec["GBs_at_median"] = round(b / (dom["median_us"] * 1e-6) / 1e9, 1)
+            rec["frac_of_hbm_peak_at_median"] = round(rec["GBs_at_median"] / HBM_PEAK_GBS, 4)
+    lines += ["", f"Kernel source hash (sha256 of gemm_qgemv_amd/csrc except probe.hip, first 16 hex): "
+              f"`{src_hash}`.", "", "```json", json.dumps(rec), "```", ""]
+    return "\n".join(lines)
+
+
+def load_trace(workload, src_hash):
+    """The committed kernel-trace summary of this workload, if it was taken
+    from the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"trace_{workload}.md")
+    if not os.path.exists(p):
+        return None
+    text = open(p).read()
+    if "```json" not in text:
+        return None
+    rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    if rec.get("kernel_source_hash") != src_hash:
+        return None
+    rec["file"] = os.path.relpath(p, ROOT)
+    return rec
+
+
 def load_traffic(workload, src_hash):
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
@@ -349,6 +540,13 @@ def main():
     ap.add_argument("--vendor", action="store_true",
                     help="prefill workloads: also time the vendor FP32 GEMM on weights dequantized "
                          "once (benchmark-only comparison, reported as vendor_ceiling)")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="summarize a rocprofv3 kernel-trace CSV of this workload (markdown with a "
+                         "JSON line, as committed under profiles/trace_<workload>.md) and exit")
+    ap.add_argument("--trace-command", default="",
+                    help="the command that produced the trace, quoted in the summary")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip timing the streaming-read ceiling over the step's weight bytes")
     ap.add_argument("--probe", choices=["copy", "read", "stream"],
                     help="run only a measurement probe: 'copy' copies 256 MiB 8 times (a kernel of "
                          "known traffic, to calibrate FETCH_SIZE / WRITE_SIZE); 'read' times cold "
@@ -362,6 +560,11 @@ def main():
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the kernels work on one "
               "GPU's share of the matrix; there is no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.workload, kernel_source_hash(),
+                            args.trace_command))
+        return
 
     import torch
 
@@ -390,9 +593,9 @@ def main():
     per_step_launch_target = 2000 // len(launches) if not gemm else 20
     steps = args.steps or max(rot, per_step_launch_target)
     warmup = args.warmup or max(rot, 20 if not gemm else 3)
-    # graph of `rot` consecutive steps (one pass over the weight copies)
-    chunk = rot if not gemm else 1
-    steps = math.ceil(steps / chunk) * chunk
+    # one HIP graph of all the timed steps (step i reads weight copy
+    # i mod copies), so the host's graph launch is paid once, not per step
+    chunk = steps
 
     with torch.cuda.stream(stream):
         for i in range(warmup):
@@ -416,6 +619,7 @@ def main():
         graph.replay()
         torch.cuda.synchronize()
 
+    state_before = gpu_state(torch)
     # ---- timed region -------------------------------------------------
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -436,43 +640,58 @@ def main():
     ms_per_step = ms_total / steps
     log(f"timed {steps} steps: {ms_total:.3f} ms on the stream, {wall * 1e3:.3f} ms wall")
 
-    # ---- per-launch durations of each kernel call ------------------------
+    state_after = gpu_state(torch)
+
+    # ---- per-call durations ---------------------------------------------
+    # A step of one call: the call's duration is the timed region's step
+    # time. A step of several calls: each call timed alone the same way (a
+    # HIP graph of one pass over its weight copies, replayed, between HIP
+    # events on the stream the kernels run on).
     per_case = []
-    for L in launches:
-        n = L.copies if not gemm else 4
-        avg = per_launch_ms(torch, L, stream, n, reps=max(1, 400 // n) if not gemm else 5)
-        per_case.append((L, avg, avg))
+    if len(launches) == 1:
+        per_case.append((launches[0], ms_per_step))
+    else:
+        for L in launches:
+            n = L.copies if not gemm else 4
+            per_case.append((L, per_launch_ms(torch, L, stream, n,
+                                              reps=max(1, 400 // n) if not gemm else 5)))
+    for L, avg in per_case:
         unit = L.weight_bytes / (avg * 1e-3) / 1e9
-        log(f"  {L.case.name}: {avg * 1e3:.2f} us per launch, {unit:.1f} GB/s weight"
+        log(f"  {L.case.name}: {avg * 1e3:.2f} us per call, {unit:.1f} GB/s weight"
             + (f", {L.case.flops / (avg * 1e-3) / 1e12:.2f} TFLOP/s"
                if gemm or (L.case.rows > 1 and L.case.op != "embed") else ""))
 
     src_hash = kernel_source_hash()
     traffic = load_traffic(args.workload, src_hash)
+    trace = load_trace(args.workload, src_hash)
+    dom = max(per_case, key=lambda t: t[1])
     if gemm:
         flops = sum(L.case.flops for L in launches)
         value = flops / (ms_per_step * 1e-3) / 1e12
         unit = "TFLOP/s"
-        dom = max(per_case, key=lambda t: t[1])
         ach = dom[0].case.flops / (dom[1] * 1e-3) / 1e12
         # the products run on bf16 MFMA (three exact passes per algorithmic
         # multiply-add), so the bf16 dense peak is the ceiling
         roof = {"bound": "mfma", "achieved": round(ach, 3), "peak": BF16_MATRIX_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / BF16_MATRIX_PEAK_TFLOPS, 4),
                 "traffic": traffic, "kernel_call": dom[0].case.name,
-                "mfma_passes_per_mac": 3}
+                "us_per_call": round(dom[1] * 1e3, 3), "mfma_passes_per_mac": 3,
+                "frac_of_fp32_matrix_peak": round(ach / FP32_MATRIX_PEAK_TFLOPS, 4)}
         dtype = "f32"
     else:
         wbytes = sum(L.weight_bytes for L in launches)
         value = wbytes / (ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
-        tot_b = sum(L.weight_bytes for L, _, _ in per_case)
-        tot_t = sum(avg for _, avg, _ in per_case)
-        ach = tot_b / (tot_t * 1e-3) / 1e9
+        ach = dom[0].weight_bytes / (dom[1] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel_calls": [L.case.name for L, _, _ in per_case]}
+                "kernel_call": dom[0].case.name, "us_per_call": round(dom[1] * 1e3, 3),
+                "algorithmic_bytes_per_call": dom[0].weight_bytes}
         dtype = "f32"
+    roof["timing"] = ("timed region (the step is this one call)" if len(launches) == 1 else
+                      "this call alone, timed like the step")
+    if trace is not None:
+        roof["trace"] = trace
 
     embed = cases[0].op == "embed"
     out = {
@@ -496,8 +715,14 @@ def main():
                    "launch": "hip graph" if graph is not None else "eager"},
         "roofline": roof,
     }
+    out["gpu_state"] = {"before": state_before, "after": state_after}
     if not gemm:
         out["pct_of_hbm_peak"] = round(100 * value / HBM_PEAK_GBS, 2)
+        if not args.no_read_ceiling and cases[0].op != "embed":
+            rc, how = read_ceiling(torch, dom[0].weight_bytes, args.rotate_mib)
+            if rc is not None:
+                out["read_ceiling"] = {"GB/s": round(rc, 1), "how": how,
+                                       "pct_of_ceiling": round(100 * ach / rc, 2)}
     if not gemm and not embed:
         out["tok_s_equiv"] = round(value * 1e9 / BYTES_PER_TOKEN[cases[0].fmt], 1)
     if gemm and args.vendor:

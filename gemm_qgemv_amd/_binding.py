@@ -18,7 +18,7 @@ QG_ERR_NULL, QG_ERR_FORMAT, QG_ERR_SHAPE, QG_ERR_ALIGN = -1, -2, -3, -4
 QG_ERR_WORKSPACE, QG_ERR_ALIAS, QG_ERR_LAUNCH, QG_ERR_UNSUPPORTED = -5, -6, -7, -8
 QG_MAX_GEMV_BATCH = 16
 QG_MAX_ARGMAX_BATCH = 256
-QG_WS_CONTROL_BYTES = 4096
+QG_WS_CONTROL_BYTES = 8192
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqg.so")
 

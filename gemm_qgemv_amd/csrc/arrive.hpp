@@ -1,0 +1,217 @@
+// arrive.hpp -- cross-workgroup completion for the greedy head and the
+// in-kernel split-K combine, robust to whatever the workspace's control
+// words hold when a call starts.
+//
+// Completion word. A 64-bit word whose high half is the tag of the dispatch
+// that owns it and whose low half counts the workgroups of that dispatch that
+// have arrived. The tag is derived from the dispatch's AQL packet index and
+// its queue, so two dispatches that use the same workspace one after the
+// other carry different tags. Thread 0 of every workgroup reads the word when
+// the workgroup starts (arrival_peek; the value is only used at the end, so
+// nothing waits for it). When the workgroup arrives and its early read showed
+// another tag (leftovers of an earlier call, a call that never finished, or
+// uninitialised memory), it first claims the word with one compare-and-swap
+// from that value to (tag, 0); the swap fails harmlessly when another
+// workgroup of the same dispatch has already claimed it (the word can then
+// only hold this dispatch's tag, since no other dispatch touches it
+// meanwhile). The increment waits for that swap, so every increment of a
+// dispatch lands on a word that already carries its tag, and the workgroup
+// that sees the count reach total - 1 is the last one. Nothing has to be
+// zero on entry, nothing is cleared on exit, and a call that was cut short
+// or raced with another on the same workspace cannot disturb the calls
+// after it.
+//
+// Ordering. Data moves between workgroups only through device-scope atomics
+// (the parked keys and partial sums, the counters), which are performed at
+// the device's coherence point rather than in an XCD's own L2. A returning
+// atomic has been performed when its value comes back. Each workgroup issues
+// its counter increment with an address that depends, through one vector
+// AND with zero, on the values returned by its claim and by every atomic
+// that carried its data; the increment therefore cannot be performed before
+// them. The last workgroup reads the parked data with device-scope atomic
+// loads issued after its increment has returned, so it sees every value
+// that was performed before the other workgroups counted themselves in. No
+// cache writeback or invalidate is needed, because no plain store or load
+// carries data between workgroups.
+#pragma once
+
+#include "qg_device.hpp"
+
+namespace qg {
+
+// Packet index of this dispatch in its queue (an implicit input of every
+// kernel that asks for it).
+extern "C" __device__ unsigned long long qg_llvm_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+
+// 32-bit tag of this dispatch: its packet index mixed with its queue's
+// address (dispatches on different queues count from the same start).
+__device__ __forceinline__ uint32_t dispatch_tag()
+{
+    const uint64_t id = qg_llvm_dispatch_id();
+    const uint64_t q = reinterpret_cast<uint64_t>(__builtin_amdgcn_queue_ptr());
+    const uint64_t h = (q >> 6) * 0x9E3779B97F4A7C15ull;
+    return static_cast<uint32_t>(id) ^ static_cast<uint32_t>(h >> 32);
+}
+
+// Control words at the start of every workspace: the greedy head's
+// completion word, then one completion word per row tile for the in-kernel
+// split-K combine.
+struct GreedyCtl {
+    unsigned long long arrive;
+};
+constexpr int kCtlBytes = 8192;
+constexpr int kCtlTileOffset = 256;
+constexpr int kCtlTileCounters = (kCtlBytes - kCtlTileOffset) / 8;
+
+__device__ __forceinline__ unsigned long long *tile_counters(GreedyCtl *ctl)
+{
+    return reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(ctl) + kCtlTileOffset);
+}
+
+// The word as it stands when the workgroup starts (thread 0).
+__device__ __forceinline__ unsigned long long arrival_peek(const unsigned long long *word)
+{
+    return __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Claim `word` for this dispatch (thread 0, at arrival): swap the early read
+// for (tag, 0), or, when the early read already showed this tag, for itself
+// (then the swap changes nothing whether or not it succeeds). No branch, so
+// the swap goes out beside the workgroup's other atomics instead of after
+// them. Returns a token of the swap's result for arrival_last to depend on.
+__device__ __forceinline__ uint32_t arrival_claim(unsigned long long *word, uint32_t tag,
+                                                  unsigned long long peek)
+{
+    unsigned long long expected = peek;
+    const unsigned long long mine = static_cast<uint32_t>(peek >> 32) == tag
+                                        ? peek
+                                        : static_cast<unsigned long long>(tag) << 32;
+    __hip_atomic_compare_exchange_strong(word, &expected, mine, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return static_cast<uint32_t>(expected) | static_cast<uint32_t>(expected >> 32);
+}
+
+// Count the calling workgroup in (one thread); true for the last of `total`.
+// `dep` folds together the values returned by the claim and by the atomics
+// that carried the workgroup's data.
+__device__ __forceinline__ bool arrival_last(unsigned long long *word, uint32_t tag, uint32_t dep,
+                                             unsigned total)
+{
+    uint32_t zero;
+    asm volatile("v_and_b32 %0, 0, %1" : "=v"(zero) : "v"(dep));
+    const unsigned long long old =
+        __hip_atomic_fetch_add(word + zero, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return static_cast<uint32_t>(old >> 32) == tag && static_cast<uint32_t>(old) == total - 1u;
+}
+
+// ---------------------------------------------------------------------------
+// In-kernel split-K combine: several workgroups own the same rows, each for
+// a different chunk of K. splitk_put stores one partial sum with a returning
+// device-scope exchange and waits for its return; splitk_arrive (all threads
+// of the workgroup) then counts the workgroup in on its row tile's word, so
+// the count moves only after every partial of the workgroup is in place. The
+// workgroup that completes the count reads all partials back with
+// device-scope atomic loads, in split order (splitk_sum).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void splitk_put(float *dst, float v)
+{
+    const float old = __hip_atomic_exchange(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" ::"v"(old));   // the exchange has returned
+}
+
+__device__ __forceinline__ float splitk_get(const float *src)
+{
+    return __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Sum of the nsplit partials part[s * stride], s = 0 .. nsplit-1, added in
+// split order. The device-scope loads go out in batches of 8 before any of
+// them is used (a plain loop would wait for each one in turn); a batch
+// past the last split re-reads the last partial and drops it.
+__device__ __forceinline__ float splitk_sum(const float *part, int64_t stride, int nsplit)
+{
+    constexpr int kBatch = 8;
+    float acc = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
+        float v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) v[i] = splitk_get(part + min(s0 + i, nsplit - 1) * stride);
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            if (s0 + i < nsplit) acc += v[i];
+    }
+    return acc;
+}
+
+// All threads. `peek` is thread 0's arrival_peek of `word`; its claim goes
+// out before the barrier, beside the other threads' exchanges.
+__device__ __forceinline__ bool splitk_arrive(unsigned long long *word, int nsplit, uint32_t tag,
+                                              unsigned long long peek)
+{
+    __shared__ unsigned s_last;
+    uint32_t dep = 0;
+    if (threadIdx.x == 0) dep = arrival_claim(word, tag, peek);
+    __syncthreads();   // every thread's exchanges have returned
+    if (threadIdx.x == 0) s_last = arrival_last(word, tag, dep, static_cast<unsigned>(nsplit));
+    __syncthreads();
+    return s_last != 0;
+}
+
+// ---------------------------------------------------------------------------
+// Greedy selection across workgroups. wg_key[b] (b < nb <= 16, in LDS) is
+// this workgroup's best (value, index) key of activation row b. Each
+// workgroup parks its nb keys in its own row of `keys` ([nwg][nb], any
+// initial contents) with returning device-scope exchanges and counts itself
+// in once; the last one reads every row back, reduces them and writes the
+// indices. `peek` is thread 0's arrival_peek of ctl->arrive; the claim and
+// the key exchanges go out together. Must be reached by all threads of the
+// workgroup.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void greedy_finish_rows(const unsigned long long *wg_key, int nb,
+                                                   GreedyCtl *ctl, unsigned long long *keys,
+                                                   int32_t *idx, int nwg, uint32_t tag,
+                                                   unsigned long long peek)
+{
+    __shared__ unsigned s_last;
+    __shared__ unsigned long long s_best[16];
+    if (threadIdx.x == 0) {
+        uint32_t dep = 0;
+        for (int b = 0; b < nb; ++b) {
+            const unsigned long long old = __hip_atomic_exchange(
+                &keys[static_cast<int64_t>(blockIdx.x) * nb + b], wg_key[b], __ATOMIC_RELAXED,
+                __HIP_MEMORY_SCOPE_AGENT);
+            dep |= static_cast<uint32_t>(old) | static_cast<uint32_t>(old >> 32);
+        }
+        dep |= arrival_claim(&ctl->arrive, tag, peek);
+        s_last = arrival_last(&ctl->arrive, tag, dep, static_cast<unsigned>(nwg));
+    }
+    if (threadIdx.x < 16) s_best[threadIdx.x] = 0ull;
+    __syncthreads();
+    if (!s_last) return;
+    const int total = nwg * nb;
+    if (nb == 1) {
+        // one key per workgroup: a maximum per thread, then per wave
+        unsigned long long best = 0ull;
+        for (int i = threadIdx.x; i < total; i += blockDim.x) {
+            const unsigned long long k =
+                __hip_atomic_load(&keys[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            best = k > best ? k : best;
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const uint64_t other = shfl_xor_u64(best, o);
+            best = other > best ? other : best;
+        }
+        if ((threadIdx.x & 63) == 0) atomicMax(&s_best[0], best);
+    } else {
+        for (int i = threadIdx.x; i < total; i += blockDim.x) {
+            const unsigned long long k =
+                __hip_atomic_load(&keys[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            atomicMax(&s_best[i % nb], k);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < nb) idx[threadIdx.x] = static_cast<int32_t>(argmax_key_index(s_best[threadIdx.x]));
+}
+
+}  // namespace qg

@@ -21,11 +21,8 @@
 // with sum(x) over the slice precomputed once per workgroup.
 #pragma once
 
+#include "arrive.hpp"
 #include "qg_device.hpp"
-
-#ifndef QG_GREEDY_SLOTS
-#define QG_GREEDY_SLOTS 16
-#endif
 
 namespace qg {
 
@@ -44,7 +41,8 @@ struct GemvParams {
     const float *x;       // [nb][K]
     float *y;             // [nb][M] final output (used when nsplit == 1)
     float *part;          // [nsplit][nb][M] partial sums (used when nsplit > 1)
-    struct GreedyCtl *ctl; // greedy head control words, or nullptr
+    GreedyCtl *ctl;       // control words (greedy head), or nullptr
+    unsigned long long *keys;  // greedy keys [nkeys][nb] in the workspace
     int32_t *idx;         // [nb] greedy indices
     int64_t M;
     int64_t K;
@@ -174,158 +172,6 @@ __device__ __forceinline__ uint32_t word_of(const uint4 &c, int j)
     return j == 0 ? c.x : j == 1 ? c.y : j == 2 ? c.z : c.w;
 }
 
-// Greedy selection across workgroups, without fences. wg_key[b] (b < nb,
-// in LDS) is this workgroup's best key of batch row b. The control words
-// hold one 64-bit slot per batch row and a counter of finished workgroups,
-// all zero on entry. Every workgroup folds its keys into the slots with
-// device-scope atomic maxima (performed at the device's coherence point; the
-// maximum does not depend on their order), then increments the counter; the
-// increment takes its address through the maxima's returned values, so it is
-// issued only after they have been performed. The workgroup that brings the
-// counter to nkeys therefore sees every key in the slots: it writes idx[b]
-// and puts the slots and the counter back to zero. No cache writeback is
-// needed because only atomics carry data between workgroups.
-// Must be reached by all threads of the workgroup.
-struct GreedyCtl {
-    unsigned long long slot[QG_GREEDY_SLOTS];
-    unsigned counter;
-};
-
-// Control words of a workspace: the greedy head's slots and counter, then
-// one counter per row tile for the fused split-K combine.
-constexpr int kCtlBytes = 4096;
-constexpr int kCtlTileOffset = 256;
-constexpr int kCtlTileCounters = (kCtlBytes - kCtlTileOffset) / 4;
-
-__device__ __forceinline__ unsigned *tile_counters(GreedyCtl *ctl)
-{
-    return reinterpret_cast<unsigned *>(reinterpret_cast<char *>(ctl) + kCtlTileOffset);
-}
-
-// Fused split-K combine without fences, used when several workgroups own
-// the same rows, each for a different chunk of K. splitk_put stores one
-// partial sum with a returning device-scope atomic exchange (performed at
-// the device's coherence point) and waits for its return; splitk_arrive then
-// counts the workgroup in on its row tile's counter (zero on entry), so the
-// count moves only after every partial of the workgroup is in place. The
-// workgroup that completes the count reads all partials back with
-// device-scope atomic loads, in split order (splitk_get), and puts the
-// counter back to zero. All threads of the workgroup call splitk_arrive.
-__device__ __forceinline__ void splitk_put(float *dst, float v)
-{
-    const float old = __hip_atomic_exchange(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("" ::"v"(old));   // the exchange has returned
-}
-
-__device__ __forceinline__ float splitk_get(const float *src)
-{
-    return __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Sum of the nsplit partials part[s * stride], s = 0 .. nsplit-1, added in
-// split order. The device-scope loads go out in batches of 8 before any of
-// them is used (a plain loop would wait for each one in turn); a batch
-// past the last split re-reads the last partial and drops it.
-__device__ __forceinline__ float splitk_sum(const float *part, int64_t stride, int nsplit)
-{
-    constexpr int kBatch = 8;
-    float acc = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += kBatch) {
-        float v[kBatch];
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) v[i] = splitk_get(part + min(s0 + i, nsplit - 1) * stride);
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i)
-            if (s0 + i < nsplit) acc += v[i];
-    }
-    return acc;
-}
-
-__device__ __forceinline__ bool splitk_arrive(unsigned *counter, int nsplit)
-{
-    __shared__ unsigned s_last;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned t = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (t == static_cast<unsigned>(nsplit) - 1u);
-        if (s_last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    return s_last != 0;
-}
-
-__device__ __forceinline__ void greedy_finish(const unsigned long long *wg_key, int nb,
-                                              GreedyCtl *ctl, int32_t *idx, int nkeys)
-{
-    __shared__ unsigned s_last;
-    if (threadIdx.x == 0) {
-        uint32_t dep = 0;
-        for (int b = 0; b < nb; ++b) {
-            const unsigned long long old = __hip_atomic_fetch_max(
-                &ctl->slot[b], wg_key[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            dep |= static_cast<uint32_t>(old) | static_cast<uint32_t>(old >> 32);
-        }
-        uint32_t zero;
-        asm volatile("v_and_b32 %0, 0, %1" : "=v"(zero) : "v"(dep));  // 0, after the maxima return
-        const unsigned t = __hip_atomic_fetch_add(&ctl->counter + zero, 1u, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (t == static_cast<unsigned>(nkeys) - 1u);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    if (threadIdx.x < nb) {
-        const unsigned long long best = __hip_atomic_exchange(
-            &ctl->slot[threadIdx.x], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        idx[threadIdx.x] = static_cast<int32_t>(argmax_key_index(best));
-    }
-    if (threadIdx.x == 0)
-        __hip_atomic_store(&ctl->counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Greedy finish for grids whose workgroups all end at about the same time:
-// rather than folding its keys into shared slots (contended atomics on one
-// line, serialized at the coherence point), each workgroup parks its nb
-// keys in its own row of `keys` ([workgroups][KS], KS >= nb, any initial
-// contents)
-// with returning device-scope exchanges, then counts itself in once. The
-// last workgroup reads every row back with device-scope atomic loads,
-// reduces them, writes the indices and puts the counter back to zero.
-template <int KS>
-__device__ __forceinline__ void greedy_finish_rows(const unsigned long long *wg_key, int nb,
-                                                   GreedyCtl *ctl, unsigned long long *keys,
-                                                   int32_t *idx, int nwg)
-{
-    __shared__ unsigned s_last;
-    __shared__ unsigned long long s_best[KS];
-    if (threadIdx.x == 0) {
-        uint32_t dep = 0;
-        for (int b = 0; b < nb; ++b) {
-            const unsigned long long old = __hip_atomic_exchange(
-                &keys[static_cast<int64_t>(blockIdx.x) * KS + b], wg_key[b], __ATOMIC_RELAXED,
-                __HIP_MEMORY_SCOPE_AGENT);
-            dep |= static_cast<uint32_t>(old) | static_cast<uint32_t>(old >> 32);
-        }
-        uint32_t zero;
-        asm volatile("v_and_b32 %0, 0, %1" : "=v"(zero) : "v"(dep));  // 0, after the exchanges return
-        const unsigned t = __hip_atomic_fetch_add(&ctl->counter + zero, 1u, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (t == static_cast<unsigned>(nwg) - 1u);
-    }
-    if (threadIdx.x < KS) s_best[threadIdx.x] = 0ull;
-    __syncthreads();
-    if (!s_last) return;
-    for (int i = threadIdx.x; i < nwg * nb; i += blockDim.x) {
-        const int w = i / nb, b = i - w * nb;
-        const unsigned long long k = __hip_atomic_load(&keys[static_cast<int64_t>(w) * KS + b],
-                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        atomicMax(&s_best[b], k);
-    }
-    __syncthreads();
-    if (threadIdx.x < nb) idx[threadIdx.x] = static_cast<int32_t>(argmax_key_index(s_best[threadIdx.x]));
-    if (threadIdx.x == 0)
-        __hip_atomic_store(&ctl->counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Main kernel. B: batch rounded up to a power of two (x rows >= nb are
 // zero in LDS and their outputs are not written). R: rows per block.
 template <int FMT, int B, int R>
@@ -344,6 +190,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
     const int xsp = static_cast<int>(xsum_floats<FMT>(kc));
     float4 *xl = lds;
     float *xs = reinterpret_cast<float *>(lds + B * pc);
+
+    // greedy head: read the completion word as it stands at the start
+    const bool greedy = p.ctl != nullptr && p.nsplit == 1;
+    const uint32_t tag = greedy ? dispatch_tag() : 0u;
+    unsigned long long peek = 0;
+    if (greedy && threadIdx.x == 0) peek = arrival_peek(&p.ctl->arrive);
 
     stage_x<FMT, B>(p, k0, kc, xl, xs);
     __syncthreads();
@@ -572,7 +424,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
         }
     }
 
-    if (p.ctl != nullptr && p.nsplit == 1) {
+    if (greedy) {
         __shared__ unsigned long long wg_key[B];
         __syncthreads();
         if (threadIdx.x < B) wg_key[threadIdx.x] = 0ull;
@@ -581,7 +433,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
             atomicMax(&wg_key[own_b], static_cast<unsigned long long>(
                                           argmax_key(best_v, static_cast<uint32_t>(best_m))));
         __syncthreads();
-        greedy_finish(wg_key, p.nb, p.ctl, p.idx, p.nkeys);
+        greedy_finish_rows(wg_key, p.nb, p.ctl, p.keys, p.idx, p.nkeys, tag, peek);
     }
 }
 
@@ -590,6 +442,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
 __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvParams p)
 {
     __shared__ unsigned long long wg_key[16];
+    const uint32_t tag = p.ctl != nullptr ? dispatch_tag() : 0u;
+    unsigned long long peek = 0;
+    if (p.ctl != nullptr && threadIdx.x == 0) peek = arrival_peek(&p.ctl->arrive);
     if (threadIdx.x < 16) wg_key[threadIdx.x] = 0ull;
     __syncthreads();
     const int64_t m_begin = static_cast<int64_t>(blockIdx.x) * p.rows_per_wg;
@@ -609,7 +464,7 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvParams p)
     }
     if (p.ctl != nullptr) {
         __syncthreads();
-        greedy_finish(wg_key, p.nb, p.ctl, p.idx, p.nkeys);
+        greedy_finish_rows(wg_key, p.nb, p.ctl, p.keys, p.idx, p.nkeys, tag, peek);
     }
 }
 

@@ -16,8 +16,8 @@
 // are combined with DPP and permlane exchanges (no LDS).
 //
 // Greedy head: each wave keeps the (value, index) of its best row; the
-// workgroup folds one key into the device-wide slot, and the last workgroup
-// to finish writes the index (see greedy_finish).
+// workgroup parks one key in its row of the workspace, and the last
+// workgroup to finish reduces them and writes the index (greedy_finish_rows).
 #pragma once
 
 #include "gemv.hpp"
@@ -31,6 +31,7 @@ struct Gemv1Params {
     const float *x;      // [K]
     float *y;            // [M]
     GreedyCtl *ctl;      // greedy head control words, or nullptr
+    unsigned long long *keys;  // greedy keys, one per workgroup, in the workspace
     int32_t *idx;        // greedy index output
     int64_t M;
     int64_t K;
@@ -154,6 +155,13 @@ __global__ __launch_bounds__(64 * WGW) void gemv1_kernel(Gemv1Params p)
         xs[j] = s;
     }
 
+    // greedy head: read the completion word as it stands at the start (after the
+    // first block's and the activations' loads, so that the first wait does
+    // not include it)
+    const uint32_t tag = p.ctl != nullptr ? dispatch_tag() : 0u;
+    unsigned long long peek = 0;
+    if (p.ctl != nullptr && threadIdx.x == 0) peek = arrival_peek(&p.ctl->arrive);
+
     float best_v = 0.f;
     int64_t best_m = -1;
 
@@ -227,7 +235,7 @@ __global__ __launch_bounds__(64 * WGW) void gemv1_kernel(Gemv1Params p)
         }
         if (lane == 0) atomicMax(&s_key, static_cast<unsigned long long>(key));
         __syncthreads();
-        greedy_finish(&s_key, 1, p.ctl, p.idx, static_cast<int>(gridDim.x));
+        greedy_finish_rows(&s_key, 1, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x), tag, peek);
     }
 }
 

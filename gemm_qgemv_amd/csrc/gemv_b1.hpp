@@ -25,7 +25,7 @@
 // loads. Chunks of K go to different workgroups; their partial sums are
 // combined in split order by the last workgroup of each row tile
 // (splitk_arrive), or by gemv_combine_kernel when there are more row tiles
-// than counters.
+// than completion words.
 #pragma once
 
 #include "gemv.hpp"
@@ -42,6 +42,7 @@ struct B1LutParams {
     float *y;             // [nb][M] (one chunk)
     float *part;          // [nsplit][nb][M] (several chunks)
     GreedyCtl *ctl;       // control words (greedy head, split-K tile counters)
+    unsigned long long *keys;  // greedy keys [row tiles][nb] in the workspace
     int32_t *idx;         // greedy index output, or nullptr
     int64_t M, K;
     int nb;               // activation rows of this launch (x [nb][K], y [nb][M])
@@ -106,6 +107,17 @@ __global__ __launch_bounds__(256) void gemv_b1_lut_kernel(B1LutParams p)
     const uint16_t *sp = p.scales + (mv ? m : 0) * groups + k0 / 128 + wave * GPW;
 #pragma unroll
     for (int j = 0; j < GPW; ++j) sc[j] = (mv && wave * GPW + j < ng) ? sp[j] : 0u;
+
+    // read the completion words this dispatch counts on as they stand at
+    // the start: the row tile's (in-kernel split-K combine) and the greedy
+    // head's
+    const bool fused_split = p.nsplit > 1 && p.fused;
+    const uint32_t tag = (fused_split || p.idx != nullptr) ? dispatch_tag() : 0u;
+    unsigned long long peek_tile = 0, peek_greedy = 0;
+    if (tid == 0) {
+        if (fused_split) peek_tile = arrival_peek(&tile_counters(p.ctl)[blockIdx.x]);
+        if (p.idx != nullptr) peek_greedy = arrival_peek(&p.ctl->arrive);
+    }
 
     // 2. tables of this chunk: thread q builds position q (16 signed sums)
     //    for every activation row (all rows' activations requested first)
@@ -213,7 +225,7 @@ __global__ __launch_bounds__(256) void gemv_b1_lut_kernel(B1LutParams p)
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
                     if (b < nb) splitk_put(part + b * p.M, acc[b]);
-            if (!splitk_arrive(&tile_counters(p.ctl)[blockIdx.x], p.nsplit)) return;
+            if (!splitk_arrive(&tile_counters(p.ctl)[blockIdx.x], p.nsplit, tag, peek_tile)) return;
 #pragma unroll
             for (int b = 0; b < NB; ++b)
                 acc[b] = own && b < nb ? splitk_sum(p.part + b * p.M + m, nb * p.M, p.nsplit) : 0.f;
@@ -244,7 +256,8 @@ __global__ __launch_bounds__(256) void gemv_b1_lut_kernel(B1LutParams p)
             if (lane == 0) atomicMax(&s_key[b], static_cast<unsigned long long>(key));
         }
         __syncthreads();
-        greedy_finish(s_key, nb, p.ctl, p.idx, static_cast<int>(gridDim.x));
+        greedy_finish_rows(s_key, nb, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x), tag,
+                           peek_greedy);
     }
 }
 

@@ -157,6 +157,11 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
     for (int u = 0; u < NB - 1; ++u)
         if (u < nt) load(ring[u], tb + u);
 
+    // greedy head: read the completion word as it stands at the start
+    const uint32_t tag = p.ctl != nullptr ? dispatch_tag() : 0u;
+    unsigned long long peek = 0;
+    if (p.ctl != nullptr && tid == 0) peek = arrival_peek(&p.ctl->arrive);
+
     // 1b. exact three-way split into operand pieces; for the 4-bit bias
     //     term the group sums X[n][g] of the activations, gathered to the
     //     lanes that hold D rows n = 4 q .. 4 q + 3
@@ -353,7 +358,7 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
         }
         if (srr == 0 && sn < p.nb) atomicMax(&wg_key[sn], static_cast<unsigned long long>(key));
         __syncthreads();
-        greedy_finish_rows<16>(wg_key, p.nb, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x));
+        greedy_finish_rows(wg_key, p.nb, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x), tag, peek);
     }
 }
 

@@ -103,14 +103,14 @@ Range range_of(const void *p, int64_t bytes)
 
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
 
-// Every written range must be disjoint from every other range.
-int check_alias(const Range *all, int n_all, const Range *written, int n_written)
+// Every written range must be disjoint from every input range and from
+// every other written range (an exact alias such as y == x is an overlap
+// like any other).
+int check_alias(const Range *inputs, int n_inputs, const Range *written, int n_written)
 {
     for (int i = 0; i < n_written; ++i)
-        for (int j = 0; j < n_all; ++j) {
-            if (written[i].lo == all[j].lo && written[i].hi == all[j].hi) continue;  // itself
-            if (overlap(written[i], all[j])) return QG_ERR_ALIAS;
-        }
+        for (int j = 0; j < n_inputs; ++j)
+            if (overlap(written[i], inputs[j])) return QG_ERR_ALIAS;
     for (int i = 0; i < n_written; ++i)
         for (int j = i + 1; j < n_written; ++j)
             if (overlap(written[i], written[j])) return QG_ERR_ALIAS;
@@ -142,8 +142,9 @@ int launch_status()
 #define QG_GEMV1_MINWAVES 1024  // fewer rows per block until this many waves
 #endif
 
-// Workspace: the first 256 bytes are control words (the greedy head's
-// workgroup counter) that every call leaves at zero; the rest is scratch.
+// Workspace: the first kCtlBytes are completion words (the greedy head's,
+// then one per row tile of the in-kernel split-K combine), claimed by each
+// dispatch that counts on them whatever they hold; the rest is scratch.
 constexpr size_t kCtlBytes = qg::kCtlBytes;
 static_assert(kCtlBytes == QG_WS_CONTROL_BYTES, "control area and header disagree");
 static_assert(sizeof(qg::GreedyCtl) <= qg::kCtlTileOffset, "greedy control words exceed their area");
@@ -180,7 +181,7 @@ struct GemvPlan {
     size_t lds_bytes;
     int64_t comb_rows_per_wg, comb_grid;
     int nkeys;
-    size_t part_off, ws_bytes;
+    size_t part_off, key_off, ws_bytes;
 };
 
 // The matrix-core prefill product over N token rows, K split when its grid
@@ -320,8 +321,10 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
         pl.grid_x = ceil_div(ceil_div(M, pl.rows_per_wave), pl.wg_waves);
         pl.nsplit = 1;
         if (argmax) {
+            // one parked greedy key per workgroup after the control words
             pl.nkeys = static_cast<int>(pl.grid_x);
-            pl.ws_bytes = kCtlBytes;
+            pl.key_off = kCtlBytes;
+            pl.ws_bytes = align256(kCtlBytes + static_cast<size_t>(pl.grid_x) * 8);
         }
         return pl;
     }
@@ -346,9 +349,9 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
             pl.ws_bytes = align256(kCtlBytes + static_cast<size_t>(pl.nsplit) * nb * M * 4);
         }
         if (argmax) {
-            // per-workgroup greedy keys (16 per workgroup) after the control words
+            // per-workgroup greedy keys (up to 16 per workgroup) after the control words
             pl.nkeys = static_cast<int>(pl.grid_x);
-            pl.part_off = kCtlBytes;
+            pl.key_off = kCtlBytes;
             pl.ws_bytes = align256(kCtlBytes + static_cast<size_t>(pl.grid_x) * 16 * 8);
         }
         return pl;
@@ -380,7 +383,12 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
             pl.part_off = off;
             off = align256(off + static_cast<size_t>(pl.nsplit) * std::min(nb, 8) * M * 4);
         }
-        if (argmax) pl.nkeys = static_cast<int>(pl.nsplit > 1 && !pl.fused ? pl.comb_grid : pl.grid_x);
+        if (argmax) {
+            // parked greedy keys (up to 8 per workgroup and launch) after the partials
+            pl.nkeys = static_cast<int>(pl.nsplit > 1 && !pl.fused ? pl.comb_grid : pl.grid_x);
+            pl.key_off = off;
+            off = align256(off + static_cast<size_t>(pl.nkeys) * 8 * 8);
+        }
         pl.ws_bytes = (off > kCtlBytes || argmax) ? off : 0;
         return pl;
     }
@@ -401,9 +409,9 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
         if (pl.fused) pl.lds_bytes += out_bytes;
         pl.nsplit = 1;
         if (argmax) {
-            // per-workgroup greedy keys after the control words
+            // per-workgroup greedy keys (up to 8 per workgroup) after the control words
             pl.nkeys = static_cast<int>(pl.grid_x);
-            pl.part_off = kCtlBytes;
+            pl.key_off = kCtlBytes;
             pl.ws_bytes = align256(kCtlBytes + static_cast<size_t>(pl.grid_x) * 8 * 8);
         }
         return pl;
@@ -436,7 +444,12 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
         pl.part_off = off;
         off = align256(off + static_cast<size_t>(pl.nsplit) * nb * M * 4);
     }
-    if (argmax) pl.nkeys = static_cast<int>(pl.nsplit > 1 ? pl.comb_grid : pl.grid_x);
+    if (argmax) {
+        // parked greedy keys (nb per workgroup) after the partials
+        pl.nkeys = static_cast<int>(pl.nsplit > 1 ? pl.comb_grid : pl.grid_x);
+        pl.key_off = off;
+        off = align256(off + static_cast<size_t>(pl.nkeys) * nb * 8);
+    }
     pl.ws_bytes = (off > kCtlBytes || argmax) ? off : 0;
     return pl;
 }
@@ -572,7 +585,7 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         q.x = x;
         q.y = y;
         q.ctl = idx ? static_cast<qg::GreedyCtl *>(ws) : nullptr;
-        q.keys = idx ? reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + pl.part_off) : nullptr;
+        q.keys = idx ? reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + pl.key_off) : nullptr;
         q.idx = idx;
         q.M = M;
         q.K = K;
@@ -599,7 +612,7 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         q.x = x;
         q.y = y;
         q.ctl = idx ? static_cast<qg::GreedyCtl *>(ws) : nullptr;
-        q.keys = idx ? reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + pl.part_off) : nullptr;
+        q.keys = idx ? reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + pl.key_off) : nullptr;
         q.idx = idx;
         q.M = M;
         q.K = K;
@@ -614,7 +627,7 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         }();
         (void)lds_set;
         // rows 8 h .. 8 h + 7 in pass h; the passes share the workspace in
-        // stream order (each leaves the control words at zero)
+        // stream order (each dispatch claims the completion word for itself)
         for (int h = 0; h < pl.passes; ++h) {
             qg::GemvMfmaParams qh = q;
             qh.x = x + static_cast<int64_t>(8) * h * K;
@@ -634,6 +647,7 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         q.x = x;
         q.y = y;
         q.ctl = idx ? static_cast<qg::GreedyCtl *>(ws) : nullptr;
+        q.keys = idx ? reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + pl.key_off) : nullptr;
         q.idx = idx;
         q.M = M;
         q.K = K;
@@ -645,7 +659,8 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
     }
     if (pl.lut) {
         // activation rows 8 h .. 8 h + 7 in pass h; the passes share the
-        // workspace in stream order (each leaves the control words at zero)
+        // workspace in stream order (each dispatch claims the completion
+        // words for itself)
         for (int h = 0; h < pl.passes; ++h) {
             const int rows = std::min(8, nb - 8 * h);
             float *yh = y ? y + static_cast<int64_t>(8) * h * M : nullptr;
@@ -657,6 +672,7 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
             q.y = yh;
             q.part = pl.nsplit > 1 ? reinterpret_cast<float *>(static_cast<char *>(ws) + pl.part_off) : nullptr;
             q.ctl = static_cast<qg::GreedyCtl *>(ws);
+            q.keys = idx ? reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + pl.key_off) : nullptr;
             q.idx = (pl.nsplit == 1 || pl.fused) ? ih : nullptr;
             q.M = M;
             q.K = K;
@@ -682,6 +698,7 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
                 c.y = yh;
                 c.part = q.part;
                 c.ctl = idx ? static_cast<qg::GreedyCtl *>(ws) : nullptr;
+                c.keys = q.keys;
                 c.idx = ih;
                 c.M = M;
                 c.K = K;
@@ -703,6 +720,7 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
     p.y = y;
     p.part = pl.nsplit > 1 ? reinterpret_cast<float *>(static_cast<char *>(ws) + pl.part_off) : nullptr;
     p.ctl = idx ? static_cast<qg::GreedyCtl *>(ws) : nullptr;
+    p.keys = idx ? reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + pl.key_off) : nullptr;
     p.idx = idx;
     p.M = M;
     p.K = K;
@@ -740,18 +758,18 @@ int gemv_entry(int fmt, const void *codes, const void *scales, const void *biase
         if (!ws || ws_bytes < pl.ws_bytes) return QG_ERR_WORKSPACE;
         if (!aligned(ws, kAlign)) return QG_ERR_ALIGN;
     }
-    Range all[7];
+    Range inputs[4];
     int n = 0;
-    all[n++] = range_of(codes, M * row_bytes(fmt, K));
-    all[n++] = range_of(scales, scale_bytes(fmt, M, K));
-    if (biases) all[n++] = range_of(biases, bias_bytes(fmt, M, K));
-    all[n++] = range_of(x, int64_t(batch) * K * 4);
+    inputs[n++] = range_of(codes, M * row_bytes(fmt, K));
+    inputs[n++] = range_of(scales, scale_bytes(fmt, M, K));
+    if (biases) inputs[n++] = range_of(biases, bias_bytes(fmt, M, K));
+    inputs[n++] = range_of(x, int64_t(batch) * K * 4);
     Range wr[3];
     int nw = 0;
-    if (y) wr[nw++] = all[n++] = range_of(y, int64_t(batch) * M * 4);
-    if (argmax) wr[nw++] = all[n++] = range_of(idx, int64_t(batch) * 4);
-    if (pl.ws_bytes > 0) wr[nw++] = all[n++] = range_of(ws, static_cast<int64_t>(pl.ws_bytes));
-    st = check_alias(all, n, wr, nw);
+    if (y) wr[nw++] = range_of(y, int64_t(batch) * M * 4);
+    if (argmax) wr[nw++] = range_of(idx, int64_t(batch) * 4);
+    if (pl.ws_bytes > 0) wr[nw++] = range_of(ws, static_cast<int64_t>(pl.ws_bytes));
+    st = check_alias(inputs, n, wr, nw);
     if (st != QG_OK) return st;
 
     (void)hipGetLastError();
@@ -822,7 +840,7 @@ int u4_row_launches(int fmt, int64_t M, int64_t K, int64_t N)
 }
 
 // Workspace of those launches: the largest of their plans (they run in
-// stream order, and each leaves the control words at zero).
+// stream order, each dispatch claiming the completion words for itself).
 size_t row_launches_workspace(int fmt, int64_t M, int64_t K, int64_t N, bool argmax)
 {
     size_t ws = 0;
@@ -1007,18 +1025,18 @@ int wide_argmax_entry(int fmt, const void *codes, const void *scales, const void
     const size_t need = wide_argmax_workspace(fmt, M, K, N);
     if (!ws || ws_bytes < need) return QG_ERR_WORKSPACE;
     if (!aligned(ws, kAlign)) return QG_ERR_ALIGN;
-    Range all[8];
+    Range inputs[4];
     int n = 0;
-    all[n++] = range_of(codes, M * row_bytes(fmt, K));
-    all[n++] = range_of(scales, scale_bytes(fmt, M, K));
-    if (biases) all[n++] = range_of(biases, bias_bytes(fmt, M, K));
-    all[n++] = range_of(x, N * K * 4);
+    inputs[n++] = range_of(codes, M * row_bytes(fmt, K));
+    inputs[n++] = range_of(scales, scale_bytes(fmt, M, K));
+    if (biases) inputs[n++] = range_of(biases, bias_bytes(fmt, M, K));
+    inputs[n++] = range_of(x, N * K * 4);
     Range wr[3];
     int nw = 0;
-    if (y) wr[nw++] = all[n++] = range_of(y, N * M * 4);
-    wr[nw++] = all[n++] = range_of(idx, N * 4);
-    wr[nw++] = all[n++] = range_of(ws, static_cast<int64_t>(need));
-    st = check_alias(all, n, wr, nw);
+    if (y) wr[nw++] = range_of(y, N * M * 4);
+    wr[nw++] = range_of(idx, N * 4);
+    wr[nw++] = range_of(ws, static_cast<int64_t>(need));
+    st = check_alias(inputs, n, wr, nw);
     if (st != QG_OK) return st;
 
     (void)hipGetLastError();
@@ -1047,17 +1065,17 @@ int gemm_entry(int fmt, const void *codes, const void *scales, const void *biase
         if (!ws || ws_bytes < need) return QG_ERR_WORKSPACE;
         if (!aligned(ws, kAlign)) return QG_ERR_ALIGN;
     }
-    Range all[7];
+    Range inputs[4];
     int n = 0;
-    all[n++] = range_of(codes, M * row_bytes(fmt, K));
-    all[n++] = range_of(scales, scale_bytes(fmt, M, K));
-    if (biases) all[n++] = range_of(biases, bias_bytes(fmt, M, K));
-    all[n++] = range_of(x, N * K * 4);
+    inputs[n++] = range_of(codes, M * row_bytes(fmt, K));
+    inputs[n++] = range_of(scales, scale_bytes(fmt, M, K));
+    if (biases) inputs[n++] = range_of(biases, bias_bytes(fmt, M, K));
+    inputs[n++] = range_of(x, N * K * 4);
     Range wr[2];
     int nw = 0;
-    wr[nw++] = all[n++] = range_of(y, N * M * 4);
-    if (need > 0) wr[nw++] = all[n++] = range_of(ws, static_cast<int64_t>(need));
-    st = check_alias(all, n, wr, nw);
+    wr[nw++] = range_of(y, N * M * 4);
+    if (need > 0) wr[nw++] = range_of(ws, static_cast<int64_t>(need));
+    st = check_alias(inputs, n, wr, nw);
     if (st != QG_OK) return st;
 
     (void)hipGetLastError();
@@ -1083,15 +1101,15 @@ int embed_entry(int fmt, const void *codes, const void *scales, const void *bias
     if (!aligned(codes, kAlign) || !aligned(scales, kAlign) || !aligned(biases, kAlign) ||
         !aligned(out, kAlign) || !aligned(ids, 4))
         return QG_ERR_ALIGN;
-    Range all[5];
+    Range inputs[4];
     int nr = 0;
-    all[nr++] = range_of(codes, M * row_bytes(fmt, K));
-    all[nr++] = range_of(scales, scale_bytes(fmt, M, K));
-    all[nr++] = range_of(biases, bias_bytes(fmt, M, K));
-    all[nr++] = range_of(ids, n * 4);
+    inputs[nr++] = range_of(codes, M * row_bytes(fmt, K));
+    inputs[nr++] = range_of(scales, scale_bytes(fmt, M, K));
+    inputs[nr++] = range_of(biases, bias_bytes(fmt, M, K));
+    inputs[nr++] = range_of(ids, n * 4);
     Range wr[1];
-    wr[0] = all[nr++] = range_of(out, n * K * 4);
-    const int st = check_alias(all, nr, wr, 1);
+    wr[0] = range_of(out, n * K * 4);
+    const int st = check_alias(inputs, nr, wr, 1);
     if (st != QG_OK) return st;
 
     (void)hipGetLastError();

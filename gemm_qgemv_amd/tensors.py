@@ -42,11 +42,11 @@ def to_device(w, device="cuda") -> DeviceWeights:
 
 
 def workspace(op: int, fmt: int, M: int, K: int, rows: int, device="cuda"):
-    """A zero-filled device workspace of qg_workspace_bytes(...) bytes (None
-    if 0). Zero-filled because its first QG_WS_CONTROL_BYTES bytes are
-    control words that must start at zero; calls leave them at zero."""
+    """A device workspace of qg_workspace_bytes(...) bytes (None if 0). Its
+    contents on entry do not matter (every kernel launch claims the
+    completion words it counts on), so it is left uninitialised."""
     import torch
     n = B.qg_workspace_bytes(op, fmt, M, K, rows)
     if n == 0:
         return None
-    return torch.zeros(n, dtype=torch.uint8, device=device)
+    return torch.empty(n, dtype=torch.uint8, device=device)

@@ -70,16 +70,23 @@
  *               path, then share the weights": a request that cannot be
  *               served fails before changing live state.)
  *   Threads     The library keeps no mutable state; calls are reentrant.
- *               Calls that share a workspace must not overlap in time.
+ *               Calls that share a workspace must not overlap in time; two
+ *               that do (on different streams) may both return wrong
+ *               results, but the calls after them are not affected.
  *   Workspace   `ws` is device memory of at least qg_workspace_bytes(...)
  *               bytes for the same (op, fmt, M, K, rows); it may be NULL
- *               when that size is 0. Its first QG_WS_CONTROL_BYTES bytes are
- *               control words (counters of finished workgroups, for the
- *               greedy head and for combining partial sums of K chunks):
- *               they must be zero before the first call that uses the
- *               workspace, and every call leaves them zero again, so one
- *               zero-filled workspace serves any sequence of calls. The rest
- *               is scratch whose contents on entry do not matter.
+ *               when that size is 0. Its contents on entry do not matter,
+ *               so freshly allocated memory serves. Its first
+ *               QG_WS_CONTROL_BYTES bytes are completion words (counters of
+ *               finished workgroups, for the greedy head and for combining
+ *               partial sums of K chunks), each tagged by the kernel launch
+ *               that counts on it and claimed afresh by every launch, so a
+ *               call that was cut short, or stale or uninitialised words,
+ *               cannot disturb a later call. The rest is scratch (partial
+ *               sums, parked argmax keys). The workspace is caller-owned
+ *               device memory because the library allocates nothing on the
+ *               hot path (I Built an LLM Inference Engine on a 15 year old
+ *               GPU..., "Cost 2").
  */
 #ifndef QG_H
 #define QG_H
@@ -92,7 +99,7 @@
 extern "C" {
 #endif
 
-#define QG_ABI_VERSION 1
+#define QG_ABI_VERSION 2
 
 typedef enum {
     QG_I8_ROW = 1,
@@ -121,7 +128,7 @@ enum {
 };
 
 /* Control words at the start of every workspace (see Workspace above). */
-#define QG_WS_CONTROL_BYTES 4096
+#define QG_WS_CONTROL_BYTES 8192
 
 /* Largest batch of qgemv / qgemv_argmax. */
 #define QG_MAX_GEMV_BATCH 16
@@ -230,7 +237,13 @@ int qembed(int fmt, const void *codes, const void *scales, const void *biases,
 /* Bytes of device workspace the call (op, fmt, M, K, rows) needs; rows is
  * the batch for QG_OP_GEMV / QG_OP_GEMV_ARGMAX and N for QG_OP_GEMM.
  * Returns 0 when no workspace is needed, and also for arguments the entry
- * point would reject (the entry point then reports the error). */
+ * point would reject (the entry point then reports the error). The caller
+ * allocates it once, off the hot path, and may reuse it for every call of
+ * the same or a smaller size (I Built an LLM Inference Engine..., "Cost 2":
+ * nothing is allocated per call; Pushing the limits of legacy hardware,
+ * "Build the execution path, then share the weights": the greedy head
+ * keeps per-tile (value, index) pairs instead of whole logits, which is
+ * what the argmax part of the workspace holds). */
 size_t qg_workspace_bytes(int op, int fmt, int64_t M, int64_t K, int64_t rows);
 
 /* Static text for a status code. */

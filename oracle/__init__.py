@@ -5,7 +5,9 @@ TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
 package ``gemm_qgemv_amd`` never does, and shares no code with it.
 
 The arithmetic lives in ``qg_oracle.c`` (plain loops, double accumulation);
-this module only builds it with gcc and marshals numpy arrays through ctypes.
+this module builds it with gcc and marshals numpy arrays through ctypes. The
+one exception is ``Oracle.qgemm_dense``: the weights decoded exactly by
+``qg_oracle.c``, then numpy's float64 matrix product as a library step.
 Inputs are host numpy arrays in the layouts documented in ``qg_oracle.c``.
 """
 from __future__ import annotations
@@ -50,6 +52,8 @@ class Oracle:
         lib.oracle_fp16_value.argtypes = [ctypes.c_uint16]
         lib.oracle_fp16_value.restype = D
         lib.oracle_num_threads.restype = I32
+        lib.oracle_set_threads.argtypes = [I32]
+        lib.oracle_set_threads.restype = None
         lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
         lib.oracle_f32_to_f16.restype = ctypes.c_uint16
         lib.oracle_embed.argtypes = [P, P, P, P, I64, I64, I64, P]
@@ -87,6 +91,10 @@ class Oracle:
     def num_threads(self) -> int:
         return self.lib.oracle_num_threads()
 
+    def set_threads(self, n: int) -> None:
+        """Threads of the per-output loops from now on."""
+        self.lib.oracle_set_threads(int(n))
+
     def decode(self, fmt, codes, scales, biases, M, K):
         """Exact weights w[M][K] as float64."""
         codes, scales, biases = self._prep(codes, scales, biases)
@@ -121,6 +129,25 @@ class Oracle:
             fmt, self._ptr(codes), self._ptr(scales), self._ptr(biases), self._ptr(x),
             M, K, x.shape[0], self._ptr(n_idx), self._ptr(m_idx), n_idx.shape[0],
             self._ptr(y), self._ptr(a)), "qgemv_sample")
+        return y, a
+
+    def qgemm_dense(self, fmt, codes, scales, biases, x, M, K):
+        """The same y[N][M] and a[N][M] as ``qgemv``, for products too large
+        for the per-output loops: the exact weights from ``decode`` (float64,
+        the plain definition of each format) times the activations with
+        numpy's float64 matrix product, y = x w^T and a = |x| |w|^T. Every
+        term is exact or within one double rounding, so the result differs
+        from ``qgemv`` only by the order of the float64 additions (relative
+        error about K * 2^-53 of a). (MiniCPM-V-4.6 on a Tesla C2075, section
+        3.1 "Prefill projections: dequantize, then call the vendor": the
+        prompt's projections expand the codes to float once and hand them to
+        a dense matrix product.)"""
+        w = self.decode(fmt, codes, scales, biases, M, K)
+        xd = np.ascontiguousarray(x, dtype=np.float32).reshape(-1, K).astype(np.float64)
+        y = xd @ w.T
+        np.abs(w, out=w)
+        np.abs(xd, out=xd)
+        a = xd @ w.T
         return y, a
 
     def f32_to_f16(self, v: float) -> int:

@@ -352,3 +352,15 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Set the threads of the (n, m) loops (no effect without OpenMP); used to
+ * time the oracle on one core and on all of them. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -517,7 +517,60 @@ def pin_embed_exact_reference(orc):
             assert got == want, f"row {i} k {k}: {got:#x} vs {want:#x}"
 
 
+def pin_sampled_outputs(orc):
+    """The sampled form of the product (chosen (row, output) pairs only, the
+    reference of the large prefill cases) against numpy's independent decode
+    and a float64 matmul, and against the oracle's full product, for all four
+    formats. The activation rows and outputs are equal in number (N == M), so
+    a mistake that swaps the two indices, or indexes the activations by the
+    output, still reads in bounds and shows up as a wrong value; the pairs
+    include the first and last row and output and both orders of each
+    off-diagonal pair."""
+    rng = np.random.default_rng(23)
+    for fmt, K in ((I8, 96), (I8G, 192), (U4, 128), (B1, 256)):
+        M = N = 19
+        codes, scales, biases = random_tiny(fmt, M, K, rng)
+        x = rng.standard_normal((N, K)).astype(np.float32)
+        w = numpy_weights(fmt, codes, scales, biases, M, K)
+        ref = x.astype(np.float64) @ w.T
+        refa = np.abs(x.astype(np.float64)) @ np.abs(w).T
+        ends = [0, 1, M - 2, M - 1]
+        n = [a for a in ends for b in ends] + list(rng.integers(0, N, 40))
+        m = [b for a in ends for b in ends] + list(rng.integers(0, M, 40))
+        n, m = np.asarray(n, np.int64), np.asarray(m, np.int64)
+        y, a = orc.qgemv_sample(fmt, codes, scales, biases, x, M, K, n, m)
+        tol = 1e-12 * refa[n, m] + 1e-300
+        assert np.all(np.abs(y - ref[n, m]) <= tol), f"fmt {fmt}: sampled y"
+        assert np.all(np.abs(a - refa[n, m]) <= tol), f"fmt {fmt}: sampled absdot"
+        yf, af = orc.qgemv(fmt, codes, scales, biases, x, M, K)
+        assert np.array_equal(y, yf[n, m]) and np.array_equal(a, af[n, m]), \
+            f"fmt {fmt}: sampled and full products differ"
+
+
+def pin_dense_product(orc):
+    """The decode-then-matmul form of the product (the reference of the full
+    prefill comparisons) equals numpy's independent decode times the
+    activations, and the oracle's per-output loops, on random tiny matrices
+    of all four formats with several activation rows."""
+    rng = np.random.default_rng(29)
+    for fmt, K in ((I8, 80), (I8G, 192), (U4, 192), (B1, 384)):
+        for M, N in ((1, 1), (7, 3), (33, 20)):
+            codes, scales, biases = random_tiny(fmt, M, K, rng)
+            x = rng.standard_normal((N, K)).astype(np.float32)
+            w = numpy_weights(fmt, codes, scales, biases, M, K)
+            ref = x.astype(np.float64) @ w.T
+            refa = np.abs(x.astype(np.float64)) @ np.abs(w).T
+            y, a = orc.qgemm_dense(fmt, codes, scales, biases, x, M, K)
+            tol = 1e-12 * refa + 1e-300
+            assert np.all(np.abs(y - ref) <= tol), f"fmt {fmt} M {M} N {N}: dense y"
+            assert np.all(np.abs(a - refa) <= tol), f"fmt {fmt} M {M} N {N}: dense absdot"
+            yl, al = orc.qgemv(fmt, codes, scales, biases, x, M, K)
+            assert np.all(np.abs(y - yl) <= tol) and np.all(np.abs(a - al) <= tol), \
+                f"fmt {fmt} M {M} N {N}: dense and per-output products differ"
+
+
 PINS = [pin_hand_fixtures, pin_decode_values, pin_worked_example, pin_one_hot,
         pin_zero_and_sign_codes, pin_exact_integer_arithmetic,
         pin_numpy_second_opinion, pin_invariants, pin_argmax_brute_force,
-        pin_f16_rounding, pin_embed_hand_cases, pin_embed_exact_reference]
+        pin_f16_rounding, pin_embed_hand_cases, pin_embed_exact_reference,
+        pin_sampled_outputs, pin_dense_product]

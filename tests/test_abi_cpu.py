@@ -50,7 +50,7 @@ def test_probe_library_exports_and_rejects_bad_arguments():
 
 
 def test_version_and_status_strings():
-    assert q.qg_abi_version() == 1
+    assert q.qg_abi_version() == 2
     for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert q.qg_status_str(st) and q.qg_status_str(st) != "unknown status"
     assert q.qg_status_str(12345) == "unknown status"
@@ -129,6 +129,35 @@ def test_aliasing_outputs():
     base = 1 << 30
     assert _err(q.qgemv_argmax, q.QG_I8_ROW, A, base, None, base + 65536, base + 131072,
                 base + 131072 + 64, M, K, 1, ws=base + (1 << 24), ws_bytes=need) == q.QG_ERR_ALIAS
+
+
+def test_exact_alias_is_rejected():
+    """A written buffer that coincides exactly with an input (same start,
+    same length) is an overlap like any other: y == x with M == K, and the
+    gather's output on top of its codes."""
+    M = K = 64
+    codes, scales, x = A, A + 65536, A + 131072
+    # 8-bit per-row: y == x (M * 4 bytes == K * 4 bytes)
+    assert _err(q.qgemv, q.QG_I8_ROW, codes, scales, None, x, x, M, K, 1) == q.QG_ERR_ALIAS
+    assert _err(q.qgemm, q.QG_I8_ROW, codes, scales, None, x, x, M, K, 20) == q.QG_ERR_ALIAS
+    need = q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_I8_ROW, M, K, 1)
+    ws = A + (1 << 24)
+    assert _err(q.qgemv_argmax, q.QG_I8_ROW, codes, scales, None, x, x, A + (1 << 23), M, K, 1,
+                ws=ws, ws_bytes=need) == q.QG_ERR_ALIAS
+    # idx exactly on top of x (batch * 4 bytes == K * 4 bytes needs batch == K: use K = 16)
+    need16 = q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_I8_ROW, 4, 16, 16)
+    assert _err(q.qgemv_argmax, q.QG_I8_ROW, codes, scales, None, x, A + (1 << 22), x, 4, 16, 1,
+                ws=ws, ws_bytes=need16) == q.QG_ERR_ALIAS
+    # y exactly on top of the codes: 8-bit codes of 16 x 64 bytes, y of 16 x 64 floats
+    # needs batch * M * 4 == M * K: M = 16, K = 64, batch = 16
+    assert _err(q.qgemv, q.QG_I8_ROW, codes, scales, None, x, codes, 16, 64, 16,
+                ws=ws, ws_bytes=1 << 20) == q.QG_ERR_ALIAS
+    # the gather writing over its own codes: n * K * 4 == M * K / 2 for M = 8 n
+    M2, K2, n = 64, 128, 8
+    with pytest.raises(q.QGError) as e:
+        q.qembed(q.QG_U4_G64, codes, A + (1 << 21), A + (1 << 22), A + (1 << 23), codes,
+                 M2, K2, n, stream=0)
+    assert e.value.status == q.QG_ERR_ALIAS
 
 
 def test_prefill_affine_format_checks():

@@ -51,6 +51,15 @@ MUTANTS = [
      "const uint8_t *code = (const uint8_t *)A->codes;"),
     ("i8g_scale_dropped", "return (double)gs[m * (K / 64) + k / 64] * (double)code[m * K + k];",
      "(void)gs; return (double)code[m * K + k];"),
+    # the sampled product (the reference of the large prefill cases)
+    ("sample_n_m_swapped", "dot_one(&A, x, n_idx[i], m_idx[i], &y[i], &a[i]);",
+     "dot_one(&A, x, m_idx[i], n_idx[i], &y[i], &a[i]);"),
+    ("sample_x_by_output", "dot_one(&A, x, n_idx[i], m_idx[i], &y[i], &a[i]);",
+     "dot_one(&A, x, m_idx[i], m_idx[i], &y[i], &a[i]);"),
+    ("sample_outputs_reversed", "dot_one(&A, x, n_idx[i], m_idx[i], &y[i], &a[i]);",
+     "dot_one(&A, x, n_idx[i], m_idx[i], &y[count - 1 - i], &a[count - 1 - i]);"),
+    ("sample_first_pair_only", "dot_one(&A, x, n_idx[i], m_idx[i], &y[i], &a[i]);",
+     "dot_one(&A, x, n_idx[0], m_idx[0], &y[i], &a[i]);"),
 ]
 
 
