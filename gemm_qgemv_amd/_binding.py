@@ -16,14 +16,16 @@ QG_OP_GEMV, QG_OP_GEMM, QG_OP_GEMV_ARGMAX = 1, 2, 3
 QG_OK = 0
 QG_ERR_NULL, QG_ERR_FORMAT, QG_ERR_SHAPE, QG_ERR_ALIGN = -1, -2, -3, -4
 QG_ERR_WORKSPACE, QG_ERR_ALIAS, QG_ERR_LAUNCH, QG_ERR_UNSUPPORTED = -5, -6, -7, -8
+QG_ERR_SCRATCH = -9
+QG_STATIC_SCRATCH_BYTES = 8 << 20
 QG_MAX_GEMV_BATCH = 16
 QG_MAX_ARGMAX_BATCH = 256
 QG_WS_CONTROL_BYTES = 8192
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqg.so")
 
-EXPORTS = ("qgemv", "qgemm", "qgemv_argmax", "qembed", "qg_workspace_bytes",
-           "qg_status_str", "qg_abi_version")
+EXPORTS = ("qgemv", "qgemm", "qgemv_argmax", "qgemv_argmax_noalloc", "qembed",
+           "qg_workspace_bytes", "qg_status_str", "qg_abi_version")
 
 _lib = None
 
@@ -47,13 +49,15 @@ def lib() -> ctypes.CDLL:
         L.qgemv.argtypes = [I32, P, P, P, P, P, I64, I64, I32, P, SZ, P]
         L.qgemm.argtypes = [I32, P, P, P, P, P, I64, I64, I64, P, SZ, P]
         L.qgemv_argmax.argtypes = [I32, P, P, P, P, P, P, I64, I64, I32, P, SZ, P]
+        L.qgemv_argmax_noalloc.argtypes = [I32, P, P, P, P, P, P, I64, I64, I32, P]
         L.qembed.argtypes = [I32, P, P, P, P, P, I64, I64, I64, P]
         L.qg_workspace_bytes.argtypes = [I32, I32, I64, I64, I64]
         L.qg_workspace_bytes.restype = SZ
         L.qg_status_str.argtypes = [I32]
         L.qg_status_str.restype = ctypes.c_char_p
         L.qg_abi_version.argtypes = []
-        for f in (L.qgemv, L.qgemm, L.qgemv_argmax, L.qembed, L.qg_abi_version):
+        for f in (L.qgemv, L.qgemm, L.qgemv_argmax, L.qgemv_argmax_noalloc, L.qembed,
+                  L.qg_abi_version):
             f.restype = I32
         _lib = L
     return _lib
@@ -104,6 +108,12 @@ def qgemv_argmax(fmt, codes, scales, biases, x, logits, idx, M, K, batch, ws=Non
     _check(lib().qgemv_argmax(fmt, _ptr(codes), _ptr(scales), _ptr(biases), _ptr(x),
                               _ptr(logits), _ptr(idx), M, K, batch, _ptr(ws),
                               _nbytes(ws, ws_bytes), _stream(stream)), "qgemv_argmax")
+
+
+def qgemv_argmax_noalloc(fmt, codes, scales, biases, x, logits, idx, M, K, batch, stream=None):
+    _check(lib().qgemv_argmax_noalloc(fmt, _ptr(codes), _ptr(scales), _ptr(biases), _ptr(x),
+                                      _ptr(logits), _ptr(idx), M, K, batch, _stream(stream)),
+           "qgemv_argmax_noalloc")
 
 
 def qembed(fmt, codes, scales, biases, ids, out, M, K, n, stream=None):

@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/qg.h"
 #include "embed.hpp"
@@ -1120,6 +1121,36 @@ int embed_entry(int fmt, const void *codes, const void *scales, const void *bias
     return launch_status();
 }
 
+// ---------------------------------------------------------------------------
+// The library's own scratch, for callers that cannot allocate
+// (qgemv_argmax_noalloc): one array per GPU, in the code object's device
+// memory, held until the process ends. Kernels receive its device address,
+// looked up once per device with that device current; the array's name in
+// host code is only a handle for that lookup, never an address.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[QG_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+int static_scratch(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QG_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return QG_ERR_LAUNCH;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return QG_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1145,6 +1176,30 @@ int qgemv_argmax(int fmt, const void *codes, const void *scales, const void *bia
                                  ws_bytes, stream);
     return gemv_entry(fmt, codes, scales, biases, x, logits, idx, M, K, batch, ws, ws_bytes,
                       stream);
+}
+
+int qgemv_argmax_noalloc(int fmt, const void *codes, const void *scales, const void *biases,
+                         const float *x, float *logits, int32_t *idx, int64_t M, int64_t K,
+                         int batch, hipStream_t stream)
+{
+    // the argument checks of qgemv_argmax that come before its workspace,
+    // so that they are reported before the scratch is looked up
+    if (!idx) return QG_ERR_NULL;
+    const int st0 = check_weights(fmt, codes, scales, biases, x, M, K);
+    if (st0 != QG_OK) return st0;
+    if (batch < 1 || batch > QG_MAX_ARGMAX_BATCH) return QG_ERR_SHAPE;
+    if ((logits && !aligned(logits, kAlign)) || !aligned(idx, 4)) return QG_ERR_ALIGN;
+    // the workspace qgemv_argmax would need (0 for the arguments it still
+    // rejects, which it then reports without the scratch)
+    const size_t need = qg_workspace_bytes(QG_OP_GEMV_ARGMAX, fmt, M, K, batch);
+    if (need > QG_STATIC_SCRATCH_BYTES) return QG_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (need > 0) {
+        const int st = static_scratch(&ws);
+        if (st != QG_OK) return st;
+    }
+    return qgemv_argmax(fmt, codes, scales, biases, x, logits, idx, M, K, batch, ws,
+                        need > 0 ? static_cast<size_t>(QG_STATIC_SCRATCH_BYTES) : 0, stream);
 }
 
 int qgemm(int fmt, const void *codes, const void *scales, const void *biases,
@@ -1189,6 +1244,9 @@ const char *qg_status_str(int status)
     case QG_ERR_ALIAS: return "a written buffer overlaps another buffer";
     case QG_ERR_LAUNCH: return "kernel launch failed";
     case QG_ERR_UNSUPPORTED: return "format not implemented by this entry point";
+    case QG_ERR_SCRATCH:
+        return "the call needs more scratch than the library's static array holds "
+               "(QG_STATIC_SCRATCH_BYTES); use the entry point with a caller workspace";
     default: return "unknown status";
     }
 }

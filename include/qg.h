@@ -123,8 +123,10 @@ enum {
     QG_ERR_WORKSPACE = -5,   /* ws_bytes smaller than qg_workspace_bytes(...) */
     QG_ERR_ALIAS = -6,       /* a written buffer overlaps another buffer */
     QG_ERR_LAUNCH = -7,      /* the kernel launch failed */
-    QG_ERR_UNSUPPORTED = -8  /* a known format this entry point does not implement
+    QG_ERR_UNSUPPORTED = -8, /* a known format this entry point does not implement
                                 (only qembed returns it: 4-bit rows only) */
+    QG_ERR_SCRATCH = -9      /* the call needs more than QG_STATIC_SCRATCH_BYTES of
+                                the library's own scratch (qgemv_argmax_noalloc) */
 };
 
 /* Control words at the start of every workspace (see Workspace above). */
@@ -205,6 +207,28 @@ int qgemv_argmax(int fmt, const void *codes, const void *scales,
                  const void *biases, const float *x, float *logits,
                  int32_t *idx, int64_t M, int64_t K, int batch,
                  void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * qgemv_argmax_noalloc -- qgemv_argmax without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). Same arguments,
+ * results and limits as qgemv_argmax; the workspace it would need comes from
+ * a static array of QG_STATIC_SCRATCH_BYTES bytes that the library keeps on
+ * each GPU it runs on until the process ends. The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); its first call on
+ * a device looks up that device's array (the device must be current, as
+ * for every call). Calls that need more scratch than the array holds return
+ * QG_ERR_SCRATCH before anything is enqueued. Every call on a GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (different
+ * streams or host threads) race and may return wrong results, though calls
+ * after them are not affected. Nothing in the array has to be cleared
+ * between calls (its completion words are claimed by each launch).
+ */
+#define QG_STATIC_SCRATCH_BYTES (8u << 20)
+int qgemv_argmax_noalloc(int fmt, const void *codes, const void *scales,
+                         const void *biases, const float *x, float *logits,
+                         int32_t *idx, int64_t M, int64_t K, int batch,
+                         hipStream_t stream);
 
 /*
  * qembed -- embedding rows gathered from the (tied) 4-bit weight matrix.

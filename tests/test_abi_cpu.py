@@ -51,7 +51,7 @@ def test_probe_library_exports_and_rejects_bad_arguments():
 
 def test_version_and_status_strings():
     assert q.qg_abi_version() == 2
-    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert q.qg_status_str(st) and q.qg_status_str(st) != "unknown status"
     assert q.qg_status_str(12345) == "unknown status"
 
@@ -158,6 +158,36 @@ def test_exact_alias_is_rejected():
         q.qembed(q.QG_U4_G64, codes, A + (1 << 21), A + (1 << 22), A + (1 << 23), codes,
                  M2, K2, n, stream=0)
     assert e.value.status == q.QG_ERR_ALIAS
+
+
+def test_noalloc_greedy_checks():
+    """qgemv_argmax_noalloc: argument errors as qgemv_argmax (reported
+    before the library's scratch is touched), and calls that need more than
+    QG_STATIC_SCRATCH_BYTES of scratch rejected with QG_ERR_SCRATCH."""
+    codes, scales, biases = A, A + (1 << 28), A + (1 << 29)
+    x, y, idx = A + (1 << 30), A + (1 << 31), A + (1 << 32)
+
+    def err(*a):
+        with pytest.raises(q.QGError) as e:
+            q.qgemv_argmax_noalloc(*a, stream=0)
+        return e.value.status
+
+    assert err(9, codes, scales, None, x, y, idx, 64, 64, 1) == q.QG_ERR_FORMAT
+    assert err(q.QG_U4_G64, codes, scales, None, x, y, idx, 64, 64, 1) == q.QG_ERR_NULL
+    assert err(q.QG_U4_G64, codes, scales, biases, x, y, None, 64, 64, 1) == q.QG_ERR_NULL
+    assert err(q.QG_U4_G64, codes, scales, biases, x, y, idx, 64, 96, 1) == q.QG_ERR_SHAPE
+    assert err(q.QG_U4_G64, codes, scales, biases, x, y, idx, 64, 64, 0) == q.QG_ERR_SHAPE
+    M, K, n = 10_000_000, 64, 256
+    assert q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_U4_G64, M, K, n) > q.QG_STATIC_SCRATCH_BYTES
+    assert err(q.QG_U4_G64, codes, scales, biases, x, y, idx, M, K, n) == q.QG_ERR_SCRATCH
+    assert "QG_STATIC_SCRATCH_BYTES" in q.qg_status_str(q.QG_ERR_SCRATCH)
+    hdr = open(HEADER).read()
+    assert "#define QG_STATIC_SCRATCH_BYTES (8u << 20)" in hdr
+    assert q.QG_STATIC_SCRATCH_BYTES == 8 << 20
+    # the configurations' greedy heads fit
+    for rows in (1, 8, 16, 64, 128, 256):
+        assert q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_U4_G64, 151936, 2048, rows) <= \
+            q.QG_STATIC_SCRATCH_BYTES
 
 
 def test_prefill_affine_format_checks():
