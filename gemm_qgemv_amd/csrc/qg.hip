@@ -19,6 +19,7 @@
 #include "gemv_b1.hpp"
 #include "gemv_mfma.hpp"
 #include "gemv_mfma16.hpp"
+#include "gemv_stream.hpp"
 
 namespace {
 
@@ -170,6 +171,8 @@ struct GemvPlan {
     bool lut;            // batch-1 1-bit kernel (table lookup, lanes along rows)
     bool fused;          // split-K combined inside the kernel (per-tile counters);
                          // small-batch kernel: outputs staged in LDS
+    bool stream;         // batch-1 4-bit kernel with loader waves (large M, K = 2048 nc)
+    int nc;              // stream kernel: 1 KiB code chunks per row
     bool one;            // batch-1 kernel (8-bit / 4-bit, activations in registers)
     int ns;              // batch-1 kernel: slices per lane
     bool full;           // batch-1 kernel: every lane owns all NS slices
@@ -296,12 +299,37 @@ bool batch_on_gemm(int fmt, int64_t M, int64_t K, int nb)
     return fmt == QG_B1_G128 && t_gemm < 8.0 + nb * w / 14e6;
 }
 
+// The batch-1 stream kernel: 4-bit rows of 1, 2 or 4 KiB of codes (K =
+// 2048, 4096, 8192), and at least four stages of rows per workgroup when
+// each compute unit takes one workgroup (fewer leave the ring unfilled; the
+// register-streaming kernel serves those).
+bool stream_ok(int fmt, int64_t M, int64_t K)
+{
+    if (fmt != QG_U4_G64 || (K != 2048 && K != 4096 && K != 8192)) return false;
+    const int64_t rows_per_stage = 32 / (K / 2048);
+    return M >= kComputeUnits * rows_per_stage * 4;
+}
+
 GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
 {
     GemvPlan pl{};
     if (!argmax && nb >= 2 && batch_on_gemm(fmt, M, K, nb)) {
         pl.gemm = true;
         pl.ws_bytes = gemm_mfma_workspace(fmt, M, K, nb);
+        return pl;
+    }
+    if (nb == 1 && stream_ok(fmt, M, K)) {
+        // batch 1, 4-bit, large M: one workgroup per compute unit, loader
+        // waves streaming the rows through LDS
+        pl.stream = true;
+        pl.nc = static_cast<int>(K / 2048);
+        pl.grid_x = kComputeUnits;
+        pl.nsplit = 1;
+        if (argmax) {
+            pl.nkeys = static_cast<int>(pl.grid_x);
+            pl.key_off = kCtlBytes;
+            pl.ws_bytes = align256(kCtlBytes + static_cast<size_t>(pl.grid_x) * 8);
+        }
         return pl;
     }
     const int64_t S = K / k_per_slice(fmt);
@@ -541,6 +569,19 @@ void launch_gemv1_fmt(const GemvPlan &pl, const qg::Gemv1Params &p, hipStream_t 
     }
 }
 
+template <int NC>
+void launch_stream(const GemvPlan &pl, const qg::GemvStreamParams &q, hipStream_t s)
+{
+    static const bool lds_set = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(qg::gemv_stream_u4_kernel<NC>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, qg::kStreamLdsBytes);
+        return true;
+    }();
+    (void)lds_set;
+    hipLaunchKernelGGL((qg::gemv_stream_u4_kernel<NC>), dim3(static_cast<unsigned>(pl.grid_x)),
+                       dim3(qg::kStreamThreads), qg::kStreamLdsBytes, s, q);
+}
+
 // Enqueue one planned GEMV (+ split-K combine). The greedy selection
 // finishes inside the last kernel.
 // Launch the one-pass kernel for GW groups of 64 inputs per wave (8-bit: 1,
@@ -638,6 +679,23 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
             hipLaunchKernelGGL(qg::gemv_mfma_u4_kernel, dim3(static_cast<unsigned>(pl.grid_x)),
                                dim3(64 * qg::kMfmaWaves), pl.lds_bytes, s, qh);
         }
+        return;
+    }
+    if (pl.stream) {
+        qg::GemvStreamParams q{};
+        q.codes = static_cast<const uint8_t *>(codes);
+        q.scales = static_cast<const uint16_t *>(scales);
+        q.biases = static_cast<const uint16_t *>(biases);
+        q.x = x;
+        q.y = y;
+        q.ctl = idx ? static_cast<qg::GreedyCtl *>(ws) : nullptr;
+        q.keys = idx ? reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + pl.key_off) : nullptr;
+        q.idx = idx;
+        q.M = M;
+        q.K = K;
+        if (pl.nc == 1) launch_stream<1>(pl, q, s);
+        else if (pl.nc == 2) launch_stream<2>(pl, q, s);
+        else launch_stream<4>(pl, q, s);
         return;
     }
     if (pl.one) {

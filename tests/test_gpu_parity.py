@@ -841,3 +841,65 @@ def test_greedy_with_garbage_control_words(torch, orc, fmt, M, K, N):
         assert np.array_equal(got, want), f"{how}: idx differs from the oracle"
         if i == 0:
             check_bound(y.cpu().numpy().reshape(N, M), ref, a, f"garbage {how}")
+
+
+# ---------------------------------------------------------------------------
+# the batch-1 4-bit kernel with loader waves (large M, K = 2048, 4096, 8192)
+# ---------------------------------------------------------------------------
+
+STREAM_SHAPES = [(32768, 2048), (151937, 2048), (40001, 2048), (16384 + 5, 4096), (8192 * 3 + 7, 8192)]
+
+
+@pytest.mark.parametrize("M,K", STREAM_SHAPES)
+def test_stream_kernel_random(torch, orc, M, K):
+    """Random inputs, with and without the greedy index and logits; every
+    workgroup's run of rows ends in a partial stage at these M."""
+    say(f"stream kernel M={M} K={K}")
+    rng = synth.rng_for(600, M + K)
+    w = synth.draw_weights(synth.U4_G64, M, K, rng)
+    x = synth.draw_x(1, K, rng)
+    ref, a = orc.qgemv(w.fmt, w.codes, w.scales, w.biases, x, M, K)
+    wd = dev(w)
+    y, _ = gpu_gemv(torch, wd, x)
+    check_bound(y, ref, a, f"stream {M}x{K}")
+    y2, idx = gpu_gemv(torch, wd, x, argmax=True)
+    assert np.array_equal(y, y2), "logits differ from the plain product"
+    check_argmax(idx, y2, ref, a, orc, f"stream {M}x{K}")
+    _, idx3 = gpu_greedy(torch, wd, x, logits=False)
+    assert np.array_equal(idx, idx3), "greedy index without logits differs"
+
+
+@pytest.mark.parametrize("M,K", [(40000, 2048), (20000, 4096), (9000, 8192)])
+def test_stream_kernel_exact(torch, orc, M, K):
+    """Exact-arithmetic inputs: bit-exact against the oracle."""
+    say(f"stream kernel exact M={M} K={K}")
+    rng = np.random.default_rng([7, M, K])
+    w, x = exact_inputs(synth.U4_G64, M, K, 1, rng)
+    ref, _ = orc.qgemv(w.fmt, w.codes, w.scales, w.biases, x, M, K)
+    want = ref.astype(np.float32)
+    assert np.array_equal(want.astype(np.float64), ref), "fixture is not exact in float32"
+    y, _ = gpu_gemv(torch, dev(w), x)
+    assert np.array_equal(y, want), f"not bit-exact: max diff {np.max(np.abs(y - want))}"
+
+
+def test_stream_kernel_ties(torch, orc):
+    """Ties of the maximum across workgroups and within a stage: rows
+    duplicated at the first row, in the middle of a stage, at the last row
+    of a workgroup's run and at the last row; the lowest index wins."""
+    M, K = 151936, 2048
+    say("stream kernel ties")
+    rng = synth.rng_for(601, 0)
+    w = synth.draw_weights(synth.U4_G64, M, K, rng)
+    x = synth.draw_x(1, K, rng)
+    ref, _ = orc.qgemv(w.fmt, w.codes, w.scales, w.biases, x, M, K)
+    best = int(np.argmax(ref[0]))
+    codes, scales, biases = w.codes.copy(), w.scales.copy(), w.biases.copy()
+    per_wg = M // 256
+    for dst in (per_wg * 37 - 1, per_wg * 37 + 13, M - 1, 5, best):
+        codes[dst], scales[dst], biases[dst] = codes[best], scales[best], biases[best]
+    w2 = synth.QWeights(w.fmt, M, K, codes, scales, biases)
+    ref2, a2 = orc.qgemv(w2.fmt, w2.codes, w2.scales, w2.biases, x, M, K)
+    y, idx = gpu_gemv(torch, dev(w2), x, argmax=True)
+    check_bound(y, ref2, a2, "stream ties")
+    check_argmax(idx, y, ref2, a2, orc, "stream ties")
+    assert idx[0] == 5
