@@ -956,6 +956,15 @@ void gemm_tile(int fmt, int64_t M, int64_t N, int &bm, int &bn, int &wn)
         if (fmt == QG_B1_G128 || tiles(128, bn) >= 2 * kComputeUnits) bm = 128;
         return;
     }
+    // the grouped formats: 128 weight rows by 64 token rows (each activation
+    // split feeds twice the MFMAs of a 64-row tile; 128 x 128 would spill
+    // their second set of accumulators), for the 1-bit format always
+    // (17408 x 5120, N = 512: 431 -> 318 us), for the others once every
+    // compute unit gets two tiles
+    if (fmt != QG_I8_ROW && (fmt == QG_B1_G128 || tiles(128, 64) >= 2 * kComputeUnits)) {
+        bm = 128;
+        return;
+    }
     // 128 token rows per tile only where that pads no more than 64 would
     // (64 token rows with 128-row tiles would halve the useful MFMA work)
     const bool n128 = N % 128 == 0 || N % 128 > 64;
@@ -981,6 +990,12 @@ void launch_gemm_fmt(int bm, int bn, dim3 grid, hipStream_t s, const qg::GemmPar
         if (bm == 128) hipLaunchKernelGGL((qg::gemm_kernel<FMT, 128, 32, 2>), grid, block, 0, s, p);
         else hipLaunchKernelGGL((qg::gemm_kernel<FMT, 64, 32, 2>), grid, block, 0, s, p);
     } else if (bn == 64) {
+        if constexpr (FMT != qg::FMT_I8_ROW) {
+            if (bm == 128) {
+                hipLaunchKernelGGL((qg::gemm_kernel<FMT, 128, 64>), grid, block, 0, s, p);
+                return;
+            }
+        }
         hipLaunchKernelGGL((qg::gemm_kernel<FMT, 64, 64>), grid, block, 0, s, p);
     } else if constexpr (FMT == qg::FMT_I8_ROW) {
         if (bm == 128) hipLaunchKernelGGL((qg::gemm_kernel<FMT, 128, 128>), grid, block, 0, s, p);

@@ -139,7 +139,8 @@ def test_exact_alias_is_rejected():
     codes, scales, x = A, A + 65536, A + 131072
     # 8-bit per-row: y == x (M * 4 bytes == K * 4 bytes)
     assert _err(q.qgemv, q.QG_I8_ROW, codes, scales, None, x, x, M, K, 1) == q.QG_ERR_ALIAS
-    assert _err(q.qgemm, q.QG_I8_ROW, codes, scales, None, x, x, M, K, 20) == q.QG_ERR_ALIAS
+    assert _err(q.qgemm, q.QG_I8_ROW, codes, scales, None, x, x, M, K, 20, ws=A + (1 << 24),
+                ws_bytes=1 << 22) == q.QG_ERR_ALIAS
     need = q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_I8_ROW, M, K, 1)
     ws = A + (1 << 24)
     assert _err(q.qgemv_argmax, q.QG_I8_ROW, codes, scales, None, x, x, A + (1 << 23), M, K, 1,
@@ -194,8 +195,8 @@ def test_prefill_affine_format_checks():
     # the 4-bit prefill needs its biases, and its biases must not overlap Y
     assert _err(q.qgemm, q.QG_U4_G64, A, A + 4096, None, A + 8192, A + 65536, 4, 64, 8) == \
         q.QG_ERR_NULL
-    assert _err(q.qgemm, q.QG_U4_G64, A, A + 4096, A + 65536, A + 8192, A + 65536, 4, 64, 8) == \
-        q.QG_ERR_ALIAS
+    assert _err(q.qgemm, q.QG_U4_G64, A, A + 4096, A + 65536, A + 8192, A + 65536, 4, 64, 8,
+                ws=A + (1 << 24), ws_bytes=1 << 22) == q.QG_ERR_ALIAS
 
 
 def test_wide_greedy_head_checks():
