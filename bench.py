@@ -497,6 +497,85 @@ def trace_summary(csv_path, workload, src_hash, command):
     return "\n".join(lines)
 
 
+def counter_summary(csv_paths, workload, src_hash, commands):
+    """Markdown summary of rocprofv3 --pmc counter runs of one workload: per
+    counter the average value per dispatch of the dominant kernel (the
+    library kernel with the largest GRBM_GUI_ACTIVE), and the derived
+    fractions with their formulas, plus a JSON line."""
+    import csv
+    from gemm_qgemv_amd import synth
+    vals, meta = {}, {}
+    for path in csv_paths:
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                k = row["Kernel_Name"]
+                if "qg::" not in k:
+                    continue
+                vals.setdefault(k, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+                meta[k] = {"grid": int(row["Grid_Size"]), "workgroup": int(row["Workgroup_Size"]),
+                           "lds": int(row["LDS_Block_Size"]), "vgpr": int(row["VGPR_Count"]),
+                           "agpr": int(row.get("Accum_VGPR_Count") or 0)}
+    if not vals:
+        raise SystemExit("no library kernel in the counter files")
+    kern = max(vals, key=lambda k: sum(vals[k].get("GRBM_GUI_ACTIVE", [0])) / max(1, len(vals[k].get("GRBM_GUI_ACTIVE", [1]))))
+    avg = {c: sum(v) / len(v) for c, v in vals[kern].items()}
+    names = WORKLOADS.get(workload, [workload])
+    case = synth.CASES_BY_NAME[names[0]] if len(names) == 1 else None
+    simds, xcds = 1024, 8
+    # GRBM_GUI_ACTIVE is summed over the 8 XCDs: cycles of the dispatch = sum / 8
+    cycles = avg.get("GRBM_GUI_ACTIVE", 0.0) / xcds
+    d = {}
+    if cycles > 0:
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            d["mfma_busy_frac"] = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * simds)
+        if "SQ_INSTS_VALU" in avg:
+            valu = avg["SQ_INSTS_VALU"] - avg.get("SQ_INSTS_MFMA", 0.0)
+            d["valu_busy_frac"] = 4.0 * valu / (cycles * simds)
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+            d["valu_mfma_coexec_frac"] = avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / (cycles * simds)
+    if "SQ_WAIT_INST_ANY" in avg and "SQ_WAVE_CYCLES" in avg and avg["SQ_WAVE_CYCLES"] > 0:
+        d["wave_wait_frac"] = avg["SQ_WAIT_INST_ANY"] / avg["SQ_WAVE_CYCLES"]
+    if case is not None and "SQ_INSTS_VALU" in avg:
+        weights = case.M * case.K
+        lane_ops = 64.0 * (avg["SQ_INSTS_VALU"] - avg.get("SQ_INSTS_MFMA", 0.0))
+        if case.op == "gemm":
+            d["valu_lane_ops_per_mac"] = lane_ops / (weights * case.rows)
+        else:
+            d["valu_lane_ops_per_weight"] = lane_ops / weights
+    if case is not None and "SQ_INSTS_MFMA" in avg and avg["SQ_INSTS_MFMA"] > 0:
+        d["mfma_instructions"] = avg["SQ_INSTS_MFMA"]
+        d["mfma_flops_over_algorithmic"] = avg["SQ_INSTS_MFMA"] * 16 * 16 * 32 * 2 / case.flops
+    lines = [f"# Counters: workload {workload} ({', '.join(names)})", "",
+             "Commands (repository root, one MI355X; one counter set per run):", "", "```"] + \
+        list(commands) + ["```", "",
+             f"Kernel: `{kern}` (grid {meta[kern]['grid']}, workgroup {meta[kern]['workgroup']}, "
+             f"LDS {meta[kern]['lds']} B, {meta[kern]['vgpr']} VGPRs, {meta[kern]['agpr']} AGPRs).", "",
+             "| counter | average per dispatch |", "|---|---|"]
+    for c in sorted(avg):
+        lines.append(f"| {c} | {avg[c]:.4g} |")
+    lines += ["", "Derived (GRBM_GUI_ACTIVE is summed over the 8 XCDs, so the dispatch's cycles are "
+              "its value / 8; 1024 SIMDs; a 64-lane VALU instruction occupies a 16-lane SIMD for 4 "
+              "cycles; a 16x16x32 bf16 MFMA is 16384 flops):", "",
+              "| quantity | value | formula |", "|---|---|---|"]
+    formulas = {
+        "mfma_busy_frac": "SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024)",
+        "valu_busy_frac": "4 (SQ_INSTS_VALU - SQ_INSTS_MFMA) / (cycles x 1024)",
+        "valu_mfma_coexec_frac": "SQ_VALU_MFMA_COEXEC_CYCLES / (cycles x 1024)",
+        "wave_wait_frac": "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES",
+        "valu_lane_ops_per_weight": "64 (SQ_INSTS_VALU - SQ_INSTS_MFMA) / (M K)",
+        "valu_lane_ops_per_mac": "64 (SQ_INSTS_VALU - SQ_INSTS_MFMA) / (M K N)",
+        "mfma_instructions": "SQ_INSTS_MFMA",
+        "mfma_flops_over_algorithmic": "SQ_INSTS_MFMA x 16384 / (2 M K N)",
+    }
+    for k, v in d.items():
+        lines.append(f"| {k} | {v:.4g} | {formulas[k]} |")
+    rec = {"workload": workload, "kernel": kern, "kernel_source_hash": src_hash,
+           **{k: round(v, 5) for k, v in d.items()}}
+    lines += ["", f"Kernel source hash (sha256 of gemm_qgemv_amd/csrc except probe.hip, first 16 hex): "
+              f"`{src_hash}`.", "", "```json", json.dumps(rec), "```", ""]
+    return "\n".join(lines)
+
+
 def load_trace(workload, src_hash):
     """The committed kernel-trace summary of this workload, if it was taken
     from the current kernel sources."""
@@ -545,6 +624,10 @@ def main():
                          "JSON line, as committed under profiles/trace_<workload>.md) and exit")
     ap.add_argument("--trace-command", default="",
                     help="the command that produced the trace, quoted in the summary")
+    ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
+                    help="summarize rocprofv3 --pmc counter CSVs of this workload (markdown with a "
+                         "JSON line, as committed under profiles/counters_<workload>.md) and exit; "
+                         "--trace-command may be given once per run")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip timing the streaming-read ceiling over the step's weight bytes")
     ap.add_argument("--probe", choices=["copy", "read", "stream"],
@@ -564,6 +647,10 @@ def main():
     if args.trace_summary:
         print(trace_summary(args.trace_summary, args.workload, kernel_source_hash(),
                             args.trace_command))
+        return
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary, args.workload, kernel_source_hash(),
+                              args.trace_command.split(" ;; ") if args.trace_command else []))
         return
 
     import torch
