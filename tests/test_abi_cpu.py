@@ -208,7 +208,7 @@ def test_wide_greedy_head_checks():
     M, K = 151936, 2048
     for n in (64, 128, q.QG_MAX_ARGMAX_BATCH):
         need = q.qg_workspace_bytes(q.QG_OP_GEMV_ARGMAX, q.QG_U4_G64, M, K, n)
-        assert need >= q.QG_WS_CONTROL_BYTES + n * (M // 64) * 8
+        assert need >= q.QG_WS_CONTROL_BYTES + n * (M // 128) * 8   # one key per 128-row tile
     # 17..48 rows of this 4-bit head run as launches of up to 16 rows of the
     # matrix-vector kernels: control words plus 16 keys per workgroup
     for n in (17, 33, 48):
