@@ -576,6 +576,56 @@ def counter_summary(csv_paths, workload, src_hash, commands):
     return "\n".join(lines)
 
 
+def traffic_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, workload, src_hash,
+                    commands):
+    """HBM traffic per launch of the workload's library kernel from
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch), each scaled
+    by what the same counter reads for the copy probe of known size
+    (`bench.py --probe copy`: 256 MiB read and 256 MiB written per
+    dispatch). Writes profiles/traffic_<workload>.{md,json} content:
+    returns (markdown, record)."""
+    import csv
+
+    def per_dispatch(path, kernel_filter):
+        v = []
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                if kernel_filter(row["Kernel_Name"]):
+                    v.append(float(row["Counter_Value"]))
+        return v
+
+    lib = lambda k: "qg::" in k
+    probe = lambda k: "qg_probe_copy" in k
+    fe, wr = per_dispatch(fetch_csv, lib), per_dispatch(write_csv, lib)
+    cf, cw = per_dispatch(copy_fetch_csv, probe), per_dispatch(copy_write_csv, probe)
+    kib = 256 * 1024
+    ff, wf = kib / (sum(cf) / len(cf)), kib / (sum(cw) / len(cw))
+    fa, wa = sum(fe) / len(fe), sum(wr) / len(wr)
+    rec = {"workload": workload, "kernel_source_hash": src_hash,
+           "fetch_size_kib_per_dispatch": round(fa, 3), "write_size_kib_per_dispatch": round(wa, 3),
+           "dispatches": [len(fe), len(wr)], "copy_probe_kib": kib,
+           "copy_fetch_size_kib": round(sum(cf) / len(cf), 3),
+           "copy_write_size_kib": round(sum(cw) / len(cw), 3),
+           "fetch_factor": round(ff, 5), "write_factor": round(wf, 5),
+           "hbm_read_bytes_per_launch": int(fa * ff * 1024),
+           "hbm_write_bytes_per_launch": int(wa * wf * 1024)}
+    rec["traffic_bytes_per_launch"] = rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
+    names = WORKLOADS.get(workload, [workload])
+    lines = [f"# HBM traffic per launch: workload {workload} ({', '.join(names)})", "",
+             "Commands (repository root, one MI355X), each counter in its own run:", "", "```"] + \
+        list(commands) + ["```", "",
+             f"Calibration: the copy probe moves 256 MiB in and 256 MiB out per dispatch; FETCH_SIZE "
+             f"reads {rec['copy_fetch_size_kib']} KiB and WRITE_SIZE {rec['copy_write_size_kib']} KiB "
+             f"for it, so the factors are {ff:.4f} (fetch) and {wf:.4f} (write).", "",
+             "| counter | KiB per dispatch | dispatches | scaled bytes per launch |", "|---|---|---|---|",
+             f"| FETCH_SIZE | {fa:.1f} | {len(fe)} | {rec['hbm_read_bytes_per_launch']:,} |",
+             f"| WRITE_SIZE | {wa:.1f} | {len(wr)} | {rec['hbm_write_bytes_per_launch']:,} |",
+             f"| total | | | {rec['traffic_bytes_per_launch']:,} |", "",
+             f"Kernel source hash (sha256 of gemm_qgemv_amd/csrc except probe.hip, first 16 hex): "
+             f"`{src_hash}`.", ""]
+    return "\n".join(lines), rec
+
+
 def load_trace(workload, src_hash):
     """The committed kernel-trace summary of this workload, if it was taken
     from the current kernel sources."""
@@ -628,6 +678,10 @@ def main():
                     help="summarize rocprofv3 --pmc counter CSVs of this workload (markdown with a "
                          "JSON line, as committed under profiles/counters_<workload>.md) and exit; "
                          "--trace-command may be given once per run")
+    ap.add_argument("--traffic-summary", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.md and .json from rocprofv3 FETCH_SIZE / "
+                         "WRITE_SIZE runs of the workload and of --probe copy, and exit")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip timing the streaming-read ceiling over the step's weight bytes")
     ap.add_argument("--probe", choices=["copy", "read", "stream"],
@@ -647,6 +701,15 @@ def main():
     if args.trace_summary:
         print(trace_summary(args.trace_summary, args.workload, kernel_source_hash(),
                             args.trace_command))
+        return
+    if args.traffic_summary:
+        md, rec = traffic_summary(*args.traffic_summary, args.workload, kernel_source_hash(),
+                                  args.trace_command.split(" ;; ") if args.trace_command else [])
+        with open(os.path.join(ROOT, "profiles", f"traffic_{args.workload}.md"), "w") as f:
+            f.write(md)
+        with open(os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        print(md)
         return
     if args.counter_summary:
         print(counter_summary(args.counter_summary, args.workload, kernel_source_hash(),
