@@ -305,8 +305,6 @@ def run_probe(args, torch, synth):
     L.qg_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                                 ctypes.c_void_p]
     L.qg_probe_read_blocked.argtypes = L.qg_probe_read.argtypes
-    L.qg_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
-                                  ctypes.c_int, ctypes.c_void_p]
     s = torch.cuda.current_stream().cuda_stream
     if args.probe == "copy":
         n = 256 << 20
@@ -323,14 +321,8 @@ def run_probe(args, torch, synth):
     bufs = [torch.empty(size, dtype=torch.uint8, device="cuda") for _ in range(copies)]
     out = torch.empty(8192, dtype=torch.int32, device="cuda")
     best, best_cfg = None, None
-    if args.probe == "stream":
-        modes = ("LDS-direct loads", "LDS-direct loads, read back", "LDS-direct, matrix-core work",
-                 "register loads, matrix-core work")
-        variants = [(modes[m], lambda p, n, o, g, st, m=m: L.qg_probe_stream(p, n, o, g, m, st)) for m in range(4)]
-        grids = (256, 512, 1024, 2048)
-    else:
-        variants = [("grid-stride", L.qg_probe_read), ("blocked", L.qg_probe_read_blocked)]
-        grids = (1024, 2048, 4096, 8192)
+    variants = [("grid-stride", L.qg_probe_read), ("blocked", L.qg_probe_read_blocked)]
+    grids = (1024, 2048, 4096, 8192)
     per = {}
     for name, fn in variants:
         for grid in grids:
@@ -356,8 +348,7 @@ def run_probe(args, torch, synth):
                 best, best_cfg = us, f"{name}, grid {grid}"
     rec = {"probe": args.probe, "bytes": size, "us": round(best, 3),
            "GB/s": round(size / best / 1e3, 1), "best": best_cfg}
-    if args.probe == "stream":
-        rec["per_variant_GB/s"] = {k: round(size / v[0] / 1e3, 1) for k, v in per.items()}
+    rec["per_variant_GB/s"] = {k: round(size / v[0] / 1e3, 1) for k, v in per.items()}
     print(json.dumps(rec))
 
 
@@ -684,13 +675,11 @@ def main():
                          "WRITE_SIZE runs of the workload and of --probe copy, and exit")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip timing the streaming-read ceiling over the step's weight bytes")
-    ap.add_argument("--probe", choices=["copy", "read", "stream"],
+    ap.add_argument("--probe", choices=["copy", "read"],
                     help="run only a measurement probe: 'copy' copies 256 MiB 8 times (a kernel of "
                          "known traffic, to calibrate FETCH_SIZE / WRITE_SIZE); 'read' times cold "
                          "streaming reads of the workload's weight size (two read kernels, four "
-                         "grid sizes, best reported); 'stream' the same size through LDS-direct "
-                         "loads, with and without read-back, and with the arithmetic of a "
-                         "matrix-core batch-1 kernel on LDS-direct or register loads")
+                         "grid sizes, best reported)")
     args = ap.parse_args()
 
     if args.gpus != 1:

@@ -40,13 +40,7 @@ constexpr int kEmbedThreads = 256;
 // workgroup with streaming stores writes faster than a plain fill kernel of
 // the same output (4.7 us); two or four rows per workgroup, or ordinary
 // stores, are slower (5.1 - 7.5 us).
-#ifndef QG_EMBED_ROWS
-#define QG_EMBED_ROWS 1
-#endif
-#ifndef QG_EMBED_NT
-#define QG_EMBED_NT 1
-#endif
-constexpr int kEmbedRows = QG_EMBED_ROWS;
+constexpr int kEmbedRows = 1;
 
 __device__ __forceinline__ float embed_value(float s, float b, uint32_t q)
 {
@@ -57,13 +51,9 @@ __device__ __forceinline__ float embed_value(float s, float b, uint32_t q)
 
 __device__ __forceinline__ void embed_store(float4 *dst, float4 v)
 {
-#if QG_EMBED_NT
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     const f32x4 w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, reinterpret_cast<f32x4 *>(dst));
-#else
-    *dst = v;
-#endif
 }
 
 // Each thread produces float4 f of a row (inputs 4f .. 4f+3: two code bytes)

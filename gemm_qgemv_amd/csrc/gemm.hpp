@@ -20,13 +20,14 @@
 // all BM weight rows, so a wave reads BM / 16 weight fragments and 3 * BN / 64
 // activation fragments per k-step for 3 * BM * BN / 1024 MFMAs. For up to 32
 // token rows the tile is 16 or 32 tokens wide and the waves split the
-// weight rows instead (see gemm_kernel). A k-step
-// stages 32 k of W (converted to bf16) and X (split into 3 bf16 planes) in
-// LDS, double-buffered: the step after the current one is staged from
-// registers while the current MFMAs run, and the loads of the step after
-// that are issued behind it, so one barrier per step suffices. LDS rows are
-// 64 bytes with an XOR swizzle of their four 16-byte chunks (conflict-free
-// fragment reads).
+// weight rows instead (see gemm_kernel). A k-step stages 32 k of W
+// (converted to bf16) in LDS, double-buffered: the step after the current
+// one is staged from registers while the current MFMAs run, and the loads of
+// the step after that are issued behind it, so one barrier per step
+// suffices. LDS rows are 64 bytes with an XOR swizzle of their four 16-byte
+// chunks (conflict-free fragment reads). The activations go from global
+// memory straight into registers in the MFMA operand layout (each token row
+// is used by one wave only) and are split there into their three bf16 pieces.
 //
 // MFMA 16x16x32 bf16 operand layout (lane l of 64):
 //   A (16 x 32, here W rows):    row l % 16, k = 8 * (l / 16) .. + 7
@@ -113,21 +114,9 @@ constexpr int kGemmThreads = 256;
 // the group close at the same place of every unrolled pass. The 1-bit
 // format keeps 4 (one 128-input group; 514 us at depth 2, 461 at 4 for
 // 17408 x 5120, N = 512).
-#ifndef QG_GEMM_DEPTH_I8
-#define QG_GEMM_DEPTH_I8 2
-#endif
-#ifndef QG_GEMM_DEPTH_B1
-#define QG_GEMM_DEPTH_B1 4
-#endif
-#ifndef QG_GEMM_DEPTH_U4
-#define QG_GEMM_DEPTH_U4 2
-#endif
-#ifndef QG_GEMM_DEPTH_I8G
-#define QG_GEMM_DEPTH_I8G 2
-#endif
-#ifndef QG_GEMM_INTERLEAVE
-#define QG_GEMM_INTERLEAVE 5   // VALU instructions issued after each MFMA
-#endif
+template <int FMT> struct GemmDepth { static constexpr int value = 2; };
+template <> struct GemmDepth<FMT_B1_G128> { static constexpr int value = 4; };
+constexpr int kGemmInterleave = 5;   // VALU instructions issued after each MFMA
 
 // Largest K of the matrix-core prefill: the buffer loads below address a
 // tile's activation rows (128 rows of 4 K bytes) with 32-bit offsets, and
@@ -421,10 +410,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
     // the activations split; the split pieces of the step being computed
     // stay in registers (bx), so a step's MFMAs never wait for its own
     // VALU work, which runs beside the previous step's MFMAs
-    constexpr int D = FMT == FMT_I8_ROW   ? QG_GEMM_DEPTH_I8
-                      : FMT == FMT_I8_G64 ? QG_GEMM_DEPTH_I8G
-                      : FMT == FMT_U4_G64 ? QG_GEMM_DEPTH_U4
-                                          : QG_GEMM_DEPTH_B1;
+    constexpr int D = GemmDepth<FMT>::value;
     Regs R[D];
 #pragma unroll
     for (int u = 0; u < D; ++u)
@@ -458,7 +444,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
             for (int j = 0; j < TJ; ++j)
 #pragma unroll
                 for (int c = 0; c < 3; ++c) bx[j][c] = bn[j][c];
-#if QG_GEMM_INTERLEAVE
             // issue order: the fragment reads, then each MFMA followed by a
             // few VALU instructions (the next step's split and staging), so
             // that they run while the matrix pipe is busy
@@ -466,9 +451,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
 #pragma unroll
             for (int i = 0; i < 3 * TI * TJ; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, QG_GEMM_INTERLEAVE, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, kGemmInterleave, 0);
             }
-#endif
             __syncthreads();
         }
     }

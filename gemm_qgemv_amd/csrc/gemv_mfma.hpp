@@ -65,23 +65,11 @@ struct GemvMfmaParams {
                            // greedy head unused), else nullptr
 };
 
-#ifndef QG_MFMA_WAVES
-#define QG_MFMA_WAVES 8
-#endif
-constexpr int kMfmaWaves = QG_MFMA_WAVES;   // waves per workgroup
+constexpr int kMfmaWaves = 8;          // waves per workgroup
 constexpr int kMfmaThreads = 64 * kMfmaWaves;
 constexpr int kStageItems = 8;          // staging items per thread: K <= 4096
 constexpr int kMfmaChunk = 8;           // groups per register chunk
-#ifndef QG_MFMA_BUFS
-#define QG_MFMA_BUFS 3
-#endif
-constexpr int kMfmaBufs = QG_MFMA_BUFS; // register chunks in the ring
-#ifndef QG_MFMA_CHAINS
-#define QG_MFMA_CHAINS 1                // accumulation chains per group
-#endif
-#ifndef QG_MFMA_NT
-#define QG_MFMA_NT 1                    // non-temporal code loads
-#endif
+constexpr int kMfmaBufs = 3;           // register chunks in the ring
 // One operand block in LDS: 1 KiB top/middle pieces [q][row 16] and 512 B
 // halved bottom pieces [q][n 8] (read by operand rows n and 8 + n). A group
 // has two (one per k-step); each 32 groups of the bias contraction have one.
@@ -192,12 +180,8 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_u4_kernel(GemvMfmaPara
     auto load = [&](MfmaChunk &k) {
 #pragma unroll
         for (int j = 0; j < kMfmaChunk / 2; ++j) {
-#if QG_MFMA_NT
             const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(lc_c + 64 * j));
             k.c[j] = make_uint4(v.x, v.y, v.z, v.w);
-#else
-            k.c[j] = *reinterpret_cast<const uint4 *>(lc_c + 64 * j);
-#endif
         }
         k.s = *reinterpret_cast<const uint4 *>(lc_s);
         if (lc_chunk < NBS)   // biases of groups 32 c + 8 q .. + 7
@@ -317,16 +301,6 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_u4_kernel(GemvMfmaPara
                 const uint8_t *b = gb + g * kMfmaGroupBytes;
                 const bf16x8_t w0 = nibbles_to_bf16(dw[h][0]), w1 = nibbles_to_bf16(dw[h][1]);
                 const float sc = bf16_at(k.s, g);
-#if QG_MFMA_CHAINS == 2
-                // two independent accumulation chains (top/middle, bottom)
-                floatx4_t t = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
-                t = mfma(*reinterpret_cast<const uint4 *>(b + hm_off), w0, t);
-                u = mfma(*reinterpret_cast<const uint4 *>(b + lo_off), w0, u);
-                t = mfma(*reinterpret_cast<const uint4 *>(b + kMfmaBlockBytes + hm_off), w1, t);
-                u = mfma(*reinterpret_cast<const uint4 *>(b + kMfmaBlockBytes + lo_off), w1, u);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, u[i], fmaf(sc, t[i], acc[i]));
-#else
                 floatx4_t t = {0.f, 0.f, 0.f, 0.f};
                 t = mfma(*reinterpret_cast<const uint4 *>(b + hm_off), w0, t);
                 t = mfma(*reinterpret_cast<const uint4 *>(b + lo_off), w0, t);
@@ -334,7 +308,6 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_u4_kernel(GemvMfmaPara
                 t = mfma(*reinterpret_cast<const uint4 *>(b + kMfmaBlockBytes + lo_off), w1, t);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, t[i], acc[i]);
-#endif
             }
         }
         if (cc < NBS) {

@@ -130,12 +130,8 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
                                                           : 64 * gw + 32 * (q & 1) + 16 * (q >> 1));
 #pragma unroll
         for (int j = 0; j < NC; ++j) {
-#if QG_MFMA_NT
             const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(c + 64 * j));
             T.c[j] = make_uint4(v.x, v.y, v.z, v.w);
-#else
-            T.c[j] = *reinterpret_cast<const uint4 *>(c + 64 * j);
-#endif
         }
         if constexpr (U4) {
             const uint32_t *sc = reinterpret_cast<const uint32_t *>(p.scales + m * G + gw);

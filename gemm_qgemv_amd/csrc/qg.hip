@@ -131,18 +131,10 @@ int launch_status()
 
 // Batch-1 kernel tuning (compile-time; the plan is a pure function of the
 // call's shape).
-#ifndef QG_GEMV1_WAVES
-#define QG_GEMV1_WAVES 2048   // waves the rows are spread over (at most)
-#endif
-#ifndef QG_GEMV1_NT
-#define QG_GEMV1_NT 1         // non-temporal weight loads (streamed once)
-#endif
-#ifndef QG_GEMV1_R
-#define QG_GEMV1_R 4          // rows per block when K fits in one or two slices per lane
-#endif
-#ifndef QG_GEMV1_MINWAVES
-#define QG_GEMV1_MINWAVES 1024  // fewer rows per block until this many waves
-#endif
+constexpr int64_t kGemv1Waves = 2048;     // waves the rows are spread over (at most)
+constexpr bool kGemv1Nt = true;           // non-temporal weight loads (streamed once)
+constexpr int kGemv1R = 4;                // rows per block when K fits in one or two slices per lane
+constexpr int64_t kGemv1MinWaves = 1024;  // fewer rows per block until this many waves
 
 // Workspace: the first kCtlBytes are completion words (the greedy head's,
 // then one per row tile of the in-kernel split-K combine), claimed by each
@@ -339,9 +331,9 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
         pl.one = true;
         pl.ns = static_cast<int>(ceil_div(S, 64));
         pl.full = S % 64 == 0;
-        pl.R = pl.ns >= 3 ? 2 : QG_GEMV1_R;
-        while (pl.R > 1 && ceil_div(M, pl.R) < QG_GEMV1_MINWAVES) pl.R /= 2;
-        pl.rows_per_wave = round_up(ceil_div(M, QG_GEMV1_WAVES), pl.R);
+        pl.R = pl.ns >= 3 ? 2 : kGemv1R;
+        while (pl.R > 1 && ceil_div(M, pl.R) < kGemv1MinWaves) pl.R /= 2;
+        pl.rows_per_wave = round_up(ceil_div(M, kGemv1Waves), pl.R);
         // greedy head: 8-wave workgroups where K takes one or two slices per
         // lane (half the workgroups folding their keys into the shared slot
         // at the end: 6144 x 2048 4-bit 11.0 -> 8.9 us); the 3- and 4-slice
@@ -529,7 +521,7 @@ void launch_gemv_fmt(const GemvPlan &pl, const GemvParams &p, hipStream_t s)
 template <int FMT, int NS, bool FULL, int WGW>
 void launch_gemv1_wg(const GemvPlan &pl, const qg::Gemv1Params &p, hipStream_t s)
 {
-    constexpr bool NT = QG_GEMV1_NT != 0;
+    constexpr bool NT = kGemv1Nt;
     const dim3 grid(static_cast<unsigned>(pl.grid_x)), block(64 * WGW);
     switch (pl.R) {
     case 8: hipLaunchKernelGGL((qg::gemv1_kernel<FMT, NS, 8, FULL, NT, WGW>), grid, block, 0, s, p); break;

@@ -40,13 +40,13 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     if not os.path.exists(path):
         pytest.skip("libqgprobe.so not built")
     lib = ctypes.CDLL(path)
-    for name in ("qg_probe_read", "qg_probe_read_blocked", "qg_probe_copy", "qg_probe_stream"):
+    for name in ("qg_probe_read", "qg_probe_read_blocked", "qg_probe_copy"):
         assert hasattr(lib, name), name
-    lib.qg_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
-                                    ctypes.c_int, ctypes.c_void_p]
-    assert lib.qg_probe_stream(A, 1024, A, 256, 4, None) == -1      # no such mode
-    assert lib.qg_probe_stream(A, 1000, A, 256, 0, None) == -1      # not a multiple of 16 bytes
-    assert lib.qg_probe_stream(None, 1024, A, 256, 0, None) == -1
+    lib.qg_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_void_p]
+    assert lib.qg_probe_read(A, 1000, A, 256, None) == -1     # not a multiple of 16 bytes
+    assert lib.qg_probe_read(None, 1024, A, 256, None) == -1
+    assert lib.qg_probe_read(A, 1024, A, 0, None) == -1       # no grid
 
 
 def test_version_and_status_strings():
