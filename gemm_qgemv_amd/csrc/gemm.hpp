@@ -56,6 +56,13 @@ struct GemmParams {
     int tiles_m, tiles_n;
     int keys_m;       // greedy head: keys per token row (tiles_m x waves along m)
     int kt_split;     // 32-input steps per split of K (a multiple of 4), or 0: no split
+    // Split tail: workgroups 0 .. nfull-1 each take one of tiles 0 .. nfull-1
+    // over all of K; the workgroups after them take the remaining tiles in
+    // tsplit pieces of kt_tail steps each (a multiple of 4) and store their
+    // partial tiles in tpart [tsplit][tiles - nfull][BN][BM] (y unused for
+    // them). tsplit = 0: no split tail.
+    float *tpart;
+    int nfull, tsplit, kt_tail;
 };
 
 // 8 nibbles of one dword (8 consecutive inputs, even k in the low nibbles)
@@ -179,7 +186,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
     // that share an X block meet in the same L2.
     const int ntiles = p.tiles_m * p.tiles_n;
     int bid = blockIdx.x;
-    if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
+    int piece = -1;   // split tail: this workgroup's piece of K
+    if (p.tsplit > 0 && bid >= p.nfull) {
+        piece = (bid - p.nfull) % p.tsplit;
+        bid = p.nfull + (bid - p.nfull) / p.tsplit;
+    } else {
+        const int nmap = p.tsplit > 0 ? p.nfull : ntiles;
+        if ((nmap & 7) == 0) bid = (bid & 7) * (nmap >> 3) + (bid >> 3);
+    }
     const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
     const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * BN;
 
@@ -213,8 +227,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
     // counts local steps below; loads add ktb; ktb is a multiple of every
     // group's step count, so group boundaries stay where they are)
     const int nk_all = static_cast<int>((p.K + GT_K - 1) / GT_K);   // K is a multiple of 16
-    const int ktb = p.kt_split > 0 ? static_cast<int>(blockIdx.y) * p.kt_split : 0;
-    const int nk = p.kt_split > 0 ? min(p.kt_split, nk_all - ktb) : nk_all;
+    const int kts = piece >= 0 ? p.kt_tail : p.kt_split;
+    const int ktb = piece >= 0 ? piece * p.kt_tail : p.kt_split > 0 ? static_cast<int>(blockIdx.y) * p.kt_split : 0;
+    const int nk = kts > 0 ? min(kts, nk_all - ktb) : nk_all;
     const int64_t groups = p.K / (32 * GSTEPS);
     constexpr int SBYTES = FMT == FMT_I8_G64 ? 4 : 2;   // bytes per group coefficient
     const auto sbuf = buffer_rsrc(static_cast<const uint8_t *>(p.scales) + m0 * groups * SBYTES,
@@ -501,6 +516,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
             if (n >= p.N) continue;
             const float v[4] = {s[0] * acc[i][j][0], s[1] * acc[i][j][1], s[2] * acc[i][j][2],
                                 s[3] * acc[i][j][3]};
+            if (piece >= 0) {
+                // partial tile, stored whole ([token][row] within the tile)
+                float *dst = p.tpart + ((static_cast<int64_t>(piece) * (ntiles - p.nfull) + (bid - p.nfull)) * BN +
+                                        (n - n0)) * BM + (mb - m0);
+                *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+                continue;
+            }
             if (p.keys != nullptr) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -561,6 +583,42 @@ __global__ __launch_bounds__(256) void gemm_splitk_combine_kernel(const float *p
             for (int s = 1; s < nsplit; ++s) a += part[s * total + e];
             y[e] = a;
         }
+    }
+}
+
+// Split tail: Y of tiles nfull .. tiles-1 = sum over pieces s of
+// tpart[s][t][n][m] (tile-local token n, row m), added in piece order. One
+// thread per 4 outputs of a tile, tiles of BM x BN.
+__global__ __launch_bounds__(256) void gemm_tail_combine_kernel(const float *tpart, float *y, int64_t M,
+                                                                int64_t N, int tiles_m, int nfull, int ntail,
+                                                                int tsplit, int bm, int bn)
+{
+    const int64_t tile_elems = static_cast<int64_t>(bm) * bn;
+    const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+    if (i >= ntail * tile_elems) return;
+    const int t = static_cast<int>(i / tile_elems);
+    const int e = static_cast<int>(i % tile_elems);
+    const int tile = nfull + t;
+    const int64_t m = static_cast<int64_t>(tile % tiles_m) * bm + e % bm;
+    const int64_t n = static_cast<int64_t>(tile / tiles_m) * bn + e / bm;
+    if (n >= N || m >= M) return;
+    const int64_t stride = static_cast<int64_t>(ntail) * tile_elems;
+    float4 a = *reinterpret_cast<const float4 *>(tpart + i);
+    for (int s = 1; s < tsplit; ++s) {
+        const float4 b = *reinterpret_cast<const float4 *>(tpart + s * stride + i);
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+    }
+    float *dst = y + n * M + m;
+    if ((M & 3) == 0 && m + 3 < M) {
+        *reinterpret_cast<float4 *>(dst) = a;
+    } else {
+        dst[0] = a.x;
+        if (m + 1 < M) dst[1] = a.y;
+        if (m + 2 < M) dst[2] = a.z;
+        if (m + 3 < M) dst[3] = a.w;
     }
 }
 

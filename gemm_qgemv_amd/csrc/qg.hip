@@ -20,6 +20,7 @@
 #include "gemv_mfma.hpp"
 #include "gemv_mfma16.hpp"
 #include "gemv_stream.hpp"
+#include "gemv_stream_mfma.hpp"
 
 namespace {
 
@@ -165,6 +166,7 @@ struct GemvPlan {
                          // small-batch kernel: outputs staged in LDS
     bool stream;         // batch-1 4-bit kernel with loader waves (large M, K = 2048 nc)
     int nc;              // stream kernel: 1 KiB code chunks per row
+    bool smfma;          // 2..8 rows, 4-bit, K = 2048: loader waves + matrix cores
     bool one;            // batch-1 kernel (8-bit / 4-bit, activations in registers)
     int ns;              // batch-1 kernel: slices per lane
     bool full;           // batch-1 kernel: every lane owns all NS slices
@@ -302,6 +304,14 @@ bool stream_ok(int fmt, int64_t M, int64_t K)
     return M >= kComputeUnits * rows_per_stage * 4;
 }
 
+// The small-batch stream kernel: 4-bit rows of K = 2048 inputs, 2..8
+// activation rows, at least four stages of 32 rows per workgroup.
+bool stream_mfma_ok(int fmt, int64_t M, int64_t K, int nb)
+{
+    return fmt == QG_U4_G64 && K == qg::kStreamMfmaK && nb >= 2 && nb <= qg::kStreamMfmaRows &&
+           M >= kComputeUnits * 32 * 4;
+}
+
 GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
 {
     GemvPlan pl{};
@@ -321,6 +331,19 @@ GemvPlan plan_gemv(int fmt, int64_t M, int64_t K, int nb, bool argmax)
             pl.nkeys = static_cast<int>(pl.grid_x);
             pl.key_off = kCtlBytes;
             pl.ws_bytes = align256(kCtlBytes + static_cast<size_t>(pl.grid_x) * 8);
+        }
+        return pl;
+    }
+    if (stream_mfma_ok(fmt, M, K, nb)) {
+        // a few rows, 4-bit, large M: one workgroup per compute unit, loader
+        // waves streaming the rows through LDS, matrix cores reducing them
+        pl.smfma = true;
+        pl.grid_x = kComputeUnits;
+        pl.nsplit = 1;
+        if (argmax) {
+            pl.nkeys = static_cast<int>(pl.grid_x);
+            pl.key_off = kCtlBytes;
+            pl.ws_bytes = align256(kCtlBytes + static_cast<size_t>(pl.grid_x) * nb * 8);
         }
         return pl;
     }
@@ -673,6 +696,28 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
         }
         return;
     }
+    if (pl.smfma) {
+        qg::GemvStreamMfmaParams q{};
+        q.codes = static_cast<const uint8_t *>(codes);
+        q.scales = static_cast<const uint16_t *>(scales);
+        q.biases = static_cast<const uint16_t *>(biases);
+        q.x = x;
+        q.y = y;
+        q.ctl = idx ? static_cast<qg::GreedyCtl *>(ws) : nullptr;
+        q.keys = idx ? reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + pl.key_off) : nullptr;
+        q.idx = idx;
+        q.M = M;
+        q.nb = nb;
+        static const bool lds_set = [] {
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(qg::gemv_stream_mfma_u4_kernel),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, qg::kStreamMfmaLdsBytes);
+            return true;
+        }();
+        (void)lds_set;
+        hipLaunchKernelGGL(qg::gemv_stream_mfma_u4_kernel, dim3(static_cast<unsigned>(pl.grid_x)),
+                           dim3(qg::kStreamThreads), qg::kStreamMfmaLdsBytes, s, q);
+        return;
+    }
     if (pl.stream) {
         qg::GemvStreamParams q{};
         q.codes = static_cast<const uint8_t *>(codes);
@@ -865,12 +910,54 @@ void gemm_split(int fmt, int64_t M, int64_t K, int64_t N, int &kt_split, int &ns
     if (nsplit < 2) kt_split = 0, nsplit = 1;
 }
 
+// Split tail of grids of at least one full round (two workgroups per
+// compute unit): when the last round would be at most a quarter full, its
+// tiles are cut along K into tsplit pieces (of kt_tail steps, a multiple of
+// 4) that fill it, the full rounds keep whole tiles, and a second launch
+// adds the pieces (17408 x 5120 1-bit, 512 token rows: 320 -> 273 us;
+// 1024 x 3584 8-bit, 10240 rows: 227 -> 210 us). A fuller last round gains
+// less than the partial stores and the second launch cost (3584 x 1024
+// 8-bit, 10240 rows, last round 3/8 full: 217 -> 240 us).
+// nfull: tiles computed whole. tsplit = 0: no split tail.
+struct GemmTail {
+    int nfull = 0, ntail = 0, tsplit = 0, kt_tail = 0;
+};
+
+GemmTail gemm_tail(int fmt, int64_t M, int64_t K, int64_t N)
+{
+    GemmTail t;
+    int kt_split, nsplit, bm, bn, wn;
+    gemm_split(fmt, M, K, N, kt_split, nsplit);
+    if (nsplit > 1) return t;
+    gemm_tile(fmt, M, N, bm, bn, wn);
+    const int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
+    const int64_t slots = 2 * kComputeUnits;
+    const int64_t ntail = tiles % slots;
+    if (tiles < slots || ntail == 0 || 4 * ntail > slots) return t;
+    const int64_t nk = ceil_div(K, 32);
+    const int64_t want = std::min(slots / ntail, nk / 4);
+    if (want < 2) return t;
+    const int64_t kt = round_up(ceil_div(nk, want), 4);
+    const int64_t pieces = ceil_div(nk, kt);
+    if (pieces < 2) return t;
+    t.nfull = static_cast<int>(tiles - ntail);
+    t.ntail = static_cast<int>(ntail);
+    t.tsplit = static_cast<int>(pieces);
+    t.kt_tail = static_cast<int>(kt);
+    return t;
+}
+
 size_t gemm_mfma_workspace(int fmt, int64_t M, int64_t K, int64_t N)
 {
     int kt_split, nsplit;
     gemm_split(fmt, M, K, N, kt_split, nsplit);
-    // partial products after the control words, which every call leaves zero
-    return nsplit > 1 ? align256(kCtlBytes + static_cast<size_t>(nsplit) * N * M * 4) : 0;
+    // partial products after the control words
+    if (nsplit > 1) return align256(kCtlBytes + static_cast<size_t>(nsplit) * N * M * 4);
+    const GemmTail t = gemm_tail(fmt, M, K, N);
+    if (t.tsplit == 0) return 0;
+    int bm, bn, wn;
+    gemm_tile(fmt, M, N, bm, bn, wn);
+    return align256(kCtlBytes + static_cast<size_t>(t.tsplit) * t.ntail * bm * bn * 4);
 }
 
 // 17..48 rows of the 4-bit format at K = 1024 or 2048 as launches of up to
@@ -1001,11 +1088,16 @@ void launch_gemm_fmt(int bm, int bn, dim3 grid, hipStream_t s, const qg::GemmPar
 // keys [N][tiles_m x waves along m] as well (y may then be nullptr).
 void launch_gemm(int fmt, const void *codes, const void *scales, const void *biases,
                  const float *x, float *y, unsigned long long *keys, int64_t M, int64_t K,
-                 int64_t N, hipStream_t s, float *part = nullptr, int kt_split = 0, int nsplit = 1)
+                 int64_t N, hipStream_t s, float *part = nullptr, int kt_split = 0, int nsplit = 1,
+                 const GemmTail &tail = GemmTail{})
 {
     qg::GemmParams p{};
     p.part = part;
     p.kt_split = kt_split;
+    p.tpart = tail.tsplit > 0 ? part : nullptr;
+    p.nfull = tail.nfull;
+    p.tsplit = tail.tsplit;
+    p.kt_tail = tail.kt_tail;
     p.codes = static_cast<const uint8_t *>(codes);
     p.scales = scales;
     p.biases = static_cast<const uint16_t *>(biases);
@@ -1020,7 +1112,9 @@ void launch_gemm(int fmt, const void *codes, const void *scales, const void *bia
     p.tiles_m = static_cast<int>(ceil_div(M, bm));
     p.tiles_n = static_cast<int>(ceil_div(N, bn));
     p.keys_m = p.tiles_m * (4 / wn);
-    const dim3 grid(static_cast<unsigned>(int64_t(p.tiles_m) * p.tiles_n), static_cast<unsigned>(nsplit));
+    const int64_t wgs = tail.tsplit > 0 ? int64_t(tail.nfull) + int64_t(tail.ntail) * tail.tsplit
+                                        : int64_t(p.tiles_m) * p.tiles_n;
+    const dim3 grid(static_cast<unsigned>(wgs), static_cast<unsigned>(nsplit));
     if (fmt == QG_I8_ROW) launch_gemm_fmt<qg::FMT_I8_ROW>(bm, bn, grid, s, p);
     else if (fmt == QG_I8_G64) launch_gemm_fmt<qg::FMT_I8_G64>(bm, bn, grid, s, p);
     else if (fmt == QG_U4_G64) launch_gemm_fmt<qg::FMT_U4_G64>(bm, bn, grid, s, p);
@@ -1033,11 +1127,22 @@ void run_gemm_mfma(int fmt, const void *codes, const void *scales, const void *b
 {
     int kt_split, nsplit;
     gemm_split(fmt, M, K, N, kt_split, nsplit);
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + kCtlBytes);
     if (nsplit == 1) {
-        launch_gemm(fmt, codes, scales, biases, x, y, nullptr, M, K, N, s);
+        const GemmTail t = gemm_tail(fmt, M, K, N);
+        if (t.tsplit == 0) {
+            launch_gemm(fmt, codes, scales, biases, x, y, nullptr, M, K, N, s);
+            return;
+        }
+        launch_gemm(fmt, codes, scales, biases, x, y, nullptr, M, K, N, s, part, 0, 1, t);
+        int bm, bn, wn;
+        gemm_tile(fmt, M, N, bm, bn, wn);
+        const int64_t quads = static_cast<int64_t>(t.ntail) * bm * bn / 4;
+        hipLaunchKernelGGL(qg::gemm_tail_combine_kernel, dim3(static_cast<unsigned>(ceil_div(quads, 256))),
+                           dim3(256), 0, s, part, y, M, N, static_cast<int>(ceil_div(M, bm)), t.nfull,
+                           t.ntail, t.tsplit, bm, bn);
         return;
     }
-    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + kCtlBytes);
     launch_gemm(fmt, codes, scales, biases, x, nullptr, nullptr, M, K, N, s, part, kt_split, nsplit);
     const int64_t quads = ceil_div(M * N, 4);
     hipLaunchKernelGGL(qg::gemm_splitk_combine_kernel, dim3(static_cast<unsigned>(ceil_div(quads, 256))),

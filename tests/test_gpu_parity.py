@@ -218,6 +218,24 @@ def test_exact_arithmetic_prefill_large_grid(torch, orc, M, K, N):
 
 
 @pytest.mark.parametrize("fmt,M,K,N", [
+    (synth.I8_ROW, 2000, 272, 5100), (synth.U4_G64, 2100, 576, 2000), (synth.B1_G128, 1100, 1152, 3900),
+    (synth.I8_G64, 2100, 576, 2000),
+])
+def test_exact_arithmetic_prefill_split_tail(torch, orc, fmt, M, K, N):
+    """Grids of one or more full rounds of tiles plus a short last round,
+    whose tiles are computed in pieces of K and added by a second launch:
+    ragged M and N in the last round, a short last piece of K."""
+    say(f"exact prefill split tail fmt={fmt} M={M} K={K} N={N}")
+    rng = np.random.default_rng([13, fmt, M, K, N])
+    w, x = exact_inputs(fmt, M, K, N, rng)
+    ref, _ = orc.qgemv(fmt, w.codes, w.scales, w.biases, x, M, K)
+    want = ref.astype(np.float32)
+    assert np.array_equal(want.astype(np.float64), ref), "fixture is not exact in float32"
+    yg = gpu_gemm(torch, dev(w), x)
+    assert np.array_equal(yg, want), f"prefill not bit-exact: max diff {np.max(np.abs(yg - want))}"
+
+
+@pytest.mark.parametrize("fmt,M,K,N", [
     (synth.I8_ROW, 1, 16, 17), (synth.I8_ROW, 127, 1040, 129), (synth.I8_ROW, 1000, 1024, 300),
     (synth.I8_ROW, 4001, 1040, 1503),
     (synth.I8_ROW, 130, 3584, 33), (synth.B1_G128, 1, 128, 40), (synth.B1_G128, 250, 5120, 131),
@@ -903,3 +921,65 @@ def test_stream_kernel_ties(torch, orc):
     check_bound(y, ref2, a2, "stream ties")
     check_argmax(idx, y, ref2, a2, orc, "stream ties")
     assert idx[0] == 5
+
+
+# ---------------------------------------------------------------------------
+# 2..8 activation rows, 4-bit, K = 2048, large M: loader waves + matrix cores
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N", [(32768, 8), (151937, 2), (40001, 3), (70000, 5), (151936, 8), (33000, 7)])
+def test_stream_mfma_kernel_random(torch, orc, M, N):
+    """Random inputs, with and without the greedy indices and logits; every
+    workgroup's run of rows ends in a partial stage at most of these M."""
+    K = 2048
+    say(f"stream mfma kernel M={M} N={N}")
+    rng = synth.rng_for(610, M + N)
+    w = synth.draw_weights(synth.U4_G64, M, K, rng)
+    x = synth.draw_x(N, K, rng)
+    ref, a = orc.qgemv(w.fmt, w.codes, w.scales, w.biases, x, M, K)
+    wd = dev(w)
+    y, _ = gpu_gemv(torch, wd, x)
+    check_bound(y, ref, a, f"stream mfma {M} n{N}")
+    y2, idx = gpu_gemv(torch, wd, x, argmax=True)
+    assert np.array_equal(y, y2), "logits differ from the plain product"
+    check_argmax(idx, y2, ref, a, orc, f"stream mfma {M} n{N}")
+    _, idx3 = gpu_greedy(torch, wd, x, logits=False)
+    assert np.array_equal(idx, idx3), "greedy indices without logits differ"
+
+
+@pytest.mark.parametrize("M,N", [(40000, 8), (33001, 2), (65536, 5)])
+def test_stream_mfma_kernel_exact(torch, orc, M, N):
+    """Exact-arithmetic inputs: bit-exact against the oracle."""
+    K = 2048
+    say(f"stream mfma kernel exact M={M} N={N}")
+    rng = np.random.default_rng([8, M, N])
+    w, x = exact_inputs(synth.U4_G64, M, K, N, rng)
+    ref, _ = orc.qgemv(w.fmt, w.codes, w.scales, w.biases, x, M, K)
+    want = ref.astype(np.float32)
+    assert np.array_equal(want.astype(np.float64), ref), "fixture is not exact in float32"
+    y, _ = gpu_gemv(torch, dev(w), x)
+    assert np.array_equal(y, want), f"not bit-exact: max diff {np.max(np.abs(y - want))}"
+
+
+def test_stream_mfma_kernel_ties(torch, orc):
+    """Per activation row, ties of its maximum across workgroups and within
+    a stage (rows duplicated at the first row, mid-stage, at the end of a
+    workgroup's run, at the last row); the lowest index wins in every row."""
+    M, K, N = 151936, 2048, 8
+    say("stream mfma kernel ties")
+    rng = synth.rng_for(611, 0)
+    w = synth.draw_weights(synth.U4_G64, M, K, rng)
+    x = synth.draw_x(N, K, rng)
+    ref, _ = orc.qgemv(w.fmt, w.codes, w.scales, w.biases, x, M, K)
+    codes, scales, biases = w.codes.copy(), w.scales.copy(), w.biases.copy()
+    per_wg = M // 256
+    # activation row 3's best row copied to the tie positions
+    best = int(np.argmax(ref[3]))
+    for dst in (per_wg * 37 - 1, per_wg * 37 + 13, M - 1, 5, best):
+        codes[dst], scales[dst], biases[dst] = codes[best], scales[best], biases[best]
+    w2 = synth.QWeights(w.fmt, M, K, codes, scales, biases)
+    ref2, a2 = orc.qgemv(w2.fmt, w2.codes, w2.scales, w2.biases, x, M, K)
+    y, idx = gpu_gemv(torch, dev(w2), x, argmax=True)
+    check_bound(y, ref2, a2, "stream mfma ties")
+    check_argmax(idx, y, ref2, a2, orc, "stream mfma ties")
+    assert idx[3] == 5
