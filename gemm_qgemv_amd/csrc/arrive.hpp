@@ -165,15 +165,17 @@ __device__ __forceinline__ bool splitk_arrive(unsigned long long *word, int nspl
 // in once; the last one reads every row back, reduces them and writes the
 // indices. `peek` is thread 0's arrival_peek of ctl->arrive; the claim and
 // the key exchanges go out together. Must be reached by all threads of the
-// workgroup.
+// workgroup. `lds_last` and `lds_best` (16 keys) are LDS scratch of the
+// caller's choosing (greedy_finish_rows below brings its own).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void greedy_finish_rows(const unsigned long long *wg_key, int nb,
-                                                   GreedyCtl *ctl, unsigned long long *keys,
-                                                   int32_t *idx, int nwg, uint32_t tag,
-                                                   unsigned long long peek)
+__device__ __forceinline__ void greedy_finish_rows_in(const unsigned long long *wg_key, int nb,
+                                                      GreedyCtl *ctl, unsigned long long *keys,
+                                                      int32_t *idx, int nwg, uint32_t tag,
+                                                      unsigned long long peek, unsigned *lds_last,
+                                                      unsigned long long *lds_best)
 {
-    __shared__ unsigned s_last;
-    __shared__ unsigned long long s_best[16];
+    unsigned &s_last = *lds_last;
+    unsigned long long *s_best = lds_best;
     if (threadIdx.x == 0) {
         uint32_t dep = 0;
         for (int b = 0; b < nb; ++b) {
@@ -212,6 +214,16 @@ __device__ __forceinline__ void greedy_finish_rows(const unsigned long long *wg_
     }
     __syncthreads();
     if (threadIdx.x < nb) idx[threadIdx.x] = static_cast<int32_t>(argmax_key_index(s_best[threadIdx.x]));
+}
+
+__device__ __forceinline__ void greedy_finish_rows(const unsigned long long *wg_key, int nb,
+                                                   GreedyCtl *ctl, unsigned long long *keys,
+                                                   int32_t *idx, int nwg, uint32_t tag,
+                                                   unsigned long long peek)
+{
+    __shared__ unsigned s_last;
+    __shared__ unsigned long long s_best[16];
+    greedy_finish_rows_in(wg_key, nb, ctl, keys, idx, nwg, tag, peek, &s_last, s_best);
 }
 
 }  // namespace qg

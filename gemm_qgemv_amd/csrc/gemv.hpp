@@ -153,6 +153,43 @@ __device__ __forceinline__ float dot_u4x8(uint32_t d, float4 xa, float4 xb, floa
     return acc;
 }
 
+// 2^-24 sum_i q_i * x_i for one dword of 8 nibbles, same activation layout
+// as dot_u4x8 (odd k pre-divided by 16). A 16-bit half that holds only a
+// nibble in bits 0..3 (or 4..7) is the fp16 subnormal q 2^-24 (or 16 q
+// 2^-24), exactly, so masking both halves of the dword at once yields two
+// weights, and the mixed-precision FMA widens the selected half inside the
+// multiply-add: one instruction per weight plus five per dword for the
+// masks and the shift, instead of a convert and an FMA per weight. Products
+// and sums are the fp32 ones of dot_u4x8 scaled by 2^-24 (exact, fp16 and
+// fp32 subnormals are kept); the caller multiplies by 2^24.
+__device__ __forceinline__ float h16_lo(uint32_t v)
+{
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v)));
+}
+__device__ __forceinline__ float h16_hi(uint32_t v)
+{
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v >> 16)));
+}
+constexpr float kMixScale = 16777216.f;   // 2^24
+
+__device__ __forceinline__ float dot_u4x8_mix(uint32_t d, float4 xa, float4 xb, float acc)
+{
+    const uint32_t e = d >> 8;
+    const uint32_t q04 = d & 0x000F000Fu;   // k = 0 and 4
+    const uint32_t q15 = d & 0x00F000F0u;   // k = 1 and 5 (times 16)
+    const uint32_t q26 = e & 0x000F000Fu;   // k = 2 and 6
+    const uint32_t q37 = e & 0x00F000F0u;   // k = 3 and 7 (times 16)
+    acc = fmaf(h16_lo(q04), xa.x, acc);
+    acc = fmaf(h16_lo(q15), xa.y, acc);
+    acc = fmaf(h16_lo(q26), xa.z, acc);
+    acc = fmaf(h16_lo(q37), xa.w, acc);
+    acc = fmaf(h16_hi(q04), xb.x, acc);
+    acc = fmaf(h16_hi(q15), xb.y, acc);
+    acc = fmaf(h16_hi(q26), xb.z, acc);
+    acc = fmaf(h16_hi(q37), xb.w, acc);
+    return acc;
+}
+
 // sum over the set bits of one byte (k = 8j .. 8j+7) of x_k.
 __device__ __forceinline__ float sum_b1x8(uint32_t byte, float4 xa, float4 xb, float acc)
 {

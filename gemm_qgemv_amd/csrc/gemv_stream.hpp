@@ -78,6 +78,77 @@ __device__ __forceinline__ void stream_barrier()
     asm volatile("s_barrier" ::: "memory");
 }
 
+// One loader wave's part of stage st (ring slot st % kStreamStages): code
+// rows RS = 32 / NC (rows past r1 - 1 repeat row r1 - 1, so every stage
+// issues the same number of loads) and one coefficient block (loader 0: the
+// scales, loader 1: the biases), 1 KiB per instruction. With SWZ, lane l of
+// the load of code row rr fetches the row's 16-byte chunk l ^ (rr % 16), so
+// that chunk c of row rr sits at position c ^ (rr % 16) of its LDS row.
+template <int NC, bool SWZ>
+__device__ __forceinline__ void stream_issue(const uint8_t *codes, const uint16_t *scales,
+                                             const uint16_t *biases, unsigned char *lds, int L,
+                                             int lane, int st, int64_t r0, int64_t r1)
+{
+    constexpr int RS = 32 / NC;
+    constexpr int GPR = 32 * NC;
+    constexpr int CODE_LOADS = RS * NC / kStreamLoaders;
+    constexpr int64_t row_bytes = 1024 * NC;
+    constexpr int coef_row_bytes = 2 * GPR;
+    unsigned char *slot = lds + (st % kStreamStages) * kStreamStageBytes;
+    const int64_t rb = r0 + static_cast<int64_t>(st) * RS;
+#pragma unroll
+    for (int i = 0; i < CODE_LOADS; ++i) {
+        const int li = L * CODE_LOADS + i;
+        const int rr = li / NC, cc = li % NC;
+        const int64_t row = min(rb + rr, r1 - 1);
+        const int chunk = SWZ ? (lane ^ (rr & 15)) : lane;
+        const uint8_t *g = codes + row * row_bytes + cc * 1024 + 16 * chunk;
+        __builtin_amdgcn_global_load_lds((stream_gptr_t)g, (stream_lptr_t)(slot + (rr * NC + cc) * 1024), 16, 0, 2);
+    }
+    // the stage's coefficients: 2 KiB of consecutive rows, 16 bytes per lane
+    const uint16_t *coef = L == 0 ? scales : biases;
+    unsigned char *cslot = slot + kStreamCodeBytes + L * kStreamCoefBytes;
+#pragma unroll
+    for (int i = 0; i < kStreamCoefBytes / 1024; ++i) {
+        const int off = 1024 * i + 16 * lane;   // byte within the stage's block
+        const int rr = off / coef_row_bytes;
+        const int64_t row = min(rb + rr, r1 - 1);
+        const int64_t src = row * coef_row_bytes + off % coef_row_bytes;
+        __builtin_amdgcn_global_load_lds((stream_gptr_t)(reinterpret_cast<const uint8_t *>(coef) + src),
+                                         (stream_lptr_t)(cslot + 1024 * i), 16, 0, 2);
+    }
+}
+
+// A loader wave's whole life: fill the ring, then for every stage s wait
+// (vector-memory count) until only the later stages' loads are outstanding,
+// take the barrier that opens stage s, refill the slot that stage s - 1
+// freed, and take the BARRIERS - 1 further barriers the compute waves take
+// per stage.
+template <int NC, bool SWZ, int BARRIERS>
+__device__ __forceinline__ void stream_loader(const uint8_t *codes, const uint16_t *scales,
+                                              const uint16_t *biases, unsigned char *lds, int L,
+                                              int lane, int64_t r0, int64_t r1, int nstages)
+{
+    constexpr int RS = 32 / NC;
+    constexpr int CODE_LOADS = RS * NC / kStreamLoaders;
+    constexpr int LPS = CODE_LOADS + kStreamCoefBytes / 1024;   // loads per loader and stage
+    constexpr int D = kStreamStages;
+    static_assert((D - 2) * LPS < 64, "outstanding loads fit the vector-memory count");
+    for (int st = 0; st < D - 1 && st < nstages; ++st)
+        stream_issue<NC, SWZ>(codes, scales, biases, lds, L, lane, st, r0, r1);
+    for (int s = 0; s < nstages; ++s) {
+        // stage s has landed once only the later stages' loads are outstanding
+        const int later = min(D - 2, nstages - 1 - s);
+        if (later >= 2) wait_vmcnt<2 * LPS>();
+        else if (later == 1) wait_vmcnt<LPS>();
+        else wait_vmcnt<0>();
+        stream_barrier();
+        if (s + D - 1 < nstages) stream_issue<NC, SWZ>(codes, scales, biases, lds, L, lane, s + D - 1, r0, r1);
+#pragma unroll
+        for (int b = 1; b < BARRIERS; ++b) stream_barrier();
+    }
+}
+
 // NC: 1 KiB chunks of codes per row (K = 2048 NC).
 template <int NC>
 __global__ __launch_bounds__(kStreamThreads) void gemv_stream_u4_kernel(GemvStreamParams p)
@@ -85,12 +156,9 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_u4_kernel(GemvStre
     constexpr int RS = 32 / NC;                    // rows per stage
     constexpr int RPW = RS / kStreamComputes;      // rows per compute wave and stage
     constexpr int GPR = 32 * NC;                   // groups of 64 inputs per row
-    constexpr int CODE_LOADS = RS * NC / kStreamLoaders;   // per loader and stage
-    constexpr int LPS = CODE_LOADS + kStreamCoefBytes / 1024;   // loads per loader and stage
     constexpr int D = kStreamStages;
     static_assert(RPW >= 1 && RS * NC == 32, "32 KiB of codes per stage");
     static_assert(RS * GPR * 2 == kStreamCoefBytes, "one coefficient block per stage");
-    static_assert((D - 2) * LPS < 64, "outstanding loads fit the vector-memory count");
     extern __shared__ __attribute__((aligned(16))) unsigned char stream_lds[];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -98,8 +166,6 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_u4_kernel(GemvStre
     const int64_t r0 = static_cast<int64_t>(blockIdx.x) * p.M / gridDim.x;
     const int64_t r1 = static_cast<int64_t>(blockIdx.x + 1) * p.M / gridDim.x;
     const int nstages = static_cast<int>((r1 - r0 + RS - 1) / RS);
-    constexpr int64_t row_bytes = 1024 * NC;
-    constexpr int64_t coef_row_bytes = 2 * GPR;
 
     // greedy head: the completion word as it stands at the start (thread 0,
     // before any of its loader loads, so that it is the oldest outstanding
@@ -113,43 +179,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_u4_kernel(GemvStre
     bool writer = false;
 
     if (wave < kStreamLoaders) {
-        // ---- loader wave ----------------------------------------------
-        const int L = wave;
-        auto issue = [&](int st) {
-            unsigned char *slot = stream_lds + (st % D) * kStreamStageBytes;
-            const int64_t rb = r0 + static_cast<int64_t>(st) * RS;
-#pragma unroll
-            for (int i = 0; i < CODE_LOADS; ++i) {
-                const int li = L * CODE_LOADS + i;
-                const int rr = li / NC, cc = li % NC;
-                const int64_t row = min(rb + rr, r1 - 1);
-                const uint8_t *g = p.codes + row * row_bytes + cc * 1024 + 16 * lane;
-                __builtin_amdgcn_global_load_lds((stream_gptr_t)g,
-                                                 (stream_lptr_t)(slot + (rr * NC + cc) * 1024), 16, 0, 2);
-            }
-            // the stage's coefficients: 2 KiB of consecutive rows, 16 bytes per lane
-            const uint16_t *coef = L == 0 ? p.scales : p.biases;
-            unsigned char *cslot = slot + kStreamCodeBytes + L * kStreamCoefBytes;
-#pragma unroll
-            for (int i = 0; i < kStreamCoefBytes / 1024; ++i) {
-                const int off = 1024 * i + 16 * lane;      // byte within the stage's block
-                const int rr = off / static_cast<int>(coef_row_bytes);
-                const int64_t row = min(rb + rr, r1 - 1);
-                const int64_t src = row * coef_row_bytes + off % static_cast<int>(coef_row_bytes);
-                __builtin_amdgcn_global_load_lds((stream_gptr_t)(reinterpret_cast<const uint8_t *>(coef) + src),
-                                                 (stream_lptr_t)(cslot + 1024 * i), 16, 0, 2);
-            }
-        };
-        for (int st = 0; st < D - 1 && st < nstages; ++st) issue(st);
-        for (int s = 0; s < nstages; ++s) {
-            // stage s has landed once only the later stages' loads are outstanding
-            const int later = min(D - 2, nstages - 1 - s);
-            if (later >= 2) wait_vmcnt<2 * LPS>();
-            else if (later == 1) wait_vmcnt<LPS>();
-            else wait_vmcnt<0>();
-            stream_barrier();
-            if (s + D - 1 < nstages) issue(s + D - 1);
-        }
+        stream_loader<NC, false, 1>(p.codes, p.scales, p.biases, stream_lds, wave, lane, r0, r1, nstages);
     } else {
         // ---- compute wave ---------------------------------------------
         const int c = wave - kStreamLoaders;
@@ -200,11 +230,12 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_u4_kernel(GemvStre
 #pragma unroll
                 for (int j = 0; j < NC; ++j) {
                     float d = 0.f;
-                    d = dot_u4x8(cw[r][j].x, xv[j][0], xv[j][1], d);
-                    d = dot_u4x8(cw[r][j].y, xv[j][2], xv[j][3], d);
-                    d = dot_u4x8(cw[r][j].z, xv[j][4], xv[j][5], d);
-                    d = dot_u4x8(cw[r][j].w, xv[j][6], xv[j][7], d);
-                    a = fmaf(bf16_bits_to_f32(sw[r][j]), d, fmaf(bf16_bits_to_f32(bw[r][j]), xs[j], a));
+                    d = dot_u4x8_mix(cw[r][j].x, xv[j][0], xv[j][1], d);
+                    d = dot_u4x8_mix(cw[r][j].y, xv[j][2], xv[j][3], d);
+                    d = dot_u4x8_mix(cw[r][j].z, xv[j][4], xv[j][5], d);
+                    d = dot_u4x8_mix(cw[r][j].w, xv[j][6], xv[j][7], d);
+                    a = fmaf(bf16_bits_to_f32(sw[r][j]), d * kMixScale,
+                             fmaf(bf16_bits_to_f32(bw[r][j]), xs[j], a));
                 }
                 acc[r] = a;
             }
