@@ -6,29 +6,34 @@
 // that owns it and whose low half counts the workgroups of that dispatch that
 // have arrived. The tag is derived from the dispatch's AQL packet index and
 // its queue, so two dispatches that use the same workspace one after the
-// other carry different tags. Thread 0 of every workgroup reads the word when
-// the workgroup starts (arrival_peek; the value is only used at the end, so
-// nothing waits for it). When the workgroup arrives and its early read showed
-// another tag (leftovers of an earlier call, a call that never finished, or
-// uninitialised memory), it first claims the word with one compare-and-swap
-// from that value to (tag, 0); the swap fails harmlessly when another
-// workgroup of the same dispatch has already claimed it (the word can then
-// only hold this dispatch's tag, since no other dispatch touches it
-// meanwhile). The increment waits for that swap, so every increment of a
-// dispatch lands on a word that already carries its tag, and the workgroup
-// that sees the count reach total - 1 is the last one. Nothing has to be
-// zero on entry, nothing is cleared on exit, and a call that was cut short
-// or raced with another on the same workspace cannot disturb the calls
-// after it.
+// other carry different tags. A workgroup that arrives increments the word
+// and looks at the value it returns. If that value carries this dispatch's
+// tag, the low half is the number of workgroups that arrived before it, and
+// the one that sees total - 1 is the last. Otherwise the word still held
+// something else (leftovers of an earlier call, a call that never finished,
+// uninitialised memory) and the increment did not count: the workgroup then
+// claims the word with a compare-and-swap of the value it expects there for
+// (tag, 1), which counts it in as the first; if the swap fails because the
+// word changed, it retries against the new value, or, once the word carries
+// the tag (another workgroup claimed it), counts itself in with a second
+// increment. A claim only ever replaces a word without the tag, so counted
+// increments are never lost, and every workgroup is counted exactly once.
+// The dispatch's first workgroup claims the word as it starts
+// (arrival_preclaim), long before any workgroup arrives, so normally no
+// arrival takes the slow path, no swap reaches the word at the end, and the
+// last workgroup's path to the end of the kernel is its data atomics, one
+// increment and the final reads. Nothing has to be zero on
+// entry, nothing is cleared on exit, and a call that was cut short or raced
+// with another on the same workspace cannot disturb the calls after it.
 //
 // Ordering. Data moves between workgroups only through device-scope atomics
 // (the parked keys and partial sums, the counters), which are performed at
 // the device's coherence point rather than in an XCD's own L2. A returning
 // atomic has been performed when its value comes back. Each workgroup issues
 // its counter increment with an address that depends, through one vector
-// AND with zero, on the values returned by its claim and by every atomic
-// that carried its data; the increment therefore cannot be performed before
-// them. The last workgroup reads the parked data with device-scope atomic
+// AND with zero, on the values returned by every atomic that carried its
+// data (or after a barrier that all those values have passed); the
+// increment therefore cannot be performed before them. The last workgroup reads the parked data with device-scope atomic
 // loads issued after its increment has returned, so it sees every value
 // that was performed before the other workgroups counted themselves in. No
 // cache writeback or invalidate is needed, because no plain store or load
@@ -68,40 +73,52 @@ __device__ __forceinline__ unsigned long long *tile_counters(GreedyCtl *ctl)
     return reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(ctl) + kCtlTileOffset);
 }
 
-// The word as it stands when the workgroup starts (thread 0).
-__device__ __forceinline__ unsigned long long arrival_peek(const unsigned long long *word)
+// Claim `word` for this dispatch as the kernel starts: one thread of one
+// workgroup per word (the dispatch's first workgroup, which starts before
+// the others arrive), so that the arrivals find the word claimed and take
+// the fast path. Swaps only a word without the tag; a failed swap means the
+// word changed, and the loop retries against the new value (it ends, since
+// every change is one of the dispatch's few increments or claims).
+__device__ __forceinline__ void arrival_preclaim(unsigned long long *word, uint32_t tag)
 {
-    return __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Claim `word` for this dispatch (thread 0, at arrival): swap the early read
-// for (tag, 0), or, when the early read already showed this tag, for itself
-// (then the swap changes nothing whether or not it succeeds). No branch, so
-// the swap goes out beside the workgroup's other atomics instead of after
-// them. Returns a token of the swap's result for arrival_last to depend on.
-__device__ __forceinline__ uint32_t arrival_claim(unsigned long long *word, uint32_t tag,
-                                                  unsigned long long peek)
-{
-    unsigned long long expected = peek;
-    const unsigned long long mine = static_cast<uint32_t>(peek >> 32) == tag
-                                        ? peek
-                                        : static_cast<unsigned long long>(tag) << 32;
-    __hip_atomic_compare_exchange_strong(word, &expected, mine, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    return static_cast<uint32_t>(expected) | static_cast<uint32_t>(expected >> 32);
+    unsigned long long cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while (static_cast<uint32_t>(cur >> 32) != tag) {
+        if (__hip_atomic_compare_exchange_strong(word, &cur, static_cast<unsigned long long>(tag) << 32,
+                                                 __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            break;
+    }
 }
 
 // Count the calling workgroup in (one thread); true for the last of `total`.
-// `dep` folds together the values returned by the claim and by the atomics
-// that carried the workgroup's data.
+// `dep` folds together the values returned by the atomics that carried the
+// workgroup's data: the increment's address depends on them (through one
+// vector AND with zero), so it cannot be performed before them.
 __device__ __forceinline__ bool arrival_last(unsigned long long *word, uint32_t tag, uint32_t dep,
                                              unsigned total)
 {
     uint32_t zero;
     asm volatile("v_and_b32 %0, 0, %1" : "=v"(zero) : "v"(dep));
-    const unsigned long long old =
+    unsigned long long old =
         __hip_atomic_fetch_add(word + zero, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return static_cast<uint32_t>(old >> 32) == tag && static_cast<uint32_t>(old) == total - 1u;
+    if (static_cast<uint32_t>(old >> 32) != tag) {
+        // the word was not claimed for this dispatch yet: claim it, counted
+        // as the first, or count again once another workgroup has claimed it
+        unsigned long long cur = old + 1ull;
+        for (;;) {
+            if (static_cast<uint32_t>(cur >> 32) == tag) {
+                old = __hip_atomic_fetch_add(word, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            if (__hip_atomic_compare_exchange_strong(word, &cur, (static_cast<unsigned long long>(tag) << 32) | 1ull,
+                                                     __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT)) {
+                old = static_cast<unsigned long long>(tag) << 32;
+                break;
+            }
+            // cur now holds the word's current value
+        }
+    }
+    return static_cast<uint32_t>(old) == total - 1u;
 }
 
 // ---------------------------------------------------------------------------
@@ -143,16 +160,12 @@ __device__ __forceinline__ float splitk_sum(const float *part, int64_t stride, i
     return acc;
 }
 
-// All threads. `peek` is thread 0's arrival_peek of `word`; its claim goes
-// out before the barrier, beside the other threads' exchanges.
-__device__ __forceinline__ bool splitk_arrive(unsigned long long *word, int nsplit, uint32_t tag,
-                                              unsigned long long peek)
+// All threads, after their splitk_put calls.
+__device__ __forceinline__ bool splitk_arrive(unsigned long long *word, int nsplit, uint32_t tag)
 {
     __shared__ unsigned s_last;
-    uint32_t dep = 0;
-    if (threadIdx.x == 0) dep = arrival_claim(word, tag, peek);
     __syncthreads();   // every thread's exchanges have returned
-    if (threadIdx.x == 0) s_last = arrival_last(word, tag, dep, static_cast<unsigned>(nsplit));
+    if (threadIdx.x == 0) s_last = arrival_last(word, tag, 0u, static_cast<unsigned>(nsplit));
     __syncthreads();
     return s_last != 0;
 }
@@ -163,16 +176,13 @@ __device__ __forceinline__ bool splitk_arrive(unsigned long long *word, int nspl
 // workgroup parks its nb keys in its own row of `keys` ([nwg][nb], any
 // initial contents) with returning device-scope exchanges and counts itself
 // in once; the last one reads every row back, reduces them and writes the
-// indices. `peek` is thread 0's arrival_peek of ctl->arrive; the claim and
-// the key exchanges go out together. Must be reached by all threads of the
-// workgroup. `lds_last` and `lds_best` (16 keys) are LDS scratch of the
+// indices. Must be reached by all threads of the workgroup. `lds_last` and `lds_best` (16 keys) are LDS scratch of the
 // caller's choosing (greedy_finish_rows below brings its own).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void greedy_finish_rows_in(const unsigned long long *wg_key, int nb,
                                                       GreedyCtl *ctl, unsigned long long *keys,
                                                       int32_t *idx, int nwg, uint32_t tag,
-                                                      unsigned long long peek, unsigned *lds_last,
-                                                      unsigned long long *lds_best)
+                                                      unsigned *lds_last, unsigned long long *lds_best)
 {
     unsigned &s_last = *lds_last;
     unsigned long long *s_best = lds_best;
@@ -184,7 +194,6 @@ __device__ __forceinline__ void greedy_finish_rows_in(const unsigned long long *
                 __HIP_MEMORY_SCOPE_AGENT);
             dep |= static_cast<uint32_t>(old) | static_cast<uint32_t>(old >> 32);
         }
-        dep |= arrival_claim(&ctl->arrive, tag, peek);
         s_last = arrival_last(&ctl->arrive, tag, dep, static_cast<unsigned>(nwg));
     }
     if (threadIdx.x < 16) s_best[threadIdx.x] = 0ull;
@@ -218,12 +227,11 @@ __device__ __forceinline__ void greedy_finish_rows_in(const unsigned long long *
 
 __device__ __forceinline__ void greedy_finish_rows(const unsigned long long *wg_key, int nb,
                                                    GreedyCtl *ctl, unsigned long long *keys,
-                                                   int32_t *idx, int nwg, uint32_t tag,
-                                                   unsigned long long peek)
+                                                   int32_t *idx, int nwg, uint32_t tag)
 {
     __shared__ unsigned s_last;
     __shared__ unsigned long long s_best[16];
-    greedy_finish_rows_in(wg_key, nb, ctl, keys, idx, nwg, tag, peek, &s_last, s_best);
+    greedy_finish_rows_in(wg_key, nb, ctl, keys, idx, nwg, tag, &s_last, s_best);
 }
 
 }  // namespace qg

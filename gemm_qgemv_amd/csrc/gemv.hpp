@@ -231,8 +231,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
     // greedy head: read the completion word as it stands at the start
     const bool greedy = p.ctl != nullptr && p.nsplit == 1;
     const uint32_t tag = greedy ? dispatch_tag() : 0u;
-    unsigned long long peek = 0;
-    if (greedy && threadIdx.x == 0) peek = arrival_peek(&p.ctl->arrive);
+    if (greedy && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) arrival_preclaim(&p.ctl->arrive, tag);
 
     stage_x<FMT, B>(p, k0, kc, xl, xs);
     __syncthreads();
@@ -470,7 +469,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
             atomicMax(&wg_key[own_b], static_cast<unsigned long long>(
                                           argmax_key(best_v, static_cast<uint32_t>(best_m))));
         __syncthreads();
-        greedy_finish_rows(wg_key, p.nb, p.ctl, p.keys, p.idx, p.nkeys, tag, peek);
+        greedy_finish_rows(wg_key, p.nb, p.ctl, p.keys, p.idx, p.nkeys, tag);
     }
 }
 
@@ -480,8 +479,7 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvParams p)
 {
     __shared__ unsigned long long wg_key[16];
     const uint32_t tag = p.ctl != nullptr ? dispatch_tag() : 0u;
-    unsigned long long peek = 0;
-    if (p.ctl != nullptr && threadIdx.x == 0) peek = arrival_peek(&p.ctl->arrive);
+    if (p.ctl != nullptr && blockIdx.x == 0 && threadIdx.x == 0) arrival_preclaim(&p.ctl->arrive, tag);
     if (threadIdx.x < 16) wg_key[threadIdx.x] = 0ull;
     __syncthreads();
     const int64_t m_begin = static_cast<int64_t>(blockIdx.x) * p.rows_per_wg;
@@ -501,7 +499,7 @@ __global__ __launch_bounds__(256) void gemv_combine_kernel(GemvParams p)
     }
     if (p.ctl != nullptr) {
         __syncthreads();
-        greedy_finish_rows(wg_key, p.nb, p.ctl, p.keys, p.idx, p.nkeys, tag, peek);
+        greedy_finish_rows(wg_key, p.nb, p.ctl, p.keys, p.idx, p.nkeys, tag);
     }
 }
 

@@ -159,8 +159,7 @@ __global__ __launch_bounds__(64 * WGW) void gemv1_kernel(Gemv1Params p)
     // first block's and the activations' loads, so that the first wait does
     // not include it)
     const uint32_t tag = p.ctl != nullptr ? dispatch_tag() : 0u;
-    unsigned long long peek = 0;
-    if (p.ctl != nullptr && threadIdx.x == 0) peek = arrival_peek(&p.ctl->arrive);
+    if (p.ctl != nullptr && blockIdx.x == 0 && threadIdx.x == 0) arrival_preclaim(&p.ctl->arrive, tag);
 
     float best_v = 0.f;
     int64_t best_m = -1;
@@ -235,7 +234,7 @@ __global__ __launch_bounds__(64 * WGW) void gemv1_kernel(Gemv1Params p)
         }
         if (lane == 0) atomicMax(&s_key, static_cast<unsigned long long>(key));
         __syncthreads();
-        greedy_finish_rows(&s_key, 1, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x), tag, peek);
+        greedy_finish_rows(&s_key, 1, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x), tag);
     }
 }
 

@@ -108,15 +108,13 @@ __global__ __launch_bounds__(256) void gemv_b1_lut_kernel(B1LutParams p)
 #pragma unroll
     for (int j = 0; j < GPW; ++j) sc[j] = (mv && wave * GPW + j < ng) ? sp[j] : 0u;
 
-    // read the completion words this dispatch counts on as they stand at
-    // the start: the row tile's (in-kernel split-K combine) and the greedy
-    // head's
+    // tag of this dispatch for the completion words it counts on: the row
+    // tile's (in-kernel split-K combine) and the greedy head's
     const bool fused_split = p.nsplit > 1 && p.fused;
     const uint32_t tag = (fused_split || p.idx != nullptr) ? dispatch_tag() : 0u;
-    unsigned long long peek_tile = 0, peek_greedy = 0;
-    if (tid == 0) {
-        if (fused_split) peek_tile = arrival_peek(&tile_counters(p.ctl)[blockIdx.x]);
-        if (p.idx != nullptr) peek_greedy = arrival_peek(&p.ctl->arrive);
+    if (tid == 0 && split == 0) {
+        if (fused_split) arrival_preclaim(&tile_counters(p.ctl)[blockIdx.x], tag);
+        if (p.idx != nullptr && blockIdx.x == 0) arrival_preclaim(&p.ctl->arrive, tag);
     }
 
     // 2. tables of this chunk: thread q builds position q (16 signed sums)
@@ -225,7 +223,7 @@ __global__ __launch_bounds__(256) void gemv_b1_lut_kernel(B1LutParams p)
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
                     if (b < nb) splitk_put(part + b * p.M, acc[b]);
-            if (!splitk_arrive(&tile_counters(p.ctl)[blockIdx.x], p.nsplit, tag, peek_tile)) return;
+            if (!splitk_arrive(&tile_counters(p.ctl)[blockIdx.x], p.nsplit, tag)) return;
 #pragma unroll
             for (int b = 0; b < NB; ++b)
                 acc[b] = own && b < nb ? splitk_sum(p.part + b * p.M + m, nb * p.M, p.nsplit) : 0.f;
@@ -256,8 +254,7 @@ __global__ __launch_bounds__(256) void gemv_b1_lut_kernel(B1LutParams p)
             if (lane == 0) atomicMax(&s_key[b], static_cast<unsigned long long>(key));
         }
         __syncthreads();
-        greedy_finish_rows(s_key, nb, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x), tag,
-                           peek_greedy);
+        greedy_finish_rows(s_key, nb, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x), tag);
     }
 }
 

@@ -223,8 +223,7 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_u4_kernel(GemvMfmaPara
 
     // greedy head: read the completion word as it stands at the start
     const uint32_t tag = p.ctl != nullptr ? dispatch_tag() : 0u;
-    unsigned long long peek = 0;
-    if (p.ctl != nullptr && tid == 0) peek = arrival_peek(&p.ctl->arrive);
+    if (p.ctl != nullptr && blockIdx.x == 0 && tid == 0) arrival_preclaim(&p.ctl->arrive, tag);
 
     // split and store the pieces; the 8 items of one group of one row sit
     // in 8 consecutive lanes, which add their sums into the group sum X[n][g]
@@ -389,7 +388,7 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma_u4_kernel(GemvMfmaPara
             if (r == 0 && q < 2 && n < p.nb) atomicMax(&wg_key[n], static_cast<unsigned long long>(key));
         }
         __syncthreads();
-        greedy_finish_rows(wg_key, p.nb, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x), tag, peek);
+        greedy_finish_rows(wg_key, p.nb, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x), tag);
     }
 }
 

@@ -155,8 +155,7 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
 
     // greedy head: read the completion word as it stands at the start
     const uint32_t tag = p.ctl != nullptr ? dispatch_tag() : 0u;
-    unsigned long long peek = 0;
-    if (p.ctl != nullptr && tid == 0) peek = arrival_peek(&p.ctl->arrive);
+    if (p.ctl != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) arrival_preclaim(&p.ctl->arrive, tag);
 
     // 1b. exact three-way split into operand pieces; for the 4-bit bias
     //     term the group sums X[n][g] of the activations, gathered to the
@@ -354,7 +353,7 @@ __global__ __launch_bounds__(kMfmaThreads) void gemv_mfma16_kernel(GemvMfmaParam
         }
         if (srr == 0 && sn < p.nb) atomicMax(&wg_key[sn], static_cast<unsigned long long>(key));
         __syncthreads();
-        greedy_finish_rows(wg_key, p.nb, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x), tag, peek);
+        greedy_finish_rows(wg_key, p.nb, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x), tag);
     }
 }
 

@@ -167,12 +167,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_u4_kernel(GemvStre
     const int64_t r1 = static_cast<int64_t>(blockIdx.x + 1) * p.M / gridDim.x;
     const int nstages = static_cast<int>((r1 - r0 + RS - 1) / RS);
 
-    // greedy head: the completion word as it stands at the start (thread 0,
-    // before any of its loader loads, so that it is the oldest outstanding
-    // load of its wave and leaves the stage counts exact)
     const uint32_t tag = p.ctl != nullptr ? dispatch_tag() : 0u;
-    unsigned long long peek = 0;
-    if (p.ctl != nullptr && tid == 0) peek = arrival_peek(&p.ctl->arrive);
 
     float best_v = 0.f;
     int64_t best_m = -1;
@@ -204,6 +199,10 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_u4_kernel(GemvStre
             }
             xs[j] = s;
         }
+        // the dispatch's first workgroup claims the completion word (this
+        // wave only reads LDS from here on, so the wait costs the stream
+        // nothing beyond this wave's start)
+        if (p.ctl != nullptr && blockIdx.x == 0 && lane == 0 && c == 0) arrival_preclaim(&p.ctl->arrive, tag);
 
         for (int s = 0; s < nstages; ++s) {
             // the previous stage's LDS reads are complete before its slot
@@ -264,7 +263,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_u4_kernel(GemvStre
         }
         if (lane == 0) atomicMax(&s_key, static_cast<unsigned long long>(key));
         __syncthreads();
-        greedy_finish_rows(&s_key, 1, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x), tag, peek);
+        greedy_finish_rows(&s_key, 1, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x), tag);
     }
 }
 

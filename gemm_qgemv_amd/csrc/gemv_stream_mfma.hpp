@@ -86,12 +86,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_mfma_u4_kernel(Gem
     const int64_t r1 = static_cast<int64_t>(blockIdx.x + 1) * p.M / gridDim.x;
     const int nstages = static_cast<int>((r1 - r0 + RS - 1) / RS);
 
-    // greedy head: the completion word as it stands at the start (thread 0,
-    // before any of its loader loads, so that it is the oldest outstanding
-    // load of its wave and leaves the stage counts exact)
     const uint32_t tag = p.ctl != nullptr ? dispatch_tag() : 0u;
-    unsigned long long peek = 0;
-    if (p.ctl != nullptr && tid == 0) peek = arrival_peek(&p.ctl->arrive);
 
     if (wave < kStreamLoaders) {
         stream_loader<1, true, 1>(p.codes, p.scales, p.biases, stream_lds, wave, lane, r0, r1, nstages);
@@ -131,6 +126,8 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_mfma_u4_kernel(Gem
             sum += __shfl_xor(sum, 32);
             xs[u] = sum;
         }
+        // the dispatch's first workgroup claims the completion word
+        if (p.ctl != nullptr && blockIdx.x == 0 && lane == 0 && c == 0) arrival_preclaim(&p.ctl->arrive, tag);
         uint32_t bh[4], bm[4], bl[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) split3h(xs[u], bh[u], bm[u], bl[u]);
@@ -232,8 +229,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_mfma_u4_kernel(Gem
 
     if (p.ctl != nullptr) {
         __syncthreads();
-        greedy_finish_rows_in(s_wkey, p.nb, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x), tag, peek,
-                              s_last, s_best);
+        greedy_finish_rows_in(s_wkey, p.nb, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x), tag, s_last, s_best);
     }
 }
 
