@@ -478,7 +478,8 @@ def trace_summary(csv_path, workload, src_hash, command):
             rec["tflops_at_median"] = round(c.flops / (dom["median_us"] * 1e-6) / 1e12, 2)
             rec["frac_of_bf16_peak_at_median"] = round(rec["tflops_at_median"] / BF16_MATRIX_PEAK_TFLOPS, 4)
         else:
-            b = c.weight_bytes
+            # the gather: ids, the packed rows of those ids and the float32 rows
+            b = c.rows * (4 + c.weight_bytes // c.M + 4 * c.K) if c.op == "embed" else c.weight_bytes
             rec["algorithmic_bytes"] = b
             rec["GBs_at_average"] = round(b / (dom["avg_us"] * 1e-6) / 1e9, 1)
             rec["GBs_at_median"] = round(b / (dom["median_us"] * 1e-6) / 1e9, 1)
