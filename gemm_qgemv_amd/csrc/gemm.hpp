@@ -123,6 +123,16 @@ constexpr int kGemmThreads = 256;
 // 17408 x 5120, N = 512).
 template <int FMT> struct GemmDepth { static constexpr int value = 2; };
 template <> struct GemmDepth<FMT_B1_G128> { static constexpr int value = 4; };
+// Workgroups per compute unit the register budget is set for: three for the
+// 8-bit per-row 128 x 64 tile (no group accumulators: 132 VGPRs, so a third
+// wave per SIMD hides the activation loads and splits; 3584 x 1024, N =
+// 10240: 245 -> 233 us, 1024 x 3584, N = 2048: 68 -> 60 us against the
+// 128 x 128 and 64 x 64 tiles), two for every other tile.
+template <int FMT, int BM, int BN>
+constexpr int gemm_occupancy()
+{
+    return FMT == FMT_I8_ROW && BM == 128 && BN == 64 ? 3 : 2;
+}
 constexpr int kGemmInterleave = 5;   // VALU instructions issued after each MFMA
 
 // Largest K of the matrix-core prefill: the buffer loads below address a
@@ -165,7 +175,7 @@ __device__ __forceinline__ int swz_chunk(int r, int c)
 // 32) put 4 or 2 along m, so that no MFMA works on more padding than the
 // last 16-token block holds.
 template <int FMT, int BM, int BN, int WN = 4>
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(GemmParams p)
+__global__ __launch_bounds__(kGemmThreads, (gemm_occupancy<FMT, BM, BN>())) void gemm_kernel(GemmParams p)
 {
     static_assert(WN == 1 || WN == 2 || WN == 4, "4 waves in a WM x WN grid");
     constexpr int WM = 4 / WN;

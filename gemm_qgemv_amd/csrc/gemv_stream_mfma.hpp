@@ -184,25 +184,36 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_mfma_u4_kernel(Gem
                 const uint2 sv = *reinterpret_cast<const uint2 *>(slot + kStreamCodeBytes + row * 2 * G + 8 * c);
                 const uint2 bv = *reinterpret_cast<const uint2 *>(slot + kStreamCodeBytes + kStreamCoefBytes +
                                                                   row * 2 * G + 8 * c);
-                floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+                // the bias term (operand B: this row's four biases at k
+                // positions 0..3 of quarter 0) on the accumulator, then the
+                // four groups as four independent MFMA chains issued in turn,
+                // so that no MFMA waits for the one before it
+                const uint4 bb = q == 0 ? make_uint4(bv.x, bv.y, 0u, 0u) : make_uint4(0u, 0u, 0u, 0u);
+                const floatx4_t zero = {0.f, 0.f, 0.f, 0.f};
+                floatx4_t acc = mfma(ab_hm, __builtin_bit_cast(bf16x8_t, bb), zero);
+                acc = mfma(ab_lo, __builtin_bit_cast(bf16x8_t, bb), acc);
+                bf16x8_t w[4][2];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const bf16x8_t w0 = nibbles_to_bf16(cw[u].x), w1 = nibbles_to_bf16(cw[u].y);
-                    floatx4_t t = {0.f, 0.f, 0.f, 0.f};
-                    t = mfma(a_hm[u][0], w0, t);
-                    t = mfma(a_lo[u][0], w0, t);
-                    t = mfma(a_hm[u][1], w1, t);
-                    t = mfma(a_lo[u][1], w1, t);
+                    w[u][0] = nibbles_to_bf16(cw[u].x);
+                    w[u][1] = nibbles_to_bf16(cw[u].y);
+                }
+                floatx4_t t[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) t[u] = mfma(a_hm[u][0], w[u][0], zero);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) t[u] = mfma(a_lo[u][0], w[u][0], t[u]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) t[u] = mfma(a_hm[u][1], w[u][1], t[u]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) t[u] = mfma(a_lo[u][1], w[u][1], t[u]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
                     const uint32_t sw = (u < 2) ? sv.x : sv.y;
                     const float sc = (u & 1) ? __uint_as_float(sw & 0xFFFF0000u) : __uint_as_float(sw << 16);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, t[i], acc[i]);
+                    for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, t[u][i], acc[i]);
                 }
-                // bias term: operand B holds this row's four biases at k
-                // positions 0..3 of quarter 0
-                const uint4 bb = q == 0 ? make_uint4(bv.x, bv.y, 0u, 0u) : make_uint4(0u, 0u, 0u, 0u);
-                acc = mfma(ab_hm, __builtin_bit_cast(bf16x8_t, bb), acc);
-                acc = mfma(ab_lo, __builtin_bit_cast(bf16x8_t, bb), acc);
                 // lane (r, q) holds D rows 4q .. 4q + 3 of weight row r: add
                 // rows 8..15 (quarters 2, 3) to rows 0..7 (quarters 0, 1)
                 float v[4];
