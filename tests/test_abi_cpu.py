@@ -80,7 +80,9 @@ def test_prefill_split_tail_planning():
                   q.QG_I8_G64: 128 * 64 * 4}
     for fmt, M, K, N in [(q.QG_I8_ROW, 2000, 272, 3100), (q.QG_U4_G64, 2100, 576, 2000),
                          (q.QG_B1_G128, 1100, 1152, 3900), (q.QG_I8_G64, 2100, 576, 2000),
-                         (q.QG_B1_G128, 17408, 5120, 512), (q.QG_I8_ROW, 3584, 1024, 2048)]:
+                         (q.QG_B1_G128, 17408, 5120, 512), (q.QG_I8_ROW, 3584, 1024, 2048),
+                         (q.QG_U4_G64, 2101, 576, 2000), (q.QG_I8_G64, 2099, 576, 2000),
+                         (q.QG_I8_ROW, 2001, 272, 3100)]:
         ws = q.qg_workspace_bytes(q.QG_OP_GEMM, fmt, M, K, N)
         # control words plus at least two pieces of one tile
         assert ws >= q.QG_WS_CONTROL_BYTES + 2 * tile_bytes[fmt], (fmt, M, K, N, ws)
