@@ -160,12 +160,16 @@ __device__ __forceinline__ uint32_t in_range_or_out(uint32_t off, int64_t i, int
 }
 
 // Physical 16-byte chunk of logical chunk c (0..3) in LDS row r (rows of
-// 64 bytes). Under this XOR swizzle any 16 consecutive rows read at one
-// logical chunk hit 16 distinct 16-byte bank groups of a 256-byte bank
-// cycle, and any 8 consecutive rows 8 distinct groups of a 128-byte cycle.
+// 64 bytes). Under this XOR swizzle both access patterns are free of bank
+// conflicts, whether the LDS serves a 16-byte-per-lane access 16 lanes per
+// 256-byte cycle or 8 lanes per 128-byte cycle: the fragment reads (16
+// consecutive rows from a multiple of 16, one logical chunk) and the
+// staging writes (8 consecutive rows from a multiple of 8, logical chunks
+// c and c ^ 2 on alternate lanes). The earlier swizzle c ^ ((r/2 ^ r/8) & 3)
+// left the staging writes 2-way conflicted in 16-lane cycles.
 __device__ __forceinline__ int swz_chunk(int r, int c)
 {
-    return c ^ (((r >> 1) ^ (r >> 3)) & 3);
+    return c ^ ((((r >> 1) ^ (r >> 2)) & 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 1));
 }
 
 // Workgroup tile BM (weight rows m) x BN (token rows n); the 4 waves form a
