@@ -13,12 +13,11 @@
 //
 // Per format, one 16-byte slice holds:
 //   QG_I8_ROW   16 weights (k .. k+15), row scale applied once per row;
-//   QG_U4_G64   32 weights = half a group of 64: one (scale, bias) pair;
-//   QG_B1_G128 128 weights = one group of 128: one fp16 scale.
-// The affine and sign formats are evaluated per slice as
-//   U4:  s * sum(q * x) + b * sum(x)
-//   B1:  s * (2 * sum_{bit=1}(x) - sum(x))
-// with sum(x) over the slice precomputed once per workgroup.
+//   QG_I8_G64   16 weights of one group of 64 (its fp32 scale);
+//   QG_U4_G64   32 weights = half a group of 64: one (scale, bias) pair.
+// The affine format is evaluated per slice as s * sum(q * x) + b * sum(x),
+// with sum(x) over the slice precomputed once per workgroup. (The 1-bit
+// format has its own kernels: gemv_b1.hpp, gemv_mfma16.hpp, gemm.hpp.)
 #pragma once
 
 #include "arrive.hpp"
@@ -187,20 +186,6 @@ __device__ __forceinline__ float dot_u4x8_mix(uint32_t d, float4 xa, float4 xb, 
     acc = fmaf(h16_hi(q15), xb.y, acc);
     acc = fmaf(h16_hi(q26), xb.z, acc);
     acc = fmaf(h16_hi(q37), xb.w, acc);
-    return acc;
-}
-
-// sum over the set bits of one byte (k = 8j .. 8j+7) of x_k.
-__device__ __forceinline__ float sum_b1x8(uint32_t byte, float4 xa, float4 xb, float acc)
-{
-    acc += (byte & 0x01u) ? xa.x : 0.f;
-    acc += (byte & 0x02u) ? xa.y : 0.f;
-    acc += (byte & 0x04u) ? xa.z : 0.f;
-    acc += (byte & 0x08u) ? xa.w : 0.f;
-    acc += (byte & 0x10u) ? xb.x : 0.f;
-    acc += (byte & 0x20u) ? xb.y : 0.f;
-    acc += (byte & 0x40u) ? xb.z : 0.f;
-    acc += (byte & 0x80u) ? xb.w : 0.f;
     return acc;
 }
 
@@ -406,34 +391,6 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p)
 #pragma unroll
                     for (int r = 0; r < R; ++r)
                         acc[r * B + b] = fmaf(sc[r], dot[r][b], fmaf(bi[r], xsum, acc[r * B + b]));
-                }
-            } else {  // FMT_B1_G128
-                float s[R];
-                const uint16_t *sp = static_cast<const uint16_t *>(p.scales);
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int64_t m = rb + r;
-                    s[r] = fp16_bits_to_f32(sp[(m < m_end ? m : m_begin) * (p.K / 128) + gslice]);
-                }
-#pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    const float4 *xp = xl + b * pc;
-                    float on[R];
-#pragma unroll
-                    for (int r = 0; r < R; ++r) on[r] = 0.f;
-#pragma unroll
-                    for (int o = 0; o < 16; ++o) {
-                        const float4 xa = xp[swz<CPS>(t * CPS + 2 * o)];
-                        const float4 xb = xp[swz<CPS>(t * CPS + 2 * o + 1)];
-#pragma unroll
-                        for (int r = 0; r < R; ++r)
-                            on[r] = sum_b1x8((word_of(c[r], o >> 2) >> (8 * (o & 3))) & 0xffu,
-                                             xa, xb, on[r]);
-                    }
-                    const float xsum = xs[b * xsp + t];
-#pragma unroll
-                    for (int r = 0; r < R; ++r)
-                        acc[r * B + b] = fmaf(s[r], fmaf(2.f, on[r], -xsum), acc[r * B + b]);
                 }
             }
         }

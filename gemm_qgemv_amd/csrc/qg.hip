@@ -547,7 +547,6 @@ void launch_gemv1_wg(const GemvPlan &pl, const qg::Gemv1Params &p, hipStream_t s
     constexpr bool NT = kGemv1Nt;
     const dim3 grid(static_cast<unsigned>(pl.grid_x)), block(64 * WGW);
     switch (pl.R) {
-    case 8: hipLaunchKernelGGL((qg::gemv1_kernel<FMT, NS, 8, FULL, NT, WGW>), grid, block, 0, s, p); break;
     case 4: hipLaunchKernelGGL((qg::gemv1_kernel<FMT, NS, 4, FULL, NT, WGW>), grid, block, 0, s, p); break;
     case 2: hipLaunchKernelGGL((qg::gemv1_kernel<FMT, NS, 2, FULL, NT, WGW>), grid, block, 0, s, p); break;
     default: hipLaunchKernelGGL((qg::gemv1_kernel<FMT, NS, 1, FULL, NT, WGW>), grid, block, 0, s, p); break;
@@ -826,10 +825,11 @@ void run_gemv(int fmt, const GemvPlan &pl, const void *codes, const void *scales
     p.nb = nb;
     p.nsplit = pl.nsplit;
     p.nkeys = pl.nkeys;
+    // (1-bit calls never get here: the planner sends them to the lookup,
+    // one-pass or prefill kernels)
     if (fmt == QG_I8_ROW) launch_gemv_fmt<qg::FMT_I8_ROW>(pl, p, s);
     else if (fmt == QG_I8_G64) launch_gemv_fmt<qg::FMT_I8_G64>(pl, p, s);
-    else if (fmt == QG_U4_G64) launch_gemv_fmt<qg::FMT_U4_G64>(pl, p, s);
-    else launch_gemv_fmt<qg::FMT_B1_G128>(pl, p, s);
+    else launch_gemv_fmt<qg::FMT_U4_G64>(pl, p, s);
     if (pl.nsplit > 1) {
         GemvParams c = p;
         c.rows_per_wg = pl.comb_rows_per_wg;

@@ -45,11 +45,24 @@ __device__ __forceinline__ uint32_t argmax_key_index(uint64_t key)
     return 0xFFFFFFFFu - static_cast<uint32_t>(key & 0xFFFFFFFFu);
 }
 
+// Value of lane (this lane ^ mask) of the wave, 0 < mask < 64 (a plain
+// ds_bpermute: the partner always exists in a 64-lane wave, so no width
+// check is needed).
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v, int mask)
+{
+    const int src = static_cast<int>(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u))) ^ mask;
+    return static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src << 2, static_cast<int>(v)));
+}
+
+__device__ __forceinline__ float lane_xor_f32(float v, int mask)
+{
+    return __uint_as_float(lane_xor_u32(__float_as_uint(v), mask));
+}
+
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask)
 {
-    uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
-    lo = __shfl_xor(lo, mask);
-    hi = __shfl_xor(hi, mask);
+    const uint32_t lo = lane_xor_u32(static_cast<uint32_t>(v), mask);
+    const uint32_t hi = lane_xor_u32(static_cast<uint32_t>(v >> 32), mask);
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
