@@ -15,13 +15,15 @@
 //
 // Contraction. As in the register-streaming small-batch kernel
 // (gemv_mfma.hpp): v_mfma_f32_16x16x32_bf16 with operand A = activation
-// pieces (rows 0..7: the top bf16 piece of activation rows 0..7, rows
-// 8..15: their middle piece; a second MFMA gives rows n and 8 + n half the
-// bottom piece each, so that D[n] + D[8 + n] restores the float32 product
-// exactly) and operand B = 16 weight rows of bf16 codes (0..15, exact). The
-// scale of a 64-input group multiplies the group's MFMA result in float32;
-// the bias term sum_g bias[m][g] X[n][g] (X: group sums of the activations,
-// split in three pieces like x) is one more pair of MFMAs per tile.
+// pieces and operand B = 16 weight rows of bf16 codes (0..15, exact), but
+// with the pieces of one activation row in adjacent operand rows: row 2n
+// holds the top bf16 piece of activation row n, row 2n + 1 its middle
+// piece, and a second MFMA gives both rows half the bottom piece, so that
+// D[2n] + D[2n + 1] restores the float32 product exactly and is added in
+// the lane that holds both (no lane exchange). The scale of a 64-input
+// group multiplies the group's MFMA result in float32; the bias term
+// sum_g bias[m][g] X[n][g] (X: group sums of the activations, split in
+// three pieces like x) is one more pair of MFMAs per tile.
 //
 // Mapping. Compute wave c owns inputs 256 c .. 256 c + 255 (groups 4c ..
 // 4c + 3) of every row; its activation pieces for those inputs stay in
@@ -34,10 +36,11 @@
 // rr % 16, so the 16 rows of a tile read 16 different bank groups. A stage
 // (32 rows, two tiles) ends with every wave's partial sums of its inputs in
 // LDS ([wave][row][activation row], two buffers used in turn); after the
-// barrier that opens the next stage, wave n adds the eight partials of
-// activation row n, in wave order, writes the 32 outputs and keeps its
-// greedy best, then computes its share of that next stage. So one barrier
-// per stage suffices, and the ring, the two partial buffers and nothing
+// barrier that opens the next stage, each wave first reads that stage's
+// codes and coefficients (both tiles), computes its share of it, and then
+// wave n adds the eight partials of activation row n of the previous stage,
+// in wave order, writes the 32 outputs and keeps its greedy best. So one
+// barrier per stage suffices, and the ring, the two partial buffers and nothing
 // else fill the 160 KiB of LDS (the greedy epilogue's scratch reuses the
 // ring once the last stage is done).
 #pragma once
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_mfma_u4_kernel(Gem
     } else {
         const int c = wave - kStreamLoaders;
         const int r = lane & 15, q = lane >> 4;
-        const int n = r & 7;   // activation row of operand row r
+        const int n = r >> 1;   // activation row of operand row r (top piece in even rows)
 
         // 1. activation pieces of this wave's inputs, in operand order, and
         //    the pieces of their group sums (operand A of the bias MFMAs:
@@ -118,12 +121,12 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_mfma_u4_kernel(Gem
                 uint32_t h[4], md[4], lo[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) split3h_pair(v[2 * j], v[2 * j + 1], h[j], md[j], lo[j]);
-                a_hm[u][t] = r < 8 ? make_uint4(h[0], h[1], h[2], h[3]) : make_uint4(md[0], md[1], md[2], md[3]);
+                a_hm[u][t] = (r & 1) == 0 ? make_uint4(h[0], h[1], h[2], h[3]) : make_uint4(md[0], md[1], md[2], md[3]);
                 a_lo[u][t] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
             }
             // the four quarters hold the group's 64 inputs
-            sum += __shfl_xor(sum, 16);
-            sum += __shfl_xor(sum, 32);
+            sum += lane_xor_f32(sum, 16);
+            sum += lane_xor_f32(sum, 32);
             xs[u] = sum;
         }
         // the dispatch's first workgroup claims the completion word
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_mfma_u4_kernel(Gem
         for (int u = 0; u < 4; ++u) split3h(xs[u], bh[u], bm[u], bl[u]);
         uint4 ab_hm = make_uint4(0u, 0u, 0u, 0u), ab_lo = ab_hm;
         if (q == 0) {
-            ab_hm = r < 8 ? make_uint4(bh[0] | (bh[1] << 16), bh[2] | (bh[3] << 16), 0u, 0u)
+            ab_hm = (r & 1) == 0 ? make_uint4(bh[0] | (bh[1] << 16), bh[2] | (bh[3] << 16), 0u, 0u)
                           : make_uint4(bm[0] | (bm[1] << 16), bm[2] | (bm[3] << 16), 0u, 0u);
             ab_lo = make_uint4(bl[0] | (bl[1] << 16), bl[2] | (bl[3] << 16), 0u, 0u);
         }
@@ -168,35 +171,40 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_mfma_u4_kernel(Gem
             // with stage s - 1 (its slot, and the partial buffer of stage s - 2)
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             stream_barrier();
-            if (s > 0) reduce(s - 1);
             const unsigned char *slot = stream_lds + (s % kStreamStages) * kStreamStageBytes;
             float *part = part0 + (s & 1) * (kStreamMfmaPartBytes / 4);
+            // every LDS read of the stage first (both tiles), so that the
+            // second tile's codes arrive while the first tile is reduced
+            uint2 cw[2][4], sv[2], bv[2];
 #pragma unroll
             for (int tile = 0; tile < 2; ++tile) {
                 const int row = 16 * tile + r;
                 const unsigned char *crow = slot + row * 1024;
-                uint2 cw[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int chunk = (2 * (4 * c + u) + (q >> 1)) ^ r;   // row % 16 == r
-                    cw[u] = *reinterpret_cast<const uint2 *>(crow + 16 * chunk + 8 * (q & 1));
+                    cw[tile][u] = *reinterpret_cast<const uint2 *>(crow + 16 * chunk + 8 * (q & 1));
                 }
-                const uint2 sv = *reinterpret_cast<const uint2 *>(slot + kStreamCodeBytes + row * 2 * G + 8 * c);
-                const uint2 bv = *reinterpret_cast<const uint2 *>(slot + kStreamCodeBytes + kStreamCoefBytes +
-                                                                  row * 2 * G + 8 * c);
+                sv[tile] = *reinterpret_cast<const uint2 *>(slot + kStreamCodeBytes + row * 2 * G + 8 * c);
+                bv[tile] = *reinterpret_cast<const uint2 *>(slot + kStreamCodeBytes + kStreamCoefBytes +
+                                                            row * 2 * G + 8 * c);
+            }
+            float v[2][2];
+#pragma unroll
+            for (int tile = 0; tile < 2; ++tile) {
                 // the bias term (operand B: this row's four biases at k
                 // positions 0..3 of quarter 0) on the accumulator, then the
                 // four groups as four independent MFMA chains issued in turn,
                 // so that no MFMA waits for the one before it
-                const uint4 bb = q == 0 ? make_uint4(bv.x, bv.y, 0u, 0u) : make_uint4(0u, 0u, 0u, 0u);
+                const uint4 bb = q == 0 ? make_uint4(bv[tile].x, bv[tile].y, 0u, 0u) : make_uint4(0u, 0u, 0u, 0u);
                 const floatx4_t zero = {0.f, 0.f, 0.f, 0.f};
                 floatx4_t acc = mfma(ab_hm, __builtin_bit_cast(bf16x8_t, bb), zero);
                 acc = mfma(ab_lo, __builtin_bit_cast(bf16x8_t, bb), acc);
                 bf16x8_t w[4][2];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    w[u][0] = nibbles_to_bf16(cw[u].x);
-                    w[u][1] = nibbles_to_bf16(cw[u].y);
+                    w[u][0] = nibbles_to_bf16(cw[tile][u].x);
+                    w[u][1] = nibbles_to_bf16(cw[tile][u].y);
                 }
                 floatx4_t t[4];
 #pragma unroll
@@ -209,20 +217,21 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_mfma_u4_kernel(Gem
                 for (int u = 0; u < 4; ++u) t[u] = mfma(a_lo[u][1], w[u][1], t[u]);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const uint32_t sw = (u < 2) ? sv.x : sv.y;
+                    const uint32_t sw = (u < 2) ? sv[tile].x : sv[tile].y;
                     const float sc = (u & 1) ? __uint_as_float(sw & 0xFFFF0000u) : __uint_as_float(sw << 16);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, t[u][i], acc[i]);
                 }
-                // lane (r, q) holds D rows 4q .. 4q + 3 of weight row r: add
-                // rows 8..15 (quarters 2, 3) to rows 0..7 (quarters 0, 1)
-                float v[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = pair_sum<5>(acc[i]);
-                if (q < 2)
-                    *reinterpret_cast<float4 *>(part + ((c * 32 + row) * kStreamMfmaRows + 4 * q)) =
-                        make_float4(v[0], v[1], v[2], v[3]);
+                // lane (r, q) holds D rows 4q .. 4q + 3 of weight row r:
+                // the two pieces of activation rows 2q and 2q + 1
+                v[tile][0] = acc[0] + acc[1];
+                v[tile][1] = acc[2] + acc[3];
             }
+#pragma unroll
+            for (int tile = 0; tile < 2; ++tile)
+                *reinterpret_cast<float2 *>(part + ((c * 32 + 16 * tile + r) * kStreamMfmaRows + 2 * q)) =
+                    make_float2(v[tile][0], v[tile][1]);
+            if (s > 0) reduce(s - 1);
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         stream_barrier();
