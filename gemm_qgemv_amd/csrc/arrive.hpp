@@ -208,11 +208,7 @@ __device__ __forceinline__ void greedy_finish_rows_in(const unsigned long long *
                 __hip_atomic_load(&keys[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             best = k > best ? k : best;
         }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const uint64_t other = shfl_xor_u64(best, o);
-            best = other > best ? other : best;
-        }
+        best = wave_max_u64(best);
         if ((threadIdx.x & 63) == 0) atomicMax(&s_best[0], best);
     } else {
         for (int i = threadIdx.x; i < total; i += blockDim.x) {

@@ -189,6 +189,40 @@ __device__ __forceinline__ float dot_u4x8_mix(uint32_t d, float4 xa, float4 xb, 
     return acc;
 }
 
+// dot_u4x8_mix for R rows at once (dword dw[r] of row r, the same eight
+// activations), each row's chain in the same order as dot_u4x8_mix, the
+// chains advanced in turn: consecutive instructions belong to different
+// rows, so none waits for the result of the one before it.
+template <int R>
+__device__ __forceinline__ void dot_u4x8_mix_rows(const uint32_t (&dw)[R], float4 xa, float4 xb, float (&acc)[R])
+{
+    uint32_t q04[R], q15[R], q26[R], q37[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint32_t e = dw[r] >> 8;
+        q04[r] = dw[r] & 0x000F000Fu;
+        q15[r] = dw[r] & 0x00F000F0u;
+        q26[r] = e & 0x000F000Fu;
+        q37[r] = e & 0x00F000F0u;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = fmaf(h16_lo(q04[r]), xa.x, acc[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = fmaf(h16_lo(q15[r]), xa.y, acc[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = fmaf(h16_lo(q26[r]), xa.z, acc[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = fmaf(h16_lo(q37[r]), xa.w, acc[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = fmaf(h16_hi(q04[r]), xb.x, acc[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = fmaf(h16_hi(q15[r]), xb.y, acc[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = fmaf(h16_hi(q26[r]), xb.z, acc[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = fmaf(h16_hi(q37[r]), xb.w, acc[r]);
+}
+
 __device__ __forceinline__ uint32_t word_of(const uint4 &c, int j)
 {
     return j == 0 ? c.x : j == 1 ? c.y : j == 2 ? c.z : c.w;

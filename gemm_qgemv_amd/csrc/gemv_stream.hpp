@@ -168,6 +168,11 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_u4_kernel(GemvStre
     const int nstages = static_cast<int>((r1 - r0 + RS - 1) / RS);
 
     const uint32_t tag = p.ctl != nullptr ? dispatch_tag() : 0u;
+    __shared__ unsigned long long s_key;   // the workgroup's greedy key
+    if (tid == 0) {
+        s_key = 0ull;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // done before this wave's first barrier
+    }
 
     float best_v = 0.f;
     int64_t best_m = -1;
@@ -222,21 +227,28 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_u4_kernel(GemvStre
                     sw[r][j] = *reinterpret_cast<const uint16_t *>(slot + kStreamCodeBytes + ci);
                     bw[r][j] = *reinterpret_cast<const uint16_t *>(slot + kStreamCodeBytes + kStreamCoefBytes + ci);
                 }
+            // the RPW rows' dot products as independent chains advanced in
+            // turn (a single chain would make every instruction wait for
+            // the one before it)
             float acc[RPW];
 #pragma unroll
-            for (int r = 0; r < RPW; ++r) {
-                float a = 0.f;
+            for (int r = 0; r < RPW; ++r) acc[r] = 0.f;
 #pragma unroll
-                for (int j = 0; j < NC; ++j) {
-                    float d = 0.f;
-                    d = dot_u4x8_mix(cw[r][j].x, xv[j][0], xv[j][1], d);
-                    d = dot_u4x8_mix(cw[r][j].y, xv[j][2], xv[j][3], d);
-                    d = dot_u4x8_mix(cw[r][j].z, xv[j][4], xv[j][5], d);
-                    d = dot_u4x8_mix(cw[r][j].w, xv[j][6], xv[j][7], d);
-                    a = fmaf(bf16_bits_to_f32(sw[r][j]), d * kMixScale,
-                             fmaf(bf16_bits_to_f32(bw[r][j]), xs[j], a));
+            for (int j = 0; j < NC; ++j) {
+                float d[RPW];
+#pragma unroll
+                for (int r = 0; r < RPW; ++r) d[r] = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    uint32_t dw[RPW];
+#pragma unroll
+                    for (int r = 0; r < RPW; ++r) dw[r] = word_of(cw[r][j], w);
+                    dot_u4x8_mix_rows<RPW>(dw, xv[j][2 * w], xv[j][2 * w + 1], d);
                 }
-                acc[r] = a;
+#pragma unroll
+                for (int r = 0; r < RPW; ++r)
+                    acc[r] = fmaf(bf16_bits_to_f32(sw[r][j]), d[r] * kMixScale,
+                                  fmaf(bf16_bits_to_f32(bw[r][j]), xs[j], acc[r]));
             }
             wave_reduce_dpp<RPW>(acc, lane);
             const int64_t m = r0 + static_cast<int64_t>(s) * RS + rw + own;
@@ -252,16 +264,9 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_u4_kernel(GemvStre
     }
 
     if (p.ctl != nullptr) {
-        __shared__ unsigned long long s_key;
-        if (tid == 0) s_key = 0ull;
-        __syncthreads();
-        uint64_t key = (writer && best_m >= 0) ? argmax_key(best_v, static_cast<uint32_t>(best_m)) : 0ull;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const uint64_t other = shfl_xor_u64(key, o);
-            key = other > key ? other : key;
-        }
-        if (lane == 0) atomicMax(&s_key, static_cast<unsigned long long>(key));
+        // the writer lanes' bests straight into the workgroup's key (s_key
+        // was cleared before the first stage barrier)
+        if (writer && best_m >= 0) atomicMax(&s_key, argmax_key(best_v, static_cast<uint32_t>(best_m)));
         __syncthreads();
         greedy_finish_rows(&s_key, 1, p.ctl, p.keys, p.idx, static_cast<int>(gridDim.x), tag);
     }

@@ -237,12 +237,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_mfma_u4_kernel(Gem
         stream_barrier();
         if (nstages > 0) reduce(nstages - 1);
         if (p.ctl != nullptr && c < p.nb) {
-            uint64_t key = best_m >= 0 ? argmax_key(best_v, static_cast<uint32_t>(best_m)) : 0ull;
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const uint64_t other = shfl_xor_u64(key, o);
-                key = other > key ? other : key;
-            }
+            const uint64_t key = wave_max_u64(best_m >= 0 ? argmax_key(best_v, static_cast<uint32_t>(best_m)) : 0ull);
             if (lane == 0) s_wkey[c] = key;
         }
     }

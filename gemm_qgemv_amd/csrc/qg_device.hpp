@@ -132,6 +132,43 @@ __device__ __forceinline__ float pair_sum(float x)
     }
 }
 
+// The larger of a 64-bit key and its partner's at exchange step S (the
+// steps of pair_sum; S=2 and S=3 together give the maximum over the four
+// lanes that differ in bits 2 and 3, as max is idempotent).
+template <int S>
+__device__ __forceinline__ uint64_t pair_max_u64(uint64_t k)
+{
+    const uint32_t lo = static_cast<uint32_t>(k), hi = static_cast<uint32_t>(k >> 32);
+    uint64_t a, b;
+    if constexpr (S <= 3) {
+        constexpr int ctrl = S == 0 ? 0xB1 : S == 1 ? 0x4E : S == 2 ? 0x124 : 0x128;
+        const uint32_t plo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(lo), ctrl, 0xF, 0xF, false));
+        const uint32_t phi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(hi), ctrl, 0xF, 0xF, false));
+        a = k;
+        b = (static_cast<uint64_t>(phi) << 32) | plo;
+    } else {
+        const auto rl = S == 4 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                               : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+        const auto rh = S == 4 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                               : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+        a = (static_cast<uint64_t>(rh[0]) << 32) | rl[0];
+        b = (static_cast<uint64_t>(rh[1]) << 32) | rl[1];
+    }
+    return a > b ? a : b;
+}
+
+// Maximum of a 64-bit key over the 64 lanes of the wave, in every lane
+// (DPP and permlane swaps: no LDS round trips).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k)
+{
+    k = pair_max_u64<0>(k);
+    k = pair_max_u64<1>(k);
+    k = pair_max_u64<2>(k);
+    k = pair_max_u64<3>(k);
+    k = pair_max_u64<4>(k);
+    return pair_max_u64<5>(k);
+}
+
 // Exchange steps used to halve the value count: partners must hold the same
 // value indices, so only the xor steps (bits 0, 1, 4, 5) qualify. The other
 // steps then sum the single remaining value.
