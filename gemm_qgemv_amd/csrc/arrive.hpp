@@ -201,15 +201,47 @@ __device__ __forceinline__ void greedy_finish_rows_in(const unsigned long long *
     if (!s_last) return;
     const int total = nwg * nb;
     if (nb == 1) {
-        // one key per workgroup: a maximum per thread, then per wave
+        // one key per workgroup: the first wave alone reads them (each lane
+        // a few, all requests in flight at once) and reduces them across
+        // its lanes; no further barrier
+        if (threadIdx.x >= 64) return;
+        constexpr int kBatch = 8;   // loads per lane issued before any is used
         unsigned long long best = 0ull;
-        for (int i = threadIdx.x; i < total; i += blockDim.x) {
-            const unsigned long long k =
-                __hip_atomic_load(&keys[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            best = k > best ? k : best;
+        for (int i0 = threadIdx.x; i0 < total; i0 += 64 * kBatch) {
+            unsigned long long k[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                k[u] = __hip_atomic_load(&keys[min(i0 + 64 * u, total - 1)], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) best = k[u] > best ? k[u] : best;
         }
         best = wave_max_u64(best);
-        if ((threadIdx.x & 63) == 0) atomicMax(&s_best[0], best);
+        if (threadIdx.x == 0) idx[0] = static_cast<int32_t>(argmax_key_index(best));
+        return;
+    } else if ((nb & (nb - 1)) == 0 && nb <= 8 && blockDim.x % 64 == 0) {
+        // nb = 2, 4, 8: key i belongs to row i % nb = threadIdx.x % nb for
+        // every key a thread reads (blockDim.x is a multiple of nb), so each
+        // lane keeps one maximum, the lanes of a row meet across the wave
+        // (DPP and permlane swaps), and each wave adds nb keys to LDS
+        constexpr int kBatch = 4;   // loads per lane issued before any is used
+        unsigned long long best = 0ull;
+        for (int i0 = threadIdx.x; i0 < total; i0 += static_cast<int>(blockDim.x) * kBatch) {
+            unsigned long long k[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int i = i0 + static_cast<int>(blockDim.x) * u;
+                k[u] = __hip_atomic_load(&keys[i < total ? i : i0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) best = k[u] > best ? k[u] : best;
+        }
+        if (nb <= 2) best = pair_max_u64<1>(best);
+        if (nb <= 4) best = pair_max_u64<2>(best);
+        best = pair_max_u64<3>(best);
+        best = pair_max_u64<4>(best);
+        best = pair_max_u64<5>(best);
+        if ((threadIdx.x & 63) < nb) atomicMax(&s_best[threadIdx.x & 63], best);
     } else {
         for (int i = threadIdx.x; i < total; i += blockDim.x) {
             const unsigned long long k =
