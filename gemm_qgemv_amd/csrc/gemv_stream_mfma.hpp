@@ -91,11 +91,16 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_stream_mfma_u4_kernel(Gem
 
     const uint32_t tag = p.ctl != nullptr ? dispatch_tag() : 0u;
 
-    if (wave < kStreamLoaders) {
-        stream_loader<1, true, 1>(p.codes, p.scales, p.biases, stream_lds, wave, lane, r0, r1, nstages);
+    // the loader waves come last: a SIMD gives its oldest waves the first
+    // issue slots, and in this kernel the compute waves bound each stage
+    // (with the loaders first, as in the batch-1 kernel, the stages of the
+    // two SIMDs that host a loader take longest)
+    if (wave >= kStreamComputes) {
+        stream_loader<1, true, 1>(p.codes, p.scales, p.biases, stream_lds, wave - kStreamComputes, lane, r0, r1,
+                                  nstages);
         stream_barrier();   // the compute waves' last reduction
     } else {
-        const int c = wave - kStreamLoaders;
+        const int c = wave;
         const int r = lane & 15, q = lane >> 4;
         const int n = r >> 1;   // activation row of operand row r (top piece in even rows)
 
