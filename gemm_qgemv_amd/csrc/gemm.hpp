@@ -91,17 +91,23 @@ __device__ __forceinline__ void split3_pair(float a, float b, uint32_t &hi, uint
     const float ra = a - __uint_as_float(ha), rb = b - __uint_as_float(hb);     // exact
     const uint32_t ma = __float_as_uint(ra) & 0xFFFF0000u, mb = __float_as_uint(rb) & 0xFFFF0000u;
     const float la = ra - __uint_as_float(ma), lb = rb - __uint_as_float(mb);   // exact
-    hi = (ha >> 16) | hb;
-    mid = (ma >> 16) | mb;
-    lo = (__float_as_uint(la) >> 16) | (__float_as_uint(lb) & 0xFFFF0000u);
+    // each piece is the high half of its float32: one byte permute packs a
+    // pair (bytes 2, 3 of the a word low, of the b word high)
+    hi = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+    mid = __builtin_amdgcn_perm(__float_as_uint(rb), __float_as_uint(ra), 0x07060302u);
+    lo = __builtin_amdgcn_perm(__float_as_uint(lb), __float_as_uint(la), 0x07060302u);
 }
 
-// int8 code pair -> packed bf16x2 (exact).
+// int8 code pair -> packed bf16x2 (exact: integers of at most 8 bits,
+// converted with the packing conversion, whose rounding leaves them as they are).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2v_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t d, int byte0)
 {
     const float a = static_cast<float>(static_cast<int8_t>((d >> (8 * byte0)) & 0xff));
     const float b = static_cast<float>(static_cast<int8_t>((d >> (8 * byte0 + 8)) & 0xff));
-    return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+    const float2v_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 // Two sign bits (bit0 -> low half) -> packed bf16x2 of +-1: bit 1 -> +1.0
