@@ -815,6 +815,8 @@ GARBAGE_CASES = [
     (synth.U4_G64, 6000, 6144, 1),       # batch-1 kernel, 4-wave workgroups
     (synth.I8_ROW, 3000, 1024, 1),       # batch-1 8-bit
     (synth.U4_G64, 40000, 2048, 8),      # batch-8 matrix-core head (parked key rows)
+    (synth.U4_G64, 40000, 2048, 4),      # the same at 4 rows
+    (synth.I8_ROW, 3000, 1024, 4),       # small-batch kernel, 4 parked key rows
     (synth.U4_G64, 5000, 2048, 16),      # one-pass 16-row head
     (synth.B1_G128, 5000, 5120, 1),      # 1-bit lookup, K chunks combined in the kernel
     (synth.B1_G128, 70000, 5120, 3),     # 1-bit lookup, more tiles than completion words
@@ -929,7 +931,7 @@ def test_stream_kernel_ties(torch, orc):
 # 2..8 activation rows, 4-bit, K = 2048, large M: loader waves + matrix cores
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M,N", [(32768, 8), (151937, 2), (40001, 3), (70000, 5), (151936, 8), (33000, 7)])
+@pytest.mark.parametrize("M,N", [(32768, 8), (151937, 2), (40001, 3), (100001, 4), (70000, 5), (151936, 8), (33000, 7)])
 def test_stream_mfma_kernel_random(torch, orc, M, N):
     """Random inputs, with and without the greedy indices and logits; every
     workgroup's run of rows ends in a partial stage at most of these M."""
