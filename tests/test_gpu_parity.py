@@ -814,6 +814,7 @@ GARBAGE_CASES = [
     (synth.U4_G64, 151936, 2048, 1),     # batch-1 kernel, 8-wave workgroups
     (synth.U4_G64, 6000, 6144, 1),       # batch-1 kernel, 4-wave workgroups
     (synth.I8_ROW, 3000, 1024, 1),       # batch-1 8-bit
+    (synth.U4_G64, 100000, 2048, 1),     # batch-1 streaming head
     (synth.U4_G64, 40000, 2048, 8),      # batch-8 matrix-core head (parked key rows)
     (synth.U4_G64, 40000, 2048, 4),      # the same at 4 rows
     (synth.I8_ROW, 3000, 1024, 4),       # small-batch kernel, 4 parked key rows
@@ -891,17 +892,22 @@ def test_stream_kernel_random(torch, orc, M, K):
     assert np.array_equal(idx, idx3), "greedy index without logits differs"
 
 
-@pytest.mark.parametrize("M,K", [(40000, 2048), (20000, 4096), (9000, 8192)])
+@pytest.mark.parametrize("M,K", [(40000, 2048), (100000, 2048), (20000, 4096), (9000, 8192), (50001, 8192)])
 def test_stream_kernel_exact(torch, orc, M, K):
-    """Exact-arithmetic inputs: bit-exact against the oracle."""
+    """Exact-arithmetic inputs: bit-exact against the oracle, the plain
+    product and the greedy head's logits and index."""
     say(f"stream kernel exact M={M} K={K}")
     rng = np.random.default_rng([7, M, K])
     w, x = exact_inputs(synth.U4_G64, M, K, 1, rng)
     ref, _ = orc.qgemv(w.fmt, w.codes, w.scales, w.biases, x, M, K)
     want = ref.astype(np.float32)
     assert np.array_equal(want.astype(np.float64), ref), "fixture is not exact in float32"
-    y, _ = gpu_gemv(torch, dev(w), x)
+    wd = dev(w)
+    y, _ = gpu_gemv(torch, wd, x)
     assert np.array_equal(y, want), f"not bit-exact: max diff {np.max(np.abs(y - want))}"
+    y2, idx = gpu_gemv(torch, wd, x, argmax=True)
+    assert np.array_equal(y2, want), f"greedy logits not bit-exact: max diff {np.max(np.abs(y2 - want))}"
+    assert idx[0] == int(np.argmax(want[0])), "greedy index"
 
 
 def test_stream_kernel_ties(torch, orc):
@@ -917,7 +923,7 @@ def test_stream_kernel_ties(torch, orc):
     best = int(np.argmax(ref[0]))
     codes, scales, biases = w.codes.copy(), w.scales.copy(), w.biases.copy()
     per_wg = M // 256
-    for dst in (per_wg * 37 - 1, per_wg * 37 + 13, M - 1, 5, best):
+    for dst in (per_wg * 37 - 1, per_wg * 37 + 13, M - 1, 5, 131072, 140000 + 17, best):
         codes[dst], scales[dst], biases[dst] = codes[best], scales[best], biases[best]
     w2 = synth.QWeights(w.fmt, M, K, codes, scales, biases)
     ref2, a2 = orc.qgemv(w2.fmt, w2.codes, w2.scales, w2.biases, x, M, K)
@@ -979,7 +985,7 @@ def test_stream_mfma_kernel_ties(torch, orc):
     per_wg = M // 256
     # activation row 3's best row copied to the tie positions
     best = int(np.argmax(ref[3]))
-    for dst in (per_wg * 37 - 1, per_wg * 37 + 13, M - 1, 5, best):
+    for dst in (per_wg * 37 - 1, per_wg * 37 + 13, M - 1, 5, 131072, 140000 + 17, best):
         codes[dst], scales[dst], biases[dst] = codes[best], scales[best], biases[best]
     w2 = synth.QWeights(w.fmt, M, K, codes, scales, biases)
     ref2, a2 = orc.qgemv(w2.fmt, w2.codes, w2.scales, w2.biases, x, M, K)
