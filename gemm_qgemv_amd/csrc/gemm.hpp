@@ -371,8 +371,7 @@ __global__ __launch_bounds__(kGemmThreads, (gemm_occupancy<FMT, BM, BN>())) void
                 split3_pair(v.y, v.w, h[3], md[3], lo[3]);
                 // this lane's 8 inputs, then the other three blocks of the step
                 float t = ((u.x + u.y) + (u.z + u.w)) + ((v.x + v.y) + (v.z + v.w));
-                t += __shfl_xor(t, 16);
-                t += __shfl_xor(t, 32);
+                t = pair_sum<5>(pair_sum<4>(t));   // the other three blocks (lanes ^ 16, ^ 32)
                 xs[j] = kt % GSTEPS == 0 ? t : xs[j] + t;
             } else {
                 split3_pair(u.x, u.y, h[0], md[0], lo[0]);
