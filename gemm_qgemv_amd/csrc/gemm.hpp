@@ -15,8 +15,9 @@
 // the weights packed instead of dequantizing them to a float scratch first.)
 //
 // Tiling. A workgroup of 4 waves computes a BM (m) x BN (n) tile of Y
-// (128 x 128, 64 x 128 or 64 x 64, chosen by the host so that the grid fills
-// the 256 compute units); the waves sit side by side along n, each covering
+// (256 x 64, 128 x 128, 128 x 64, 64 x 128 or 64 x 64, chosen by the host
+// so that the grid fills the 256 compute units); the waves sit side by side
+// along n, each covering
 // all BM weight rows, so a wave reads BM / 16 weight fragments and 3 * BN / 64
 // activation fragments per k-step for 3 * BM * BN / 1024 MFMAs. For up to 32
 // token rows the tile is 16 or 32 tokens wide and the waves split the
@@ -130,14 +131,15 @@ constexpr int kGemmThreads = 256;
 template <int FMT> struct GemmDepth { static constexpr int value = 2; };
 template <> struct GemmDepth<FMT_B1_G128> { static constexpr int value = 4; };
 // Workgroups per compute unit the register budget is set for: three for the
-// 8-bit per-row 128 x 64 tile (no group accumulators: 132 VGPRs, so a third
-// wave per SIMD hides the activation loads and splits; 3584 x 1024, N =
-// 10240: 245 -> 233 us, 1024 x 3584, N = 2048: 68 -> 60 us against the
-// 128 x 128 and 64 x 64 tiles), two for every other tile.
+// 8-bit per-row 128 x 64 and 256 x 64 tiles (no group accumulators: 153 and
+// 164 VGPRs, so a third wave per SIMD hides the activation loads and splits;
+// 3584 x 1024, N = 10240: 245 -> 233 us at 128 x 64 against 128 x 128, 232
+// -> 201 us at 256 x 64, where each activation split feeds twice the
+// MFMAs), two for every other tile.
 template <int FMT, int BM, int BN>
 constexpr int gemm_occupancy()
 {
-    return FMT == FMT_I8_ROW && BM == 128 && BN == 64 ? 3 : 2;
+    return FMT == FMT_I8_ROW && (BM == 128 || BM == 256) && BN == 64 ? 3 : 2;
 }
 constexpr int kGemmInterleave = 5;   // VALU instructions issued after each MFMA
 
@@ -191,7 +193,10 @@ __global__ __launch_bounds__(kGemmThreads, (gemm_occupancy<FMT, BM, BN>())) void
     constexpr int WM = 4 / WN;
     constexpr int TI = BM / (16 * WM);   // 16-row weight blocks per wave
     constexpr int TJ = BN / (16 * WN);   // 16-token blocks per wave
-    static_assert(TI >= 1 && TJ >= 1 && BM * 2 <= kGemmThreads, "one staging item per thread");
+    // staging items per thread: a row half (16 k of the 32-k step) each,
+    // rows sr and sr + 128
+    constexpr int SI = BM * 2 > kGemmThreads ? BM * 2 / kGemmThreads : 1;
+    static_assert(TI >= 1 && TJ >= 1 && BM * 2 <= kGemmThreads * SI && SI <= 2, "staging items");
     // double-buffered weight stages: [buffer][row][4 chunks of 8 bf16]
     __shared__ uint4 lw[2][BM * 4];
     // per-group coefficients of the current and next group: scales (grouped
@@ -221,7 +226,8 @@ __global__ __launch_bounds__(kGemmThreads, (gemm_occupancy<FMT, BM, BN>())) void
     const int wn = (wave % WN) * (BN / WN), wm = (wave / WN) * (BM / WM);
     const int fr = lane & 15, fq = lane >> 4;
 
-    // weight staging assignment: thread -> (row, half of the 32-k step)
+    // weight staging assignment: thread -> (row, half of the 32-k step), and
+    // row + 128 for the 256-row tile
     const int sr = tid >> 1, sh = tid & 1;
     const bool wst = 2 * BM >= kGemmThreads || sr < BM;   // constant when every thread stages
     constexpr bool I8 = FMT == FMT_I8_ROW || FMT == FMT_I8_G64;   // int8 codes
@@ -234,7 +240,10 @@ __global__ __launch_bounds__(kGemmThreads, (gemm_occupancy<FMT, BM, BN>())) void
     // moved out of range explicitly.
     const auto wbuf = buffer_rsrc(p.codes + m0 * row_bytes, wrows * row_bytes);
     const auto xbuf = buffer_rsrc(p.x + n0 * p.K, xrows * p.K * 4);
-    const uint32_t woff = wst ? static_cast<uint32_t>(sr * row_bytes) : kOutOfRange;
+    uint32_t woff[SI];
+#pragma unroll
+    for (int it = 0; it < SI; ++it)
+        woff[it] = wst ? static_cast<uint32_t>((sr + 128 * it) * row_bytes) : kOutOfRange;
     // activation fragments: this lane feeds the MFMA operand of token
     // n0 + wn + 16 j + fr with inputs 8 fq .. 8 fq + 7 of each step; each
     // token row is used by this wave only, so it goes straight from global
@@ -260,7 +269,7 @@ __global__ __launch_bounds__(kGemmThreads, (gemm_occupancy<FMT, BM, BN>())) void
     const uint32_t boff = tid < BM ? static_cast<uint32_t>(tid * groups * 2) : kOutOfRange;
 
     struct Regs {
-        uint4 w;          // I8: 16 codes; U4: w.x, w.y = 16 nibbles; B1: low 16 bits = 16 sign bits
+        uint4 w[SI];      // per item, I8: 16 codes; U4: w.x, w.y = 16 nibbles; B1: low 16 bits = 16 sign bits
         uint32_t s, b;    // grouped formats, first step of a group: scale (and bias) bits of row m0 + tid
         float4 x[TJ][2];  // this lane's activations of the step (8 consecutive inputs per block)
     };
@@ -271,15 +280,18 @@ __global__ __launch_bounds__(kGemmThreads, (gemm_occupancy<FMT, BM, BN>())) void
     auto load_w = [&](Regs &R, int kt) {
         const int64_t k = static_cast<int64_t>(kt + ktb) * GT_K + 16 * sh;
         constexpr int KSHIFT = I8 ? 0 : FMT == FMT_U4_G64 ? 1 : 3;   // input index -> byte in the row
-        const uint32_t off = in_range_or_out(woff + static_cast<uint32_t>(k >> KSHIFT), k, p.K);
-        if (I8) {
-            R.w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wbuf, off, 0, 0));
-        } else if (FMT == FMT_U4_G64) {
-            const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wbuf, off, 0, 0));
-            R.w.x = v.x;
-            R.w.y = v.y;
-        } else {
-            R.w.x = __builtin_amdgcn_raw_buffer_load_b16(wbuf, off, 0, 0);
+#pragma unroll
+        for (int it = 0; it < SI; ++it) {
+            const uint32_t off = in_range_or_out(woff[it] + static_cast<uint32_t>(k >> KSHIFT), k, p.K);
+            if (I8) {
+                R.w[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wbuf, off, 0, 0));
+            } else if (FMT == FMT_U4_G64) {
+                const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wbuf, off, 0, 0));
+                R.w[it].x = v.x;
+                R.w[it].y = v.y;
+            } else {
+                R.w[it].x = __builtin_amdgcn_raw_buffer_load_b16(wbuf, off, 0, 0);
+            }
         }
         if (GROUPED && kt % GSTEPS == 0) {
             const uint32_t o = soff + static_cast<uint32_t>(((kt + ktb) / GSTEPS) * SBYTES);
@@ -306,10 +318,14 @@ __global__ __launch_bounds__(kGemmThreads, (gemm_occupancy<FMT, BM, BN>())) void
     };
 
     auto stage = [&](const Regs &R, int kt, int b) {
-        if (wst) {
+#pragma unroll
+        for (int it = 0; it < SI; ++it) {
+            if (!wst) break;
+            const uint4 rw = R.w[it];
+            const int row = sr + 128 * it;
             uint32_t wv[8];
             if (I8) {
-                const uint32_t d[4] = {R.w.x, R.w.y, R.w.z, R.w.w};
+                const uint32_t d[4] = {rw.x, rw.y, rw.z, rw.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     wv[2 * j] = i8pair_to_bf16x2(d[j], 0);
@@ -317,18 +333,18 @@ __global__ __launch_bounds__(kGemmThreads, (gemm_occupancy<FMT, BM, BN>())) void
                 }
             } else if (FMT == FMT_U4_G64) {
                 // codes in the order k = 0, 2, 4, 6, 1, 3, 5, 7 of each 8
-                const uint4 c0 = __builtin_bit_cast(uint4, nibbles_to_bf16(R.w.x));
-                const uint4 c1 = __builtin_bit_cast(uint4, nibbles_to_bf16(R.w.y));
+                const uint4 c0 = __builtin_bit_cast(uint4, nibbles_to_bf16(rw.x));
+                const uint4 c1 = __builtin_bit_cast(uint4, nibbles_to_bf16(rw.y));
                 wv[0] = c0.x; wv[1] = c0.y; wv[2] = c0.z; wv[3] = c0.w;
                 wv[4] = c1.x; wv[5] = c1.y; wv[6] = c1.z; wv[7] = c1.w;
             } else {
                 // rows beyond M carry no codes: their (unused) weights become -1
-                const uint32_t nbits = ~R.w.x;
+                const uint32_t nbits = ~rw.x;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) wv[j] = signpair_to_bf16x2((nbits >> (2 * j)) & 3u);
             }
-            lw[b][sr * 4 + swz_chunk(sr, 2 * sh)] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-            lw[b][sr * 4 + swz_chunk(sr, 2 * sh + 1)] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+            lw[b][row * 4 + swz_chunk(row, 2 * sh)] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+            lw[b][row * 4 + swz_chunk(row, 2 * sh + 1)] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
         }
         if (GROUPED && kt % GSTEPS == 0 && tid < BM) {
             const int gb = (kt / GSTEPS) & 1;
@@ -389,16 +405,37 @@ __global__ __launch_bounds__(kGemmThreads, (gemm_occupancy<FMT, BM, BN>())) void
     // activation pieces bx, then the group close
     auto compute = [&](int kt, const bf16x8_t (&bx)[TJ][3]) {
         const int b = kt & 1;
+        // the first MFMA of a group starts its sum from zero (the group's
+        // position is known at compile time in the unrolled pipeline)
+        const bool first = GROUPED && kt % GSTEPS == 0;
+        const floatx4_t zero = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (TI >= 16 && !GROUPED) {
+            // 16 weight fragments: two at a time through all three pieces
+            // (registers)
+#pragma unroll
+            for (int i = 0; i < TI; i += 2) {
+                bf16x8_t a2[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int r = wm + 16 * (i + u) + fr;
+                    a2[u] = __builtin_bit_cast(bf16x8_t, lw[b][r * 4 + swz_chunk(r, fq)]);
+                }
+#pragma unroll
+                for (int pc = 0; pc < 3; ++pc)
+#pragma unroll
+                    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                        for (int u = 0; u < 2; ++u)
+                            acc[i + u][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2[u], bx[j][pc], acc[i + u][j], 0, 0, 0);
+            }
+            return;
+        }
         bf16x8_t a[TI];
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
             const int r = wm + 16 * i + fr;
             a[i] = __builtin_bit_cast(bf16x8_t, lw[b][r * 4 + swz_chunk(r, fq)]);
         }
-        // the first MFMA of a group starts its sum from zero (the group's
-        // position is known at compile time in the unrolled pipeline)
-        const bool first = GROUPED && kt % GSTEPS == 0;
-        const floatx4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int pc = 0; pc < 3; ++pc) {
 #pragma unroll

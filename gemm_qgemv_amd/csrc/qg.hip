@@ -931,7 +931,7 @@ GemmTail gemm_tail(int fmt, int64_t M, int64_t K, int64_t N)
     if (nsplit > 1) return t;
     gemm_tile(fmt, M, N, bm, bn, wn);
     const int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
-    const int64_t slots = (fmt == QG_I8_ROW && bm == 128 && bn == 64 ? 3 : 2) * kComputeUnits;
+    const int64_t slots = (fmt == QG_I8_ROW && bm >= 128 && bn == 64 ? 3 : 2) * kComputeUnits;
     const int64_t ntail = tiles % slots;
     if (tiles < slots || ntail == 0 || 4 * ntail > slots) return t;
     const int64_t nk = ceil_div(K, 32);
@@ -1044,8 +1044,13 @@ void gemm_tile(int fmt, int64_t M, int64_t N, int &bm, int &bn, int &wn)
         bm = 128;
         return;
     }
-    // the 8-bit per-row format: 128 x 64 at three workgroups per compute
-    // unit once every compute unit gets a tile (gemm_occupancy)
+    // the 8-bit per-row format: 256 x 64 once every compute unit gets two
+    // tiles, else 128 x 64 at three workgroups per compute unit once every
+    // compute unit gets a tile (gemm_occupancy)
+    if (fmt == QG_I8_ROW && tiles(256, 64) >= 2 * kComputeUnits) {
+        bm = 256;
+        return;
+    }
     if (fmt == QG_I8_ROW && tiles(128, 64) >= kComputeUnits) {
         bm = 128;
         return;
@@ -1075,6 +1080,12 @@ void launch_gemm_fmt(int bm, int bn, dim3 grid, hipStream_t s, const qg::GemmPar
         if (bm == 128) hipLaunchKernelGGL((qg::gemm_kernel<FMT, 128, 32, 2>), grid, block, 0, s, p);
         else hipLaunchKernelGGL((qg::gemm_kernel<FMT, 64, 32, 2>), grid, block, 0, s, p);
     } else if (bn == 64) {
+        if constexpr (FMT == qg::FMT_I8_ROW) {
+            if (bm == 256) {
+                hipLaunchKernelGGL((qg::gemm_kernel<FMT, 256, 64>), grid, block, 0, s, p);
+                return;
+            }
+        }
         if (bm == 128) hipLaunchKernelGGL((qg::gemm_kernel<FMT, 128, 64>), grid, block, 0, s, p);
         else hipLaunchKernelGGL((qg::gemm_kernel<FMT, 64, 64>), grid, block, 0, s, p);
     } else if constexpr (FMT == qg::FMT_I8_ROW) {

@@ -203,10 +203,12 @@ def test_exact_arithmetic_prefill_bit_exact(torch, orc, fmt, M, K, N):
     assert np.array_equal(yg, want), f"prefill not bit-exact: max diff {np.max(np.abs(yg - want))}"
 
 
-@pytest.mark.parametrize("M,K,N", [(4001, 160, 1503), (4096, 176, 1536), (3841, 1040, 1665)])
+@pytest.mark.parametrize("M,K,N", [(4001, 160, 1503), (4096, 176, 1536), (3841, 1040, 1665),
+                                   (4097, 176, 8001)])
 def test_exact_arithmetic_prefill_large_grid(torch, orc, M, K, N):
-    """8-bit prefill on grids of several hundred 128 x 128 tiles: ragged M
-    and N, K with a half step at the end."""
+    """8-bit prefill on grids of several hundred 128 x 128 tiles, and of
+    two thousand 256 x 64 tiles (4097 x 8001): ragged M and N, K with a half
+    step at the end."""
     say(f"exact prefill large grid M={M} K={K} N={N}")
     rng = np.random.default_rng([11, M, K, N])
     w, x = exact_inputs(synth.I8_ROW, M, K, N, rng)
@@ -222,6 +224,8 @@ def test_exact_arithmetic_prefill_large_grid(torch, orc, M, K, N):
     (synth.I8_G64, 2100, 576, 2000),
     # M not a multiple of 4: the combine's scalar stores
     (synth.U4_G64, 2101, 576, 2000), (synth.I8_G64, 2099, 576, 2000), (synth.I8_ROW, 2001, 272, 3100),
+    # 256 x 64 tiles: 800 tiles, a last round of 32 (ragged M)
+    (synth.I8_ROW, 1000, 272, 12800),
 ])
 def test_exact_arithmetic_prefill_split_tail(torch, orc, fmt, M, K, N):
     """Grids of one or more full rounds of tiles plus a short last round,
