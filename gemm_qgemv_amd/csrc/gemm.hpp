@@ -131,15 +131,18 @@ constexpr int kGemmThreads = 256;
 template <int FMT> struct GemmDepth { static constexpr int value = 2; };
 template <> struct GemmDepth<FMT_B1_G128> { static constexpr int value = 4; };
 // Workgroups per compute unit the register budget is set for: three for the
-// 8-bit per-row 128 x 64 and 256 x 64 tiles (no group accumulators: 153 and
-// 164 VGPRs, so a third wave per SIMD hides the activation loads and splits;
-// 3584 x 1024, N = 10240: 245 -> 233 us at 128 x 64 against 128 x 128, 232
-// -> 201 us at 256 x 64, where each activation split feeds twice the
-// MFMAs), two for every other tile.
+// 8-bit tiles of 64 token rows (128 x 64 per-row: 110 VGPRs, group-64: 168;
+// 256 x 64 per-row: 164), so a third wave per SIMD hides the activation
+// loads and splits (3584 x 1024, N = 10240: 245 -> 233 us at 128 x 64
+// against 128 x 128; 232 -> 201 us at 256 x 64, where each activation split
+// feeds twice the MFMAs; 1024 x 3584, N = 2048: 64 -> 61 us with the weight
+// fragments read in pairs); two for every other tile (the 4-bit and 1-bit
+// 128 x 64 tiles need 202 and 204).
 template <int FMT, int BM, int BN>
 constexpr int gemm_occupancy()
 {
-    return FMT == FMT_I8_ROW && (BM == 128 || BM == 256) && BN == 64 ? 3 : 2;
+    constexpr bool i8 = FMT == FMT_I8_ROW || FMT == FMT_I8_G64;
+    return i8 && BN == 64 && (BM == 128 || (FMT == FMT_I8_ROW && BM == 256)) ? 3 : 2;
 }
 constexpr int kGemmInterleave = 5;   // VALU instructions issued after each MFMA
 
@@ -409,9 +412,10 @@ __global__ __launch_bounds__(kGemmThreads, (gemm_occupancy<FMT, BM, BN>())) void
         // position is known at compile time in the unrolled pipeline)
         const bool first = GROUPED && kt % GSTEPS == 0;
         const floatx4_t zero = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (TI >= 16 && !GROUPED) {
-            // 16 weight fragments: two at a time through all three pieces
-            // (registers)
+        if constexpr (TI >= 8) {
+            // the weight fragments two at a time through all three pieces,
+            // so that only two are held (registers: the 256-row tile needs
+            // this to fit at all, the 128-row tiles need 12 to 43 fewer)
 #pragma unroll
             for (int i = 0; i < TI; i += 2) {
                 bf16x8_t a2[2];
@@ -426,10 +430,13 @@ __global__ __launch_bounds__(kGemmThreads, (gemm_occupancy<FMT, BM, BN>())) void
                     for (int j = 0; j < TJ; ++j)
 #pragma unroll
                         for (int u = 0; u < 2; ++u)
-                            acc[i + u][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2[u], bx[j][pc], acc[i + u][j], 0, 0, 0);
+                            if (FMT == FMT_I8_ROW)
+                                acc[i + u][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2[u], bx[j][pc], acc[i + u][j], 0, 0, 0);
+                            else
+                                gacc[i + u][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    a2[u], bx[j][pc], first && pc == 0 ? zero : gacc[i + u][j], 0, 0, 0);
             }
-            return;
-        }
+        } else {
         bf16x8_t a[TI];
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
@@ -449,6 +456,7 @@ __global__ __launch_bounds__(kGemmThreads, (gemm_occupancy<FMT, BM, BN>())) void
                             a[i], bx[j][pc], first && pc == 0 ? zero : gacc[i][j], 0, 0, 0);
                 }
             }
+        }
         }
         if (GROUPED && kt % GSTEPS == GSTEPS - 1) {
             // close the group: acc += scale[m][g] * (sum of code * x over the

@@ -931,7 +931,7 @@ GemmTail gemm_tail(int fmt, int64_t M, int64_t K, int64_t N)
     if (nsplit > 1) return t;
     gemm_tile(fmt, M, N, bm, bn, wn);
     const int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
-    const int64_t slots = (fmt == QG_I8_ROW && bm >= 128 && bn == 64 ? 3 : 2) * kComputeUnits;
+    const int64_t slots = ((fmt == QG_I8_ROW || fmt == QG_I8_G64) && bm >= 128 && bn == 64 ? 3 : 2) * kComputeUnits;
     const int64_t ntail = tiles % slots;
     if (tiles < slots || ntail == 0 || 4 * ntail > slots) return t;
     const int64_t nk = ceil_div(K, 32);
