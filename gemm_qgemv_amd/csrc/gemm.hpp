@@ -130,17 +130,20 @@ constexpr int kGemmThreads = 256;
 // 17408 x 5120, N = 512).
 template <int FMT> struct GemmDepth { static constexpr int value = 2; };
 template <> struct GemmDepth<FMT_B1_G128> { static constexpr int value = 4; };
-// Workgroups per compute unit the register budget is set for: three for the
-// 8-bit tiles of 64 token rows (128 x 64 per-row: 110 VGPRs, group-64: 168;
-// 256 x 64 per-row: 164), so a third wave per SIMD hides the activation
-// loads and splits (3584 x 1024, N = 10240: 245 -> 233 us at 128 x 64
-// against 128 x 128; 232 -> 201 us at 256 x 64, where each activation split
-// feeds twice the MFMAs; 1024 x 3584, N = 2048: 64 -> 61 us with the weight
-// fragments read in pairs); two for every other tile (the 4-bit and 1-bit
-// 128 x 64 tiles need 202 and 204).
+// Workgroups per compute unit the register budget is set for: four for the
+// 8-bit per-row 128 x 64 tile (110 VGPRs; 3584 x 1024, N = 2048: 62 -> 58
+// us against three), three for the other 8-bit tiles of 64 token rows
+// (group-64 128 x 64: 168 VGPRs; per-row 256 x 64: 164), so that further
+// waves per SIMD hide the activation loads and splits (3584 x 1024, N =
+// 10240: 245 -> 233 us at 128 x 64 against 128 x 128; 232 -> 201 us at
+// 256 x 64, where each activation split feeds twice the MFMAs); two for
+// every other tile (the 4-bit and 1-bit 128 x 64 tiles need 202 and 204;
+// the 1-bit tile at prefetch depth 2 fits three, but 17408 x 5120, N = 512
+// then takes 336 us instead of 269).
 template <int FMT, int BM, int BN>
 constexpr int gemm_occupancy()
 {
+    if (FMT == FMT_I8_ROW && BM == 128 && BN == 64) return 4;
     constexpr bool i8 = FMT == FMT_I8_ROW || FMT == FMT_I8_G64;
     return i8 && BN == 64 && (BM == 128 || (FMT == FMT_I8_ROW && BM == 256)) ? 3 : 2;
 }

@@ -931,7 +931,11 @@ GemmTail gemm_tail(int fmt, int64_t M, int64_t K, int64_t N)
     if (nsplit > 1) return t;
     gemm_tile(fmt, M, N, bm, bn, wn);
     const int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
-    const int64_t slots = ((fmt == QG_I8_ROW || fmt == QG_I8_G64) && bm >= 128 && bn == 64 ? 3 : 2) * kComputeUnits;
+    // workgroups per compute unit (gemm_occupancy)
+    const bool i8 = fmt == QG_I8_ROW || fmt == QG_I8_G64;
+    const int per_cu = fmt == QG_I8_ROW && bm == 128 && bn == 64 ? 4
+                       : i8 && bn == 64 && (bm == 128 || (fmt == QG_I8_ROW && bm == 256)) ? 3 : 2;
+    const int64_t slots = per_cu * kComputeUnits;
     const int64_t ntail = tiles % slots;
     if (tiles < slots || ntail == 0 || 4 * ntail > slots) return t;
     const int64_t nk = ceil_div(K, 32);
@@ -1044,9 +1048,9 @@ void gemm_tile(int fmt, int64_t M, int64_t N, int &bm, int &bn, int &wn)
         bm = 128;
         return;
     }
-    // the 8-bit per-row format: 256 x 64 once every compute unit gets two
-    // tiles, else 128 x 64 at three workgroups per compute unit once every
-    // compute unit gets a tile (gemm_occupancy)
+    // the 8-bit per-row format: 256 x 64 (three workgroups per compute unit)
+    // once every compute unit gets two tiles, else 128 x 64 (four per unit)
+    // once every compute unit gets a tile (gemm_occupancy)
     if (fmt == QG_I8_ROW && tiles(256, 64) >= 2 * kComputeUnits) {
         bm = 256;
         return;
