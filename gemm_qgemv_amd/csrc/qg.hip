@@ -890,8 +890,11 @@ void gemm_tile(int fmt, int64_t M, int64_t N, int &bm, int &bn, int &wn);
 // does the most work per k-step beside its MFMAs (sign unpacking and a
 // barrier for few MFMAs), so it splits grids of up to four tiles per
 // compute unit, into about four workgroups per compute unit (17408 x 5120,
-// 128 token rows: 148 -> 131 us; 64 rows: 101 -> 75 us); the other formats
-// lose from such splits (8-bit 3584 x 1024, 128 rows: 16.7 -> 21.6 us).
+// 128 token rows: 148 -> 131 us; 64 rows: 101 -> 75 us); the 8-bit per-row
+// format splits grids of up to two tiles per compute unit (its 128 x 64
+// tile runs four to a unit; 1024 x 3584, N = 2048, 256 tiles: 65 -> 56 us);
+// deeper splits lose (8-bit 3584 x 1024, 128 rows, four workgroups per
+// compute unit instead of two: 16.7 -> 21.6 us).
 // kt_split = 0: no split.
 void gemm_split(int fmt, int64_t M, int64_t K, int64_t N, int &kt_split, int &nsplit)
 {
@@ -901,7 +904,7 @@ void gemm_split(int fmt, int64_t M, int64_t K, int64_t N, int &kt_split, int &ns
     gemm_tile(fmt, M, N, bm, bn, wn);
     const int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
     const int64_t nk = ceil_div(K, 32);
-    const int below = fmt == QG_B1_G128 ? 4 : 1, per_cu = fmt == QG_B1_G128 ? 4 : 2;
+    const int below = fmt == QG_B1_G128 ? 4 : fmt == QG_I8_ROW ? 2 : 1, per_cu = fmt == QG_B1_G128 ? 4 : 2;
     if (tiles >= below * kComputeUnits || nk < 8) return;
     const int64_t want = std::min(ceil_div(per_cu * kComputeUnits, tiles), nk / 4);
     if (want < 2) return;
