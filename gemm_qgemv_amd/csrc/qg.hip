@@ -892,7 +892,8 @@ void gemm_tile(int fmt, int64_t M, int64_t N, int &bm, int &bn, int &wn);
 // compute unit, into about four workgroups per compute unit (17408 x 5120,
 // 128 token rows: 148 -> 131 us; 64 rows: 101 -> 75 us); the 8-bit per-row
 // format splits grids of up to two tiles per compute unit (its 128 x 64
-// tile runs four to a unit; 1024 x 3584, N = 2048, 256 tiles: 65 -> 56 us);
+// tile runs four to a unit; 1024 x 3584, N = 2048, 256 tiles: 65 -> 56 us),
+// and so does the 8-bit group-64 format (three to a unit);
 // deeper splits lose (8-bit 3584 x 1024, 128 rows, four workgroups per
 // compute unit instead of two: 16.7 -> 21.6 us).
 // kt_split = 0: no split.
@@ -904,7 +905,7 @@ void gemm_split(int fmt, int64_t M, int64_t K, int64_t N, int &kt_split, int &ns
     gemm_tile(fmt, M, N, bm, bn, wn);
     const int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
     const int64_t nk = ceil_div(K, 32);
-    const int below = fmt == QG_B1_G128 ? 4 : fmt == QG_I8_ROW ? 2 : 1, per_cu = fmt == QG_B1_G128 ? 4 : 2;
+    const int below = fmt == QG_B1_G128 ? 4 : fmt == QG_I8_ROW || fmt == QG_I8_G64 ? 2 : 1, per_cu = fmt == QG_B1_G128 ? 4 : 2;
     if (tiles >= below * kComputeUnits || nk < 8) return;
     const int64_t want = std::min(ceil_div(per_cu * kComputeUnits, tiles), nk / 4);
     if (want < 2) return;
@@ -1045,9 +1046,12 @@ void gemm_tile(int fmt, int64_t M, int64_t N, int &bm, int &bn, int &wn)
     // the grouped formats: 128 weight rows by 64 token rows (each activation
     // split feeds twice the MFMAs of a 64-row tile; 128 x 128 would spill
     // their second set of accumulators), for the 1-bit format always
-    // (17408 x 5120, N = 512: 431 -> 318 us), for the others once every
-    // compute unit gets two tiles
-    if (fmt != QG_I8_ROW && (fmt == QG_B1_G128 || tiles(128, 64) >= 2 * kComputeUnits)) {
+    // (17408 x 5120, N = 512: 431 -> 318 us), for the 8-bit group-64 format
+    // (three to a compute unit) once every compute unit gets a tile, with K
+    // split below two (1024 x 3584, N = 2048: 77 -> 67 us against 512 tiles
+    // of 64 x 64), for the 4-bit format once every compute unit gets two
+    if (fmt != QG_I8_ROW && (fmt == QG_B1_G128 || tiles(128, 64) >= 2 * kComputeUnits ||
+                             (fmt == QG_I8_G64 && tiles(128, 64) >= kComputeUnits))) {
         bm = 128;
         return;
     }

@@ -191,7 +191,7 @@ def test_exact_arithmetic_bit_exact(torch, orc, fmt, M, K, N):
     (synth.I8_G64, 129, 1024, 17), (synth.I8_G64, 300, 1088, 130), (synth.I8_G64, 7, 64, 257),
     (synth.I8_G64, 4001, 192, 1503), (synth.I8_G64, 1024, 3584, 64),
     # 288 tiles of 128 x 64, K split in two
-    (synth.I8_ROW, 1025, 1040, 2000),
+    (synth.I8_ROW, 1025, 1040, 2000), (synth.I8_G64, 1025, 1088, 2000),
 ])
 def test_exact_arithmetic_prefill_bit_exact(torch, orc, fmt, M, K, N):
     """The matrix-core prefill path (more than 16 token rows) on exact inputs."""
