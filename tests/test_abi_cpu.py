@@ -76,18 +76,19 @@ def test_prefill_split_tail_planning():
     (their partial tiles need workspace) only where that round is at most a
     quarter full: the shapes of the exact split-tail GPU test take that
     path, the configurations whose last round is fuller do not."""
-    tile_bytes = {q.QG_I8_ROW: 128 * 64 * 4, q.QG_U4_G64: 128 * 64 * 4, q.QG_B1_G128: 128 * 64 * 4,
+    tile_bytes = {q.QG_I8_ROW: 256 * 64 * 4, q.QG_U4_G64: 128 * 64 * 4, q.QG_B1_G128: 128 * 64 * 4,
                   q.QG_I8_G64: 128 * 64 * 4}
-    for fmt, M, K, N in [(q.QG_I8_ROW, 2000, 272, 3100), (q.QG_U4_G64, 2100, 576, 2000),
-                         (q.QG_B1_G128, 1100, 1152, 3900), (q.QG_I8_G64, 2100, 576, 2000),
-                         (q.QG_B1_G128, 17408, 5120, 512), (q.QG_I8_ROW, 3584, 1024, 2048),
-                         (q.QG_U4_G64, 2101, 576, 2000), (q.QG_I8_G64, 2099, 576, 2000),
-                         (q.QG_I8_ROW, 2001, 272, 3100)]:
+    for fmt, M, K, N in [(q.QG_I8_ROW, 1000, 272, 12800), (q.QG_U4_G64, 2100, 576, 2000),
+                         (q.QG_B1_G128, 1100, 1152, 3900), (q.QG_I8_G64, 2100, 576, 2900),
+                         (q.QG_B1_G128, 17408, 5120, 512),
+                         (q.QG_U4_G64, 2101, 576, 2000), (q.QG_I8_G64, 2099, 576, 2900),
+                         (q.QG_I8_ROW, 1001, 272, 12290)]:
         ws = q.qg_workspace_bytes(q.QG_OP_GEMM, fmt, M, K, N)
         # control words plus at least two pieces of one tile
         assert ws >= q.QG_WS_CONTROL_BYTES + 2 * tile_bytes[fmt], (fmt, M, K, N, ws)
     for fmt, M, K, N in [(q.QG_I8_ROW, 3584, 1024, 10240), (q.QG_I8_ROW, 1024, 3584, 10240),
-                         (q.QG_U4_G64, 6144, 2048, 2048)]:
+                         (q.QG_U4_G64, 6144, 2048, 2048), (q.QG_I8_ROW, 3584, 1024, 2048),
+                         (q.QG_I8_ROW, 2000, 272, 3100)]:
         assert q.qg_workspace_bytes(q.QG_OP_GEMM, fmt, M, K, N) == 0, (fmt, M, K, N)
 
 

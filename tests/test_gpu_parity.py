@@ -222,12 +222,10 @@ def test_exact_arithmetic_prefill_large_grid(torch, orc, M, K, N):
 
 
 @pytest.mark.parametrize("fmt,M,K,N", [
-    (synth.I8_ROW, 2000, 272, 3100), (synth.U4_G64, 2100, 576, 2000), (synth.B1_G128, 1100, 1152, 3900),
-    (synth.I8_G64, 2100, 576, 2000),
+    (synth.I8_ROW, 1000, 272, 12800), (synth.U4_G64, 2100, 576, 2000), (synth.B1_G128, 1100, 1152, 3900),
+    (synth.I8_G64, 2100, 576, 2900),
     # M not a multiple of 4: the combine's scalar stores
-    (synth.U4_G64, 2101, 576, 2000), (synth.I8_G64, 2099, 576, 2000), (synth.I8_ROW, 2001, 272, 3100),
-    # 256 x 64 tiles: 800 tiles, a last round of 32 (ragged M)
-    (synth.I8_ROW, 1000, 272, 12800),
+    (synth.U4_G64, 2101, 576, 2000), (synth.I8_G64, 2099, 576, 2900), (synth.I8_ROW, 1001, 272, 12290),
 ])
 def test_exact_arithmetic_prefill_split_tail(torch, orc, fmt, M, K, N):
     """Grids of one or more full rounds of tiles plus a short last round,
