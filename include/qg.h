@@ -169,10 +169,11 @@ int qgemv(int fmt, const void *codes, const void *scales, const void *biases,
  *   X[n][k] over group g) is added per group beside the scaled code sums.
  *   Needs a workspace when qg_workspace_bytes(QG_OP_GEMM, ...) is nonzero:
  *   up to QG_MAX_GEMV_BATCH rows as qgemv, and above that whenever the
- *   output has fewer tiles than the chip has compute units, since K is then
- *   cut into pieces whose float32 partial products are added in a fixed
- *   order by a second launch (the result does not depend on the stream or
- *   the schedule). 17..48 rows of the 4-bit format at K = 1024 or 2048 may
+ *   output has too few tiles to fill the chip (fewer than one per compute
+ *   unit; two for the 8-bit formats, four for the 1-bit format) or a short
+ *   last round of tiles, since K is then cut into pieces whose float32
+ *   partial products are added in a fixed order by a second launch (the
+ *   result does not depend on the stream or the schedule). 17..48 rows of the 4-bit format at K = 1024 or 2048 may
  *   run as launches of up to QG_MAX_GEMV_BATCH rows of the matrix-vector
  *   product where that reads the weights for less than the prefill kernel's
  *   padded work costs.
