@@ -891,12 +891,23 @@ void gemm_tile(int fmt, int64_t M, int64_t N, int &bm, int &bn, int &wn);
 // barrier for few MFMAs), so it splits grids of up to four tiles per
 // compute unit, into about four workgroups per compute unit (17408 x 5120,
 // 128 token rows: 148 -> 131 us; 64 rows: 101 -> 75 us); the 8-bit per-row
-// format splits grids of up to two tiles per compute unit (its 128 x 64
-// tile runs four to a unit; 1024 x 3584, N = 2048, 256 tiles: 65 -> 56 us),
-// and so does the 8-bit group-64 format (three to a unit);
+// format splits grids of up to two tiles per compute unit into about two
+// workgroups per unit (its 128 x 64 tile runs four to a unit; 1024 x 3584,
+// N = 2048, 256 tiles: 65 -> 56 us; three or four pieces: 59, 63 us), the
+// 8-bit group-64 format into about as many as its tile runs to a unit
+// (three for 128 x 64; 77 -> 67 -> 64 us for two, then three pieces); the 1-bit format's 5120 x 17408, N = 512
+// (320 tiles) takes 277 us in four pieces, 285 in three, 295 in eight;
 // deeper splits lose (8-bit 3584 x 1024, 128 rows, four workgroups per
 // compute unit instead of two: 16.7 -> 21.6 us).
 // kt_split = 0: no split.
+// Workgroups of the prefill kernel per compute unit (gemm_occupancy).
+int gemm_wg_per_cu(int fmt, int bm, int bn)
+{
+    const bool i8 = fmt == QG_I8_ROW || fmt == QG_I8_G64;
+    return fmt == QG_I8_ROW && bm == 128 && bn == 64 ? 4
+           : i8 && bn == 64 && (bm == 128 || (fmt == QG_I8_ROW && bm == 256)) ? 3 : 2;
+}
+
 void gemm_split(int fmt, int64_t M, int64_t K, int64_t N, int &kt_split, int &nsplit)
 {
     kt_split = 0;
@@ -905,7 +916,8 @@ void gemm_split(int fmt, int64_t M, int64_t K, int64_t N, int &kt_split, int &ns
     gemm_tile(fmt, M, N, bm, bn, wn);
     const int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
     const int64_t nk = ceil_div(K, 32);
-    const int below = fmt == QG_B1_G128 ? 4 : fmt == QG_I8_ROW || fmt == QG_I8_G64 ? 2 : 1, per_cu = fmt == QG_B1_G128 ? 4 : 2;
+    const int below = fmt == QG_B1_G128 ? 4 : fmt == QG_I8_ROW || fmt == QG_I8_G64 ? 2 : 1;
+    const int per_cu = fmt == QG_B1_G128 ? 4 : fmt == QG_I8_G64 ? gemm_wg_per_cu(fmt, bm, bn) : 2;
     if (tiles >= below * kComputeUnits || nk < 8) return;
     const int64_t want = std::min(ceil_div(per_cu * kComputeUnits, tiles), nk / 4);
     if (want < 2) return;
@@ -935,11 +947,7 @@ GemmTail gemm_tail(int fmt, int64_t M, int64_t K, int64_t N)
     if (nsplit > 1) return t;
     gemm_tile(fmt, M, N, bm, bn, wn);
     const int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
-    // workgroups per compute unit (gemm_occupancy)
-    const bool i8 = fmt == QG_I8_ROW || fmt == QG_I8_G64;
-    const int per_cu = fmt == QG_I8_ROW && bm == 128 && bn == 64 ? 4
-                       : i8 && bn == 64 && (bm == 128 || (fmt == QG_I8_ROW && bm == 256)) ? 3 : 2;
-    const int64_t slots = per_cu * kComputeUnits;
+    const int64_t slots = int64_t(gemm_wg_per_cu(fmt, bm, bn)) * kComputeUnits;
     const int64_t ntail = tiles % slots;
     if (tiles < slots || ntail == 0 || 4 * ntail > slots) return t;
     const int64_t nk = ceil_div(K, 32);
