@@ -92,6 +92,22 @@ def test_prefill_split_tail_planning():
         assert q.qg_workspace_bytes(q.QG_OP_GEMM, fmt, M, K, N) == 0, (fmt, M, K, N)
 
 
+def test_prefill_split_k_planning():
+    """Grids too small for the chip are cut along K into as many pieces as
+    the host planner chooses for the format (their float32 partials fill the
+    workspace after the control words): two for the 8-bit per-row 1024 x
+    3584 grid at 2048 token rows, three for the 8-bit group-64 one, four for
+    the 1-bit 5120 x 17408 grid at 512 rows; grids that fill the chip in
+    whole rounds are not cut."""
+    for fmt, M, K, N, pieces in [(q.QG_I8_ROW, 1024, 3584, 2048, 2), (q.QG_I8_G64, 1024, 3584, 2048, 3),
+                                 (q.QG_B1_G128, 5120, 17408, 512, 4)]:
+        ws = q.qg_workspace_bytes(q.QG_OP_GEMM, fmt, M, K, N)
+        assert ws == q.QG_WS_CONTROL_BYTES + pieces * N * M * 4, (fmt, M, K, N, ws)
+    for fmt, M, K, N in [(q.QG_I8_ROW, 3584, 1024, 2048), (q.QG_I8_G64, 3584, 1024, 10240),
+                         (q.QG_U4_G64, 2048, 6144, 2048)]:
+        assert q.qg_workspace_bytes(q.QG_OP_GEMM, fmt, M, K, N) == 0, (fmt, M, K, N)
+
+
 def _err(fn, *args, **kw):
     with pytest.raises(q.QGError) as e:
         fn(*args, stream=0, **kw)
