@@ -22,7 +22,7 @@ Reported (one JSON line):
                  measurement-only read kernels, and the call's rate as a
                  percentage of it
   gpu_state      clocks, temperatures and power before and after the timed
-                 region (the driver's hwmon files)
+                 region (the amdgpu kernel module's hwmon and pp_dpm files)
   cpu_baseline   the CPU oracle on the same workload, on all of this host's
                  threads and on one (with the CPU model)
 
