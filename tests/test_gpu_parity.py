@@ -489,6 +489,8 @@ def gpu_greedy(torch, w, x, logits=True):
     (synth.B1_G128, 66001, 256, 30),
     (synth.U4_G64, 40000, 1024, 33), (synth.U4_G64, 60000, 2048, 48),
     (synth.B1_G128, 3000, 2048, 7), (synth.I8_ROW, 20000, 1024, 12),
+    # 8-bit per-row 256 x 64 tiles with per-tile keys (628 tiles, ragged M and N)
+    (synth.I8_ROW, 40001, 256, 200),
 ])
 def test_greedy_head_with_and_without_logits(torch, orc, fmt, M, K, N):
     say(f"greedy fmt={fmt} M={M} K={K} N={N}")
